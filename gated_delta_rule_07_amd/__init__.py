@@ -1,0 +1,181 @@
+"""Python binding for libkda, the MI355X-native Kimi Delta Attention operator.
+
+Argument marshalling only: every step of the operator runs in the HIP kernels of
+``libkda.so`` (built by ``gated_delta_rule_07_amd.build``), called through its C
+ABI (``include/kda.h``).  PyTorch supplies device memory and the current HIP
+stream; nothing here computes any part of the recurrence, and there is no CPU
+fallback: if the library is missing the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+import torch
+
+__all__ = ["kda_chunk_fwd", "kda_decode_step", "kda_status_string", "kda_version",
+           "kda_last_hip_error", "library_path", "load_library", "KdaError",
+           "KDA_F32", "KDA_BF16"]
+
+KDA_F32, KDA_BF16 = 0, 1
+_PKG = Path(__file__).resolve().parent
+_LIB_PATH = _PKG / "libkda.so"
+_lib = None
+
+
+class KdaError(RuntimeError):
+    """A libkda call returned a non-OK status."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {kda_status_string(status)}")
+
+
+def library_path() -> Path:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libkda.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not _LIB_PATH.exists():
+        raise RuntimeError(f"libkda is not built ({_LIB_PATH} missing); run "
+                           "`python -m gated_delta_rule_07_amd.build` first")
+    lib = ctypes.CDLL(str(_LIB_PATH))
+    vp, i32 = ctypes.c_void_p, ctypes.c_int
+    lib.kda_chunk_fwd.restype = i32
+    lib.kda_chunk_fwd.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, i32, vp,
+                                  i32, i32, i32, i32, i32, i32, vp]
+    lib.kda_decode_step.restype = i32
+    lib.kda_decode_step.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_status_string.argtypes = [i32]
+    lib.kda_last_hip_error.restype = i32
+    lib.kda_last_hip_error.argtypes = []
+    lib.kda_version.restype = i32
+    lib.kda_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def kda_status_string(status: int) -> str:
+    return load_library().kda_status_string(int(status)).decode()
+
+
+def kda_version() -> int:
+    return load_library().kda_version()
+
+
+def kda_last_hip_error() -> int:
+    return load_library().kda_last_hip_error()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError(f"libkda: q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _check(t: torch.Tensor, name: str, dtype=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"libkda: {name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"libkda: {name} must be on a HIP device, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"libkda: {name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"libkda: {name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"libkda: {name} must be {dtype}, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device, stream):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def kda_chunk_fwd(q, k, v, alpha, beta, S0=None, *, chunk: int = 64, o=None, S_T=None,
+                  o_dtype=torch.float32, want_state: bool = True, stream=None):
+    """Prefill: returns ``(o, S_T)`` (``S_T`` is None when ``want_state`` is False).
+
+    q, k: [B,T,H,d_k]; v: [B,T,H,d_v] (bf16 or fp32, same dtype); alpha: [B,T,H,d_k]
+    fp32; beta: [B,T,H] fp32; S0: [B,H,d_k,d_v] fp32 or None (zeros).  ``o`` is
+    float32 (default) or bfloat16 (``o_dtype``, or the dtype of a preallocated
+    ``o``).  ``S_T`` may be preallocated (it may be ``S0`` for an in-place update).
+    """
+    lib = load_library()
+    _check(q, "q")
+    dev = q.device
+    for t, n in ((k, "k"), (v, "v")):
+        _check(t, n, q.dtype, dev)
+    _check(alpha, "alpha", torch.float32, dev)
+    _check(beta, "beta", torch.float32, dev)
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("libkda: q/k/v must be [B,T,H,d]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or alpha.shape != q.shape or v.shape[:3] != q.shape[:3] or beta.shape != (B, T, H):
+        raise ValueError("libkda: inconsistent shapes")
+    if S0 is not None:
+        _check(S0, "S0", torch.float32, dev)
+        if S0.shape != (B, H, dk, dv):
+            raise ValueError("libkda: S0 must be [B,H,d_k,d_v]")
+    if o is None:
+        o = torch.empty(B, T, H, dv, device=dev, dtype=o_dtype)
+    else:
+        _check(o, "o", None, dev)
+        if o.shape != (B, T, H, dv):
+            raise ValueError("libkda: o must be [B,T,H,d_v]")
+    if want_state and S_T is None:
+        S_T = torch.empty(B, H, dk, dv, device=dev, dtype=torch.float32)
+    elif S_T is not None:
+        _check(S_T, "S_T", torch.float32, dev)
+        if S_T.shape != (B, H, dk, dv):
+            raise ValueError("libkda: S_T must be [B,H,d_k,d_v]")
+    st = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(alpha), _ptr(beta),
+                           _ptr(S0), _ptr(o), _dtype_code(o), _ptr(S_T), B, T, H, dk, dv, int(chunk),
+                           _stream(dev, stream))
+    if st != 0:
+        raise KdaError(st, "kda_chunk_fwd")
+    return o, S_T
+
+
+def kda_decode_step(q, k, v, alpha, beta, S, *, o=None, o_dtype=torch.float32, stream=None):
+    """Decode one token per (sequence, head); ``S`` ([B,H,d_k,d_v] fp32) is updated
+    in place.  q, k: [B,H,d_k]; v: [B,H,d_v]; alpha: [B,H,d_k]; beta: [B,H].
+    Returns ``o`` ([B,H,d_v], float32 by default or bfloat16)."""
+    lib = load_library()
+    _check(q, "q")
+    dev = q.device
+    for t, n in ((k, "k"), (v, "v")):
+        _check(t, n, q.dtype, dev)
+    _check(alpha, "alpha", torch.float32, dev)
+    _check(beta, "beta", torch.float32, dev)
+    _check(S, "S", torch.float32, dev)
+    if q.dim() != 3:
+        raise ValueError("libkda: decode q/k/v must be [B,H,d]")
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or alpha.shape != q.shape or v.shape[:2] != (B, H) or beta.shape != (B, H):
+        raise ValueError("libkda: inconsistent shapes")
+    if S.shape != (B, H, dk, dv):
+        raise ValueError("libkda: S must be [B,H,d_k,d_v]")
+    if o is None:
+        o = torch.empty(B, H, dv, device=dev, dtype=o_dtype)
+    else:
+        _check(o, "o", None, dev)
+        if o.shape != (B, H, dv):
+            raise ValueError("libkda: o must be [B,H,d_v]")
+    st = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(alpha), _ptr(beta),
+                             _ptr(S), _ptr(o), _dtype_code(o), B, H, dk, dv, _stream(dev, stream))
+    if st != 0:
+        raise KdaError(st, "kda_decode_step")
+    return o

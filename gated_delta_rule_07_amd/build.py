@@ -1,0 +1,69 @@
+"""Build libkda.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
+
+Usage: ``python -m gated_delta_rule_07_amd.build`` (or ``build()`` from Python).
+Each source compiles to an object in parallel, then one shared library is linked
+next to this file.  hipcc cross-compiles for gfx950 without a GPU present.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+from pathlib import Path
+
+PKG = Path(__file__).resolve().parent
+CSRC = PKG / "csrc"
+INCLUDE = PKG.parent / "include"
+LIB = PKG / "libkda.so"
+OBJDIR = PKG / "_build"
+
+SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_prefill.hip"]
+
+ARCH = "gfx950"
+# Packed-fp32 VALU forms are disabled: plain fp32 code only.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", f"-I{INCLUDE}", f"-I{CSRC}"]
+
+
+def hipcc() -> str:
+    path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(path):
+        raise RuntimeError("hipcc not found; libkda needs ROCm to build")
+    return path
+
+
+def _compile(src: str, verbose: bool) -> Path:
+    out = OBJDIR / (Path(src).stem + ".o")
+    cmd = [hipcc(), *COMMON, *DEVICE_FLAGS, "-c", str(CSRC / src), "-o", str(out)]
+    if src.endswith(".cpp"):
+        cmd[1:1] = ["-x", "hip"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+    return out
+
+
+def build(verbose: bool = False, jobs: int | None = None) -> Path:
+    """Compile every source and link libkda.so; always rebuilds."""
+    OBJDIR.mkdir(exist_ok=True)
+    jobs = jobs or min(len(SOURCES), max(1, os.cpu_count() or 1))
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+    tmp = LIB.with_suffix(".so.tmp%d" % os.getpid())
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *map(str, objs), "-o", str(tmp)]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose="-v" in sys.argv)
+    print(LIB)

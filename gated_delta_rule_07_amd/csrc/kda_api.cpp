@@ -1,0 +1,161 @@
+// libkda C ABI: argument validation, dispatch and error mapping.
+//
+// Every check runs before any HIP call, so invalid arguments return a status
+// without touching the device.  Kernels are enqueued on the caller's stream and
+// the calls return without synchronising.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "../../include/kda.h"
+#include "kda_launch.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int kVersion = 100;  // 0.1.0
+
+bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Span {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+Span span(const void* p, size_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Span{a, a + bytes};
+}
+bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+
+// Element counts fit in size_t and every row index used by the kernels fits in
+// an int64; the kernels index tokens with 64-bit arithmetic.
+bool sizes_ok(long long B, long long T, long long H, long long dk, long long dv) {
+  const long long lim = (1LL << 40);
+  if (B * H > (1LL << 26)) return false;
+  if (B * T * H > lim / 128) return false;
+  (void)dk;
+  (void)dv;
+  return true;
+}
+
+// Number of state columns per prefill workgroup: the widest slab that still
+// gives at least one workgroup per compute unit (256), else 16.
+int choose_slab(int B, int H, int dv, int io_dtype) {
+  const char* env = getenv("KDA_PREFILL_SLAB");  // tuning override
+  if (env) {
+    const int s = atoi(env);
+    if ((s == 16 || s == 32) && dv % s == 0) return s;
+  }
+  if (io_dtype == KDA_BF16 && dv % 32 == 0 && (long long)B * H * (dv / 32) >= 256) return 32;
+  return 16;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_string(kda_status s) {
+  switch (s) {
+    case KDA_OK: return "KDA_OK: success";
+    case KDA_ERR_NULL: return "KDA_ERR_NULL: a required pointer is NULL";
+    case KDA_ERR_SHAPE: return "KDA_ERR_SHAPE: invalid B/T/H or sizes too large";
+    case KDA_ERR_DTYPE: return "KDA_ERR_DTYPE: unknown q/k/v or o dtype";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: head size, chunk size or dtype combination not built";
+    case KDA_ERR_MISALIGNED: return "KDA_ERR_MISALIGNED: a pointer is not 16-byte aligned";
+    case KDA_ERR_ALIAS: return "KDA_ERR_ALIAS: an output overlaps an input";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP: kernel launch failed (see kda_last_hip_error)";
+  }
+  return "KDA: unknown status";
+}
+
+int kda_last_hip_error(void) { return g_last_hip_error; }
+
+int kda_version(void) { return kVersion; }
+
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
+                         const float* alpha, const float* beta, const float* S0,
+                         void* o, kda_dtype o_dtype, float* S_T,
+                         int B, int T, int H, int d_k, int d_v, int chunk, void* stream) {
+  if (qkv_dtype != KDA_F32 && qkv_dtype != KDA_BF16) return KDA_ERR_DTYPE;
+  if (o_dtype != KDA_F32 && o_dtype != KDA_BF16) return KDA_ERR_DTYPE;
+  if (B < 1 || H < 1 || T < 0) return KDA_ERR_SHAPE;
+  if (!dim_ok(d_k) || !dim_ok(d_v)) return KDA_ERR_UNSUPPORTED;
+  if (chunk != 16 && chunk != 32 && chunk != 64) return KDA_ERR_UNSUPPORTED;
+  if (!sizes_ok(B, T, H, d_k, d_v)) return KDA_ERR_SHAPE;
+  if (T > 0 && (!q || !k || !v || !alpha || !beta || !o)) return KDA_ERR_NULL;
+  const void* ptrs[] = {q, k, v, alpha, beta, S0, o, S_T};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return KDA_ERR_MISALIGNED;
+  const int io = (qkv_dtype == KDA_BF16) ? 1 : 0;
+  const int slab = choose_slab(B, H, d_v, qkv_dtype);
+  if (!kda::prefill_supported(io, d_k, chunk, slab)) return KDA_ERR_UNSUPPORTED;
+
+  const size_t esz = (qkv_dtype == KDA_BF16) ? 2 : 4;
+  const size_t osz = (o_dtype == KDA_BF16) ? 2 : 4;
+  const size_t ntok = (size_t)B * T * H;
+  const size_t sbytes = (size_t)B * H * d_k * d_v * 4;
+  if (T > 0) {
+    const Span so = span(o, ntok * d_v * osz);
+    const Span ins[] = {span(q, ntok * d_k * esz), span(k, ntok * d_k * esz), span(v, ntok * d_v * esz),
+                        span(alpha, ntok * d_k * 4), span(beta, ntok * 4),
+                        S0 ? span(S0, sbytes) : Span{0, 0}, S_T ? span(S_T, sbytes) : Span{0, 0}};
+    for (const Span& s : ins)
+      if (overlap(so, s)) return KDA_ERR_ALIAS;
+  }
+  if (S_T) {
+    const Span st = span(S_T, sbytes);
+    if (S0 && S0 != S_T && overlap(st, span(S0, sbytes))) return KDA_ERR_ALIAS;
+    if (T > 0) {
+      const Span ins[] = {span(q, ntok * d_k * esz), span(k, ntok * d_k * esz), span(v, ntok * d_v * esz),
+                          span(alpha, ntok * d_k * 4), span(beta, ntok * 4)};
+      for (const Span& s : ins)
+        if (overlap(st, s)) return KDA_ERR_ALIAS;
+    }
+  }
+
+  kda::PrefillParams p{q, k, v, alpha, beta, S0, o, S_T, B, T, H, d_k, d_v, o_dtype == KDA_F32 ? 1 : 0};
+  const hipError_t e = kda::launch_prefill(p, io, chunk, slab, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return KDA_ERR_HIP;
+  }
+  return KDA_OK;
+}
+
+kda_status kda_decode_step(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
+                           const float* alpha, const float* beta, float* S, void* o, kda_dtype o_dtype,
+                           int B, int H, int d_k, int d_v, void* stream) {
+  if (qkv_dtype != KDA_F32 && qkv_dtype != KDA_BF16) return KDA_ERR_DTYPE;
+  if (o_dtype != KDA_F32 && o_dtype != KDA_BF16) return KDA_ERR_DTYPE;
+  if (B < 1 || H < 1) return KDA_ERR_SHAPE;
+  if (!dim_ok(d_k) || !dim_ok(d_v)) return KDA_ERR_UNSUPPORTED;
+  if (!sizes_ok(B, 1, H, d_k, d_v)) return KDA_ERR_SHAPE;
+  if (!q || !k || !v || !alpha || !beta || !S || !o) return KDA_ERR_NULL;
+  const void* ptrs[] = {q, k, v, alpha, beta, S, o};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return KDA_ERR_MISALIGNED;
+  const int io = (qkv_dtype == KDA_BF16) ? 1 : 0;
+  if (!kda::decode_supported(io, d_k, d_v)) return KDA_ERR_UNSUPPORTED;
+
+  const size_t esz = (qkv_dtype == KDA_BF16) ? 2 : 4;
+  const size_t osz = (o_dtype == KDA_BF16) ? 2 : 4;
+  const size_t nbh = (size_t)B * H;
+  const Span so = span(o, nbh * d_v * osz);
+  const Span ss = span(S, nbh * d_k * d_v * 4);
+  const Span ins[] = {span(q, nbh * d_k * esz), span(k, nbh * d_k * esz), span(v, nbh * d_v * esz),
+                      span(alpha, nbh * d_k * 4), span(beta, nbh * 4)};
+  if (overlap(so, ss)) return KDA_ERR_ALIAS;
+  for (const Span& s : ins)
+    if (overlap(so, s) || overlap(ss, s)) return KDA_ERR_ALIAS;
+
+  kda::DecodeParams p{q, k, v, alpha, beta, S, o, B, H, d_k, d_v, o_dtype == KDA_F32 ? 1 : 0};
+  const hipError_t e = kda::launch_decode(p, io, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return KDA_ERR_HIP;
+  }
+  return KDA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,157 @@
+// Device helpers shared by the libkda kernels (gfx950 / CDNA4, wave64).
+//
+// MFMA conventions used throughout (16x16 output tiles, K = 32 per step):
+//   A fragment : lane l holds 8 operand values of row m = l % 16
+//   B fragment : lane l holds 8 operand values of column n = l % 16
+//   C tile     : lane l holds D[4*(l/16) + r][l % 16] for r = 0..3 (fp32)
+// The value a lane holds in slot e stands for the same reduction index k in A
+// and in B (k is a fixed function of (l / 16, e)), so only the packing of A and
+// B relative to each other matters.  Two packings are used:
+//   natural  : slot e of lane group g <-> column 8*g + e of the K32 step
+//   stacked  : slot e <-> column 4*g + e (e < 4) or 16 + 4*g + (e - 4) (e >= 4)
+// The stacked packing is exactly what two vertically adjacent C tiles hold in
+// their 4 registers, so a product's result can feed the next product as a B
+// operand without leaving registers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ---- element conversions ---------------------------------------------------
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(_Float16 x) { return (float)x; }
+
+// fp32 -> 16-bit conversions round to nearest even.
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
+template <> __device__ __forceinline__ _Float16 from_f32<_Float16>(float x) { return (_Float16)x; }
+
+// ---- 8-value operand fragments --------------------------------------------
+
+template <typename OP> struct Frag;
+
+template <> struct Frag<__bf16> {
+  bf16x8 v;
+  __device__ __forceinline__ void zero() { v = (bf16x8)(__bf16)0.0f; }
+};
+template <> struct Frag<_Float16> {
+  f16x8 v;
+  __device__ __forceinline__ void zero() { v = (f16x8)(_Float16)0.0f; }
+  __device__ __forceinline__ void negate() {
+    u32x4 u = __builtin_bit_cast(u32x4, v);
+    u ^= 0x80008000u;
+    v = __builtin_bit_cast(f16x8, u);
+  }
+};
+template <> struct Frag<float> {
+  float v[8];
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+  }
+  __device__ __forceinline__ void negate() {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = -v[e];
+  }
+};
+
+// acc += A * B over one K32 step.
+__device__ __forceinline__ f32x4 mma(const Frag<__bf16>& a, const Frag<__bf16>& b, f32x4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(const Frag<_Float16>& a, const Frag<_Float16>& b, f32x4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(const Frag<float>& a, const Frag<float>& b, f32x4 acc) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[e], b.v[e], acc, 0, 0, 0);
+  return acc;
+}
+
+// ---- LDS fragment loads ----------------------------------------------------
+
+// Natural packing: (row, columns c0..c0+7) of a row-major LDS matrix with
+// leading dimension ld; reads zero when c0 >= kmax.  c0 and kmax are multiples
+// of 8 and rows start 16-byte aligned.
+template <typename T>
+__device__ __forceinline__ Frag<T> lds_frag(const T* base, int ld, int row, int c0, int kmax) {
+  Frag<T> f;
+  if constexpr (sizeof(T) == 2) {
+    typedef T v8 __attribute__((ext_vector_type(8)));
+    if (c0 < kmax) f.v = *reinterpret_cast<const v8*>(base + row * ld + c0);
+    else f.zero();
+  } else {
+    if (c0 < kmax) {
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(base + row * ld + c0);
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(base + row * ld + c0 + 4);
+      f.v[0] = lo.x; f.v[1] = lo.y; f.v[2] = lo.z; f.v[3] = lo.w;
+      f.v[4] = hi.x; f.v[5] = hi.y; f.v[6] = hi.z; f.v[7] = hi.w;
+    } else {
+      f.zero();
+    }
+  }
+  return f;
+}
+
+// Stacked packing for an A operand whose partner B comes from C tiles: for lane
+// group g, slots 0..3 read columns k0+4g..k0+4g+3 and slots 4..7 read columns
+// k0+16+4g..k0+16+4g+3.  A 16-column half reads zero when it starts at or past
+// kmax (a multiple of 16).
+template <typename T>
+__device__ __forceinline__ Frag<T> lds_frag_stacked(const T* base, int ld, int row, int k0, int g, int kmax) {
+  Frag<T> f;
+  const T* p = base + row * ld + k0 + 4 * g;
+  if constexpr (sizeof(T) == 2) {
+    typedef T v4 __attribute__((ext_vector_type(4)));
+    typedef T v8 __attribute__((ext_vector_type(8)));
+    const v4 z = (v4)(T)0.0f;
+    const v4 a = (k0 < kmax) ? *reinterpret_cast<const v4*>(p) : z;
+    const v4 b = (k0 + 16 < kmax) ? *reinterpret_cast<const v4*>(p + 16) : z;
+    f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    (void)sizeof(v8);
+  } else {
+    f32x4 a = (f32x4)0.0f, b = (f32x4)0.0f;
+    if (k0 < kmax) a = *reinterpret_cast<const f32x4*>(p);
+    if (k0 + 16 < kmax) b = *reinterpret_cast<const f32x4*>(p + 16);
+    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+  }
+  return f;
+}
+
+// B operand in stacked packing from two C tiles held in registers (rows of the
+// first tile are K indices 0..15 of the step, rows of the second 16..31), each
+// value multiplied by `scale` before rounding to T.
+template <typename T>
+__device__ __forceinline__ Frag<T> frag_from_tiles(const f32x4& t0, const f32x4& t1, float scale) {
+  Frag<T> f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    f.v[r] = from_f32<T>(t0[r] * scale);
+    f.v[4 + r] = from_f32<T>(t1[r] * scale);
+  }
+  return f;
+}
+
+// Order this wave's earlier LDS writes before its later LDS reads (values
+// exchanged between lanes of one wave through LDS).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+}  // namespace kda

@@ -1,0 +1,42 @@
+// Internal host-side interface between the C ABI (kda_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace kda {
+
+struct PrefillParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* alpha;
+  const float* beta;
+  const float* S0;  // may be null (zeros)
+  void* o;
+  float* S_T;       // may be null (not written)
+  int B, T, H, dk, dv;
+  int o_f32;        // 1: o is fp32, 0: o is bf16
+};
+
+struct DecodeParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* alpha;
+  const float* beta;
+  float* S;
+  void* o;
+  int B, H, dk, dv;
+  int o_f32;
+};
+
+// io_dtype: 0 = fp32, 1 = bf16.  `slab` is the number of state columns one
+// workgroup owns (16, 32 or 64).  Returns hipErrorInvalidValue when no kernel is
+// built for the combination.
+bool prefill_supported(int io_dtype, int dk, int chunk, int slab);
+hipError_t launch_prefill(const PrefillParams& p, int io_dtype, int chunk, int slab, hipStream_t s);
+
+bool decode_supported(int io_dtype, int dk, int dv);
+hipError_t launch_decode(const DecodeParams& p, int io_dtype, hipStream_t s);
+
+}  // namespace kda

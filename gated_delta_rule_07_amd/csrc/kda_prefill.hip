@@ -1,0 +1,670 @@
+// Chunkwise-parallel KDA prefill for gfx950.
+//
+// Method.  The recurrence of the "Kimi K3 Technical Report review"
+// (jw9603.github.io, sections 3.2-3.3) is evaluated in chunks of C tokens, as
+// described on "Kimi 모델 분석" (rlaope.github.io, section on putting the
+// recurrence on the GPU): inside a chunk the sequential rank-1 updates are
+// compressed into dense products (WY representation; the lower-triangular
+// inverse rewritten as products, the UT transform), and only the state is
+// carried from chunk to chunk.  With incoming state S, chunk-local cumulative
+// decay G_t = sum_{s<=t} ln alpha_s (per key channel) and t, i = 1..C:
+//
+//   L_ti = beta_t sum_c k_t[c] k_i[c] e^{G_t[c]-G_i[c]}   (i < t)     intra-chunk K K^T
+//   P_ti =        sum_c q_t[c] k_i[c] e^{G_t[c]-G_i[c]}   (i <= t)    intra-chunk Q K^T
+//   T    = (I + L)^{-1} diag(beta)                                     UT transform
+//   U    = T (V - (K o e^G) S)                                         WY-form corrections
+//   O    = (Q o e^G) S + P U                                           outputs
+//   S'   = Diag(e^{G_C}) S + (K o e^{G_C-G})^T U                       state carry (fp32)
+//
+// Decay factors come from cumulative products of alpha (no logarithms).  L and P
+// use the chunk-start reference, K o e^{G} times K o e^{-G}; e^{-G} <= e^{80} is
+// guaranteed for any 16 tokens by the lower bound alpha >= e^{-5} (section 3.5 of
+// the first page), so a chunk whose total decay falls below e^{-80} in some
+// channel is processed as 16-token sub-chunks (an exact regrouping).
+//
+// Precision.  The state and every accumulation are fp32.  Operands of the
+// state-side products (K o e^G, Q o e^G, K o e^{G_C-G}, T, P and the values S, X,
+// U) are fp16: they are bounded by |k|, |q| or are values, and the values are
+// rescaled by a power of two per state column and chunk.  L and P need the full
+// decay range, so their operands are bf16 high/low pairs (three products for P,
+// two for L).  The fp32 q/k/v path uses fp32 operands throughout.
+//
+// Parallel decomposition.  The columns of S evolve independently, so a
+// workgroup owns one (sequence, head, slab of J state columns) and runs the chunk
+// loop sequentially; the key-side work (decay, L, P, T) is recomputed by the
+// slabs of a head, whose workgroups are placed on one XCD so the shared
+// q/k/alpha reads hit the same L2.  Each of the J/16 state waves keeps a
+// d_k x 16 slice of S in fp32 accumulators for the whole sequence; S, X and U
+// reach the next product straight from registers.
+#include "kda_device.h"
+#include "kda_launch.h"
+
+namespace kda {
+namespace {
+
+template <typename IO_, int DK_, int J_, int CS_>
+struct Cfg {
+  using IO = IO_;
+  static constexpr bool SPLIT = sizeof(IO_) == 2;           // bf16 q/k/v
+  using SOP = typename std::conditional<SPLIT, _Float16, float>::type;  // state-side operands
+  using LOP = typename std::conditional<SPLIT, __bf16, float>::type;    // L/P operands
+  static constexpr int DK = DK_, J = J_, CS = CS_;
+  static constexpr int NT = 256, NW = 4;
+  static constexpr int NSW = J / 16;                 // state waves
+  static constexpr int NKT = DK / 16;                // 16-row channel tiles
+  static constexpr int NCT = CS / 16;                // 16-row token tiles
+  static constexpr int NKS = (NKT + 1) / 2;          // K32 steps over channels
+  static constexpr int NTS = (NCT + 1) / 2;          // K32 steps over tokens
+  static constexpr int HC = DK < 64 ? DK : 64;       // channels per L/P pass
+  static constexpr int NH = DK / HC;                 // L/P passes
+  static constexpr int NKSH = (HC + 31) / 32;        // K32 steps per pass
+  static constexpr int PADS = 16 / sizeof(SOP);
+  static constexpr int PADL = 16 / sizeof(LOP);
+  static constexpr int LDK = DK + PADS;              // SOP [rows][DK]
+  static constexpr int LDC = CS + PADS;              // SOP [rows][CS]
+  static constexpr int LDH = HC + PADL;              // LOP [rows][HC]
+  static constexpr int LDL = CS + 4;                 // fp32 [CS][CS]
+  static constexpr int LDY = 16 + PADS;
+  static constexpr int TGS = 4;                      // tokens per scan thread
+  static constexpr int NTG = CS / TGS;
+  static constexpr int NCQ = HC / 4;                 // channel quads per pass
+  static constexpr int VV = 16 / sizeof(IO);         // V elements per 16-byte load
+  static constexpr int VTPR = J / VV;                // threads per V row
+  static constexpr int VRPP = NT / VTPR;             // V rows per pass
+  static constexpr int VPASS = (CS + VRPP - 1) / VRPP;
+  static constexpr int NTILE = NCT * (NCT + 1) / 2;  // lower-triangular 16x16 tiles
+  static constexpr int TPW = (2 * NTILE + NW - 1) / NW;  // L/P tiles per wave
+  static constexpr int NLO = SPLIT ? 1 : 0;
+  static_assert(NSW >= 1 && NSW <= NW, "slab must be 16..64 columns");
+  static_assert(NCQ * NTG <= NT, "scan mapping exceeds the workgroup");
+  static_assert(DK % 16 == 0 && CS % 16 == 0 && DK % HC == 0, "tile sizes");
+};
+
+template <class C>
+struct Smem {
+  using SOP = typename C::SOP;
+  using LOP = typename C::LOP;
+  using IO = typename C::IO;
+  alignas(16) SOP kg[C::CS * C::LDK];    // K o e^{G}
+  alignas(16) SOP qg[C::CS * C::LDK];    // Q o e^{G}
+  alignas(16) SOP kht[C::DK * C::LDC];   // (K o e^{G_C - G})^T
+  alignas(16) SOP p[C::CS * C::LDC];     // P (lower triangle)
+  alignas(16) SOP t[C::CS * C::LDC];     // T (lower triangle)
+  alignas(16) IO v[C::CS * C::J];        // V slab
+  alignas(16) float beta[C::CS];
+  alignas(16) float gam[C::DK];          // e^{G_C}
+  alignas(16) float tot[C::NTG * C::HC];
+  alignas(16) float l[C::CS * C::LDL];   // L (strictly lower, beta folded in)
+  union R {
+    struct LP {                          // one pass of L/P operands (HC channels)
+      alignas(16) LOP kgb[C::CS * C::LDH];   // K o e^{G}
+      alignas(16) LOP qgh[C::CS * C::LDH];   // Q o e^{G}, high part
+      alignas(16) LOP kch[C::CS * C::LDH];   // K o e^{-G}, high part
+      alignas(16) LOP qgl[C::NLO ? C::CS * C::LDH : 8];  // low parts (bf16 path)
+      alignas(16) LOP kcl[C::NLO ? C::CS * C::LDH : 8];
+    } lp;
+    struct Solve {
+      alignas(16) SOP tt[C::CS * C::LDC];    // T^T
+      alignas(16) SOP ad[C::CS * C::LDC];    // diagonal blocks of (I+L)^{-1}
+      alignas(16) SOP y[C::NW][16 * C::LDY]; // per-wave 16x16 scratch
+    } solve;
+  } u;
+};
+
+// Barrier that waits only for LDS traffic (global prefetches stay in flight).
+__device__ __forceinline__ void block_sync_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// ---- raw per-chunk inputs held in registers (prefetched one chunk ahead) ----
+
+template <typename IO> struct Quad;
+template <> struct Quad<__bf16> {
+  u32x2 w;
+  __device__ __forceinline__ void load(const __bf16* p) { w = *reinterpret_cast<const u32x2*>(p); }
+  __device__ __forceinline__ void clear() { w = (u32x2)0u; }
+  __device__ __forceinline__ void unpack(float (&f)[4]) const {
+    f[0] = __builtin_bit_cast(float, w.x << 16);
+    f[1] = __builtin_bit_cast(float, w.x & 0xffff0000u);
+    f[2] = __builtin_bit_cast(float, w.y << 16);
+    f[3] = __builtin_bit_cast(float, w.y & 0xffff0000u);
+  }
+};
+template <> struct Quad<float> {
+  f32x4 w;
+  __device__ __forceinline__ void load(const float* p) { w = *reinterpret_cast<const f32x4*>(p); }
+  __device__ __forceinline__ void clear() { w = (f32x4)0.0f; }
+  __device__ __forceinline__ void unpack(float (&f)[4]) const { f[0] = w.x; f[1] = w.y; f[2] = w.z; f[3] = w.w; }
+};
+
+template <class C>
+struct Raw {
+  f32x4 a[C::NH][C::TGS];                 // alpha, 4 channels per token
+  Quad<typename C::IO> k[C::NH][C::TGS];
+  Quad<typename C::IO> q[C::NH][C::TGS];
+  u32x4 v[C::VPASS];                      // 16 bytes of the V slab per pass
+  float beta;
+};
+
+struct Ctx {
+  PrefillParams p;
+  int bh, b, h, col0;  // col0: first state column of this slab
+};
+
+template <class C>
+__device__ __forceinline__ void load_raw(Raw<C>& raw, const Ctx& cx, int t0, int tid) {
+  using IO = typename C::IO;
+  const PrefillParams& p = cx.p;
+  const int cq = tid % C::NCQ, tg = tid / C::NCQ;
+  if (tg < C::NTG) {
+#pragma unroll
+    for (int hh = 0; hh < C::NH; ++hh)
+#pragma unroll
+      for (int i = 0; i < C::TGS; ++i) {
+        const int t = t0 + tg * C::TGS + i;
+        const int c = hh * C::HC + 4 * cq;
+        if (t < p.T) {
+          const size_t row = ((size_t)cx.b * p.T + t) * p.H + cx.h;
+          raw.a[hh][i] = *reinterpret_cast<const f32x4*>(p.alpha + row * C::DK + c);
+          raw.k[hh][i].load(static_cast<const IO*>(p.k) + row * C::DK + c);
+          raw.q[hh][i].load(static_cast<const IO*>(p.q) + row * C::DK + c);
+        } else {
+          raw.a[hh][i] = (f32x4)1.0f;
+          raw.k[hh][i].clear();
+          raw.q[hh][i].clear();
+        }
+      }
+  }
+#pragma unroll
+  for (int ps = 0; ps < C::VPASS; ++ps) {
+    const int r = ps * C::VRPP + tid / C::VTPR;
+    const int t = t0 + r;
+    if (r < C::CS && t < p.T) {
+      const size_t row = ((size_t)cx.b * p.T + t) * p.H + cx.h;
+      raw.v[ps] = *reinterpret_cast<const u32x4*>(static_cast<const IO*>(p.v) + row * p.dv + cx.col0 +
+                                                  (tid % C::VTPR) * C::VV);
+    } else {
+      raw.v[ps] = (u32x4)0u;
+    }
+  }
+  raw.beta = 0.0f;
+  if (tid < C::CS && t0 + tid < p.T) raw.beta = p.beta[((size_t)cx.b * p.T + t0 + tid) * p.H + cx.h];
+}
+
+// ---- phase 1: decay scan and decayed operands for one pass of HC channels ----
+// Tokens outside [lo, hi) act as identity steps (alpha = 1, k = q = 0, beta = 0).
+// Returns true (uniformly) if `check` is set and the chunk's total decay in some
+// channel of the pass is below e^{-80}; nothing is written in that case.
+template <class C>
+__device__ bool phase_scan(Smem<C>& sm, const Raw<C>& raw, int hh, int lo, int hi, bool check, int tid) {
+  using SOP = typename C::SOP;
+  using LOP = typename C::LOP;
+  const int cq = tid % C::NCQ, tg = tid / C::NCQ;
+  const bool act = tg < C::NTG;
+  float lp[C::TGS][4];
+  if (act) {
+    float run[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+#pragma unroll
+    for (int i = 0; i < C::TGS; ++i) {
+      const int t = tg * C::TGS + i;
+      const bool in = t >= lo && t < hi;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        run[e] *= in ? raw.a[hh][i][e] : 1.0f;
+        lp[i][e] = run[e];
+      }
+    }
+    *reinterpret_cast<f32x4*>(&sm.tot[tg * C::HC + 4 * cq]) = f32x4{run[0], run[1], run[2], run[3]};
+  }
+  block_sync_lds();
+  float ep[4] = {1.0f, 1.0f, 1.0f, 1.0f}, gm[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+  int steep = 0;
+  if (act) {
+#pragma unroll
+    for (int g2 = 0; g2 < C::NTG; ++g2) {
+      const f32x4 tv = *reinterpret_cast<const f32x4*>(&sm.tot[g2 * C::HC + 4 * cq]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (g2 < tg) ep[e] *= tv[e];
+        gm[e] *= tv[e];
+      }
+    }
+    // e^{-80}: below this a single chunk-start reference could overflow e^{-G}.
+#pragma unroll
+    for (int e = 0; e < 4; ++e) steep |= !(gm[e] >= 1.8048513e-35f);
+  }
+  if (check) {
+    if (__syncthreads_or(steep)) return true;
+  }
+  if (act) {
+    const int c0 = hh * C::HC + 4 * cq;  // first global channel of this thread
+    SOP kh[4][C::TGS];
+#pragma unroll
+    for (int i = 0; i < C::TGS; ++i) {
+      const int t = tg * C::TGS + i;
+      const bool in = t >= lo && t < hi;
+      float kf[4], qf[4];
+      raw.k[hh][i].unpack(kf);
+      raw.q[hh][i].unpack(qf);
+      SOP kgs[4], qgs[4];
+      LOP kgb[4], qgh[4], kch[4], qgl[4], kcl[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float pre = ep[e] * lp[i][e];
+        const float inv = __builtin_amdgcn_rcpf(pre);
+        const float kk = in ? kf[e] : 0.0f, qq = in ? qf[e] : 0.0f;
+        const float KG = kk * pre, QG = qq * pre, KC = kk * inv;
+        kgs[e] = from_f32<SOP>(KG);
+        qgs[e] = from_f32<SOP>(QG);
+        kh[e][i] = from_f32<SOP>(KC * gm[e]);
+        kgb[e] = from_f32<LOP>(KG);
+        qgh[e] = from_f32<LOP>(QG);
+        kch[e] = from_f32<LOP>(KC);
+        qgl[e] = from_f32<LOP>(QG - to_f32(qgh[e]));
+        kcl[e] = from_f32<LOP>(KC - to_f32(kch[e]));
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sm.kg[t * C::LDK + c0 + e] = kgs[e];
+        sm.qg[t * C::LDK + c0 + e] = qgs[e];
+        sm.u.lp.kgb[t * C::LDH + 4 * cq + e] = kgb[e];
+        sm.u.lp.qgh[t * C::LDH + 4 * cq + e] = qgh[e];
+        sm.u.lp.kch[t * C::LDH + 4 * cq + e] = kch[e];
+        if constexpr (C::SPLIT) {
+          sm.u.lp.qgl[t * C::LDH + 4 * cq + e] = qgl[e];
+          sm.u.lp.kcl[t * C::LDH + 4 * cq + e] = kcl[e];
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int i = 0; i < C::TGS; ++i) sm.kht[(c0 + e) * C::LDC + tg * C::TGS + i] = kh[e][i];
+    if (tg == 0) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sm.gam[c0 + e] = gm[e];
+    }
+  }
+  if (hh == 0) {
+    if (tid < C::CS) sm.beta[tid] = (tid >= lo && tid < hi) ? raw.beta : 0.0f;
+#pragma unroll
+    for (int ps = 0; ps < C::VPASS; ++ps) {
+      const int r = ps * C::VRPP + tid / C::VTPR;
+      if (r < C::CS) *reinterpret_cast<u32x4*>(&sm.v[r * C::J + (tid % C::VTPR) * C::VV]) = raw.v[ps];
+    }
+  }
+  return false;
+}
+
+// ---- phase 2: intra-chunk L = beta K K^T and P = Q K^T (decayed) ------------
+// Tiles are dealt to waves round-robin; accumulators persist over the passes.
+template <class C>
+__device__ __forceinline__ void tile_of(int idx, bool& isP, int& a, int& b) {
+  isP = idx & 1;
+  const int tile = idx >> 1;
+  a = 0;
+  while ((a + 1) * (a + 2) / 2 <= tile) ++a;
+  b = tile - a * (a + 1) / 2;
+}
+
+template <class C>
+__device__ void phase_lp(Smem<C>& sm, f32x4 (&acc)[C::TPW], int wave, int lane, int blo, int bhi) {
+  using LOP = typename C::LOP;
+  const int g = lane / 16, m = lane % 16;
+  const auto& lp = sm.u.lp;
+#pragma unroll
+  for (int j = 0; j < C::TPW; ++j) {
+    const int idx = wave + C::NW * j;
+    if (idx >= 2 * C::NTILE) break;
+    bool isP;
+    int a, b;
+    tile_of<C>(idx, isP, a, b);
+    if (!(a >= blo && a < bhi && b >= blo && b < bhi)) continue;
+#pragma unroll
+    for (int ks = 0; ks < C::NKSH; ++ks) {
+      const int c0 = 32 * ks + 8 * g;
+      const Frag<LOP> Bh = lds_frag(lp.kch, C::LDH, 16 * b + m, c0, C::HC);
+      if (!isP) {
+        const Frag<LOP> A = lds_frag(lp.kgb, C::LDH, 16 * a + m, c0, C::HC);
+        acc[j] = mma(A, Bh, acc[j]);
+        if constexpr (C::SPLIT) acc[j] = mma(A, lds_frag(lp.kcl, C::LDH, 16 * b + m, c0, C::HC), acc[j]);
+      } else {
+        const Frag<LOP> Ah = lds_frag(lp.qgh, C::LDH, 16 * a + m, c0, C::HC);
+        acc[j] = mma(Ah, Bh, acc[j]);
+        if constexpr (C::SPLIT) {
+          acc[j] = mma(Ah, lds_frag(lp.kcl, C::LDH, 16 * b + m, c0, C::HC), acc[j]);
+          acc[j] = mma(lds_frag(lp.qgl, C::LDH, 16 * a + m, c0, C::HC), Bh, acc[j]);
+        }
+      }
+    }
+  }
+}
+
+template <class C>
+__device__ void lp_epilogue(Smem<C>& sm, const f32x4 (&acc)[C::TPW], int wave, int lane) {
+  using SOP = typename C::SOP;
+  const int g = lane / 16, m = lane % 16;
+#pragma unroll
+  for (int j = 0; j < C::TPW; ++j) {
+    const int idx = wave + C::NW * j;
+    if (idx >= 2 * C::NTILE) break;
+    bool isP;
+    int a, b;
+    tile_of<C>(idx, isP, a, b);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * a + 4 * g + r, i = 16 * b + m;
+      if (isP) sm.p[t * C::LDC + i] = from_f32<SOP>(t >= i ? acc[j][r] : 0.0f);
+      else sm.l[t * C::LDL + i] = t > i ? acc[j][r] * sm.beta[t] : 0.0f;
+    }
+  }
+}
+
+// ---- phase 3: T = (I + L)^{-1} diag(beta) -------------------------------------
+// Diagonal 16x16 blocks by fp32 forward substitution; off-diagonal blocks by
+// T_ab = -(I + L_aa)^{-1} sum_{c=b}^{a-1} L_ac T_cb on the matrix cores.
+template <class C>
+__device__ void phase_solve(Smem<C>& sm, int tid, int wave, int lane) {
+  using SOP = typename C::SOP;
+  auto& sv = sm.u.solve;
+  if (tid < 16 * C::NCT) {
+    const int a = tid / 16, s = tid % 16;
+    float x[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) x[u] = (u == s) ? 1.0f : 0.0f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const float xu = x[u];
+#pragma unroll
+      for (int t = u + 1; t < 16; ++t) x[t] -= sm.l[(16 * a + t) * C::LDL + 16 * a + u] * xu;
+    }
+    const float bs = sm.beta[16 * a + s];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      sv.ad[(16 * a + t) * C::LDC + 16 * a + s] = from_f32<SOP>(x[t]);
+      const SOP tv = from_f32<SOP>(x[t] * bs);
+      sm.t[(16 * a + t) * C::LDC + 16 * a + s] = tv;
+      sv.tt[(16 * a + s) * C::LDC + 16 * a + t] = tv;
+    }
+  }
+  block_sync_lds();
+  const int g = lane / 16, m = lane % 16;
+  for (int d = 1; d < C::NCT; ++d) {
+    for (int a = d + wave; a < C::NCT; a += C::NW) {
+      const int b = a - d;
+      f32x4 y = (f32x4)0.0f;
+      for (int kb = 16 * b; kb < 16 * a; kb += 32) {
+        // A = L rows of block a (fp32 in LDS, rounded to the operand type)
+        Frag<SOP> A;
+        {
+          const Frag<float> lf = lds_frag(sm.l, C::LDL, 16 * a + m, kb + 8 * g, 16 * a);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) A.v[e] = from_f32<SOP>(lf.v[e]);
+        }
+        const Frag<SOP> B = lds_frag(sv.tt, C::LDC, 16 * b + m, kb + 8 * g, 16 * a);
+        y = mma(A, B, y);
+      }
+      SOP* ys = sv.y[wave];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ys[m * C::LDY + 4 * g + r] = from_f32<SOP>(y[r]);
+      wave_lds_sync();
+      const Frag<SOP> A = lds_frag(sv.ad, C::LDC, 16 * a + m, 16 * a + 8 * g, 16 * a + 16);
+      const Frag<SOP> B = lds_frag(ys, C::LDY, m, 8 * g, 16);
+      const f32x4 z = mma(A, B, (f32x4)0.0f);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const SOP tv = from_f32<SOP>(-z[r]);
+        const int t = 16 * a + 4 * g + r, s = 16 * b + m;
+        sm.t[t * C::LDC + s] = tv;
+        sv.tt[s * C::LDC + t] = tv;
+      }
+      wave_lds_sync();
+    }
+    block_sync_lds();
+  }
+}
+
+// ---- phase 4: state update for one 16-column slice (one wave) --------------
+template <class C>
+__device__ void phase_state(Smem<C>& sm, f32x4 (&S)[C::NKT], int w, int lane, const Ctx& cx,
+                            int t0, int lo, int hi) {
+  using SOP = typename C::SOP;
+  using IO = typename C::IO;
+  const int g = lane / 16, m = lane % 16;
+  const f32x4 zero4 = (f32x4)0.0f;
+
+  // Power-of-two scale for this column's values (S and V): keeps the fp16
+  // operands in range whatever the magnitudes; exact, so it cancels.
+  float vv[C::NCT][4];
+  float mx = 0.0f;
+#pragma unroll
+  for (int it = 0; it < C::NKT; ++it)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(S[it][r]));
+#pragma unroll
+  for (int a = 0; a < C::NCT; ++a)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      vv[a][r] = to_f32(sm.v[(16 * a + 4 * g + r) * C::J + 16 * w + m]);
+      mx = fmaxf(mx, fabsf(vv[a][r]));
+    }
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const int ex = (mx > 0.0f) ? __builtin_amdgcn_frexp_expf(mx) : 0;
+  const float scale = __builtin_amdgcn_ldexpf(1.0f, -ex);
+  const float unscale = __builtin_amdgcn_ldexpf(1.0f, ex);
+
+  // S~ as B operands (stacked channel tiles)
+  Frag<SOP> sf[C::NKS], sfn[C::NKS];
+#pragma unroll
+  for (int ks = 0; ks < C::NKS; ++ks) {
+    sf[ks] = frag_from_tiles<SOP>(S[2 * ks], (2 * ks + 1 < C::NKT) ? S[2 * ks + 1] : zero4, scale);
+    sfn[ks] = sf[ks];
+    sfn[ks].negate();
+  }
+  // X~ = V~ - (K o e^G) S~
+  f32x4 X[C::NCT];
+#pragma unroll
+  for (int a = 0; a < C::NCT; ++a) {
+    f32x4 acc;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = vv[a][r] * scale;
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks)
+      acc = mma(lds_frag_stacked(sm.kg, C::LDK, 16 * a + m, 32 * ks, g, C::DK), sfn[ks], acc);
+    X[a] = acc;
+  }
+  Frag<SOP> xf[C::NTS];
+#pragma unroll
+  for (int ks = 0; ks < C::NTS; ++ks)
+    xf[ks] = frag_from_tiles<SOP>(X[2 * ks], (2 * ks + 1 < C::NCT) ? X[2 * ks + 1] : zero4, 1.0f);
+  // U~ = T X~ (T lower triangular)
+  f32x4 U[C::NCT];
+#pragma unroll
+  for (int a = 0; a < C::NCT; ++a) {
+    f32x4 acc = zero4;
+#pragma unroll
+    for (int ks = 0; ks < C::NTS; ++ks)
+      if (2 * ks <= a) acc = mma(lds_frag_stacked(sm.t, C::LDC, 16 * a + m, 32 * ks, g, 16 * (a + 1)), xf[ks], acc);
+    U[a] = acc;
+  }
+  Frag<SOP> uf[C::NTS];
+#pragma unroll
+  for (int ks = 0; ks < C::NTS; ++ks)
+    uf[ks] = frag_from_tiles<SOP>(U[2 * ks], (2 * ks + 1 < C::NCT) ? U[2 * ks + 1] : zero4, 1.0f);
+  // O = (Q o e^G) S + P U
+#pragma unroll
+  for (int a = 0; a < C::NCT; ++a) {
+    f32x4 acc = zero4;
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks)
+      acc = mma(lds_frag_stacked(sm.qg, C::LDK, 16 * a + m, 32 * ks, g, C::DK), sf[ks], acc);
+#pragma unroll
+    for (int ks = 0; ks < C::NTS; ++ks)
+      if (2 * ks <= a) acc = mma(lds_frag_stacked(sm.p, C::LDC, 16 * a + m, 32 * ks, g, 16 * (a + 1)), uf[ks], acc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * a + 4 * g + r;
+      if (t >= lo && t < hi && t0 + t < cx.p.T) {
+        const size_t idx = (((size_t)cx.b * cx.p.T + t0 + t) * cx.p.H + cx.h) * cx.p.dv + cx.col0 + 16 * w + m;
+        const float ov = acc[r] * unscale;
+        if (cx.p.o_f32) static_cast<float*>(cx.p.o)[idx] = ov;
+        else static_cast<__bf16*>(cx.p.o)[idx] = (__bf16)ov;
+      }
+    }
+  }
+  // S' = Diag(e^{G_C}) S + (K o e^{G_C-G})^T U
+#pragma unroll
+  for (int it = 0; it < C::NKT; ++it) {
+    f32x4 acc;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = S[it][r] * sm.gam[16 * it + 4 * g + r] * scale;
+#pragma unroll
+    for (int ks = 0; ks < C::NTS; ++ks)
+      acc = mma(lds_frag_stacked(sm.kht, C::LDC, 16 * it + m, 32 * ks, g, C::CS), uf[ks], acc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) S[it][r] = acc[r] * unscale;
+  }
+}
+
+// One chunk (or 16-token sub-chunk when [lo, hi) is narrower): all phases.
+// Returns false without side effects if `check` finds the chunk too steep.
+// `prefetch_t0` >= 0: once the last scan has consumed `raw`, start loading the
+// chunk at that token into it (overlapping the rest of this chunk).
+template <class C>
+__device__ bool process_chunk(Smem<C>& sm, Raw<C>& raw, f32x4 (&S)[C::NKT], const Ctx& cx, int t0,
+                              int lo, int hi, bool check, int prefetch_t0, int tid, int wave, int lane) {
+  f32x4 acc[C::TPW];
+#pragma unroll
+  for (int j = 0; j < C::TPW; ++j) acc[j] = (f32x4)0.0f;
+  const int blo = lo / 16, bhi = (hi + 15) / 16;
+#pragma unroll
+  for (int hh = 0; hh < C::NH; ++hh) {
+    block_sync_lds();
+    if (phase_scan<C>(sm, raw, hh, lo, hi, check, tid)) return false;
+    if (hh == C::NH - 1 && prefetch_t0 >= 0) load_raw<C>(raw, cx, prefetch_t0, tid);
+    block_sync_lds();
+    phase_lp<C>(sm, acc, wave, lane, blo, bhi);
+  }
+  lp_epilogue<C>(sm, acc, wave, lane);
+  block_sync_lds();
+  phase_solve<C>(sm, tid, wave, lane);
+  if (wave < C::NSW) phase_state<C>(sm, S, wave, lane, cx, t0, lo, hi);
+  return true;
+}
+
+template <class C>
+__global__ __launch_bounds__(256, 1) void kda_prefill_kernel(PrefillParams p) {
+  __shared__ Smem<C> sm;
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+  const int nslab = p.dv / C::J;
+  // XCD-aware placement: consecutive workgroup ids go round-robin over the 8
+  // XCDs, so remap them so the slabs of one head share an XCD (and its L2).
+  const int G = gridDim.x;
+  int lid = blockIdx.x;
+  if (G % 8 == 0) lid = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
+  Ctx cx;
+  cx.p = p;
+  cx.bh = lid / nslab;
+  cx.b = cx.bh / p.H;
+  cx.h = cx.bh % p.H;
+  cx.col0 = (lid % nslab) * C::J;
+  const int g = lane / 16, m = lane % 16;
+
+  f32x4 S[C::NKT];
+  if (wave < C::NSW) {
+#pragma unroll
+    for (int it = 0; it < C::NKT; ++it)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        S[it][r] = p.S0 ? p.S0[((size_t)cx.bh * C::DK + 16 * it + 4 * g + r) * p.dv + cx.col0 + 16 * wave + m]
+                        : 0.0f;
+  }
+
+  const int nchunks = (p.T + C::CS - 1) / C::CS;
+  Raw<C> raw;
+  if (nchunks > 0) load_raw<C>(raw, cx, 0, tid);
+  for (int c = 0; c < nchunks; ++c) {
+    const int t0 = c * C::CS;
+    const int next = (c + 1 < nchunks) ? t0 + C::CS : -1;
+    if (!process_chunk<C>(sm, raw, S, cx, t0, 0, C::CS, C::CS > 16, next, tid, wave, lane)) {
+      // Too steep for one decay reference: regroup into 16-token sub-chunks.
+      for (int sq = 0; sq < C::NCT; ++sq)
+        process_chunk<C>(sm, raw, S, cx, t0, 16 * sq, 16 * sq + 16, false,
+                         sq == C::NCT - 1 ? next : -1, tid, wave, lane);
+    }
+  }
+
+  if (wave < C::NSW && p.S_T) {
+#pragma unroll
+    for (int it = 0; it < C::NKT; ++it)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        p.S_T[((size_t)cx.bh * C::DK + 16 * it + 4 * g + r) * p.dv + cx.col0 + 16 * wave + m] = S[it][r];
+  }
+}
+
+template <typename IO, int DK, int J, int CS>
+hipError_t launch_one(const PrefillParams& p, hipStream_t s) {
+  using C = Cfg<IO, DK, J, CS>;
+  const unsigned grid = (unsigned)(p.B * p.H * (p.dv / J));
+  hipLaunchKernelGGL((kda_prefill_kernel<C>), dim3(grid), dim3(C::NT), 0, s, p);
+  return hipGetLastError();
+}
+
+typedef hipError_t (*launch_fn)(const PrefillParams&, hipStream_t);
+
+// Instantiated kernels: bf16 for d_k in {16,32,64,128}, fp32 for d_k in {16,32};
+// slabs of 16 or 32 columns; chunks of 16, 32 or 64 tokens.
+template <typename IO, int DK, int J>
+launch_fn pick_chunk(int chunk) {
+  switch (chunk) {
+    case 16: return &launch_one<IO, DK, J, 16>;
+    case 32: return &launch_one<IO, DK, J, 32>;
+    case 64: return &launch_one<IO, DK, J, 64>;
+    default: return nullptr;
+  }
+}
+
+template <typename IO, int DK>
+launch_fn pick_slab(int chunk, int slab) {
+  switch (slab) {
+    case 16: return pick_chunk<IO, DK, 16>(chunk);
+    case 32: return pick_chunk<IO, DK, 32>(chunk);
+    default: return nullptr;
+  }
+}
+
+launch_fn pick(int io_dtype, int dk, int chunk, int slab) {
+  if (io_dtype == 1) {
+    switch (dk) {
+      case 16: return pick_slab<__bf16, 16>(chunk, slab);
+      case 32: return pick_slab<__bf16, 32>(chunk, slab);
+      case 64: return pick_slab<__bf16, 64>(chunk, slab);
+      case 128: return pick_slab<__bf16, 128>(chunk, slab);
+      default: return nullptr;
+    }
+  }
+  if (io_dtype == 0 && slab == 16) {
+    switch (dk) {
+      case 16: return pick_chunk<float, 16, 16>(chunk);
+      case 32: return pick_chunk<float, 32, 16>(chunk);
+      default: return nullptr;
+    }
+  }
+  return nullptr;
+}
+
+}  // namespace
+
+bool prefill_supported(int io_dtype, int dk, int chunk, int slab) {
+  return pick(io_dtype, dk, chunk, slab) != nullptr;
+}
+
+hipError_t launch_prefill(const PrefillParams& p, int io_dtype, int chunk, int slab, hipStream_t s) {
+  const launch_fn f = pick(io_dtype, p.dk, chunk, slab);
+  if (!f || p.dv % slab != 0) return hipErrorInvalidValue;
+  return f(p, s);
+}
+
+}  // namespace kda

@@ -1,0 +1,123 @@
+/*
+ * libkda -- Kimi Delta Attention (KDA) operator for AMD Instinct MI355X (gfx950).
+ *
+ * The operator is the per-head gated delta-rule recurrence defined in the
+ * "Kimi K3 Technical Report review" (jw9603.github.io), sections 3.2-3.3:
+ *
+ *     Sbar_{t-1} = Diag(alpha_t) S_{t-1}            (key channel i kept at rate alpha_t[i])
+ *     S_t        = Sbar_{t-1} + beta_t k_t (v_t - Sbar_{t-1}^T k_t)^T
+ *     o_t        = S_t^T q_t                          (read from the updated state)
+ *
+ * with S_t in R^{d_k x d_v}.  Decay is applied before the write.  There is no
+ * readout scale and keys are used as given (the library does not normalise them).
+ *
+ * Conventions shared by every call:
+ *  - All tensor pointers are DEVICE pointers (HIP global memory) owned by the
+ *    caller.  The library allocates nothing and keeps no state beyond a
+ *    thread-local copy of the last HIP error.  Calls are reentrant.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Each
+ *    call only enqueues work on that stream and returns without synchronising;
+ *    a device-side fault surfaces at the caller's next synchronisation.
+ *  - Layouts are dense, row-major, token-major: [B][T][H][d] for per-token
+ *    tensors and [B][H][d_k][d_v] for states.
+ *  - Every pointer must be 16-byte aligned.
+ *  - Arguments are validated before any HIP call; on error nothing is enqueued
+ *    and no output is touched.  Calls never abort and never throw.
+ *  - Supported sizes: d_k, d_v in {16, 32, 64, 128}.  fp32 q/k/v are supported
+ *    for d_k <= 32 (prefill) and any supported d_k (decode).
+ *  - Arithmetic.  The state is carried in fp32 and every product accumulates in
+ *    fp32.  With fp32 q/k/v all matrix-core operands are fp32.  With bf16 q/k/v
+ *    the operands of the state-side products are fp16 (values are rescaled by a
+ *    power of two per state column and chunk, so their magnitude is not
+ *    restricted; q and k entries should stay below 6.5e4 in magnitude), and the
+ *    intra-chunk key products are formed from bf16 high/low pairs, which keep
+ *    about 16 significant bits over the full decay range.
+ *  - Input domain: alpha in [exp(-5), 1] (the lower-bounded decay of section 3.5
+ *    of the same page); results outside it are not guaranteed.  beta may be any
+ *    finite value (it is not clamped).
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KDA_F32 = 0,  /* IEEE binary32 */
+  KDA_BF16 = 1  /* bfloat16; outputs are rounded to nearest even */
+} kda_dtype;
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_NULL = 1,        /* a required pointer is NULL */
+  KDA_ERR_SHAPE = 2,       /* B, H < 1, T < 0, or a size overflows 2^31 elements per row index */
+  KDA_ERR_DTYPE = 3,       /* qkv_dtype or o_dtype is not a kda_dtype */
+  KDA_ERR_UNSUPPORTED = 4, /* d_k/d_v not in {16,32,64,128}, chunk not in {16,32,64},
+                              or fp32 prefill with d_k > 32 */
+  KDA_ERR_MISALIGNED = 5,  /* a pointer is not 16-byte aligned */
+  KDA_ERR_ALIAS = 6,       /* an output overlaps an input it may not overlap */
+  KDA_ERR_HIP = 7          /* the launch failed; kda_last_hip_error() holds the hipError_t */
+} kda_status;
+
+/*
+ * Chunkwise-parallel prefill over T tokens for B sequences and H heads.
+ *
+ * The sequence is cut into chunks of `chunk` tokens (the chunkwise form of the
+ * second page, "Kimi 모델 분석", rlaope.github.io, section on putting the
+ * recurrence on the GPU: chunk size 64, WY representation, UT transform, only
+ * the state carried between chunks).  The result equals the token recurrence
+ * above up to rounding, for any chunk size.
+ *
+ *   q, k   : [B][T][H][d_k]  qkv_dtype          (read)
+ *   v      : [B][T][H][d_v]  qkv_dtype          (read)
+ *   alpha  : [B][T][H][d_k]  fp32, per-channel retention   (read)
+ *   beta   : [B][T][H]       fp32, write strength          (read)
+ *   S0     : [B][H][d_k][d_v] fp32 initial state, or NULL for zeros   (read)
+ *   o      : [B][T][H][d_v]  o_dtype, o_t for every token             (written)
+ *   o_dtype: KDA_F32 or KDA_BF16.  With bf16 q/k/v, an fp32 o keeps the full
+ *            accuracy; a bf16 o is that same fp32 value rounded to nearest even,
+ *            and the rounding alone can reach 2^-9 of |o_t|.
+ *   S_T    : [B][H][d_k][d_v] fp32 final state, or NULL to skip       (written)
+ *   chunk  : 16, 32 or 64 (64 is the intended size)
+ *
+ * S0 == S_T (the same buffer) is allowed and updates the state in place; any
+ * other overlap between an output and an input returns KDA_ERR_ALIAS.
+ * T == 0 writes S_T = S0 (zeros when S0 is NULL) and touches nothing else.
+ * Any T >= 1 is accepted; a partial last chunk is masked.
+ */
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
+                         const float* alpha, const float* beta, const float* S0,
+                         void* o, kda_dtype o_dtype, float* S_T,
+                         int B, int T, int H, int d_k, int d_v, int chunk, void* stream);
+
+/*
+ * One batched decode step: one new token for each of B sequences and H heads,
+ * i.e. exactly one step of the recurrence, applied to the state in place.
+ *
+ *   q, k   : [B][H][d_k] qkv_dtype        v: [B][H][d_v] qkv_dtype   (read)
+ *   alpha  : [B][H][d_k] fp32             beta: [B][H] fp32          (read)
+ *   S      : [B][H][d_k][d_v] fp32, read and overwritten with S_t    (in place)
+ *   o      : [B][H][d_v] o_dtype (KDA_F32 or KDA_BF16), o_t         (written)
+ *
+ * Each state is streamed once from HBM and written back once.  o must not
+ * overlap S or any input (KDA_ERR_ALIAS).
+ */
+kda_status kda_decode_step(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
+                           const float* alpha, const float* beta, float* S, void* o, kda_dtype o_dtype,
+                           int B, int H, int d_k, int d_v, void* stream);
+
+/* Human-readable text for a status code (static storage; never NULL). */
+const char* kda_status_string(kda_status s);
+
+/* The hipError_t of the last failed launch on the calling thread (0 if none). */
+int kda_last_hip_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

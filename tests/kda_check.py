@@ -1,0 +1,96 @@
+"""Helpers shared by the GPU tests: run libkda and the oracle on the same inputs
+and compare them.
+
+Tolerances (from the operator's specification):
+  * fp32 q/k/v: max |gpu - oracle| <= 1e-4 on o and on the final state;
+  * bf16 q/k/v (fp32 state): max |gpu - oracle| / RMS(oracle) <= 2e-2, per head,
+    on o and on the final state.
+The oracle always reads the exact tensors the GPU consumed (copied to the host).
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+
+TOL_F32_ABS = 1e-4
+TOL_BF16_REL = 2e-2
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_host(x):
+    return None if x is None else x.detach().cpu()
+
+
+def oracle_prefill(inp, heads=None, **kw):
+    """Oracle on host copies of the device inputs. Returns float64 (o [n,T,dv], S_T [n,dk,dv])."""
+    h = {k: to_host(v) for k, v in inp.items()}
+    return oracle.forward(h["q"], h["k"], h["v"], h["alpha"], h["beta"], h.get("S0"), heads=heads, **kw)
+
+
+def gpu_o_heads(o, heads=None):
+    """GPU o [B,T,H,dv] -> float64 numpy [n_sel,T,dv] in head-id (b*H+h) order."""
+    B, T, H, dv = o.shape
+    oh = o.detach().float().permute(0, 2, 1, 3).reshape(B * H, T, dv)
+    if heads is not None:
+        oh = oh[torch.as_tensor(heads, device=oh.device)]
+    return oh.cpu().double().numpy()
+
+
+def gpu_s_heads(S, heads=None):
+    B, H, dk, dv = S.shape
+    sh = S.detach().reshape(B * H, dk, dv)
+    if heads is not None:
+        sh = sh[torch.as_tensor(heads, device=sh.device)]
+    return sh.cpu().double().numpy()
+
+
+def abs_err(got, ref):
+    return float(np.abs(got - ref).max()) if got.size else 0.0
+
+
+def rel_err_per_head(got, ref):
+    """max over heads of max|got-ref| / RMS(ref) (heads along axis 0)."""
+    if got.size == 0:
+        return 0.0
+    worst = 0.0
+    for g, r in zip(got, ref):
+        rms = float(np.sqrt(np.mean(r * r)))
+        worst = max(worst, float(np.abs(g - r).max()) / max(rms, 1e-30))
+    return worst
+
+
+def assert_close(got, ref, is_bf16, what):
+    if is_bf16:
+        e = rel_err_per_head(got, ref)
+        log(f"  {what}: max|err|/RMS = {e:.3e} (tol {TOL_BF16_REL})")
+        assert e <= TOL_BF16_REL, f"{what}: relative error {e:.3e} > {TOL_BF16_REL}"
+    else:
+        e = abs_err(got, ref)
+        log(f"  {what}: max|err| = {e:.3e} (tol {TOL_F32_ABS})")
+        assert e <= TOL_F32_ABS, f"{what}: abs error {e:.3e} > {TOL_F32_ABS}"
+    return e
+
+
+def check_prefill(inp, chunk=64, heads=None, what="", S0=True):
+    """Run libkda prefill and the oracle; assert parity on o and S_T."""
+    import gated_delta_rule_07_amd as kda
+
+    s0 = inp["S0"] if S0 else None
+    o, st = kda.kda_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], s0, chunk=chunk)
+    torch.cuda.synchronize()
+    ref_in = dict(inp)
+    if not S0:
+        ref_in["S0"] = None
+    ro, rs = oracle_prefill(ref_in, heads=heads)
+    bf = inp["q"].dtype == torch.bfloat16
+    eo = assert_close(gpu_o_heads(o, heads), ro, bf, f"{what} o")
+    es = assert_close(gpu_s_heads(st, heads), rs, bf, f"{what} S_T")
+    return o, st, eo, es

@@ -1,0 +1,123 @@
+"""CPU checks of the libkda boundary: the header compiles as C, the library
+exports every declared symbol, and argument validation rejects bad calls with
+the documented status codes before any HIP call is made (so these run without a
+GPU; the pointers below are fake, aligned addresses that are never touched)."""
+import ctypes
+import re
+import subprocess
+from pathlib import Path
+
+import pytest
+
+ROOT = Path(__file__).resolve().parents[1]
+HEADER = ROOT / "include" / "kda.h"
+
+
+def _lib():
+    import gated_delta_rule_07_amd as kda
+    if not kda.library_path().exists():
+        pytest.skip("libkda.so not built")
+    return kda.load_library()
+
+
+def _declared():
+    text = HEADER.read_text()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\*?\s+\*?(kda_[a-z_]+)\(", text, re.M)))
+
+
+def test_header_compiles_as_c():
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-x", "c", str(HEADER)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert {"kda_chunk_fwd", "kda_decode_step", "kda_status_string", "kda_last_hip_error",
+            "kda_version"} <= set(names)
+    lib = _lib()
+    for n in names:
+        assert hasattr(lib, n), f"libkda.so does not export {n}"
+    out = subprocess.run(["nm", "-D", "--defined-only", str(ROOT / "gated_delta_rule_07_amd" / "libkda.so")],
+                         capture_output=True, text=True).stdout
+    for n in names:
+        assert re.search(rf"\bT {n}\b", out), f"{n} is not a defined text symbol"
+
+
+def test_status_strings_and_version():
+    lib = _lib()
+    for code in range(8):
+        s = lib.kda_status_string(code).decode()
+        assert s.startswith("KDA_")
+    assert lib.kda_status_string(99).decode().startswith("KDA")
+    assert lib.kda_version() >= 100
+    assert lib.kda_last_hip_error() == 0
+
+
+BASE = 1 << 40  # fake device addresses, 16-byte aligned, never dereferenced
+
+
+def _addr(i):
+    return ctypes.c_void_p(BASE + i * (1 << 32))
+
+
+def _prefill(lib, **over):
+    a = dict(q=_addr(0), k=_addr(1), v=_addr(2), dtype=1, alpha=_addr(3), beta=_addr(4), S0=_addr(5),
+             o=_addr(6), odt=0, S_T=_addr(7), B=1, T=64, H=2, dk=128, dv=128, chunk=64)
+    a.update(over)
+    return lib.kda_chunk_fwd(a["q"], a["k"], a["v"], a["dtype"], a["alpha"], a["beta"], a["S0"], a["o"],
+                             a["odt"], a["S_T"], a["B"], a["T"], a["H"], a["dk"], a["dv"], a["chunk"], None)
+
+
+def _decode(lib, **over):
+    a = dict(q=_addr(0), k=_addr(1), v=_addr(2), dtype=1, alpha=_addr(3), beta=_addr(4), S=_addr(5),
+             o=_addr(6), odt=0, B=4, H=2, dk=128, dv=128)
+    a.update(over)
+    return lib.kda_decode_step(a["q"], a["k"], a["v"], a["dtype"], a["alpha"], a["beta"], a["S"], a["o"],
+                               a["odt"], a["B"], a["H"], a["dk"], a["dv"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(dtype=7), 3), (dict(odt=9), 3),
+    (dict(B=0), 2), (dict(H=0), 2), (dict(T=-1), 2),
+    (dict(dk=48), 4), (dict(dv=256), 4), (dict(chunk=48), 4), (dict(chunk=128), 4),
+    (dict(dtype=0, dk=128), 4),  # fp32 prefill is built for d_k <= 32
+    (dict(q=None), 1), (dict(o=None), 1), (dict(beta=None), 1),
+    (dict(k=ctypes.c_void_p(BASE + 8)), 5), (dict(S_T=ctypes.c_void_p(BASE + (7 << 32) + 4)), 5),
+    (dict(o=_addr(0)), 6),                       # o aliases q
+    (dict(S_T=_addr(1)), 6),                     # S_T aliases k
+    (dict(S_T=ctypes.c_void_p(BASE + (5 << 32) + 16)), 6),  # S_T partially overlaps S0
+])
+def test_prefill_validation(over, code):
+    assert _prefill(_lib(), **over) == code
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(dtype=2), 3), (dict(odt=-1), 3), (dict(B=0), 2), (dict(H=-3), 2),
+    (dict(dk=8), 4), (dict(dv=100), 4),
+    (dict(S=None), 1), (dict(o=None), 1),
+    (dict(v=ctypes.c_void_p(BASE + (2 << 32) + 2)), 5),
+    (dict(o=_addr(5)), 6),                       # o aliases the state
+    (dict(S=_addr(3)), 6),                       # state aliases alpha
+])
+def test_decode_validation(over, code):
+    assert _decode(_lib(), **over) == code
+
+
+def test_python_binding_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    import gated_delta_rule_07_amd as kda
+    if not kda.library_path().exists():
+        pytest.skip("libkda.so not built")
+    x = torch.zeros(1, 4, 1, 16)
+    with pytest.raises(ValueError):
+        kda.kda_chunk_fwd(x, x, x, x, torch.zeros(1, 4, 1))
+
+
+def test_product_path_does_not_import_the_oracle():
+    """The HIP product package never imports or links the oracle."""
+    pkg = ROOT / "gated_delta_rule_07_amd"
+    for f in [*pkg.rglob("*.py"), *pkg.rglob("*.hip"), *pkg.rglob("*.cpp"), *pkg.rglob("*.h")]:
+        text = f.read_text()
+        for bad in ("import oracle", "from oracle", "kda_oracle"):
+            assert bad not in text, f"{f} mentions {bad}"

@@ -1,0 +1,265 @@
+"""GPU parity of kda_chunk_fwd (through the C ABI) against the fp64 oracle.
+
+Small and medium shapes that span several chunks and a ragged tail, plus the
+edge cases of the method: empty and one-token sequences, chunk sizes 16/32/64,
+steep decay at the lower bound (exercises the 16-token sub-chunk path), beta
+outside [0, 1], several head sizes, and the decay/write order.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import kda_inputs as ki
+import oracle
+from kda_check import (assert_close, check_prefill, gpu_o_heads, gpu_s_heads, log,
+                       oracle_prefill)
+
+pytestmark = pytest.mark.gpu
+
+
+def _kda():
+    import gated_delta_rule_07_amd as kda
+    return kda
+
+
+def _inp(gpu, B, T, H, dk, dv, dtype=torch.bfloat16, seed=0, mu=3.0, s0=0.1):
+    return ki.make_prefill(B, T, H, dk, dv, dtype, mu, s0, seed=seed, device=gpu)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_tiny_fp32_workload(gpu, seed):
+    """B=1, H=1, T=64, d=16, fp32, S0=0: max abs error <= 1e-4 on o and S_T."""
+    log(f"tiny fp32 seed={seed}")
+    inp = ki.make_workload_prefill(0, seed=seed, device=gpu)
+    check_prefill(inp, chunk=64, what=f"tiny seed{seed}")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("T", [1, 15, 16, 63, 64, 65, 100, 130, 257])
+def test_ragged_lengths(gpu, dtype, T):
+    log(f"ragged T={T} {dtype}")
+    inp = _inp(gpu, 2, T, 3, 32, 32, dtype, seed=T)
+    check_prefill(inp, what=f"T{T}")
+
+
+@pytest.mark.parametrize("dk,dv", [(16, 16), (32, 64), (64, 32), (64, 64), (128, 128), (128, 16), (16, 128)])
+def test_head_sizes_bf16(gpu, dk, dv):
+    log(f"head sizes dk={dk} dv={dv}")
+    inp = _inp(gpu, 1, 200, 2, dk, dv, seed=dk + dv)
+    check_prefill(inp, what=f"d{dk}x{dv}")
+
+
+@pytest.mark.parametrize("dk,dv", [(16, 16), (32, 32), (16, 64), (32, 128)])
+def test_head_sizes_fp32(gpu, dk, dv):
+    log(f"fp32 head sizes dk={dk} dv={dv}")
+    inp = _inp(gpu, 1, 150, 2, dk, dv, torch.float32, seed=dk * dv)
+    check_prefill(inp, what=f"f32 d{dk}x{dv}")
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_chunk_sizes_agree_with_oracle(gpu, chunk):
+    log(f"chunk={chunk}")
+    inp = _inp(gpu, 1, 333, 4, 128, 128, seed=5)
+    check_prefill(inp, chunk=chunk, what=f"C{chunk}")
+
+
+def test_chunk_size_invariance(gpu):
+    """C = 16, 32, 64 give the same result up to rounding."""
+    kda = _kda()
+    inp = _inp(gpu, 1, 512, 4, 128, 128, seed=6)
+    outs = [kda.kda_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["S0"], chunk=c)
+            for c in (16, 32, 64)]
+    ro, rs = oracle_prefill(inp)
+    for o, s in outs:
+        assert_close(gpu_o_heads(o), ro, True, "o")
+        assert_close(gpu_s_heads(s), rs, True, "S_T")
+    o16 = outs[0][0].float()
+    for o, _ in outs[1:]:
+        d = (o.float() - o16).abs().max().item() / o16.pow(2).mean().sqrt().item()
+        log(f"  chunk-to-chunk relative difference {d:.2e}")
+        assert d <= 2e-2
+
+
+@pytest.mark.parametrize("chunk", [32, 64])
+def test_steep_decay_at_lower_bound(gpu, chunk):
+    """alpha = e^{-5} in every channel: the chunk's total decay underflows, so the
+    kernel must regroup into 16-token sub-chunks; results still match the oracle."""
+    log(f"steep chunk={chunk}")
+    inp = _inp(gpu, 1, 300, 2, 64, 64, seed=7)
+    inp["alpha"].fill_(math.exp(-5.0))
+    check_prefill(inp, chunk=chunk, what="alpha=e^-5")
+
+
+def test_steep_decay_mixed_channels(gpu):
+    """Half the channels at the bound, half near 1, with some chunks steep and some not."""
+    inp = _inp(gpu, 2, 400, 2, 128, 128, seed=8)
+    a = inp["alpha"]
+    a[..., ::2] = math.exp(-5.0)
+    a[:, 200:264] = 0.999  # one chunk that is not steep in any channel
+    check_prefill(inp, what="mixed steep")
+
+
+@pytest.mark.parametrize("beta_val", [0.0, 0.5, 1.0, 2.0])
+def test_beta_values(gpu, beta_val):
+    """beta is not clamped: 0, 1/2, 1 and the Householder value 2."""
+    inp = _inp(gpu, 1, 150, 2, 64, 64, seed=9)
+    inp["beta"].fill_(beta_val)
+    check_prefill(inp, what=f"beta={beta_val}")
+
+
+def test_identity_step_leaves_state(gpu):
+    """alpha = 1, beta = 0: the state is returned bit-exactly and o_t = S0^T q_t."""
+    kda = _kda()
+    inp = _inp(gpu, 1, 130, 2, 64, 64, seed=10)
+    inp["alpha"].fill_(1.0)
+    inp["beta"].zero_()
+    o, st = kda.kda_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["S0"])
+    torch.cuda.synchronize()
+    assert torch.equal(st, inp["S0"])
+    ro, _ = oracle_prefill(inp)
+    assert_close(gpu_o_heads(o), ro, True, "o")
+
+
+def test_beta_one_unit_key_reads_back_value(gpu):
+    """beta = 1 with unit keys and q = k: o_t = S_t^T k_t = v_t."""
+    kda = _kda()
+    inp = _inp(gpu, 1, 128, 2, 32, 32, torch.float32, seed=11)
+    inp["beta"].fill_(1.0)
+    o, _ = kda.kda_chunk_fwd(inp["k"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["S0"])
+    torch.cuda.synchronize()
+    err = (o - inp["v"]).abs().max().item()
+    log(f"  max|o - v| = {err:.2e}")
+    assert err <= 1e-4
+
+
+def test_pure_decay_over_many_chunks(gpu):
+    """beta = 0 over 1024 chunks: S_T = Diag(prod_t alpha_t) S0 (closed form, fp64 product)."""
+    kda = _kda()
+    T = 65536
+    inp = _inp(gpu, 1, T, 2, 32, 32, seed=12, mu=8.0)
+    inp["beta"].zero_()
+    _, st = kda.kda_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["S0"])
+    torch.cuda.synchronize()
+    prod = inp["alpha"].double().prod(dim=1)  # [B,H,dk]
+    want = prod[..., None] * inp["S0"].double()
+    rel = ((st.double() - want).abs().max() / want.abs().max()).item()
+    log(f"  pure decay relative error {rel:.2e}")
+    assert rel <= 1e-4
+
+
+def test_matches_page1_order_not_literal_page2(gpu):
+    """Decay before write (page 1); the literal left-multiplied page-2 reading differs."""
+    kda = _kda()
+    inp = _inp(gpu, 1, 96, 2, 32, 32, torch.float32, seed=13, mu=0.0)
+    o, _ = kda.kda_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["S0"])
+    torch.cuda.synchronize()
+    r1, _ = oracle_prefill(inp)
+    r2, _ = oracle_prefill(inp, order="literal_p2")
+    g = gpu_o_heads(o)
+    e1, e2 = np.abs(g - r1).max(), np.abs(g - r2).max()
+    log(f"  err vs page-1 order {e1:.2e}, vs literal page-2 {e2:.2e}")
+    assert e1 <= 1e-4 and e2 > 1e-2
+
+
+def test_zero_length_returns_initial_state(gpu):
+    kda = _kda()
+    inp = _inp(gpu, 2, 0, 3, 64, 64, seed=14)
+    o, st = kda.kda_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["S0"])
+    torch.cuda.synchronize()
+    assert o.numel() == 0 and torch.equal(st, inp["S0"])
+    _, st0 = kda.kda_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], None)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(st0).item() == 0
+
+
+def test_no_initial_state_means_zeros(gpu):
+    inp = _inp(gpu, 1, 100, 2, 64, 64, seed=15)
+    check_prefill(inp, what="S0=None", S0=False)
+
+
+def test_split_call_equals_one_call(gpu):
+    """Resuming from S_T: [0, T1) then [T1, T) equals one call (bitwise when T1 is a chunk multiple)."""
+    kda = _kda()
+    inp = _inp(gpu, 1, 640, 4, 128, 128, seed=16)
+    o, st = kda.kda_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["S0"])
+    for T1 in (256, 300):
+        a = {k: v[:, :T1].contiguous() for k, v in inp.items() if k != "S0"}
+        b = {k: v[:, T1:].contiguous() for k, v in inp.items() if k != "S0"}
+        o1, s1 = kda.kda_chunk_fwd(a["q"], a["k"], a["v"], a["alpha"], a["beta"], inp["S0"])
+        o2, s2 = kda.kda_chunk_fwd(b["q"], b["k"], b["v"], b["alpha"], b["beta"], s1)
+        torch.cuda.synchronize()
+        oc = torch.cat([o1, o2], dim=1)
+        if T1 % 64 == 0:
+            assert torch.equal(oc, o) and torch.equal(s2, st)
+        else:
+            d = (oc.float() - o.float()).abs().max().item() / o.float().pow(2).mean().sqrt().item()
+            assert d <= 2e-2
+
+
+def test_in_place_state(gpu):
+    """S0 and S_T may be the same buffer."""
+    kda = _kda()
+    inp = _inp(gpu, 2, 200, 4, 64, 64, seed=17)
+    o_ref, s_ref = kda.kda_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["S0"])
+    S = inp["S0"].clone()
+    o, s = kda.kda_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], S, S_T=S)
+    torch.cuda.synchronize()
+    assert s.data_ptr() == S.data_ptr() and torch.equal(S, s_ref) and torch.equal(o, o_ref)
+
+
+def test_deterministic(gpu):
+    kda = _kda()
+    inp = _inp(gpu, 2, 1000, 8, 128, 128, seed=18)
+    r1 = kda.kda_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["S0"])
+    r2 = kda.kda_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["S0"])
+    torch.cuda.synchronize()
+    assert torch.equal(r1[0], r2[0]) and torch.equal(r1[1], r2[1])
+
+
+def test_slab_width_does_not_change_results(gpu, monkeypatch):
+    """Columns of S evolve independently: 16- and 32-column slabs give identical bits."""
+    kda = _kda()
+    inp = _inp(gpu, 2, 300, 32, 128, 128, seed=19)
+    res = []
+    for slab in ("16", "32"):
+        monkeypatch.setenv("KDA_PREFILL_SLAB", slab)
+        res.append(kda.kda_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["S0"]))
+    torch.cuda.synchronize()
+    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+
+
+def test_prefill_equals_repeated_decode(gpu):
+    """T decode steps reproduce one prefill over the same T tokens (up to rounding)."""
+    kda = _kda()
+    inp = _inp(gpu, 2, 70, 4, 128, 128, seed=20)
+    o, st = kda.kda_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["S0"])
+    S = inp["S0"].clone()
+    outs = []
+    for t in range(70):
+        sl = {k: inp[k][:, t].contiguous() for k in ("q", "k", "v", "alpha", "beta")}
+        outs.append(kda.kda_decode_step(sl["q"], sl["k"], sl["v"], sl["alpha"], sl["beta"], S))
+    torch.cuda.synchronize()
+    od = torch.stack(outs, dim=1)
+    d_o = (od.float() - o.float()).abs().max().item() / o.float().pow(2).mean().sqrt().item()
+    d_s = (S - st).abs().max().item() / st.pow(2).mean().sqrt().item()
+    log(f"  decode vs prefill: o {d_o:.2e}, S {d_s:.2e}")
+    assert d_o <= 2e-2 and d_s <= 2e-2
+
+
+def test_many_heads_sampled(gpu):
+    """B*H large enough for 32-column slabs and the XCD remap (B*H*dv/32 % 8 == 0)."""
+    inp = _inp(gpu, 2, 200, 64, 128, 128, seed=21)
+    check_prefill(inp, heads=[0, 17, 63, 64, 100, 127], what="B2H64")
+
+
+def test_bf16_output_is_rounded_fp32_output(gpu):
+    """o_dtype = bf16 writes exactly the fp32 result rounded to nearest even."""
+    kda = _kda()
+    inp = _inp(gpu, 2, 300, 4, 128, 128, seed=22)
+    args = (inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["S0"])
+    o32, s32 = kda.kda_chunk_fwd(*args)
+    o16, s16 = kda.kda_chunk_fwd(*args, o_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert o16.dtype == torch.bfloat16 and torch.equal(o16, o32.to(torch.bfloat16)) and torch.equal(s16, s32)
