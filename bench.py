@@ -1,0 +1,288 @@
+#!/usr/bin/env python3
+"""Benchmark libkda on one MI355X and print one JSON line.
+
+One timed step is one kda_chunk_fwd call over the 64K-token prefill workload
+(B=2, H=32, T=65536, d_k=d_v=128, bf16 q/k/v, fp32 alpha/beta/state, chunk 64,
+fp32 o), with inputs resident in HBM.  The same run also times the batched
+decode workload (B=256, H=32, d=128, 100 in-place steps) and reports it under
+"decode".  Before any timing, sampled heads of both workloads are checked
+against the fp64 oracle (the parity gate); the oracle's time on that sample,
+on this host's cores, is the CPU baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "KDA prefill tokens/s @T=64K,H=32,d=128 (%MFMA peak); decode state GB/s (%HBM)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 (fp16 is the same rate)
+TOL_REL = 2e-2
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def prefill_counts(B, T, H, dk, dv, chunk, o_bytes):
+    """Algorithmic bytes and FLOPs of one prefill call (roofline)."""
+    th = B * T * H
+    per_th_bytes = 2 * (2 * dk + dv) + 4 * dk + 4 + o_bytes * dv
+    state_bytes = 2 * 4 * dk * dv * B * H
+    per_th_flops = 6 * dk * dv + chunk * (3 * dk + 2 * dv) + chunk * chunk / 3.0
+    return th * per_th_bytes + state_bytes, th * per_th_flops, per_th_bytes, per_th_flops
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in sorted((ROOT / "gated_delta_rule_07_amd" / "csrc").glob("*")):
+        h.update(f.read_bytes())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_key):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel sources; else None."""
+    f = ROOT / "profiles" / "traffic.json"
+    if not f.exists():
+        return None
+    try:
+        d = json.loads(f.read_text())
+    except ValueError:
+        return None
+    ent = d.get(kernel_key)
+    if not ent or ent.get("source_hash") != source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def timed_launches(fn, n, torch):
+    """Run fn() n times on the current stream; return (total_ms, mean per-launch ms)
+    from HIP events recorded on that stream."""
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n):
+        starts[i].record()
+        fn()
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return wall_ms, sum(per) / len(per), starts[0].elapsed_time(ends[-1])
+
+
+def rel_err_heads(got, ref):
+    import numpy as np
+    worst = 0.0
+    for g, r in zip(got, ref):
+        rms = float(np.sqrt(np.mean(r * r)))
+        worst = max(worst, float(np.abs(g - r).max()) / max(rms, 1e-30))
+    return worst
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=100)
+    ap.add_argument("--sample-heads", type=int, default=8, help="heads checked by the oracle")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build measures one GPU only (asked for {max(args.gpus, world)}); "
+              "the operator's (sequence, head) work is independent, see DESIGN.md for how it shards",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gated_delta_rule_07_amd as kda
+    import kda_inputs as ki
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    kda.load_library()
+    props = torch.cuda.get_device_properties(dev)
+
+    # ---------------- prefill: 64K tokens, B=2, H=32, d=128 ----------------
+    w = ki.WORKLOADS[2]
+    B, T, H, dk, dv, C = w.B, w.T, w.H, w.dk, w.dv, w.chunk
+    log(f"generating prefill inputs B={B} T={T} H={H} d={dk}")
+    x = ki.make_workload_prefill(2, seed=0, device=dev)
+    o = torch.empty(B, T, H, dv, device=dev, dtype=torch.float32)
+    S_T = torch.empty(B, H, dk, dv, device=dev, dtype=torch.float32)
+
+    def step():
+        kda.kda_chunk_fwd(x["q"], x["k"], x["v"], x["alpha"], x["beta"], x["S0"], chunk=C, o=o, S_T=S_T)
+
+    step()
+    torch.cuda.synchronize()
+
+    # parity gate on sampled heads; the oracle's time on that sample is the CPU baseline
+    import oracle
+    nh = min(args.sample_heads, B * H)
+    heads = sorted(set(int(v) for v in np.linspace(0, B * H - 1, nh)))
+    log(f"parity gate: oracle on heads {heads} (full T)")
+    hq = {k: v.cpu() for k, v in x.items()}
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    ro, rs = oracle.forward(hq["q"], hq["k"], hq["v"], hq["alpha"], hq["beta"], hq["S0"], heads=heads,
+                            threads=threads)
+    cpu_s = time.perf_counter() - t0
+    go = o.permute(0, 2, 1, 3).reshape(B * H, T, dv)[heads].cpu().double().numpy()
+    gs = S_T.reshape(B * H, dk, dv)[heads].cpu().double().numpy()
+    e_o, e_s = rel_err_heads(go, ro), rel_err_heads(gs, rs)
+    del hq, ro, rs, go, gs
+    log(f"parity: o {e_o:.3e}  S_T {e_s:.3e} (tol {TOL_REL}); oracle {cpu_s:.1f} s on {threads} threads")
+
+    for _ in range(args.warmup):
+        step()
+    wall_ms, kern_ms, span_ms = timed_launches(step, args.steps, torch)
+    ms_per_step = wall_ms / args.steps
+    tokens_per_s = B * T / (ms_per_step / 1e3)
+    alg_bytes, alg_flops, per_th_bytes, per_th_flops = prefill_counts(B, T, H, dk, dv, C, 4)
+    achieved_gbs = alg_bytes / (kern_ms / 1e3) / 1e9
+    tflops = alg_flops / (kern_ms / 1e3) / 1e12
+    attainable = min(MFMA_BF16_PEAK_TFS, per_th_flops / per_th_bytes * HBM_PEAK_GBS / 1e3)
+    log(f"prefill: {ms_per_step:.3f} ms/step (kernel {kern_ms:.3f} ms), {tokens_per_s:.4g} tok/s, "
+        f"{achieved_gbs:.0f} GB/s, {tflops:.1f} TFLOP/s")
+
+    # ---------------- decode: B=256, H=32, d=128, 100 in-place steps ----------------
+    wd = ki.WORKLOADS[4]
+    DB, DH = wd.B, wd.H
+    nsteps = args.decode_steps
+    log(f"generating decode inputs B={DB} H={DH} steps={nsteps}")
+    S = ki.make_state(DB, DH, dk, dv, wd.s0_std, 1, dev)
+    toks = [ki.make_decode_token(DB, DH, dk, dv, wd.qkv_dtype, wd.alpha_mu, seed=0, step=s, device=dev)
+            for s in range(nsteps)]
+    od = torch.empty(nsteps, DB, DH, dv, device=dev, dtype=torch.float32)
+    # decode parity on sampled states: the 100 tokens of one state are a sequence
+    dheads = sorted(set(int(v) for v in np.linspace(0, DB * DH - 1, 8)))
+    S_init = S.reshape(DB * DH, dk, dv)[dheads].cpu()
+    for s, tk in enumerate(toks):
+        kda.kda_decode_step(tk["q"], tk["k"], tk["v"], tk["alpha"], tk["beta"], S, o=od[s])
+    torch.cuda.synchronize()
+
+    def gather(name):
+        return torch.stack([tk[name].reshape(DB * DH, -1)[dheads] for tk in toks], 0)[None].cpu()
+
+    seq = {n: gather(n) for n in ("q", "k", "v", "alpha")}
+    seq["beta"] = torch.stack([tk["beta"].reshape(DB * DH)[dheads] for tk in toks], 0)[None].cpu()
+    rdo, rds = oracle.forward(seq["q"], seq["k"], seq["v"], seq["alpha"], seq["beta"],
+                              S_init[None], threads=threads)
+    gdo = od.reshape(nsteps, DB * DH, dv)[:, dheads].permute(1, 0, 2).cpu().double().numpy()
+    gds = S.reshape(DB * DH, dk, dv)[dheads].cpu().double().numpy()
+    e_do = max(float(np.abs(gdo[:, s] - rdo[:, s]).max()) / float(np.sqrt(np.mean(rdo[:, s] ** 2)))
+               for s in range(nsteps))
+    e_ds = rel_err_heads(gds, rds)
+    log(f"decode parity: o {e_do:.3e}  S {e_ds:.3e}")
+
+    def dstep_all():
+        for s, tk in enumerate(toks):
+            kda.kda_decode_step(tk["q"], tk["k"], tk["v"], tk["alpha"], tk["beta"], S, o=od[s])
+
+    dstep_all()  # warm-up pass
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    dstep_all()
+    ev1.record()
+    torch.cuda.synchronize()
+    d_total_ms = ev0.elapsed_time(ev1)
+    # per-launch durations on the same stream
+    _, d_kern_ms, _ = timed_launches(
+        lambda: kda.kda_decode_step(toks[0]["q"], toks[0]["k"], toks[0]["v"], toks[0]["alpha"],
+                                    toks[0]["beta"], S, o=od[0]), 20, torch)
+    d_step_ms = d_total_ms / nsteps
+    state_bytes = 2 * DB * DH * dk * dv * 4
+    io_bytes = DB * DH * (2 * (2 * dk + dv) + 4 * dk + 4 + 4 * dv)
+    d_gbs_state = state_bytes / (d_step_ms / 1e3) / 1e9
+    d_gbs_kernel = (state_bytes + io_bytes) / (d_kern_ms / 1e3) / 1e9
+    log(f"decode: {d_step_ms * 1e3:.1f} us/step (kernel {d_kern_ms * 1e3:.1f} us), "
+        f"state {d_gbs_state:.0f} GB/s, kernel {d_gbs_kernel:.0f} GB/s")
+
+    if args.copy_probe:
+        a = torch.empty(1 << 28, device=dev, dtype=torch.float32)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log("copy probe: 1 GiB read + 1 GiB written")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        rate = len(heads) * T / cpu_s  # token-heads per second on this host
+        cpu = {"value": rate / H, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"{len(heads)} of {B * H} heads of the same workload, full T={T} "
+                         f"({len(heads) * T} token-heads, {cpu_s:.1f} s wall); tokens/s = "
+                         f"token-heads/s / H", "cpu": _cpu_model()}
+
+    parity_ok = max(e_o, e_s, e_do, e_ds) <= TOL_REL
+    out = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"prefill B={B} T={T} H={H} d_k=d_v={dk} chunk={C}; bf16 q/k/v, "
+                               f"fp32 alpha/beta/state, fp32 o",
+                   "global_batch": B, "seq_len": T, "heads": H, "head_dim": dk, "chunk": C,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved_gbs / HBM_PEAK_GBS,
+                     "traffic": measured_traffic("kda_prefill"),
+                     "kernel_ms": kern_ms, "algorithmic_bytes": alg_bytes,
+                     "bytes_per_token_head": per_th_bytes,
+                     "mfma_tflops": tflops, "mfma_frac": tflops / MFMA_BF16_PEAK_TFS,
+                     "flops_per_token_head": per_th_flops,
+                     "attainable_tflops": attainable, "frac_of_attainable": tflops / attainable},
+        "decode": {"workload": f"decode B={DB} H={DH} d={dk}, {nsteps} in-place steps, bf16 q/k/v, fp32 state",
+                   "us_per_step": d_step_ms * 1e3, "state_gbps": d_gbs_state,
+                   "roofline": {"bound": "hbm", "achieved": d_gbs_kernel, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": d_gbs_kernel / HBM_PEAK_GBS,
+                                "traffic": measured_traffic("kda_decode"),
+                                "kernel_us": d_kern_ms * 1e3, "algorithmic_bytes": state_bytes + io_bytes}},
+        "parity": {"pass": parity_ok, "tol_rel_rms": TOL_REL, "prefill_o": e_o, "prefill_S_T": e_s,
+                   "prefill_heads": heads, "decode_o": e_do, "decode_S": e_ds, "decode_states": dheads},
+        "cpu_baseline": cpu,
+        "device": props.name,
+        "source_hash": source_hash(),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+if __name__ == "__main__":
+    main()

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
+#include <string.h>
 
 #include "../../include/kda.h"
 #include "kda_launch.h"
@@ -39,16 +40,27 @@ bool sizes_ok(long long B, long long T, long long H, long long dk, long long dv)
   return true;
 }
 
-// Number of state columns per prefill workgroup: the widest slab that still
-// gives at least one workgroup per compute unit (256), else 16.
-int choose_slab(int B, int H, int dv, int io_dtype) {
-  const char* env = getenv("KDA_PREFILL_SLAB");  // tuning override
-  if (env) {
+// Prefill kernel choice.  The 32x32-tile kernel (32 state columns per
+// workgroup) serves bf16 q/k/v with d_k in {64,128} and chunk 64; the 16x16-tile
+// kernel serves everything else, with 16 columns per workgroup unless 32-column
+// slabs still give one workgroup per compute unit.  KDA_PREFILL_SLAB=16 or 32
+// overrides the slab width (16 always selects the 16x16-tile kernel).
+struct PrefillPlan {
+  bool tiles32;
+  int slab;
+};
+PrefillPlan plan_prefill(int B, int H, int dk, int dv, int chunk, int io) {
+  int forced = 0;
+  if (const char* env = getenv("KDA_PREFILL_SLAB")) {
     const int s = atoi(env);
-    if ((s == 16 || s == 32) && dv % s == 0) return s;
+    if ((s == 16 || s == 32) && dv % s == 0) forced = s;
   }
-  if (io_dtype == KDA_BF16 && dv % 32 == 0 && (long long)B * H * (dv / 32) >= 256) return 32;
-  return 16;
+  const char* impl = getenv("KDA_PREFILL_IMPL");
+  const bool tiles32 = impl && strcmp(impl, "tiles32") == 0;  // not yet the default
+  if (tiles32 && forced != 16 && kda::prefill32_supported(io, dk, dv, chunk)) return {true, 32};
+  if (forced) return {false, forced};
+  if (io == 1 && dv % 32 == 0 && (long long)B * H * (dv / 32) >= 256) return {false, 32};
+  return {false, 16};
 }
 
 }  // namespace
@@ -88,8 +100,8 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, kda_dtype 
   for (const void* ptr : ptrs)
     if (ptr && !aligned16(ptr)) return KDA_ERR_MISALIGNED;
   const int io = (qkv_dtype == KDA_BF16) ? 1 : 0;
-  const int slab = choose_slab(B, H, d_v, qkv_dtype);
-  if (!kda::prefill_supported(io, d_k, chunk, slab)) return KDA_ERR_UNSUPPORTED;
+  const PrefillPlan plan = plan_prefill(B, H, d_k, d_v, chunk, io);
+  if (!plan.tiles32 && !kda::prefill_supported(io, d_k, chunk, plan.slab)) return KDA_ERR_UNSUPPORTED;
 
   const size_t esz = (qkv_dtype == KDA_BF16) ? 2 : 4;
   const size_t osz = (o_dtype == KDA_BF16) ? 2 : 4;
@@ -115,7 +127,8 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, kda_dtype 
   }
 
   kda::PrefillParams p{q, k, v, alpha, beta, S0, o, S_T, B, T, H, d_k, d_v, o_dtype == KDA_F32 ? 1 : 0};
-  const hipError_t e = kda::launch_prefill(p, io, chunk, slab, static_cast<hipStream_t>(stream));
+  const hipError_t e = plan.tiles32 ? kda::launch_prefill32(p, static_cast<hipStream_t>(stream))
+                                    : kda::launch_prefill(p, io, chunk, plan.slab, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     g_last_hip_error = (int)e;
     return KDA_ERR_HIP;

@@ -39,6 +39,11 @@
 #include "kda_device.h"
 #include "kda_launch.h"
 
+// Phase boundary hook for external instrumentation builds; compiles to nothing here.
+#ifndef KDA_PHASE_MARK
+#define KDA_PHASE_MARK(i)
+#endif
+
 namespace kda {
 namespace {
 
@@ -541,15 +546,21 @@ __device__ bool process_chunk(Smem<C>& sm, Raw<C>& raw, f32x4 (&S)[C::NKT], cons
 #pragma unroll
   for (int hh = 0; hh < C::NH; ++hh) {
     block_sync_lds();
+    KDA_PHASE_MARK(0);
     if (phase_scan<C>(sm, raw, hh, lo, hi, check, tid)) return false;
     if (hh == C::NH - 1 && prefetch_t0 >= 0) load_raw<C>(raw, cx, prefetch_t0, tid);
     block_sync_lds();
+    KDA_PHASE_MARK(1);
     phase_lp<C>(sm, acc, wave, lane, blo, bhi);
+    KDA_PHASE_MARK(2);
   }
   lp_epilogue<C>(sm, acc, wave, lane);
   block_sync_lds();
+  KDA_PHASE_MARK(3);
   phase_solve<C>(sm, tid, wave, lane);
+  KDA_PHASE_MARK(4);
   if (wave < C::NSW) phase_state<C>(sm, S, wave, lane, cx, t0, lo, hi);
+  KDA_PHASE_MARK(5);
   return true;
 }
 

@@ -145,10 +145,16 @@ def forward(q, k, v, alpha, beta, S0=None, *, heads=None, order="page1",
     st = np.zeros((n_sel, dk, dv), np.float64) if want_state else None
     ordc = {"page1": ORDER_PAGE1, "literal_p2": ORDER_LITERAL_P2}[order]
     mut = 0 if mutation is None else MUTATIONS[mutation]
+    threads = int(threads or default_threads())
+    if col_block is None:
+        # independent state columns: split them when there are fewer heads than threads
+        col_block = dv
+        while n_sel * -(-dv // col_block) < 2 * threads and col_block > 8:
+            col_block //= 2
     rc = _load().kda_oracle_forward(
         _ptr(qa), _ptr(ka), _ptr(va), qd, _ptr(aa), ad, _ptr(ba), bd, _ptr(sa), sd,
         _ptr(o), _ptr(st), B, T, H, dk, dv, _ptr(harr), n_sel,
-        int(col_block or 0), ordc, mut, int(threads or default_threads()))
+        int(col_block), ordc, mut, threads)
     if rc != 0:
         raise ValueError("oracle: kda_oracle_forward rejected its arguments")
     return o, st

@@ -1,0 +1,122 @@
+"""Parity at the operator's full workload sizes (the configuration bench.py times).
+
+* prefill 4K:  B=1, H=8,  T=4096     - every head, o and S_T
+* prefill 64K: B=2, H=32, T=65536    - S_T of every head, o of 8 sampled heads
+* prefill 1M:  B=1, H=32, T=1048576  - S_T of every head, o of 4 sampled heads
+                                       (alpha = sigmoid(N(4,1)), long retention)
+* decode:      B=256, H=32, d=128    - 100 in-place steps; o at every step and
+                                       the final S for every state
+Tolerance: max |gpu - oracle| / RMS(oracle) <= 2e-2 per head (bf16 q/k/v, fp32
+state and output).  The oracle reads the exact device inputs.
+"""
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_07_amd as kda
+import kda_inputs as ki
+import oracle
+from kda_check import TOL_BF16_REL, gpu_o_heads, gpu_s_heads, log, rel_err_per_head
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_gpu(inp, chunk=64):
+    o, st = kda.kda_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["S0"], chunk=chunk)
+    torch.cuda.synchronize()
+    return o, st
+
+
+def _oracle_batches(host, heads, want_o, batch, label):
+    """Oracle over `heads` in batches (progress printed per batch)."""
+    outs_o, outs_s = [], []
+    t0 = time.time()
+    for i in range(0, len(heads), batch):
+        hb = heads[i:i + batch]
+        ro, rs = oracle.forward(host["q"], host["k"], host["v"], host["alpha"], host["beta"], host["S0"],
+                                heads=hb, want_o=want_o)
+        outs_s.append(rs)
+        if want_o:
+            outs_o.append(ro)
+        log(f"  {label}: oracle heads {hb[0]}..{hb[-1]} done ({time.time() - t0:.0f} s)")
+    return (np.concatenate(outs_o) if want_o else None), np.concatenate(outs_s)
+
+
+def _check(name, got, ref):
+    e = rel_err_per_head(got, ref)
+    log(f"  {name}: max|err|/RMS = {e:.3e} (tol {TOL_BF16_REL})")
+    assert e <= TOL_BF16_REL, f"{name}: {e:.3e}"
+
+
+@pytest.mark.timeout(300)
+def test_prefill_4k_all_heads(gpu):
+    inp = ki.make_workload_prefill(1, seed=0, device=gpu)
+    o, st = _run_gpu(inp)
+    host = {k: v.cpu() for k, v in inp.items()}
+    ro, rs = oracle.forward(host["q"], host["k"], host["v"], host["alpha"], host["beta"], host["S0"])
+    _check("4k o", gpu_o_heads(o), ro)
+    _check("4k S_T", gpu_s_heads(st), rs)
+
+
+@pytest.mark.timeout(600)
+def test_prefill_64k(gpu):
+    inp = ki.make_workload_prefill(2, seed=0, device=gpu)
+    log("64k: kernel")
+    o, st = _run_gpu(inp)
+    host = {k: v.cpu() for k, v in inp.items()}
+    BH = inp["q"].shape[0] * inp["q"].shape[2]
+    sample = [0, 9, 18, 27, 36, 45, 54, 63]
+    ro, rs = _oracle_batches(host, sample, True, 8, "64k sampled o")
+    _check("64k o (8 heads)", gpu_o_heads(o, sample), ro)
+    _check("64k S_T (8 heads)", gpu_s_heads(st, sample), rs)
+    rest = [h for h in range(BH) if h not in sample]
+    _, rs_all = _oracle_batches(host, rest, False, 16, "64k S_T")
+    _check("64k S_T (all other heads)", gpu_s_heads(st, rest), rs_all)
+
+
+@pytest.mark.timeout(900)
+def test_prefill_1m(gpu):
+    """1M-token context: S_T for all 32 heads, o for 4 sampled heads."""
+    log("1m: generating inputs")
+    inp = ki.make_workload_prefill(3, seed=0, device=gpu)
+    log("1m: kernel")
+    o, st = _run_gpu(inp)
+    sample = [0, 11, 22, 31]
+    o_s = gpu_o_heads(o, sample)
+    s_all = gpu_s_heads(st)
+    del o
+    host = {k: v.cpu() for k, v in inp.items()}
+    del inp
+    torch.cuda.empty_cache()
+    ro, rs = _oracle_batches(host, sample, True, 4, "1m sampled o")
+    _check("1m o (4 heads)", o_s, ro)
+    _check("1m S_T (4 heads)", s_all[sample], rs)
+    del ro
+    rest = [h for h in range(32) if h not in sample]
+    _, rs_all = _oracle_batches(host, rest, False, 4, "1m S_T")
+    _check("1m S_T (other 28 heads)", s_all[rest], rs_all)
+
+
+@pytest.mark.timeout(600)
+def test_decode_b256_100_steps(gpu):
+    w = ki.WORKLOADS[4]
+    B, H, dk, dv = w.B, w.H, w.dk, w.dv
+    S = ki.make_state(B, H, dk, dv, w.s0_std, 1, gpu)
+    S_ref = S.cpu().double().numpy()
+    worst_o = 0.0
+    t0 = time.time()
+    for step in range(w.decode_steps):
+        tok = ki.make_decode_token(B, H, dk, dv, w.qkv_dtype, w.alpha_mu, seed=0, step=step, device=gpu)
+        o = kda.kda_decode_step(tok["q"], tok["k"], tok["v"], tok["alpha"], tok["beta"], S)
+        h = {k: v.cpu() for k, v in tok.items()}
+        o_ref = oracle.decode_step(h["q"], h["k"], h["v"], h["alpha"], h["beta"], S_ref)
+        got = o.cpu().double().numpy().reshape(1, -1)
+        worst_o = max(worst_o, rel_err_per_head(got, o_ref.reshape(1, -1)))
+        if step % 25 == 0:
+            log(f"  decode step {step}: worst o err so far {worst_o:.3e} ({time.time() - t0:.0f} s)")
+    log(f"  decode o over 100 steps: {worst_o:.3e}")
+    assert worst_o <= TOL_BF16_REL
+    _check("decode S (all 8192 states)", S.cpu().double().numpy().reshape(B * H, dk, dv),
+           S_ref.reshape(B * H, dk, dv))
