@@ -98,7 +98,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=100)
-    ap.add_argument("--sample-heads", type=int, default=8, help="heads checked by the oracle")
+    ap.add_argument("--sample-heads", type=int, default=64, help="heads checked by the oracle (all 64 by default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
