@@ -40,13 +40,16 @@ bool sizes_ok(long long B, long long T, long long H, long long dk, long long dv)
   return true;
 }
 
-// Prefill kernel choice.  The 32x32-tile kernel (32 state columns per
-// workgroup) serves bf16 q/k/v with d_k in {64,128} and chunk 64; the 16x16-tile
-// kernel serves everything else, with 16 columns per workgroup unless 32-column
-// slabs still give one workgroup per compute unit.  KDA_PREFILL_SLAB=16 or 32
-// overrides the slab width (16 always selects the 16x16-tile kernel).
+// Prefill kernel choice.  The pipeline kernel serves bf16 q/k/v with d_k in
+// {64,128}, d_v % 32 == 0 and chunk 32 or 64 (it runs 32-token chunks); the
+// generic 16x16-tile kernel serves everything else, with 16 state columns per
+// workgroup unless 32-column slabs still give one workgroup per compute unit.
+// KDA_PREFILL_IMPL=generic or tiles32 selects another kernel where it applies
+// and KDA_PREFILL_SLAB=16 or 32 the generic kernel's slab width (both for tests
+// and measurements).
+enum PrefillImpl { IMPL_GENERIC, IMPL_TILES32, IMPL_PIPE };
 struct PrefillPlan {
-  bool tiles32;
+  PrefillImpl impl;
   int slab;
 };
 PrefillPlan plan_prefill(int B, int H, int dk, int dv, int chunk, int io) {
@@ -56,11 +59,13 @@ PrefillPlan plan_prefill(int B, int H, int dk, int dv, int chunk, int io) {
     if ((s == 16 || s == 32) && dv % s == 0) forced = s;
   }
   const char* impl = getenv("KDA_PREFILL_IMPL");
-  const bool tiles32 = impl && strcmp(impl, "tiles32") == 0;  // not yet the default
-  if (tiles32 && forced != 16 && kda::prefill32_supported(io, dk, dv, chunk)) return {true, 32};
-  if (forced) return {false, forced};
-  if (io == 1 && dv % 32 == 0 && (long long)B * H * (dv / 32) >= 256) return {false, 32};
-  return {false, 16};
+  const bool want_generic = impl && strcmp(impl, "generic") == 0;
+  const bool want_tiles32 = impl && strcmp(impl, "tiles32") == 0;
+  if (want_tiles32 && kda::prefill32_supported(io, dk, dv, chunk, H)) return {IMPL_TILES32, 32};
+  if (!want_generic && !forced && kda::prefill_pipe_supported(io, dk, dv, chunk, H)) return {IMPL_PIPE, 32};
+  if (forced) return {IMPL_GENERIC, forced};
+  if (io == 1 && dv % 32 == 0 && (long long)B * H * (dv / 32) >= 256) return {IMPL_GENERIC, 32};
+  return {IMPL_GENERIC, 16};
 }
 
 }  // namespace
@@ -101,7 +106,7 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, kda_dtype 
     if (ptr && !aligned16(ptr)) return KDA_ERR_MISALIGNED;
   const int io = (qkv_dtype == KDA_BF16) ? 1 : 0;
   const PrefillPlan plan = plan_prefill(B, H, d_k, d_v, chunk, io);
-  if (!plan.tiles32 && !kda::prefill_supported(io, d_k, chunk, plan.slab)) return KDA_ERR_UNSUPPORTED;
+  if (plan.impl == IMPL_GENERIC && !kda::prefill_supported(io, d_k, chunk, plan.slab)) return KDA_ERR_UNSUPPORTED;
 
   const size_t esz = (qkv_dtype == KDA_BF16) ? 2 : 4;
   const size_t osz = (o_dtype == KDA_BF16) ? 2 : 4;
@@ -127,8 +132,10 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, kda_dtype 
   }
 
   kda::PrefillParams p{q, k, v, alpha, beta, S0, o, S_T, B, T, H, d_k, d_v, o_dtype == KDA_F32 ? 1 : 0};
-  const hipError_t e = plan.tiles32 ? kda::launch_prefill32(p, static_cast<hipStream_t>(stream))
-                                    : kda::launch_prefill(p, io, chunk, plan.slab, static_cast<hipStream_t>(stream));
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  const hipError_t e = plan.impl == IMPL_PIPE      ? kda::launch_prefill_pipe(p, hs)
+                       : plan.impl == IMPL_TILES32 ? kda::launch_prefill32(p, hs)
+                                                   : kda::launch_prefill(p, io, chunk, plan.slab, hs);
   if (e != hipSuccess) {
     g_last_hip_error = (int)e;
     return KDA_ERR_HIP;

@@ -102,6 +102,19 @@ __device__ __forceinline__ f16x8 neg8(f16x8 f) {
   return __builtin_bit_cast(f16x8, u);
 }
 
+// Per-lane values routed through an empty asm so address arithmetic built on them
+// is redone inside each loop iteration instead of being hoisted into registers
+// for the whole kernel.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// Raw buffer resource over [base, base + bytes); stores past the end are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, bytes, 0x00020000);
+}
+
 template <class C>
 struct Raw32 {
   f32x4 a[C::TGS];   // alpha, 4 channels per token
@@ -123,38 +136,39 @@ __device__ __forceinline__ void unpack_bf16x4(const u32x2& w, float (&f)[4]) {
   f[3] = __builtin_bit_cast(float, w.y & 0xffff0000u);
 }
 
+// Loads chunk t0's inputs for this thread.  Rows past the sequence end read as
+// zeros (buffer range check); the segment bounds keep them out of the recurrence.
 template <class C>
 __device__ __forceinline__ void load_raw32(Raw32<C>& raw, const Ctx32& cx, int t0, int tid) {
   const PrefillParams& p = cx.p;
-  const int cq = tid % C::NCQ, tg = tid / C::NCQ;
-  // Uniform base of token t0 for this (sequence, head); per-lane offsets stay 32-bit.
-  const size_t row0 = ((size_t)cx.b * p.T + t0) * p.H + cx.h;
-  const float* ab = p.alpha + row0 * C::DK;
-  const __bf16* kb = static_cast<const __bf16*>(p.k) + row0 * C::DK;
-  const __bf16* qb = static_cast<const __bf16*>(p.q) + row0 * C::DK;
-  const int tstride = p.H * C::DK;
-  const int nt = p.T - t0;  // tokens left in the sequence
+  const int cq = opaque(tid % C::NCQ), tg = opaque(tid / C::NCQ);
+  const size_t row0 = ((size_t)cx.b * p.T + t0) * p.H + cx.h;  // token t0 of this (sequence, head)
+  const int rows = min(C::CS, p.T - t0);
+  const int tstride = p.H * C::DK;  // elements between tokens
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(const_cast<float*>(p.alpha) + row0 * C::DK, rows * tstride * 4);
+  const __amdgpu_buffer_rsrc_t rk =
+      make_rsrc(const_cast<__bf16*>(static_cast<const __bf16*>(p.k)) + row0 * C::DK, rows * tstride * 2);
+  const __amdgpu_buffer_rsrc_t rq =
+      make_rsrc(const_cast<__bf16*>(static_cast<const __bf16*>(p.q)) + row0 * C::DK, rows * tstride * 2);
+  const int e0 = tg * C::TGS * tstride + 4 * cq;  // element offset of the thread's first token
 #pragma unroll
   for (int i = 0; i < C::TGS; ++i) {
-    const int t = tg * C::TGS + i;
-    const int off = t * tstride + 4 * cq;
-    if (t < nt) {
-      raw.a[i] = *reinterpret_cast<const f32x4*>(ab + off);
-      raw.k[i] = *reinterpret_cast<const u32x2*>(kb + off);
-      raw.q[i] = *reinterpret_cast<const u32x2*>(qb + off);
-    } else {
-      raw.a[i] = (f32x4)1.0f;
-      raw.k[i] = (u32x2)0u;
-      raw.q[i] = (u32x2)0u;
-    }
+    raw.a[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, 4 * e0, 4 * i * tstride, 0));
+    raw.k[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rk, 2 * e0, 2 * i * tstride, 0));
+    raw.q[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rq, 2 * e0, 2 * i * tstride, 0));
   }
   {
-    const int r = tid / 4;  // 4 threads per V row of 32 bf16
-    const __bf16* vb = static_cast<const __bf16*>(p.v) + row0 * p.dv + cx.col0;
-    if (r < nt) raw.v = *reinterpret_cast<const u32x4*>(vb + r * (p.H * p.dv) + 8 * (tid % 4));
-    else raw.v = (u32x4)0u;
+    const int vstride = p.H * p.dv;
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(
+        const_cast<__bf16*>(static_cast<const __bf16*>(p.v)) + row0 * p.dv + cx.col0, rows * vstride * 2);
+    // 4 threads per V row of 32 bf16
+    raw.v = __builtin_bit_cast(u32x4,
+                               __builtin_amdgcn_raw_buffer_load_b128(rv, 2 * ((tid / 4) * vstride + 8 * (tid % 4)), 0, 0));
   }
-  raw.beta = (tid < C::CS && tid < nt) ? p.beta[row0 + tid * p.H] : 0.0f;
+  {
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(const_cast<float*>(p.beta) + row0, rows * p.H * 4);
+    raw.beta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, 4 * min(tid, C::CS - 1) * p.H, 0, 0));
+  }
 }
 
 // ---- scan: decay products and the fp16 operand matrices ---------------------
@@ -162,6 +176,7 @@ __device__ __forceinline__ void load_raw32(Raw32<C>& raw, const Ctx32& cx, int t
 // (uniformly, writing nothing) if some channel decays below e^{-10} over [lo, hi).
 template <class C>
 __device__ bool scan32(Smem32<C>& sm, const Raw32<C>& raw, int lo, int hi, bool check, int tid) {
+  tid = opaque(tid);
   const int cq = tid % C::NCQ, tg = tid / C::NCQ;
   float lp[C::TGS][4];  // inclusive prefix within the thread's tokens
   float run[4] = {1.0f, 1.0f, 1.0f, 1.0f};
@@ -176,7 +191,9 @@ __device__ bool scan32(Smem32<C>& sm, const Raw32<C>& raw, int lo, int hi, bool 
     }
   }
   *reinterpret_cast<f32x4*>(&sm.tot[tg * C::DK + 4 * cq]) = f32x4{run[0], run[1], run[2], run[3]};
+  KDA_PHASE_MARK(11);
   block_sync_lds();
+  KDA_PHASE_MARK(12);
   float ep[4] = {1.0f, 1.0f, 1.0f, 1.0f}, sp[4] = {1.0f, 1.0f, 1.0f, 1.0f}, gm[4];
 #pragma unroll
   for (int g2 = 0; g2 < C::NTG; ++g2) {
@@ -187,6 +204,7 @@ __device__ bool scan32(Smem32<C>& sm, const Raw32<C>& raw, int lo, int hi, bool 
       if (g2 > tg) sp[e] *= tv[e];
     }
   }
+  KDA_PHASE_MARK(13);
   int steep = 0;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -196,6 +214,7 @@ __device__ bool scan32(Smem32<C>& sm, const Raw32<C>& raw, int lo, int hi, bool 
   if (check) {
     if (__syncthreads_or(steep)) return true;
   }
+  KDA_PHASE_MARK(14);
   float ig[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) ig[e] = sp[e] * __builtin_amdgcn_rcpf(gm[e]);  // prod_{later groups} / e^{G_C}
@@ -239,28 +258,62 @@ __device__ bool scan32(Smem32<C>& sm, const Raw32<C>& raw, int lo, int hi, bool 
   return false;
 }
 
+// P tile (token tile a, column s): keep the lower part including the diagonal.
+template <class C>
+__device__ __forceinline__ void store_p_tile(Smem32<C>& sm, const f32x16& acc, int a, int h, int s) {
+  h16* prow = &sm.p[(32 * a + 4 * h) * C::LDC + spos(s)];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 32 * a + 8 * j + 4 * h + r;
+      prow[(8 * j + r) * C::LDC] = (h16)(t >= s ? acc[4 * j + r] : 0.0f);
+    }
+}
+
 // ---- L = beta K K^T and P = Q K^T (32x32 tiles (a, b), b <= a) -------------
+// wave 0: L00 and P00; wave 1: L10 and P10; wave 2: L11; wave 3: P11.  `wave`
+// is uniform, so the selections below are scalar.
 template <class C>
 __device__ void lp32(Smem32<C>& sm, int wave, int lane) {
-  const int h = lane / 32, m = lane % 32;
-  // wave 0: L00, P00; wave 1: L10, P10; wave 2: L11; wave 3: P11
+  const int h = opaque(lane / 32), m = opaque(lane % 32);
   const int a = (wave == 0) ? 0 : 1;
   const int b = (wave == 1) ? 0 : a;
-  const bool doL = wave != 3, doP = wave != 2;
-  f32x16 accL = (f32x16)0.0f, accP = (f32x16)0.0f;
+  const bool two = wave < 2;
+  const h16* A1 = (wave == 3) ? sm.qg : sm.kg;  // first product: L (P on wave 3)
+  f32x16 acc1 = (f32x16)0.0f, acc2 = (f32x16)0.0f;
+  const h16* brow = &sm.kc[(32 * b + m) * C::LDK + 8 * h];
+  const h16* arow1 = &A1[(32 * a + m) * C::LDK + 8 * h];
+  const h16* arow2 = &sm.qg[(32 * a + m) * C::LDK + 8 * h];
+  if (two) {
 #pragma unroll
-  for (int s = 0; s < C::NKS; ++s) {
-    const int col = 16 * s + 8 * h;
-    const f16x8 B = ld8(&sm.kc[(32 * b + m) * C::LDK + col]);
-    if (doL) accL = mma32(ld8(&sm.kg[(32 * a + m) * C::LDK + col]), B, accL);
-    if (doP) accP = mma32(ld8(&sm.qg[(32 * a + m) * C::LDK + col]), B, accP);
-  }
+    for (int s = 0; s < C::NKS; ++s) {
+      const f16x8 B = ld8(brow + 16 * s);
+      acc1 = mma32(ld8(arow1 + 16 * s), B, acc1);
+      acc2 = mma32(ld8(arow2 + 16 * s), B, acc2);
+    }
+  } else {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int t = 32 * a + 8 * (i / 4) + 4 * h + (i % 4), s = 32 * b + m;
-    if (doL) sm.l[t * C::LDL + s] = t > s ? accL[i] * sm.beta[t] : 0.0f;
-    if (doP) sm.p[t * C::LDC + spos(s)] = (h16)(t >= s ? accP[i] : 0.0f);
+    for (int s = 0; s < C::NKS; ++s) acc1 = mma32(ld8(arow1 + 16 * s), ld8(brow + 16 * s), acc1);
   }
+  KDA_PHASE_MARK(17);
+  // rows t = 32a + 8j + 4h + r hold element 4j + r; column s = 32b + m
+  const int s = 32 * b + m;
+  if (wave != 3) {  // acc1 holds L: keep the strictly lower part, scaled by beta_t
+    float* lrow = &sm.l[(32 * a + 4 * h) * C::LDL + s];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 bt = *reinterpret_cast<const f32x4*>(&sm.beta[32 * a + 8 * j + 4 * h]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 32 * a + 8 * j + 4 * h + r;
+        lrow[(8 * j + r) * C::LDL] = t > s ? acc1[4 * j + r] * bt[r] : 0.0f;
+      }
+    }
+  } else {
+    store_p_tile<C>(sm, acc1, a, h, s);
+  }
+  if (two) store_p_tile<C>(sm, acc2, a, h, s);
 }
 
 // ---- T = (I + L)^{-1} diag(beta) ----------------------------------------------
@@ -270,7 +323,7 @@ __device__ void solve32(Smem32<C>& sm, int wave, int lane) {
   // rows 4qd..4qd+3 of column s of (I + L_aa)^{-1}; forward substitution over u
   // with x[u] broadcast from the lane that owns row u.
   {
-    const int a = wave, s = lane % 16, qd = lane / 16;
+    const int a = wave, s = opaque(lane % 16), qd = opaque(lane / 16);
     const float* Lb = &sm.l[(16 * a + 4 * qd) * C::LDL + 16 * a];
     float x[4];
 #pragma unroll
@@ -298,9 +351,11 @@ __device__ void solve32(Smem32<C>& sm, int wave, int lane) {
       sm.tt[(16 * a + s) * C::LDC + 16 * a + t] = tv;
     }
   }
+  KDA_PHASE_MARK(18);
   block_sync_lds();
+  KDA_PHASE_MARK(19);
   // Off-diagonal blocks: T_ab = -(I+L_aa)^{-1} sum_{c=b}^{a-1} L_ac T_cb (16x16x32 steps).
-  const int g = lane / 16, m = lane % 16;
+  const int g = opaque(lane / 16), m = opaque(lane % 16);
   for (int d = 1; d < 4; ++d) {
     const int a = d + wave;
     if (a < 4) {
@@ -329,7 +384,9 @@ __device__ void solve32(Smem32<C>& sm, int wave, int lane) {
         sm.tt[s * C::LDC + t] = tv;
       }
     }
+    KDA_PHASE_MARK(20);
     block_sync_lds();
+    KDA_PHASE_MARK(21);
   }
 }
 
@@ -341,7 +398,7 @@ __device__ __forceinline__ float vload(const Smem32<C>& sm, int a, int i, int h,
 
 template <class C>
 __device__ void state32(Smem32<C>& sm, f32x16 (&S)[C::NKT], int lane, const Ctx32& cx, int t0, int lo, int hi) {
-  const int h = lane / 32, n = lane % 32;
+  const int h = opaque(lane / 32), n = opaque(lane % 32);
   // per-column power-of-two scale of the values (S, V)
   float mx = 0.0f;
 #pragma unroll
@@ -357,8 +414,9 @@ __device__ void state32(Smem32<C>& sm, f32x16 (&S)[C::NKT], int lane, const Ctx3
   const float scale = __builtin_amdgcn_ldexpf(1.0f, -ex);
   const float unscale = __builtin_amdgcn_ldexpf(1.0f, ex);
 
-  // X = V - KG S (both token tiles share each S fragment)
-  f32x16 X0, X1;
+  // X = V - KG S and O = QG S in one pass over the channels (each S fragment
+  // feeds four products)
+  f32x16 X0, X1, O0 = (f32x16)0.0f, O1 = (f32x16)0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     X0[i] = vload(sm, 0, i, h, n) * scale;
@@ -366,62 +424,75 @@ __device__ void state32(Smem32<C>& sm, f32x16 (&S)[C::NKT], int lane, const Ctx3
   }
 #pragma unroll
   for (int s = 0; s < C::NKS; ++s) {
-    const f16x8 B = neg8(bfrag(S[s / 2], s % 2, scale));
+    const f16x8 B = bfrag(S[s / 2], s % 2, scale);
+    const f16x8 nB = neg8(B);
     const int col = 16 * s + 8 * h;
-    X0 = mma32(ld8(&sm.kg[n * C::LDK + col]), B, X0);
-    X1 = mma32(ld8(&sm.kg[(32 + n) * C::LDK + col]), B, X1);
+    X0 = mma32(ld8(&sm.kg[n * C::LDK + col]), nB, X0);
+    X1 = mma32(ld8(&sm.kg[(32 + n) * C::LDK + col]), nB, X1);
+    O0 = mma32(ld8(&sm.qg[n * C::LDK + col]), B, O0);
+    O1 = mma32(ld8(&sm.qg[(32 + n) * C::LDK + col]), B, O1);
   }
+  KDA_PHASE_MARK(8);
   const f16x8 xf0 = bfrag(X0, 0, 1.0f), xf1 = bfrag(X0, 1, 1.0f);
   const f16x8 xf2 = bfrag(X1, 0, 1.0f), xf3 = bfrag(X1, 1, 1.0f);
   // U = T X (T lower triangular: token tile 0 needs steps 0-1, tile 1 steps 0-3)
   f32x16 U0 = (f32x16)0.0f, U1 = (f32x16)0.0f;
   U0 = mma32(ld8(&sm.t[n * C::LDC + 8 * h]), xf0, U0);
-  U0 = mma32(ld8(&sm.t[n * C::LDC + 16 + 8 * h]), xf1, U0);
   U1 = mma32(ld8(&sm.t[(32 + n) * C::LDC + 8 * h]), xf0, U1);
+  U0 = mma32(ld8(&sm.t[n * C::LDC + 16 + 8 * h]), xf1, U0);
   U1 = mma32(ld8(&sm.t[(32 + n) * C::LDC + 16 + 8 * h]), xf1, U1);
   U1 = mma32(ld8(&sm.t[(32 + n) * C::LDC + 32 + 8 * h]), xf2, U1);
   U1 = mma32(ld8(&sm.t[(32 + n) * C::LDC + 48 + 8 * h]), xf3, U1);
   const f16x8 uf0 = bfrag(U0, 0, 1.0f), uf1 = bfrag(U0, 1, 1.0f);
   const f16x8 uf2 = bfrag(U1, 0, 1.0f), uf3 = bfrag(U1, 1, 1.0f);
-  // O = QG S + P U
-  f32x16 O0 = (f32x16)0.0f, O1 = (f32x16)0.0f;
-#pragma unroll
-  for (int s = 0; s < C::NKS; ++s) {
-    const f16x8 B = bfrag(S[s / 2], s % 2, scale);
-    const int col = 16 * s + 8 * h;
-    O0 = mma32(ld8(&sm.qg[n * C::LDK + col]), B, O0);
-    O1 = mma32(ld8(&sm.qg[(32 + n) * C::LDK + col]), B, O1);
-  }
+  KDA_PHASE_MARK(9);
+  // O += P U
   O0 = mma32(ld8(&sm.p[n * C::LDC + 8 * h]), uf0, O0);
-  O0 = mma32(ld8(&sm.p[n * C::LDC + 16 + 8 * h]), uf1, O0);
   O1 = mma32(ld8(&sm.p[(32 + n) * C::LDC + 8 * h]), uf0, O1);
+  O0 = mma32(ld8(&sm.p[n * C::LDC + 16 + 8 * h]), uf1, O0);
   O1 = mma32(ld8(&sm.p[(32 + n) * C::LDC + 16 + 8 * h]), uf1, O1);
   O1 = mma32(ld8(&sm.p[(32 + n) * C::LDC + 32 + 8 * h]), uf2, O1);
   O1 = mma32(ld8(&sm.p[(32 + n) * C::LDC + 48 + 8 * h]), uf3, O1);
-  const bool full = lo == 0 && hi == C::CS && t0 + C::CS <= cx.p.T;
-  const int rstride = cx.p.H * cx.p.dv;
-  const size_t obase = (((size_t)cx.b * cx.p.T + t0) * cx.p.H + cx.h) * cx.p.dv + cx.col0;
-  if (full && cx.p.o_f32) {
-    float* ob = static_cast<float*>(cx.p.o) + obase;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int t = 8 * (i / 4) + 4 * h + (i % 4);
-      ob[t * rstride + n] = O0[i] * unscale;
-      ob[(32 + t) * rstride + n] = O1[i] * unscale;
-    }
-  } else {
+  {
+    // rows of this chunk in o: [t0, t0 + rows); row t of the chunk, column n at
+    // byte t*rs + 4n (fp32) or 2n (bf16); rows outside [lo, hi) are masked by an
+    // out-of-range offset, rows past the sequence end by the resource size
+    const int rows = min(C::CS, cx.p.T - t0);
+    const int esz = cx.p.o_f32 ? 4 : 2;
+    const int rs = cx.p.H * cx.p.dv * esz;
+    char* ob = static_cast<char*>(cx.p.o) +
+               ((((size_t)cx.b * cx.p.T + t0) * cx.p.H + cx.h) * cx.p.dv + cx.col0) * esz;
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(ob, rows * rs);
+    const int vbase = 4 * h * rs + n * esz;
+    int voff[2][16];
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int t = 32 * a + 8 * (i / 4) + 4 * h + (i % 4);
-        if (t >= lo && t < hi && t0 + t < cx.p.T) {
-          const float ov = (a ? O1[i] : O0[i]) * unscale;
-          if (cx.p.o_f32) static_cast<float*>(cx.p.o)[obase + t * rstride + n] = ov;
-          else static_cast<__bf16*>(cx.p.o)[obase + t * rstride + n] = (__bf16)ov;
-        }
+        const int t = 32 * a + 8 * (i / 4) + (i % 4) + 4 * h;
+        voff[a][i] = vbase + ((unsigned)(t - lo) < (unsigned)(hi - lo) ? 0 : 0x40000000);
       }
+    if (cx.p.o_f32) {
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int tr = 32 * a + 8 * (i / 4) + (i % 4);  // row without the half-wave term
+          const float ov = (a ? O1[i] : O0[i]) * unscale;
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, ov), rsrc, voff[a][i], tr * rs, 0);
+        }
+    } else {
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int tr = 32 * a + 8 * (i / 4) + (i % 4);
+          const float ov = (a ? O1[i] : O0[i]) * unscale;
+          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (__bf16)ov), rsrc, voff[a][i], tr * rs, 0);
+        }
+    }
   }
+  KDA_PHASE_MARK(10);
   // S' = Diag(e^{G_C}) (S + KC^T U)
 #pragma unroll
   for (int ct = 0; ct < C::NKT; ++ct) {
@@ -448,7 +519,9 @@ __device__ bool prep_segment(Smem32<C>& sm, Raw32<C>& raw, const Ctx32& cx, int 
   block_sync_lds();  // B0
   KDA_PHASE_MARK(0);
   if (scan32<C>(sm, raw, lo, hi, check, ptid)) return false;  // B1, B2 inside
+  KDA_PHASE_MARK(15);
   if (prefetch_t0 >= 0) load_raw32<C>(raw, cx, prefetch_t0, ptid);
+  KDA_PHASE_MARK(16);
   block_sync_lds();  // B3
   KDA_PHASE_MARK(1);
   lp32<C>(sm, pwave, lane);
@@ -479,7 +552,8 @@ __device__ bool state_segment(Smem32<C>& sm, f32x16 (&S)[C::NKT], const Ctx32& c
 template <class C>
 __global__ __launch_bounds__(320, 1) void kda_prefill32_kernel(PrefillParams p) {
   __shared__ Smem32<C> sm;
-  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+  const int tid = threadIdx.x, lane = tid % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);  // uniform: scalar branches
   const int nslab = p.dv / C::J;
   const int Gn = gridDim.x;
   int lid = blockIdx.x;
@@ -503,16 +577,21 @@ __global__ __launch_bounds__(320, 1) void kda_prefill32_kernel(PrefillParams p) 
     f32x16 S[C::NKT];
     const size_t sbase = (size_t)cx.bh * C::DK * p.dv + cx.col0;
 #pragma unroll
-    for (int ct = 0; ct < C::NKT; ++ct)
+    for (int ct = 0; ct < C::NKT; ++ct) S[ct] = (f32x16)0.0f;
+    if (p.S0) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int c = 32 * ct + 8 * (i / 4) + 4 * h + (i % 4);
-        S[ct][i] = p.S0 ? p.S0[sbase + c * p.dv + n] : 0.0f;
-      }
+      for (int ct = 0; ct < C::NKT; ++ct)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int c = 32 * ct + 8 * (i / 4) + 4 * h + (i % 4);
+          S[ct][i] = p.S0[sbase + c * p.dv + n];
+        }
+    }
     for (int c = 0; c < nchunks; ++c) {
+      const int cend = min(C::CS, p.T - c * C::CS);
       int lo = 0, size = C::CS;
-      while (lo < C::CS) {
-        const int hi = lo + size;
+      while (lo < cend) {
+        const int hi = min(lo + size, cend);
         if (!state_segment<C>(sm, S, cx, c * C::CS, lo, hi, size > 2, lane)) {
           size = (size == C::CS) ? 16 : 2;
           continue;
@@ -536,10 +615,11 @@ __global__ __launch_bounds__(320, 1) void kda_prefill32_kernel(PrefillParams p) 
     if (nchunks > 0) load_raw32<C>(raw, cx, 0, ptid);
     for (int c = 0; c < nchunks; ++c) {
       const int next = (c + 1 < nchunks) ? (c + 1) * C::CS : -1;
+      const int cend = min(C::CS, p.T - c * C::CS);
       int lo = 0, size = C::CS;
-      while (lo < C::CS) {
-        const int hi = lo + size;
-        if (!prep_segment<C>(sm, raw, cx, lo, hi, size > 2, hi == C::CS ? next : -1, ptid, pwave, lane)) {
+      while (lo < cend) {
+        const int hi = min(lo + size, cend);
+        if (!prep_segment<C>(sm, raw, cx, lo, hi, size > 2, hi == cend ? next : -1, ptid, pwave, lane)) {
           size = (size == C::CS) ? 16 : 2;
           continue;
         }
@@ -560,8 +640,10 @@ hipError_t launch32(const PrefillParams& p, hipStream_t s) {
 
 }  // namespace
 
-bool prefill32_supported(int io_dtype, int dk, int dv, int chunk) {
-  return io_dtype == 1 && (dk == 64 || dk == 128) && dv % 32 == 0 && chunk == 64;
+bool prefill32_supported(int io_dtype, int dk, int dv, int chunk, int H) {
+  // per-chunk buffer ranges (64 tokens of every head) must fit 31 bits
+  const long long chunk_bytes = 64LL * H * (dk > dv ? dk : dv) * 4;
+  return io_dtype == 1 && (dk == 64 || dk == 128) && dv % 32 == 0 && chunk == 64 && chunk_bytes < (1LL << 31);
 }
 
 hipError_t launch_prefill32(const PrefillParams& p, hipStream_t s) {

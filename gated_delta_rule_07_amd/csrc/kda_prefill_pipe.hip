@@ -1,0 +1,730 @@
+// KDA prefill as a warp-specialised pipeline (gfx950): bf16 q/k/v, d_k in
+// {64, 128}, 32 state columns per workgroup, 32-token chunks.
+//
+// Method: the chunkwise form of the recurrence (the "Kimi 모델 분석" write-up on
+// rlaope.github.io, chunkwise/WY section; the per-token rule is section 3.2 of the
+// "Kimi K3 Technical Report review" on jw9603.github.io).  With decay products
+// taken from the start of the chunk (pre_t = prod_{s<=t} alpha_s per channel,
+// gamma = pre at the chunk end):
+//
+//   KG = K o pre   QG = Q o pre   KC = K o pre^{-1}   KH = K o (gamma / pre)
+//   L  = strict_tril(diag(beta) KG KC^T)      P = tril(QG KC^T)
+//   T  = (I + L)^{-1} diag(beta)
+//   U  = T (V - KG S)      O = QG S + P U      S' = Diag(gamma) S + KH^T U
+//
+// Eight waves per workgroup, each with one job, advance together one pipeline
+// step per barrier; a step moves every item (a chunk, or a segment of one)
+// forward by one stage:
+//
+//   waves 4-7  scan   item n+2: decay products, KG/QG/KC/KH, V, beta, gamma
+//   wave 1     L,T    item n+1: L = beta KG KC^T, then T = (I+L)^{-1} diag(beta)
+//   wave 2     P      item n+1: P = QG KC^T
+//   wave 0     state  item n:   U = T (V - KG S), S' (the only serial chain)
+//   wave 3     output item n:   QG S;  item n-1: + P U, store O
+//
+// Stage outputs live in LDS rings indexed by item number.  Products run on the
+// 32x32x16 fp16 matrix cores with fp32 accumulation; the state itself stays
+// fp32 in registers and is rounded to fp16 (times a power-of-two scale per state
+// column) only as an operand.  KG, QG and KH are bounded by |k|, |q|; KC grows
+// as 1/pre, so an item whose decay falls below e^{-10} in some channel, or whose
+// KC would leave fp16 range, is redone as 16-token and then 2-token segments
+// (alpha >= e^{-5}, the lower bound in section 3.5 of the technical report
+// review, keeps any 2 tokens within range); this regrouping is exact.
+//
+// Sign conventions that save negations: the scan stores -KH, the P wave stores
+// -P, and the state wave computes Xn = KG S - V = -(V - KG S), so Un = T Xn = -U,
+// S' = gamma S + (-KH)^T Un and O = QG S + (-P) Un.
+#include "kda_device.h"
+#include "kda_launch.h"
+
+#ifndef KDA_PHASE_MARK
+#define KDA_PHASE_MARK(i)
+#endif
+#ifndef KDA_STEP_MARK
+#define KDA_STEP_MARK(i, step)
+#endif
+#ifndef KDA_PROBE_VMWAIT
+#define KDA_PROBE_VMWAIT()
+#endif
+
+namespace kda {
+namespace {
+
+typedef _Float16 h16;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int CS = 32;  // tokens per chunk
+constexpr int J = 32;   // state columns per workgroup
+constexpr int NT = 512; // 8 waves
+constexpr float STEEP = 4.5399930e-05f;  // e^{-10}
+
+template <int DK_>
+struct Cfg4 {
+  static constexpr int DK = DK_;
+  static constexpr int NKT = DK / 32;   // 32-row channel tiles of S
+  static constexpr int NKS = DK / 16;   // 16-channel reduction steps
+  static constexpr int LDK = DK + 8;    // fp16 [token][channel] row stride
+  static constexpr int LDC = CS + 8;    // fp16 [row][token] row stride
+  static constexpr int LDL = CS + 4;    // fp32 L^T row stride
+  static constexpr int LDB = 16 + 8;    // fp16 16x16 scratch row stride
+  static constexpr int CPW = DK / 4;    // channels per scan wave
+  static constexpr int PPW = CPW / 2;   // channel pairs per scan wave (one per lane)
+  static constexpr int TQ = 64 / PPW;   // token groups per channel pair
+  static constexpr int TPL = CS / TQ;   // tokens per scan lane
+  static_assert(TPL % 4 == 0, "scan layout");
+};
+
+// Storage column of logical column c: the four quads of each 16-column group are
+// stored in the order {0, 2, 1, 3}.  A 16-byte read at offset 8h of a group then
+// holds logical columns {4h..4h+3, 8+4h..8+4h+3}: the reduction indices a
+// 32x32x16 B operand built from a C tile in registers carries.
+__device__ __forceinline__ int spos(int c) {
+  const int q = (c >> 2) & 3;
+  return (c & ~15) | (((q & 1) << 1 | (q >> 1)) << 2) | (c & 3);
+}
+
+template <class C>
+struct ScanSlot {
+  alignas(16) h16 kg[CS * C::LDK];    // KG      [t][spos(c)]
+  alignas(16) h16 qg[CS * C::LDK];    // QG      [t][spos(c)]
+  alignas(16) h16 kh[C::DK * C::LDC]; // -KH^T   [c][spos(t)]
+  alignas(16) __bf16 v[CS * J];       // V slab  [t][j]
+  alignas(16) float gam[C::DK];       // gamma per channel
+  alignas(16) float beta[CS];         // beta (0 outside the item's segment)
+};
+
+template <class C>
+struct Smem4 {
+  ScanSlot<C> ss[3];
+  alignas(16) h16 kc[2][CS * C::LDK];      // KC [t][spos(c)]
+  alignas(16) h16 t[2][CS * C::LDC];       // T  [t][spos(s)]
+  alignas(16) h16 p[3][CS * C::LDC];       // -P [t][spos(s)]
+  alignas(16) h16 sf[2][C::NKS * 64 * 8];  // scaled S as B fragments [step][lane][8]
+  alignas(16) float sexp[2][J];            // 2^e of each column's scale
+  alignas(16) h16 uf[2][2 * 64 * 8];       // Un as B fragments [step][lane][8]
+  alignas(16) float lt[CS * C::LDL];       // L^T (beta folded) [s][t]
+  alignas(16) h16 dt[2][16 * C::LDB];      // diagonal blocks of (I+L)^{-1}, [s][t]
+  alignas(16) h16 dr[16 * C::LDB];         // second diagonal block, [t][s]
+  alignas(16) float xch[4][2][64];         // scan: token-group totals per wave
+  alignas(16) int flags[2][4];             // scan: regroup votes per wave
+};
+
+__device__ __forceinline__ void block_sync_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ f32x16 mma32(const f16x8& a, const f16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f16x8 ld8(const h16* p) { return *reinterpret_cast<const f16x8*>(p); }
+
+// fp16 B operand from one 16-row half of a 32x32 C tile.
+__device__ __forceinline__ f16x8 bfrag(const f32x16& t, int half) {
+  f16x8 f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = (h16)t[8 * half + e];
+  return f;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+// ---- the item sequence ---------------------------------------------------------
+// An item is the token range [lo, hi) of chunk c (tokens of the chunk outside it
+// act as identity steps).  Every wave advances the same sequence from the same
+// regroup votes, so all agree on every stage's item.
+struct Item {
+  int seq;  // < 0: no item
+  int c, lo, hi, size;
+};
+
+__device__ __forceinline__ int chunk_end(int c, int T) { return min(CS, T - c * CS); }
+
+__device__ __forceinline__ Item next_item(const Item& it, int T, int nchunks) {
+  Item n = it;
+  n.seq = it.seq + 1;
+  n.lo = it.hi;
+  if (n.lo >= chunk_end(it.c, T)) {
+    n.c = it.c + 1;
+    n.lo = 0;
+    n.size = CS;
+    if (n.c >= nchunks) n.seq = -1;
+  } else if (it.size == 2 && (n.lo & 15) == 0) {
+    n.size = 16;
+  }
+  n.hi = min(n.lo + n.size, chunk_end(n.c, T));
+  return n;
+}
+
+__device__ __forceinline__ Item split_item(const Item& it, int T) {
+  Item n = it;
+  n.size = (it.size == CS) ? 16 : 2;
+  n.hi = min(it.lo + n.size, chunk_end(it.c, T));
+  return n;
+}
+
+struct Ctx4 {
+  PrefillParams p;
+  int bh, b, h, col0, nchunks;
+};
+
+// ---- scan waves --------------------------------------------------------------------
+template <class C>
+struct Raw4 {
+  float a[C::TPL][2];  // alpha of this lane's channel pair, per token
+  uint32_t k[C::TPL];  // 2 bf16
+  uint32_t q[C::TPL];
+  u32x2 v;             // 4 bf16 of the V slab
+  float beta;
+};
+
+// Loads chunk c's inputs for scan lane (sw, lane): channels 2cp, 2cp+1 of the
+// wave's slice, tokens tq*TPL ..  Rows past the sequence end read as zeros
+// (buffer range check).
+template <class C>
+__device__ void load_raw4(Raw4<C>& raw, const Ctx4& cx, int c, int sw, int lane) {
+  const PrefillParams& p = cx.p;
+  const int cp = opaque(lane % C::PPW), tq = opaque(lane / C::PPW);
+  const int t0 = c * CS;
+  const int rows = min(CS, p.T - t0);
+  const size_t row0 = ((size_t)cx.b * p.T + t0) * p.H + cx.h;
+  const int ts = p.H * C::DK;  // elements between tokens
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.alpha + row0 * C::DK, rows * ts * 4);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(static_cast<const __bf16*>(p.k) + row0 * C::DK, rows * ts * 2);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(static_cast<const __bf16*>(p.q) + row0 * C::DK, rows * ts * 2);
+  const int e0 = tq * C::TPL * ts + C::CPW * sw + 2 * cp;
+#pragma unroll
+  for (int i = 0; i < C::TPL; ++i) {
+    // Reinterpret the loaded vector as a whole: taking single elements of the
+    // integer vector a buffer load returns and reinterpreting them as float is
+    // miscompiled by this toolchain (both read one narrowed dword).
+    const f32x2 w = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(ra, 4 * e0, 4 * i * ts, 0));
+    raw.a[i][0] = w.x;
+    raw.a[i][1] = w.y;
+    raw.k[i] = __builtin_amdgcn_raw_buffer_load_b32(rk, 2 * e0, 2 * i * ts, 0);
+    raw.q[i] = __builtin_amdgcn_raw_buffer_load_b32(rq, 2 * e0, 2 * i * ts, 0);
+  }
+  const int st = opaque(64 * sw + lane);  // 256 scan lanes: V row st/8, columns 4(st%8)..+3
+  const int vs = p.H * p.dv;
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(static_cast<const __bf16*>(p.v) + row0 * p.dv + cx.col0, rows * vs * 2);
+  raw.v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, 2 * ((st / 8) * vs + 4 * (st % 8)), 0, 0));
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.beta + row0, rows * p.H * 4);
+  raw.beta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, 4 * (st % CS) * p.H, 0, 0));
+}
+
+// Scan of item `it` by scan wave sw (one channel pair and TPL consecutive tokens
+// per lane): writes ring slot it.seq % 3, KC slot it.seq % 2 and this wave's
+// regroup vote.  FULL: the item is the whole chunk (no token is masked).
+template <class C, bool FULL>
+__device__ void scan4_body(Smem4<C>& sm, const Raw4<C>& raw, const Item& it, int sw, int lane, int par) {
+  ScanSlot<C>& sl = sm.ss[it.seq % 3];
+  h16* kc = sm.kc[it.seq % 2];
+  const int cp = opaque(lane % C::PPW), tq = opaque(lane / C::PPW);
+  const int ch = C::CPW * sw + 2 * cp;  // this lane's first channel
+  const int tb = tq * C::TPL;           // first of this lane's tokens
+  const int lo = it.lo, hi = it.hi;
+  auto in = [&](int i) { return FULL || (tb + i >= lo && tb + i < hi); };
+
+  float a[C::TPL][2];
+  float gt[2] = {1.0f, 1.0f};
+#pragma unroll
+  for (int i = 0; i < C::TPL; ++i)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      a[i][e] = in(i) ? raw.a[i][e] : 1.0f;
+      gt[e] *= a[i][e];
+    }
+  // products of the pair's other token groups
+  sm.xch[sw][0][lane] = gt[0];
+  sm.xch[sw][1][lane] = gt[1];
+  wave_lds_sync();
+  float ep[2] = {1.0f, 1.0f}, sp[2] = {1.0f, 1.0f};
+#pragma unroll
+  for (int g = 0; g < C::TQ; ++g)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const float tv = sm.xch[sw][e][g * C::PPW + cp];
+      ep[e] *= (g < tq) ? tv : 1.0f;
+      sp[e] *= (g > tq) ? tv : 1.0f;
+    }
+  float gam[2], rg[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    gam[e] = ep[e] * gt[e] * sp[e];
+    rg[e] = __builtin_amdgcn_rcpf(gam[e]);
+  }
+  // pre_t (prefix through t) and -gamma/pre_t (minus the suffix after t)
+  float pre[C::TPL][2], ns[C::TPL][2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    float run = ep[e];
+#pragma unroll
+    for (int i = 0; i < C::TPL; ++i) {
+      run *= a[i][e];
+      pre[i][e] = run;
+    }
+    float s = -sp[e];
+#pragma unroll
+    for (int i = C::TPL - 1; i >= 0; --i) {
+      ns[i][e] = s;
+      s *= a[i][e];
+    }
+  }
+  float kmax = 0.0f;
+  h16 khv[2][C::TPL];
+  const int col = spos(ch);
+#pragma unroll
+  for (int i = 0; i < C::TPL; ++i) {
+    const float kf[2] = {in(i) ? __builtin_bit_cast(float, raw.k[i] << 16) : 0.0f,
+                         in(i) ? __builtin_bit_cast(float, raw.k[i] & 0xffff0000u) : 0.0f};
+    const float qf[2] = {in(i) ? __builtin_bit_cast(float, raw.q[i] << 16) : 0.0f,
+                         in(i) ? __builtin_bit_cast(float, raw.q[i] & 0xffff0000u) : 0.0f};
+    f16x2 kg2, qg2, kc2;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      kmax = fmaxf(kmax, fabsf(kf[e]));
+      kg2[e] = (h16)(kf[e] * pre[i][e]);
+      qg2[e] = (h16)(qf[e] * pre[i][e]);
+      const float kh = kf[e] * ns[i][e];  // -KH
+      khv[e][i] = (h16)kh;
+      kc2[e] = (h16)(kh * -rg[e]);        // KC = KH / gamma
+    }
+    const int r = (tb + i) * C::LDK + col;
+    *reinterpret_cast<f16x2*>(&sl.kg[r]) = kg2;
+    *reinterpret_cast<f16x2*>(&sl.qg[r]) = qg2;
+    *reinterpret_cast<f16x2*>(&kc[r]) = kc2;
+  }
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+#pragma unroll
+    for (int j = 0; j < C::TPL / 4; ++j)
+      *reinterpret_cast<f16x4*>(&sl.kh[(ch + e) * C::LDC + spos(tb + 4 * j)]) =
+          f16x4{khv[e][4 * j], khv[e][4 * j + 1], khv[e][4 * j + 2], khv[e][4 * j + 3]};
+  if (tq == 0) *reinterpret_cast<float2*>(&sl.gam[ch]) = float2{gam[0], gam[1]};
+  const int st = 64 * sw + lane;
+  *reinterpret_cast<u32x2*>(&sl.v[(st / 8) * J + 4 * (st % 8)]) = raw.v;
+  if (st < CS) sl.beta[st] = (FULL || (st >= lo && st < hi)) ? raw.beta : 0.0f;
+  // regroup when some channel decays below e^{-10} or KC would leave fp16 range
+  const float rgm = fmaxf(rg[0], rg[1]);
+  const bool steep = !(fminf(gam[0], gam[1]) >= STEEP) || !(kmax * rgm < 32768.0f);
+  const bool any = __builtin_amdgcn_ballot_w64(steep) != 0;
+  if (lane == 0) sm.flags[par][sw] = (it.size > 2 && any) ? 1 : 0;
+}
+
+template <class C>
+__device__ void scan4(Smem4<C>& sm, const Raw4<C>& raw, const Item& it, int sw, int lane, int par) {
+  if (it.lo == 0 && it.hi == CS) scan4_body<C, true>(sm, raw, it, sw, lane, par);
+  else scan4_body<C, false>(sm, raw, it, sw, lane, par);
+}
+
+// ---- L, T wave -----------------------------------------------------------------------
+template <class C>
+__device__ void solve4(Smem4<C>& sm, const Item& it, int lane) {
+  const ScanSlot<C>& sl = sm.ss[it.seq % 3];
+  const h16* kc = sm.kc[it.seq % 2];
+  h16* tt = sm.t[it.seq % 2];
+  const int h = opaque(lane / 32), m = opaque(lane % 32);
+  // L^ = KG KC^T: lane (h, s = m) holds rows t = 8(i/4) + 4h + i%4 of column s
+  f32x16 acc = (f32x16)0.0f;
+#pragma unroll
+  for (int s = 0; s < C::NKS; ++s) {
+    const int off = m * C::LDK + 16 * s + 8 * h;
+    acc = mma32(ld8(&sl.kg[off]), ld8(&kc[off]), acc);
+  }
+  // L^T with beta_t folded in, strictly lower part only
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int t0 = 8 * j + 4 * h;
+    const f32x4 bt = *reinterpret_cast<const f32x4*>(&sl.beta[t0]);
+    f32x4 w;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) w[r] = (t0 + r > m) ? acc[4 * j + r] * bt[r] : 0.0f;
+    *reinterpret_cast<f32x4*>(&sm.lt[m * C::LDL + t0]) = w;
+  }
+  wave_lds_sync();
+  KDA_PHASE_MARK(20);
+  // Diagonal 16x16 blocks of (I + L)^{-1} by forward substitution, one column per
+  // lane (lanes 0-15: block 0, lanes 16-31: block 1).
+  if (lane < 32) {
+    const int blk = lane / 16, s = lane % 16, b0 = 16 * blk;
+    float x[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) x[t] = (t == s) ? 1.0f : 0.0f;
+#pragma unroll
+    for (int u = 0; u < 15; ++u) {
+      const float* row = &sm.lt[(b0 + u) * C::LDL + b0];  // column u of L (rows b0..b0+15)
+      float lc[16];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 w = *reinterpret_cast<const f32x4*>(row + 4 * q4);
+        lc[4 * q4] = w[0]; lc[4 * q4 + 1] = w[1]; lc[4 * q4 + 2] = w[2]; lc[4 * q4 + 3] = w[3];
+      }
+#pragma unroll
+      for (int t = u + 1; t < 16; ++t) x[t] -= lc[t] * x[u];
+    }
+    const float bs = sl.beta[b0 + s];
+    // D_blk^T row s (contiguous), T's diagonal block column s
+    f16x8 d0, d1;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      d0[t] = (h16)x[t];
+      d1[t] = (h16)x[8 + t];
+    }
+    *reinterpret_cast<f16x8*>(&sm.dt[blk][s * C::LDB]) = d0;
+    *reinterpret_cast<f16x8*>(&sm.dt[blk][s * C::LDB + 8]) = d1;
+    if (blk == 1) {
+#pragma unroll
+      for (int t = 0; t < 16; ++t) sm.dr[t * C::LDB + s] = (h16)x[t];
+    }
+#pragma unroll
+    for (int t = 0; t < 16; ++t) tt[(b0 + t) * C::LDC + spos(b0 + s)] = (h16)(x[t] * bs);
+  }
+  wave_lds_sync();
+  KDA_PHASE_MARK(21);
+  // T_10 = -D_1 L_10 D_0 diag(beta) on 16x16x16 matrix-core steps:
+  // lane (g, n): A row n / B column n, reduction indices 4g..4g+3.
+  {
+    const int g = lane / 16, n = lane % 16;
+    f16x4 A, B;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) A[kk] = (h16)sm.lt[(4 * g + kk) * C::LDL + 16 + n];  // L_10[n][4g+kk]
+    B = *reinterpret_cast<const f16x4*>(&sm.dt[0][n * C::LDB + 4 * g]);                 // D_0[4g..][n]
+    const f32x4 y = __builtin_amdgcn_mfma_f32_16x16x16f16(A, B, (f32x4)0.0f, 0, 0, 0);  // Y[4g+r][n]
+    const f16x4 A2 = *reinterpret_cast<const f16x4*>(&sm.dr[n * C::LDB + 4 * g]);       // D_1[n][4g..]
+    f16x4 B2;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) B2[r] = (h16)y[r];
+    const f32x4 z = __builtin_amdgcn_mfma_f32_16x16x16f16(A2, B2, (f32x4)0.0f, 0, 0, 0);  // Z[4g+r][n]
+    const float bs = sl.beta[n];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) tt[(16 + 4 * g + r) * C::LDC + spos(n)] = (h16)(-z[r] * bs);
+  }
+}
+
+// ---- P wave ----------------------------------------------------------------------------
+template <class C>
+__device__ void pmat4(Smem4<C>& sm, const Item& it, int lane) {
+  const ScanSlot<C>& sl = sm.ss[it.seq % 3];
+  const h16* kc = sm.kc[it.seq % 2];
+  h16* pp = sm.p[it.seq % 3];
+  const int h = opaque(lane / 32), m = opaque(lane % 32);
+  f32x16 acc = (f32x16)0.0f;
+#pragma unroll
+  for (int s = 0; s < C::NKS; ++s) {
+    const int off = m * C::LDK + 16 * s + 8 * h;
+    acc = mma32(ld8(&sl.qg[off]), ld8(&kc[off]), acc);
+  }
+  h16* prow = &pp[(4 * h) * C::LDC + spos(m)];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 8 * j + 4 * h + r;
+      prow[(8 * j + r) * C::LDC] = (h16)(t >= m ? -acc[4 * j + r] : 0.0f);
+    }
+}
+
+// ---- state wave --------------------------------------------------------------------------
+// S holds the state times 2^{-e} (e per column, sc = 2^{-e}); Sf the fp16 B
+// fragments of S for the next item, vn the next item's -V * sc in C layout.
+template <class C>
+struct StateRegs {
+  f32x16 S[C::NKT];
+  f16x8 Sf[C::NKS];
+  float vn[16];
+  float sc;
+};
+
+template <class C>
+__device__ void state_step(Smem4<C>& sm, StateRegs<C>& R, const Item& it, int lane) {
+  const ScanSlot<C>& sl = sm.ss[it.seq % 3];
+  const h16* tt = sm.t[it.seq % 2];
+  const int h = opaque(lane / 32), n = opaque(lane % 32);
+  // Xn = KG S - V (scaled)
+  f32x16 X;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) X[i] = R.vn[i];
+#pragma unroll
+  for (int s = 0; s < C::NKS; ++s) X = mma32(ld8(&sl.kg[n * C::LDK + 16 * s + 8 * h]), R.Sf[s], X);
+  // decayed state, off the critical path
+  f32x16 G[C::NKT];
+#pragma unroll
+  for (int ct = 0; ct < C::NKT; ++ct)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 gv = *reinterpret_cast<const f32x4*>(&sl.gam[32 * ct + 8 * j + 4 * h]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) G[ct][4 * j + r] = R.S[ct][4 * j + r] * gv[r];
+    }
+  KDA_PHASE_MARK(8);
+  // Un = T Xn
+  const f16x8 x0 = bfrag(X, 0), x1 = bfrag(X, 1);
+  f32x16 U = (f32x16)0.0f;
+  U = mma32(ld8(&tt[n * C::LDC + 8 * h]), x0, U);
+  U = mma32(ld8(&tt[n * C::LDC + 16 + 8 * h]), x1, U);
+  const f16x8 u0 = bfrag(U, 0), u1 = bfrag(U, 1);
+  h16* uf = sm.uf[it.seq % 2];
+  *reinterpret_cast<f16x8*>(&uf[lane * 8]) = u0;
+  *reinterpret_cast<f16x8*>(&uf[(64 + lane) * 8]) = u1;
+  KDA_PHASE_MARK(9);
+  // S' = gamma S + (-KH)^T Un
+#pragma unroll
+  for (int ct = 0; ct < C::NKT; ++ct) {
+    const int row = (32 * ct + n) * C::LDC + 8 * h;
+    G[ct] = mma32(ld8(&sl.kh[row]), u0, G[ct]);
+    G[ct] = mma32(ld8(&sl.kh[row + 16]), u1, G[ct]);
+    R.S[ct] = G[ct];
+  }
+  KDA_PHASE_MARK(10);
+}
+
+// Prepares item `it` (next for the state wave): column scale, fp16 fragments of
+// S (kept and published for the output wave) and -V * sc.
+template <class C>
+__device__ void state_prepare(Smem4<C>& sm, StateRegs<C>& R, const Item& it, int lane) {
+  const ScanSlot<C>& sl = sm.ss[it.seq % 3];
+  const int h = opaque(lane / 32), n = opaque(lane % 32);
+  float vf[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) vf[i] = (float)sl.v[(8 * (i / 4) + 4 * h + (i % 4)) * J + n];
+  float ms = 0.0f, mv = 0.0f;
+#pragma unroll
+  for (int ct = 0; ct < C::NKT; ++ct)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ms = fmaxf(ms, fabsf(R.S[ct][i]));
+#pragma unroll
+  for (int i = 0; i < 16; ++i) mv = fmaxf(mv, fabsf(vf[i]));
+  ms = fmaxf(ms, __shfl_xor(ms, 32));
+  mv = fmaxf(mv, __shfl_xor(mv, 32));
+  // keep the scaled column maximum within [2^-4, 2^4]; rescale rarely
+  const float m = fmaxf(ms, mv * R.sc);
+  const bool bad = m > 16.0f || (m > 0.0f && m < 0.0625f);
+  if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+    float f = 1.0f;
+    if (bad) {
+      const int ex = __builtin_amdgcn_frexp_expf(m);  // m = frac * 2^ex, frac in [0.5, 1)
+      f = __builtin_amdgcn_ldexpf(1.0f, -ex);
+    }
+#pragma unroll
+    for (int ct = 0; ct < C::NKT; ++ct) R.S[ct] *= f;
+    R.sc *= f;
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) R.vn[i] = -vf[i] * R.sc;
+  h16* sf = sm.sf[it.seq % 2];
+#pragma unroll
+  for (int s = 0; s < C::NKS; ++s) {
+    R.Sf[s] = bfrag(R.S[s / 2], s % 2);
+    *reinterpret_cast<f16x8*>(&sf[(s * 64 + lane) * 8]) = R.Sf[s];
+  }
+  if (h == 0) sm.sexp[it.seq % 2][n] = __builtin_amdgcn_rcpf(R.sc);
+}
+
+// ---- output wave -------------------------------------------------------------------------
+template <class C>
+__device__ void out_pu_store(Smem4<C>& sm, f32x16& O, float usc, const Item& it, const Ctx4& cx, int lane) {
+  const h16* pp = sm.p[it.seq % 3];
+  const h16* uf = sm.uf[it.seq % 2];
+  const int h = opaque(lane / 32), n = opaque(lane % 32);
+  O = mma32(ld8(&pp[n * C::LDC + 8 * h]), ld8(&uf[lane * 8]), O);
+  O = mma32(ld8(&pp[n * C::LDC + 16 + 8 * h]), ld8(&uf[(64 + lane) * 8]), O);
+  const PrefillParams& p = cx.p;
+  const int t0 = it.c * CS;
+  const int rows = chunk_end(it.c, p.T);
+  const int esz = p.o_f32 ? 4 : 2;
+  const int rs = p.H * p.dv * esz;
+  char* ob = static_cast<char*>(p.o) + ((((size_t)cx.b * p.T + t0) * p.H + cx.h) * p.dv + cx.col0) * esz;
+  const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(ob, rows * rs);
+  const int vbase = 4 * h * rs + n * esz;
+  if (p.o_f32) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int tr = 8 * (i / 4) + (i % 4);
+      const int t = tr + 4 * h;
+      const int voff = vbase + ((unsigned)(t - it.lo) < (unsigned)(it.hi - it.lo) ? 0 : 0x40000000);
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, O[i] * usc), rsrc, voff, tr * rs, 0);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int tr = 8 * (i / 4) + (i % 4);
+      const int t = tr + 4 * h;
+      const int voff = vbase + ((unsigned)(t - it.lo) < (unsigned)(it.hi - it.lo) ? 0 : 0x40000000);
+      __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (__bf16)(O[i] * usc)), rsrc, voff,
+                                            tr * rs, 0);
+    }
+  }
+}
+
+template <class C>
+__device__ void out_qs(Smem4<C>& sm, f32x16& O, float& usc, const Item& it, int lane) {
+  const ScanSlot<C>& sl = sm.ss[it.seq % 3];
+  const h16* sf = sm.sf[it.seq % 2];
+  const int h = opaque(lane / 32), n = opaque(lane % 32);
+  O = (f32x16)0.0f;
+#pragma unroll
+  for (int s = 0; s < C::NKS; ++s)
+    O = mma32(ld8(&sl.qg[n * C::LDK + 16 * s + 8 * h]), ld8(&sf[(s * 64 + lane) * 8]), O);
+  usc = sm.sexp[it.seq % 2][n];
+}
+
+// ---- kernel ---------------------------------------------------------------------------------
+enum Role { SCAN, SOLVE, PMAT, STATE, OUT };
+
+// One wave's whole life: its own copy of the item sequence and its own
+// registers (each role is a separate loop, so no role pays for another's live
+// values).  Every role executes exactly one barrier per step.
+template <class C, Role ROLE>
+__device__ void run_role(Smem4<C>& sm, const Ctx4& cx, int lane, int sw) {
+  const PrefillParams& p = cx.p;
+  StateRegs<C> R;
+  Raw4<C> raw;
+  int rc = -1;  // chunk held in raw
+  f32x16 O = (f32x16)0.0f;
+  float usc = 1.0f;
+  if constexpr (ROLE == STATE) {
+    const int h = lane / 32, n = lane % 32;
+    const size_t sbase = (size_t)cx.bh * C::DK * p.dv + cx.col0;
+#pragma unroll
+    for (int ct = 0; ct < C::NKT; ++ct) R.S[ct] = (f32x16)0.0f;
+    if (p.S0) {
+#pragma unroll
+      for (int ct = 0; ct < C::NKT; ++ct)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) R.S[ct][i] = p.S0[sbase + (32 * ct + 8 * (i / 4) + 4 * h + (i % 4)) * p.dv + n];
+    }
+    R.sc = 1.0f;
+  }
+  if constexpr (ROLE == SCAN) {
+    if (cx.nchunks > 0) {
+      load_raw4<C>(raw, cx, 0, sw, lane);
+      rc = 0;
+    }
+  }
+  block_sync_lds();  // the zeroed T ring is visible
+
+  const Item none = {-1, 0, 0, 0, 0};
+  Item sI = none, bI = none, stI = none, opI = none;
+  if (cx.nchunks > 0) sI = Item{0, 0, 0, chunk_end(0, p.T), CS};
+  int par = 0, kstep = 0;
+  while (sI.seq >= 0 || bI.seq >= 0 || stI.seq >= 0 || opI.seq >= 0) {
+    KDA_STEP_MARK(0, kstep);
+    if constexpr (ROLE == SCAN) {
+      if (sI.seq >= 0) {
+        if (rc != sI.c) {
+          load_raw4<C>(raw, cx, sI.c, sw, lane);
+          rc = sI.c;
+        }
+        KDA_PROBE_VMWAIT();
+        KDA_STEP_MARK(2, kstep);
+        scan4<C>(sm, raw, sI, sw, lane, par);
+        KDA_STEP_MARK(3, kstep);
+        if (sI.hi == chunk_end(sI.c, p.T) && sI.c + 1 < cx.nchunks) {
+          load_raw4<C>(raw, cx, sI.c + 1, sw, lane);  // prefetch the next chunk
+          rc = sI.c + 1;
+        }
+      }
+    } else if constexpr (ROLE == SOLVE) {
+      if (bI.seq >= 0) solve4<C>(sm, bI, lane);
+    } else if constexpr (ROLE == PMAT) {
+      if (bI.seq >= 0) pmat4<C>(sm, bI, lane);
+    } else if constexpr (ROLE == STATE) {
+      if (stI.seq >= 0) state_step<C>(sm, R, stI, lane);
+      KDA_STEP_MARK(2, kstep);
+      if (bI.seq >= 0) state_prepare<C>(sm, R, bI, lane);
+    } else {
+      if (opI.seq >= 0) out_pu_store<C>(sm, O, usc, opI, cx, lane);
+      KDA_STEP_MARK(2, kstep);
+      if (stI.seq >= 0) out_qs<C>(sm, O, usc, stI, lane);
+    }
+    KDA_STEP_MARK(1, kstep);
+    block_sync_lds();
+    KDA_STEP_MARK(4, kstep);
+    ++kstep;
+    bool steep = false;
+    if (sI.seq >= 0) {
+      const int4 f = *reinterpret_cast<const int4*>(&sm.flags[par][0]);
+      steep = __builtin_amdgcn_readfirstlane(f.x | f.y | f.z | f.w) != 0;
+    }
+    opI = stI;
+    stI = bI;
+    bI = (sI.seq >= 0 && !steep) ? sI : none;
+    if (sI.seq >= 0) sI = steep ? split_item(sI, p.T) : next_item(sI, p.T, cx.nchunks);
+    par ^= 1;
+  }
+
+  if constexpr (ROLE == STATE) {
+    if (p.S_T) {
+      const int h = lane / 32, n = lane % 32;
+      const size_t sbase = (size_t)cx.bh * C::DK * p.dv + cx.col0;
+      const float usc0 = __builtin_amdgcn_rcpf(R.sc);
+#pragma unroll
+      for (int ct = 0; ct < C::NKT; ++ct)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          p.S_T[sbase + (32 * ct + 8 * (i / 4) + 4 * h + (i % 4)) * p.dv + n] = R.S[ct][i] * usc0;
+    }
+  }
+}
+
+template <class C>
+__global__ __launch_bounds__(512, 1) void kda_prefill_pipe_kernel(PrefillParams p) {
+  __shared__ Smem4<C> sm;
+  const int tid = threadIdx.x, lane = tid % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int nslab = p.dv / J;
+  const int Gn = gridDim.x;
+  int lid = blockIdx.x;
+  if (Gn % 8 == 0) lid = (blockIdx.x % 8) * (Gn / 8) + blockIdx.x / 8;  // slabs of a head on one XCD
+  Ctx4 cx;
+  cx.p = p;
+  cx.bh = lid / nslab;
+  cx.b = cx.bh / p.H;
+  cx.h = cx.bh % p.H;
+  cx.col0 = (lid % nslab) * J;
+  cx.nchunks = (p.T + CS - 1) / CS;
+  // T's upper-right 16x16 block is read as zeros and never written
+  for (int i = tid; i < 2 * CS * C::LDC; i += NT) (&sm.t[0][0])[i] = (h16)0.0f;
+  if (wave >= 4) run_role<C, SCAN>(sm, cx, lane, wave - 4);
+  else if (wave == 0) run_role<C, STATE>(sm, cx, lane, 0);
+  else if (wave == 1) run_role<C, SOLVE>(sm, cx, lane, 0);
+  else if (wave == 2) run_role<C, PMAT>(sm, cx, lane, 0);
+  else run_role<C, OUT>(sm, cx, lane, 0);
+}
+
+template <int DK>
+hipError_t launch_pipe(const PrefillParams& p, hipStream_t s) {
+  using C = Cfg4<DK>;
+  const unsigned grid = (unsigned)(p.B * p.H * (p.dv / J));
+  hipLaunchKernelGGL((kda_prefill_pipe_kernel<C>), dim3(grid), dim3(NT), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool prefill_pipe_supported(int io_dtype, int dk, int dv, int chunk, int H) {
+  // per-chunk buffer ranges (32 tokens of every head) must fit 31 bits
+  const long long chunk_bytes = (long long)CS * H * (dk > dv ? dk : dv) * 4;
+  return io_dtype == 1 && (dk == 64 || dk == 128) && dv % J == 0 && (chunk == 32 || chunk == 64) &&
+         chunk_bytes < (1LL << 31);
+}
+
+hipError_t launch_prefill_pipe(const PrefillParams& p, hipStream_t s) {
+  if (p.dk == 128) return launch_pipe<128>(p, s);
+  if (p.dk == 64) return launch_pipe<64>(p, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kda
