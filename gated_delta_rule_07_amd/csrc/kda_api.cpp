@@ -44,10 +44,10 @@ bool sizes_ok(long long B, long long T, long long H, long long dk, long long dv)
 // {64,128}, d_v % 32 == 0 and chunk 32 or 64 (it runs 32-token chunks); the
 // generic 16x16-tile kernel serves everything else, with 16 state columns per
 // workgroup unless 32-column slabs still give one workgroup per compute unit.
-// KDA_PREFILL_IMPL=generic or tiles32 selects another kernel where it applies
-// and KDA_PREFILL_SLAB=16 or 32 the generic kernel's slab width (both for tests
-// and measurements).
-enum PrefillImpl { IMPL_GENERIC, IMPL_TILES32, IMPL_PIPE };
+// KDA_PREFILL_IMPL=generic selects the generic kernel where the pipeline one
+// would apply, and KDA_PREFILL_SLAB=16 or 32 the generic kernel's slab width
+// (both for tests and measurements).
+enum PrefillImpl { IMPL_GENERIC, IMPL_PIPE };
 struct PrefillPlan {
   PrefillImpl impl;
   int slab;
@@ -60,8 +60,6 @@ PrefillPlan plan_prefill(int B, int H, int dk, int dv, int chunk, int io) {
   }
   const char* impl = getenv("KDA_PREFILL_IMPL");
   const bool want_generic = impl && strcmp(impl, "generic") == 0;
-  const bool want_tiles32 = impl && strcmp(impl, "tiles32") == 0;
-  if (want_tiles32 && kda::prefill32_supported(io, dk, dv, chunk, H)) return {IMPL_TILES32, 32};
   if (!want_generic && !forced && kda::prefill_pipe_supported(io, dk, dv, chunk, H)) return {IMPL_PIPE, 32};
   if (forced) return {IMPL_GENERIC, forced};
   if (io == 1 && dv % 32 == 0 && (long long)B * H * (dv / 32) >= 256) return {IMPL_GENERIC, 32};
@@ -133,9 +131,8 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, kda_dtype 
 
   kda::PrefillParams p{q, k, v, alpha, beta, S0, o, S_T, B, T, H, d_k, d_v, o_dtype == KDA_F32 ? 1 : 0};
   const hipStream_t hs = static_cast<hipStream_t>(stream);
-  const hipError_t e = plan.impl == IMPL_PIPE      ? kda::launch_prefill_pipe(p, hs)
-                       : plan.impl == IMPL_TILES32 ? kda::launch_prefill32(p, hs)
-                                                   : kda::launch_prefill(p, io, chunk, plan.slab, hs);
+  const hipError_t e = plan.impl == IMPL_PIPE ? kda::launch_prefill_pipe(p, hs)
+                                              : kda::launch_prefill(p, io, chunk, plan.slab, hs);
   if (e != hipSuccess) {
     g_last_hip_error = (int)e;
     return KDA_ERR_HIP;

@@ -36,10 +36,6 @@ struct DecodeParams {
 bool prefill_supported(int io_dtype, int dk, int chunk, int slab);
 hipError_t launch_prefill(const PrefillParams& p, int io_dtype, int chunk, int slab, hipStream_t s);
 
-// 32x32-tile prefill (bf16 q/k/v, d_k in {64,128}, d_v % 32 == 0, chunk 64).
-bool prefill32_supported(int io_dtype, int dk, int dv, int chunk, int H);
-hipError_t launch_prefill32(const PrefillParams& p, hipStream_t s);
-
 // Warp-specialised pipeline prefill (bf16 q/k/v, d_k in {64,128}, d_v % 32 == 0,
 // requested chunk 32 or 64; runs 32-token chunks).
 bool prefill_pipe_supported(int io_dtype, int dk, int dv, int chunk, int H);

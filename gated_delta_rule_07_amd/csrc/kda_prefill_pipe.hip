@@ -67,8 +67,6 @@ struct Cfg4 {
   static constexpr int NKS = DK / 16;   // 16-channel reduction steps
   static constexpr int LDK = DK + 8;    // fp16 [token][channel] row stride
   static constexpr int LDC = CS + 8;    // fp16 [row][token] row stride
-  static constexpr int LDL = CS + 4;    // fp32 L^T row stride
-  static constexpr int LDB = 16 + 8;    // fp16 16x16 scratch row stride
   static constexpr int CPW = DK / 4;    // channels per scan wave
   static constexpr int PPW = CPW / 2;   // channel pairs per scan wave (one per lane)
   static constexpr int TQ = 64 / PPW;   // token groups per channel pair
@@ -104,9 +102,6 @@ struct Smem4 {
   alignas(16) h16 sf[2][C::NKS * 64 * 8];  // scaled S as B fragments [step][lane][8]
   alignas(16) float sexp[2][J];            // 2^e of each column's scale
   alignas(16) h16 uf[2][2 * 64 * 8];       // Un as B fragments [step][lane][8]
-  alignas(16) float lt[CS * C::LDL];       // L^T (beta folded) [s][t]
-  alignas(16) h16 dt[2][16 * C::LDB];      // diagonal blocks of (I+L)^{-1}, [s][t]
-  alignas(16) h16 dr[16 * C::LDB];         // second diagonal block, [t][s]
   alignas(16) float xch[4][2][64];         // scan: token-group totals per wave
   alignas(16) int flags[2][4];             // scan: regroup votes per wave
 };
@@ -329,87 +324,99 @@ __device__ void scan4(Smem4<C>& sm, const Raw4<C>& raw, const Item& it, int sw, 
   else scan4_body<C, false>(sm, raw, it, sw, lane, par);
 }
 
-// ---- L, T wave -----------------------------------------------------------------------
+// ---- L, T wave -------------------------------------------------------------------------
+// 16x16 matrix-core steps: lane (g = l/16, n = l%16); C tiles hold rows 4g+j,
+// column n.  A C tile feeds a B operand directly; the A operand of M is the C
+// tile of M^T, so every matrix is also carried transposed.
+typedef _Float16 f16x4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mma16x32(const f16x8& a, const f16x8& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16x16(const f16x4v& a, const f16x4v& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f16x4v h4(const f32x4& v) { return f16x4v{(h16)v[0], (h16)v[1], (h16)v[2], (h16)v[3]}; }
+
+// (I + L_bb)^{-1} for a strictly lower 16x16 block given N = -L_bb and N^T (C
+// tiles): the product (I + N)(I + N^2)(I + N^4)(I + N^8), exact because N^16 = 0.
+// Returns D and D^T.
+__device__ __forceinline__ void unit_lower_inverse(f32x4 P, f32x4 Pt, const f32x4& eye, f32x4& R, f32x4& Rt) {
+  R = eye + P;
+  Rt = eye + Pt;
+#pragma unroll
+  for (int lv = 0; lv < 3; ++lv) {
+    const f16x4v p = h4(P), pt = h4(Pt);
+    const f32x4 P2 = mma16x16(pt, p, (f32x4)0.0f);  // P P
+    const f16x4v ip2 = h4(eye + P2);
+    const f16x4v r = h4(R), rt = h4(Rt);
+    R = mma16x16(rt, ip2, (f32x4)0.0f);    // R (I + P^2)
+    Rt = mma16x16(ip2, rt, (f32x4)0.0f);   // (I + P^2)^T R^T
+    if (lv < 2) {
+      Pt = mma16x16(p, pt, (f32x4)0.0f);   // P^T P^T
+      P = P2;
+    }
+    (void)r;
+  }
+}
+
 template <class C>
 __device__ void solve4(Smem4<C>& sm, const Item& it, int lane) {
   const ScanSlot<C>& sl = sm.ss[it.seq % 3];
   const h16* kc = sm.kc[it.seq % 2];
   h16* tt = sm.t[it.seq % 2];
-  const int h = opaque(lane / 32), m = opaque(lane % 32);
-  // L^ = KG KC^T: lane (h, s = m) holds rows t = 8(i/4) + 4h + i%4 of column s
-  f32x16 acc = (f32x16)0.0f;
+  const int g = opaque(lane / 16), n = opaque(lane % 16);
+  // K fragments of token rows n and 16+n over the channel steps (same storage
+  // order on both sides of every product)
+  f16x8 kg0[C::NKS / 2], kg1[C::NKS / 2], kc0[C::NKS / 2], kc1[C::NKS / 2];
 #pragma unroll
-  for (int s = 0; s < C::NKS; ++s) {
-    const int off = m * C::LDK + 16 * s + 8 * h;
-    acc = mma32(ld8(&sl.kg[off]), ld8(&kc[off]), acc);
+  for (int s = 0; s < C::NKS / 2; ++s) {
+    const int off = n * C::LDK + 32 * s + 8 * g;
+    kg0[s] = ld8(&sl.kg[off]);
+    kg1[s] = ld8(&sl.kg[off + 16 * C::LDK]);
+    kc0[s] = ld8(&kc[off]);
+    kc1[s] = ld8(&kc[off + 16 * C::LDK]);
   }
-  // L^T with beta_t folded in, strictly lower part only
+  f32x4 a00 = (f32x4)0.0f, a00t = a00, a11 = a00, a11t = a00, a10t = a00;
+#pragma unroll
+  for (int s = 0; s < C::NKS / 2; ++s) {
+    a00 = mma16x32(kg0[s], kc0[s], a00);   // (KG KC^T)[4g+j][n]         block (0,0)
+    a00t = mma16x32(kc0[s], kg0[s], a00t); // (KG KC^T)[n][4g+j]         transposed
+    a11 = mma16x32(kg1[s], kc1[s], a11);   // block (1,1)
+    a11t = mma16x32(kc1[s], kg1[s], a11t);
+    a10t = mma16x32(kc0[s], kg1[s], a10t); // (KG KC^T)[16+n][4g+j]      block (1,0), transposed
+  }
+  const f32x4 b_r0 = *reinterpret_cast<const f32x4*>(&sl.beta[4 * g]);
+  const f32x4 b_r1 = *reinterpret_cast<const f32x4*>(&sl.beta[16 + 4 * g]);
+  const float b_c0 = sl.beta[n], b_c1 = sl.beta[16 + n];
+  // N = -L (strictly lower, beta of the row folded in) and N^T for both diagonal
+  // blocks; L_10^T; the identity tile
+  f32x4 n0, n0t, n1, n1t, l10t, eye;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int t0 = 8 * j + 4 * h;
-    const f32x4 bt = *reinterpret_cast<const f32x4*>(&sl.beta[t0]);
-    f32x4 w;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) w[r] = (t0 + r > m) ? acc[4 * j + r] * bt[r] : 0.0f;
-    *reinterpret_cast<f32x4*>(&sm.lt[m * C::LDL + t0]) = w;
+    const int r = 4 * g + j;
+    const bool lower = r > n, upper = n > r;
+    n0[j] = lower ? -a00[j] * b_r0[j] : 0.0f;
+    n0t[j] = upper ? -a00t[j] * b_c0 : 0.0f;
+    n1[j] = lower ? -a11[j] * b_r1[j] : 0.0f;
+    n1t[j] = upper ? -a11t[j] * b_c1 : 0.0f;
+    l10t[j] = a10t[j] * b_c1;
+    eye[j] = (r == n) ? 1.0f : 0.0f;
   }
-  wave_lds_sync();
-  KDA_PHASE_MARK(20);
-  // Diagonal 16x16 blocks of (I + L)^{-1} by forward substitution, one column per
-  // lane (lanes 0-15: block 0, lanes 16-31: block 1).
-  if (lane < 32) {
-    const int blk = lane / 16, s = lane % 16, b0 = 16 * blk;
-    float x[16];
+  f32x4 d0, d0t, d1, d1t;
+  unit_lower_inverse(n0, n0t, eye, d0, d0t);
+  unit_lower_inverse(n1, n1t, eye, d1, d1t);
+  // T_10 = -D_1 L_10 D_0 diag(beta)
+  const f32x4 y = mma16x16(h4(l10t), h4(d0), (f32x4)0.0f);  // L_10 D_0
+  const f32x4 z = mma16x16(h4(d1t), h4(y), (f32x4)0.0f);    // D_1 (L_10 D_0)
+  // T = (I + L)^{-1} diag(beta): rows 4g+j (+16), column n (+16)
+  const int c0 = spos(n), c1 = spos(16 + n);
 #pragma unroll
-    for (int t = 0; t < 16; ++t) x[t] = (t == s) ? 1.0f : 0.0f;
-#pragma unroll
-    for (int u = 0; u < 15; ++u) {
-      const float* row = &sm.lt[(b0 + u) * C::LDL + b0];  // column u of L (rows b0..b0+15)
-      float lc[16];
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 w = *reinterpret_cast<const f32x4*>(row + 4 * q4);
-        lc[4 * q4] = w[0]; lc[4 * q4 + 1] = w[1]; lc[4 * q4 + 2] = w[2]; lc[4 * q4 + 3] = w[3];
-      }
-#pragma unroll
-      for (int t = u + 1; t < 16; ++t) x[t] -= lc[t] * x[u];
-    }
-    const float bs = sl.beta[b0 + s];
-    // D_blk^T row s (contiguous), T's diagonal block column s
-    f16x8 d0, d1;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      d0[t] = (h16)x[t];
-      d1[t] = (h16)x[8 + t];
-    }
-    *reinterpret_cast<f16x8*>(&sm.dt[blk][s * C::LDB]) = d0;
-    *reinterpret_cast<f16x8*>(&sm.dt[blk][s * C::LDB + 8]) = d1;
-    if (blk == 1) {
-#pragma unroll
-      for (int t = 0; t < 16; ++t) sm.dr[t * C::LDB + s] = (h16)x[t];
-    }
-#pragma unroll
-    for (int t = 0; t < 16; ++t) tt[(b0 + t) * C::LDC + spos(b0 + s)] = (h16)(x[t] * bs);
-  }
-  wave_lds_sync();
-  KDA_PHASE_MARK(21);
-  // T_10 = -D_1 L_10 D_0 diag(beta) on 16x16x16 matrix-core steps:
-  // lane (g, n): A row n / B column n, reduction indices 4g..4g+3.
-  {
-    const int g = lane / 16, n = lane % 16;
-    f16x4 A, B;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) A[kk] = (h16)sm.lt[(4 * g + kk) * C::LDL + 16 + n];  // L_10[n][4g+kk]
-    B = *reinterpret_cast<const f16x4*>(&sm.dt[0][n * C::LDB + 4 * g]);                 // D_0[4g..][n]
-    const f32x4 y = __builtin_amdgcn_mfma_f32_16x16x16f16(A, B, (f32x4)0.0f, 0, 0, 0);  // Y[4g+r][n]
-    const f16x4 A2 = *reinterpret_cast<const f16x4*>(&sm.dr[n * C::LDB + 4 * g]);       // D_1[n][4g..]
-    f16x4 B2;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) B2[r] = (h16)y[r];
-    const f32x4 z = __builtin_amdgcn_mfma_f32_16x16x16f16(A2, B2, (f32x4)0.0f, 0, 0, 0);  // Z[4g+r][n]
-    const float bs = sl.beta[n];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) tt[(16 + 4 * g + r) * C::LDC + spos(n)] = (h16)(-z[r] * bs);
+  for (int j = 0; j < 4; ++j) {
+    const int r = 4 * g + j;
+    tt[r * C::LDC + c0] = (h16)(d0[j] * b_c0);
+    tt[(16 + r) * C::LDC + c1] = (h16)(d1[j] * b_c1);
+    tt[(16 + r) * C::LDC + c0] = (h16)(-z[j] * b_c0);
   }
 }
 
