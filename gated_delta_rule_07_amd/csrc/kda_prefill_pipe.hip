@@ -57,7 +57,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int CS = 32;  // tokens per chunk
 constexpr int J = 32;   // state columns per workgroup
-constexpr int NT = 512; // 8 waves
 constexpr float STEEP = 4.5399930e-05f;  // e^{-10}
 
 template <int DK_>
@@ -67,7 +66,11 @@ struct Cfg4 {
   static constexpr int NKS = DK / 16;   // 16-channel reduction steps
   static constexpr int LDK = DK + 8;    // fp16 [token][channel] row stride
   static constexpr int LDC = CS + 8;    // fp16 [row][token] row stride
-  static constexpr int CPW = DK / 4;    // channels per scan wave
+  static constexpr int LDV = CS + 4;    // bf16 V^T row stride
+  static constexpr int NSW = 4;         // scan waves
+  static constexpr int NW = 4 + NSW;    // waves per workgroup
+  static constexpr int NT = 64 * NW;
+  static constexpr int CPW = DK / NSW;  // channels per scan wave
   static constexpr int PPW = CPW / 2;   // channel pairs per scan wave (one per lane)
   static constexpr int TQ = 64 / PPW;   // token groups per channel pair
   static constexpr int TPL = CS / TQ;   // tokens per scan lane
@@ -88,7 +91,7 @@ struct ScanSlot {
   alignas(16) h16 kg[CS * C::LDK];    // KG      [t][spos(c)]
   alignas(16) h16 qg[CS * C::LDK];    // QG      [t][spos(c)]
   alignas(16) h16 kh[C::DK * C::LDC]; // -KH^T   [c][spos(t)]
-  alignas(16) __bf16 v[CS * J];       // V slab  [t][j]
+  alignas(16) __bf16 v[J * C::LDV];   // V slab transposed [j][t]
   alignas(16) float gam[C::DK];       // gamma per channel
   alignas(16) float beta[CS];         // beta (0 outside the item's segment)
 };
@@ -102,8 +105,8 @@ struct Smem4 {
   alignas(16) h16 sf[2][C::NKS * 64 * 8];  // scaled S as B fragments [step][lane][8]
   alignas(16) float sexp[2][J];            // 2^e of each column's scale
   alignas(16) h16 uf[2][2 * 64 * 8];       // Un as B fragments [step][lane][8]
-  alignas(16) float xch[4][2][64];         // scan: token-group totals per wave
-  alignas(16) int flags[2][4];             // scan: regroup votes per wave
+  alignas(16) float xch[C::NSW][2][64];    // scan: token-group totals per wave
+  alignas(16) int flags[2][C::NSW];        // scan: regroup votes per wave
 };
 
 __device__ __forceinline__ void block_sync_lds() {
@@ -211,10 +214,10 @@ __device__ void load_raw4(Raw4<C>& raw, const Ctx4& cx, int c, int sw, int lane)
     raw.k[i] = __builtin_amdgcn_raw_buffer_load_b32(rk, 2 * e0, 2 * i * ts, 0);
     raw.q[i] = __builtin_amdgcn_raw_buffer_load_b32(rq, 2 * e0, 2 * i * ts, 0);
   }
-  const int st = opaque(64 * sw + lane);  // 256 scan lanes: V row st/8, columns 4(st%8)..+3
+  const int st = opaque(64 * sw + lane);  // scan lanes 0-255: V row st/8, columns 4(st%8)..+3
   const int vs = p.H * p.dv;
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(static_cast<const __bf16*>(p.v) + row0 * p.dv + cx.col0, rows * vs * 2);
-  raw.v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, 2 * ((st / 8) * vs + 4 * (st % 8)), 0, 0));
+  raw.v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, 2 * (((st / 8) % CS) * vs + 4 * (st % 8)), 0, 0));
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.beta + row0, rows * p.H * 4);
   raw.beta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, 4 * (st % CS) * p.H, 0, 0));
 }
@@ -309,7 +312,14 @@ __device__ void scan4_body(Smem4<C>& sm, const Raw4<C>& raw, const Item& it, int
           f16x4{khv[e][4 * j], khv[e][4 * j + 1], khv[e][4 * j + 2], khv[e][4 * j + 3]};
   if (tq == 0) *reinterpret_cast<float2*>(&sl.gam[ch]) = float2{gam[0], gam[1]};
   const int st = 64 * sw + lane;
-  *reinterpret_cast<u32x2*>(&sl.v[(st / 8) * J + 4 * (st % 8)]) = raw.v;
+  if (st < 8 * CS) {
+    // V^T: this lane holds row st/8, columns 4(st%8)..+3
+    const int vr = st / 8, vc = 4 * (st % 8);
+    const uint32_t w[2] = {raw.v.x, raw.v.y};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      sl.v[(vc + e) * C::LDV + vr] = __builtin_bit_cast(__bf16, (uint16_t)(w[e / 2] >> (16 * (e % 2))));
+  }
   if (st < CS) sl.beta[st] = (FULL || (st >= lo && st < hi)) ? raw.beta : 0.0f;
   // regroup when some channel decays below e^{-10} or KC would leave fp16 range
   const float rgm = fmaxf(rg[0], rg[1]);
@@ -459,28 +469,40 @@ __device__ void state_step(Smem4<C>& sm, StateRegs<C>& R, const Item& it, int la
   const ScanSlot<C>& sl = sm.ss[it.seq % 3];
   const h16* tt = sm.t[it.seq % 2];
   const int h = opaque(lane / 32), n = opaque(lane % 32);
+  KDA_PHASE_MARK(7);
+  // operands first, so their reads overlap the products
+  f16x8 A[C::NKS];
+#pragma unroll
+  for (int s = 0; s < C::NKS; ++s) A[s] = ld8(&sl.kg[n * C::LDK + 16 * s + 8 * h]);
+  const f16x8 t0 = ld8(&tt[n * C::LDC + 8 * h]), t1 = ld8(&tt[n * C::LDC + 16 + 8 * h]);
   // Xn = KG S - V (scaled)
   f32x16 X;
 #pragma unroll
   for (int i = 0; i < 16; ++i) X[i] = R.vn[i];
 #pragma unroll
-  for (int s = 0; s < C::NKS; ++s) X = mma32(ld8(&sl.kg[n * C::LDK + 16 * s + 8 * h]), R.Sf[s], X);
-  // decayed state, off the critical path
-  f32x16 G[C::NKT];
+  for (int s = 0; s < C::NKS; ++s) X = mma32(A[s], R.Sf[s], X);
+  // decay the state in place while the products run
 #pragma unroll
   for (int ct = 0; ct < C::NKT; ++ct)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const f32x4 gv = *reinterpret_cast<const f32x4*>(&sl.gam[32 * ct + 8 * j + 4 * h]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) G[ct][4 * j + r] = R.S[ct][4 * j + r] * gv[r];
+      for (int r = 0; r < 4; ++r) R.S[ct][4 * j + r] *= gv[r];
     }
+  f16x8 KH[C::NKT][2];
+#pragma unroll
+  for (int ct = 0; ct < C::NKT; ++ct) {
+    const int row = (32 * ct + n) * C::LDC + 8 * h;
+    KH[ct][0] = ld8(&sl.kh[row]);
+    KH[ct][1] = ld8(&sl.kh[row + 16]);
+  }
   KDA_PHASE_MARK(8);
   // Un = T Xn
   const f16x8 x0 = bfrag(X, 0), x1 = bfrag(X, 1);
   f32x16 U = (f32x16)0.0f;
-  U = mma32(ld8(&tt[n * C::LDC + 8 * h]), x0, U);
-  U = mma32(ld8(&tt[n * C::LDC + 16 + 8 * h]), x1, U);
+  U = mma32(t0, x0, U);
+  U = mma32(t1, x1, U);
   const f16x8 u0 = bfrag(U, 0), u1 = bfrag(U, 1);
   h16* uf = sm.uf[it.seq % 2];
   *reinterpret_cast<f16x8*>(&uf[lane * 8]) = u0;
@@ -489,10 +511,8 @@ __device__ void state_step(Smem4<C>& sm, StateRegs<C>& R, const Item& it, int la
   // S' = gamma S + (-KH)^T Un
 #pragma unroll
   for (int ct = 0; ct < C::NKT; ++ct) {
-    const int row = (32 * ct + n) * C::LDC + 8 * h;
-    G[ct] = mma32(ld8(&sl.kh[row]), u0, G[ct]);
-    G[ct] = mma32(ld8(&sl.kh[row + 16]), u1, G[ct]);
-    R.S[ct] = G[ct];
+    R.S[ct] = mma32(KH[ct][0], u0, R.S[ct]);
+    R.S[ct] = mma32(KH[ct][1], u1, R.S[ct]);
   }
   KDA_PHASE_MARK(10);
 }
@@ -503,9 +523,16 @@ template <class C>
 __device__ void state_prepare(Smem4<C>& sm, StateRegs<C>& R, const Item& it, int lane) {
   const ScanSlot<C>& sl = sm.ss[it.seq % 3];
   const int h = opaque(lane / 32), n = opaque(lane % 32);
+  KDA_PHASE_MARK(11);
   float vf[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) vf[i] = (float)sl.v[(8 * (i / 4) + 4 * h + (i % 4)) * J + n];
+  for (int jj = 0; jj < 4; ++jj) {  // rows 8jj + 4h .. +3 of column n
+    const u32x2 w = *reinterpret_cast<const u32x2*>(&sl.v[n * C::LDV + 8 * jj + 4 * h]);
+    vf[4 * jj + 0] = __builtin_bit_cast(float, w.x << 16);
+    vf[4 * jj + 1] = __builtin_bit_cast(float, w.x & 0xffff0000u);
+    vf[4 * jj + 2] = __builtin_bit_cast(float, w.y << 16);
+    vf[4 * jj + 3] = __builtin_bit_cast(float, w.y & 0xffff0000u);
+  }
   float ms = 0.0f, mv = 0.0f;
 #pragma unroll
   for (int ct = 0; ct < C::NKT; ++ct)
@@ -537,6 +564,7 @@ __device__ void state_prepare(Smem4<C>& sm, StateRegs<C>& R, const Item& it, int
     *reinterpret_cast<f16x8*>(&sf[(s * 64 + lane) * 8]) = R.Sf[s];
   }
   if (h == 0) sm.sexp[it.seq % 2][n] = __builtin_amdgcn_rcpf(R.sc);
+  KDA_PHASE_MARK(12);
 }
 
 // ---- output wave -------------------------------------------------------------------------
@@ -662,8 +690,13 @@ __device__ void run_role(Smem4<C>& sm, const Ctx4& cx, int lane, int sw) {
     ++kstep;
     bool steep = false;
     if (sI.seq >= 0) {
-      const int4 f = *reinterpret_cast<const int4*>(&sm.flags[par][0]);
-      steep = __builtin_amdgcn_readfirstlane(f.x | f.y | f.z | f.w) != 0;
+      int any = 0;
+#pragma unroll
+      for (int w4 = 0; w4 < C::NSW; w4 += 4) {
+        const int4 f = *reinterpret_cast<const int4*>(&sm.flags[par][w4]);
+        any |= f.x | f.y | f.z | f.w;
+      }
+      steep = __builtin_amdgcn_readfirstlane(any) != 0;
     }
     opI = stI;
     stI = bI;
@@ -687,7 +720,7 @@ __device__ void run_role(Smem4<C>& sm, const Ctx4& cx, int lane, int sw) {
 }
 
 template <class C>
-__global__ __launch_bounds__(512, 1) void kda_prefill_pipe_kernel(PrefillParams p) {
+__global__ __launch_bounds__(C::NT, 1) void kda_prefill_pipe_kernel(PrefillParams p) {
   __shared__ Smem4<C> sm;
   const int tid = threadIdx.x, lane = tid % 64;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
@@ -703,7 +736,7 @@ __global__ __launch_bounds__(512, 1) void kda_prefill_pipe_kernel(PrefillParams 
   cx.col0 = (lid % nslab) * J;
   cx.nchunks = (p.T + CS - 1) / CS;
   // T's upper-right 16x16 block is read as zeros and never written
-  for (int i = tid; i < 2 * CS * C::LDC; i += NT) (&sm.t[0][0])[i] = (h16)0.0f;
+  for (int i = tid; i < 2 * CS * C::LDC; i += C::NT) (&sm.t[0][0])[i] = (h16)0.0f;
   if (wave >= 4) run_role<C, SCAN>(sm, cx, lane, wave - 4);
   else if (wave == 0) run_role<C, STATE>(sm, cx, lane, 0);
   else if (wave == 1) run_role<C, SOLVE>(sm, cx, lane, 0);
@@ -715,7 +748,7 @@ template <int DK>
 hipError_t launch_pipe(const PrefillParams& p, hipStream_t s) {
   using C = Cfg4<DK>;
   const unsigned grid = (unsigned)(p.B * p.H * (p.dv / J));
-  hipLaunchKernelGGL((kda_prefill_pipe_kernel<C>), dim3(grid), dim3(NT), 0, s, p);
+  hipLaunchKernelGGL((kda_prefill_pipe_kernel<C>), dim3(grid), dim3(C::NT), 0, s, p);
   return hipGetLastError();
 }
 
