@@ -27,11 +27,13 @@
  *    for d_k <= 32 (prefill) and any supported d_k (decode).
  *  - Arithmetic.  The state is carried in fp32 and every product accumulates in
  *    fp32.  With fp32 q/k/v all matrix-core operands are fp32.  With bf16 q/k/v
- *    the operands of the state-side products are fp16 (values are rescaled by a
- *    power of two per state column and chunk, so their magnitude is not
- *    restricted; q and k entries should stay below 6.5e4 in magnitude), and the
- *    intra-chunk key products are formed from bf16 high/low pairs, which keep
- *    about 16 significant bits over the full decay range.
+ *    the matrix-core operands are fp16: the decayed keys and queries (bounded by
+ *    |k|, |q|), the inverse-decayed keys (at most e^10 |k|: a chunk whose decay
+ *    would exceed that is processed as shorter exact segments), and the state
+ *    and values rescaled by a power of two per state column, so their magnitude
+ *    is not restricted.  q and k entries should stay below 6.5e4 in magnitude.
+ *    (Head sizes served by the generic kernel form the intra-chunk key products
+ *    from bf16 high/low pairs instead, about 16 significant bits.)
  *  - Input domain: alpha in [exp(-5), 1] (the lower-bounded decay of section 3.5
  *    of the same page); results outside it are not guaranteed.  beta may be any
  *    finite value (it is not clamped).
@@ -79,7 +81,10 @@ typedef enum {
  *            accuracy; a bf16 o is that same fp32 value rounded to nearest even,
  *            and the rounding alone can reach 2^-9 of |o_t|.
  *   S_T    : [B][H][d_k][d_v] fp32 final state, or NULL to skip       (written)
- *   chunk  : 16, 32 or 64 (64 is the intended size)
+ *   chunk  : 16, 32 or 64 (64 is the intended size).  With bf16 q/k/v,
+ *            d_k in {64, 128} and d_v a multiple of 32, chunk 32 and 64 both
+ *            run the 32-token pipelined kernel; the result does not depend on
+ *            the chunk size beyond rounding.
  *
  * S0 == S_T (the same buffer) is allowed and updates the state in place; any
  * other overlap between an output and an input returns KDA_ERR_ALIAS.
