@@ -71,10 +71,13 @@ struct Cfg4 {
   static constexpr int NW = 4 + NSW;    // waves per workgroup
   static constexpr int NT = 64 * NW;
   static constexpr int CPW = DK / NSW;  // channels per scan wave
-  static constexpr int PPW = CPW / 2;   // channel pairs per scan wave (one per lane)
-  static constexpr int TQ = 64 / PPW;   // token groups per channel pair
-  static constexpr int TPL = CS / TQ;   // tokens per scan lane
-  static_assert(TPL % 4 == 0, "scan layout");
+  // A scan lane holds CPL adjacent channels of TPL consecutive tokens; its
+  // inputs arrive in TPL loads per tensor, each CPL elements wide.
+  static constexpr int CPL = DK == 128 ? 4 : 2;
+  static constexpr int PPW = CPW / CPL;  // channel groups per scan wave
+  static constexpr int TQ = 64 / PPW;    // token groups per channel group
+  static constexpr int TPL = CS / TQ;    // tokens per scan lane
+  static_assert(TQ == 8 && TPL == 4, "scan layout");
 };
 
 // Storage column of logical column c: the four quads of each 16-column group are
@@ -105,7 +108,7 @@ struct Smem4 {
   alignas(16) h16 sf[2][C::NKS * 64 * 8];  // scaled S as B fragments [step][lane][8]
   alignas(16) float sexp[2][J];            // 2^e of each column's scale
   alignas(16) h16 uf[2][2 * 64 * 8];       // Un as B fragments [step][lane][8]
-  alignas(16) float xch[C::NSW][2][64];    // scan: token-group totals per wave
+  alignas(16) float xch[C::NSW][64][4];    // scan: token-group totals per wave
   alignas(16) int flags[2][C::NSW];        // scan: regroup votes per wave
 };
 
@@ -181,16 +184,17 @@ struct Ctx4 {
 // ---- scan waves --------------------------------------------------------------------
 template <class C>
 struct Raw4 {
-  float a[C::TPL][2];  // alpha of this lane's channel pair, per token
-  uint32_t k[C::TPL];  // 2 bf16
-  uint32_t q[C::TPL];
-  u32x2 v;             // 4 bf16 of the V slab
+  float a[C::TPL][C::CPL];         // alpha of this lane's channels, per token
+  uint32_t k[C::TPL][C::CPL / 2];  // bf16 pairs
+  uint32_t q[C::TPL][C::CPL / 2];
+  u32x2 v;                         // 4 bf16 of the V slab
   float beta;
 };
 
-// Loads chunk c's inputs for scan lane (sw, lane): channels 2cp, 2cp+1 of the
+// Loads chunk c's inputs for scan lane (sw, lane): channels CPL*cp .. of the
 // wave's slice, tokens tq*TPL ..  Rows past the sequence end read as zeros
-// (buffer range check).
+// (buffer range check).  One load per token and tensor: the load count, not
+// the byte count, sets what the scan waits for here.
 template <class C>
 __device__ void load_raw4(Raw4<C>& raw, const Ctx4& cx, int c, int sw, int lane) {
   const PrefillParams& p = cx.p;
@@ -202,24 +206,39 @@ __device__ void load_raw4(Raw4<C>& raw, const Ctx4& cx, int c, int sw, int lane)
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.alpha + row0 * C::DK, rows * ts * 4);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(static_cast<const __bf16*>(p.k) + row0 * C::DK, rows * ts * 2);
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(static_cast<const __bf16*>(p.q) + row0 * C::DK, rows * ts * 2);
-  const int e0 = tq * C::TPL * ts + C::CPW * sw + 2 * cp;
+  const int e0 = tq * C::TPL * ts + C::CPW * sw + C::CPL * cp;
 #pragma unroll
   for (int i = 0; i < C::TPL; ++i) {
-    // Reinterpret the loaded vector as a whole: taking single elements of the
+    // Reinterpret each loaded vector as a whole: taking single elements of the
     // integer vector a buffer load returns and reinterpreting them as float is
     // miscompiled by this toolchain (both read one narrowed dword).
-    const f32x2 w = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(ra, 4 * e0, 4 * i * ts, 0));
-    raw.a[i][0] = w.x;
-    raw.a[i][1] = w.y;
-    raw.k[i] = __builtin_amdgcn_raw_buffer_load_b32(rk, 2 * e0, 2 * i * ts, 0);
-    raw.q[i] = __builtin_amdgcn_raw_buffer_load_b32(rq, 2 * e0, 2 * i * ts, 0);
+    if constexpr (C::CPL == 4) {
+      const f32x4 w = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, 4 * e0, 4 * i * ts, 0));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) raw.a[i][e] = w[e];
+      const u32x2 kw = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rk, 2 * e0, 2 * i * ts, 0));
+      const u32x2 qw = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rq, 2 * e0, 2 * i * ts, 0));
+      raw.k[i][0] = kw.x;
+      raw.k[i][1] = kw.y;
+      raw.q[i][0] = qw.x;
+      raw.q[i][1] = qw.y;
+    } else {
+      const f32x2 w = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(ra, 4 * e0, 4 * i * ts, 0));
+      raw.a[i][0] = w.x;
+      raw.a[i][1] = w.y;
+      raw.k[i][0] = __builtin_amdgcn_raw_buffer_load_b32(rk, 2 * e0, 2 * i * ts, 0);
+      raw.q[i][0] = __builtin_amdgcn_raw_buffer_load_b32(rq, 2 * e0, 2 * i * ts, 0);
+    }
   }
   const int st = opaque(64 * sw + lane);  // scan lanes 0-255: V row st/8, columns 4(st%8)..+3
   const int vs = p.H * p.dv;
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(static_cast<const __bf16*>(p.v) + row0 * p.dv + cx.col0, rows * vs * 2);
   raw.v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, 2 * (((st / 8) % CS) * vs + 4 * (st % 8)), 0, 0));
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.beta + row0, rows * p.H * 4);
-  raw.beta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, 4 * (st % CS) * p.H, 0, 0));
+  raw.beta = 0.0f;
+  if (sw == 0) {  // beta is kept by the first CS scan lanes only
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.beta + row0, rows * p.H * 4);
+    raw.beta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, 4 * (st % CS) * p.H, 0, 0));
+  }
 }
 
 // Scan of item `it` by scan wave sw (one channel pair and TPL consecutive tokens
@@ -227,90 +246,121 @@ __device__ void load_raw4(Raw4<C>& raw, const Ctx4& cx, int c, int sw, int lane)
 // regroup vote.  FULL: the item is the whole chunk (no token is masked).
 template <class C, bool FULL>
 __device__ void scan4_body(Smem4<C>& sm, const Raw4<C>& raw, const Item& it, int sw, int lane, int par) {
+  constexpr int L = C::CPL, TP = C::TPL;
   ScanSlot<C>& sl = sm.ss[it.seq % 3];
   h16* kc = sm.kc[it.seq % 2];
   const int cp = opaque(lane % C::PPW), tq = opaque(lane / C::PPW);
-  const int ch = C::CPW * sw + 2 * cp;  // this lane's first channel
-  const int tb = tq * C::TPL;           // first of this lane's tokens
+  const int ch = C::CPW * sw + L * cp;  // this lane's first channel
+  const int tb = tq * TP;               // first of this lane's tokens
   const int lo = it.lo, hi = it.hi;
   auto in = [&](int i) { return FULL || (tb + i >= lo && tb + i < hi); };
 
-  float a[C::TPL][2];
-  float gt[2] = {1.0f, 1.0f};
+  float a[TP][L], gt[L];
 #pragma unroll
-  for (int i = 0; i < C::TPL; ++i)
+  for (int e = 0; e < L; ++e) gt[e] = 1.0f;
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
+  for (int i = 0; i < TP; ++i)
+#pragma unroll
+    for (int e = 0; e < L; ++e) {
       a[i][e] = in(i) ? raw.a[i][e] : 1.0f;
       gt[e] *= a[i][e];
     }
-  // products of the pair's other token groups
-  sm.xch[sw][0][lane] = gt[0];
-  sm.xch[sw][1][lane] = gt[1];
+  // Token-group products of every channel, exchanged within the wave.  Each
+  // lane runs the product over the groups in order, keeps the partial product
+  // reached at its own group (the groups before it), and takes the groups
+  // after it from the total.
+  if constexpr (L == 4) *reinterpret_cast<f32x4*>(&sm.xch[sw][lane][0]) = f32x4{gt[0], gt[1], gt[2], gt[3]};
+  else *reinterpret_cast<f32x2*>(&sm.xch[sw][lane][0]) = f32x2{gt[0], gt[1]};
   wave_lds_sync();
-  float ep[2] = {1.0f, 1.0f}, sp[2] = {1.0f, 1.0f};
+  float run[L], ep[L];
 #pragma unroll
-  for (int g = 0; g < C::TQ; ++g)
+  for (int e = 0; e < L; ++e) run[e] = ep[e] = 1.0f;
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const float tv = sm.xch[sw][e][g * C::PPW + cp];
-      ep[e] *= (g < tq) ? tv : 1.0f;
-      sp[e] *= (g > tq) ? tv : 1.0f;
+  for (int g = 0; g < C::TQ; ++g) {
+    float v[L];
+    if constexpr (L == 4) {
+      const f32x4 w = *reinterpret_cast<const f32x4*>(&sm.xch[sw][g * C::PPW + cp][0]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = w[e];
+    } else {
+      const f32x2 w = *reinterpret_cast<const f32x2*>(&sm.xch[sw][g * C::PPW + cp][0]);
+      v[0] = w.x;
+      v[1] = w.y;
     }
-  float gam[2], rg[2];
+    const bool mine = g == tq;
 #pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    gam[e] = ep[e] * gt[e] * sp[e];
+    for (int e = 0; e < L; ++e) {
+      ep[e] = mine ? run[e] : ep[e];
+      run[e] *= v[e];
+    }
+  }
+  float gam[L], rg[L], sp[L];
+#pragma unroll
+  for (int e = 0; e < L; ++e) {
+    gam[e] = run[e];
     rg[e] = __builtin_amdgcn_rcpf(gam[e]);
+    // gamma >= e^-10 for every item whose results are used (steeper ones are
+    // regrouped), so this quotient neither underflows nor loses precision
+    sp[e] = gam[e] * __builtin_amdgcn_rcpf(ep[e] * gt[e]);
   }
   // pre_t (prefix through t) and -gamma/pre_t (minus the suffix after t)
-  float pre[C::TPL][2], ns[C::TPL][2];
+  float pre[TP][L], ns[TP][L];
 #pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    float run = ep[e];
+  for (int e = 0; e < L; ++e) {
+    float r = ep[e];
 #pragma unroll
-    for (int i = 0; i < C::TPL; ++i) {
-      run *= a[i][e];
-      pre[i][e] = run;
+    for (int i = 0; i < TP; ++i) {
+      r *= a[i][e];
+      pre[i][e] = r;
     }
-    float s = -sp[e];
+    float sf = -sp[e];
 #pragma unroll
-    for (int i = C::TPL - 1; i >= 0; --i) {
-      ns[i][e] = s;
-      s *= a[i][e];
+    for (int i = TP - 1; i >= 0; --i) {
+      ns[i][e] = sf;
+      sf *= a[i][e];
     }
   }
   float kmax = 0.0f;
-  h16 khv[2][C::TPL];
+  h16 khv[L][TP];
   const int col = spos(ch);
 #pragma unroll
-  for (int i = 0; i < C::TPL; ++i) {
-    const float kf[2] = {in(i) ? __builtin_bit_cast(float, raw.k[i] << 16) : 0.0f,
-                         in(i) ? __builtin_bit_cast(float, raw.k[i] & 0xffff0000u) : 0.0f};
-    const float qf[2] = {in(i) ? __builtin_bit_cast(float, raw.q[i] << 16) : 0.0f,
-                         in(i) ? __builtin_bit_cast(float, raw.q[i] & 0xffff0000u) : 0.0f};
-    f16x2 kg2, qg2, kc2;
+  for (int i = 0; i < TP; ++i) {
+    float kf[L], qf[L];
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
+    for (int j = 0; j < L / 2; ++j) {
+      kf[2 * j] = in(i) ? bf16_lo(raw.k[i][j]) : 0.0f;
+      kf[2 * j + 1] = in(i) ? bf16_hi(raw.k[i][j]) : 0.0f;
+      qf[2 * j] = in(i) ? bf16_lo(raw.q[i][j]) : 0.0f;
+      qf[2 * j + 1] = in(i) ? bf16_hi(raw.q[i][j]) : 0.0f;
+    }
+    h16 kg[L], qg[L], kcv[L];
+#pragma unroll
+    for (int e = 0; e < L; ++e) {
       kmax = fmaxf(kmax, fabsf(kf[e]));
-      kg2[e] = (h16)(kf[e] * pre[i][e]);
-      qg2[e] = (h16)(qf[e] * pre[i][e]);
+      kg[e] = (h16)(kf[e] * pre[i][e]);
+      qg[e] = (h16)(qf[e] * pre[i][e]);
       const float kh = kf[e] * ns[i][e];  // -KH
       khv[e][i] = (h16)kh;
-      kc2[e] = (h16)(kh * -rg[e]);        // KC = KH / gamma
+      kcv[e] = (h16)(kh * -rg[e]);        // KC = KH / gamma
     }
-    const int r = (tb + i) * C::LDK + col;
-    *reinterpret_cast<f16x2*>(&sl.kg[r]) = kg2;
-    *reinterpret_cast<f16x2*>(&sl.qg[r]) = qg2;
-    *reinterpret_cast<f16x2*>(&kc[r]) = kc2;
+    const int r = (tb + i) * C::LDK + col;  // CPL adjacent channels keep adjacent positions
+    if constexpr (L == 4) {
+      *reinterpret_cast<f16x4*>(&sl.kg[r]) = f16x4{kg[0], kg[1], kg[2], kg[3]};
+      *reinterpret_cast<f16x4*>(&sl.qg[r]) = f16x4{qg[0], qg[1], qg[2], qg[3]};
+      *reinterpret_cast<f16x4*>(&kc[r]) = f16x4{kcv[0], kcv[1], kcv[2], kcv[3]};
+    } else {
+      *reinterpret_cast<f16x2*>(&sl.kg[r]) = f16x2{kg[0], kg[1]};
+      *reinterpret_cast<f16x2*>(&sl.qg[r]) = f16x2{qg[0], qg[1]};
+      *reinterpret_cast<f16x2*>(&kc[r]) = f16x2{kcv[0], kcv[1]};
+    }
   }
 #pragma unroll
-  for (int e = 0; e < 2; ++e)
-#pragma unroll
-    for (int j = 0; j < C::TPL / 4; ++j)
-      *reinterpret_cast<f16x4*>(&sl.kh[(ch + e) * C::LDC + spos(tb + 4 * j)]) =
-          f16x4{khv[e][4 * j], khv[e][4 * j + 1], khv[e][4 * j + 2], khv[e][4 * j + 3]};
-  if (tq == 0) *reinterpret_cast<float2*>(&sl.gam[ch]) = float2{gam[0], gam[1]};
+  for (int e = 0; e < L; ++e)
+    *reinterpret_cast<f16x4*>(&sl.kh[(ch + e) * C::LDC + spos(tb)]) = f16x4{khv[e][0], khv[e][1], khv[e][2], khv[e][3]};
+  if (tq == 0) {
+    if constexpr (L == 4) *reinterpret_cast<f32x4*>(&sl.gam[ch]) = f32x4{gam[0], gam[1], gam[2], gam[3]};
+    else *reinterpret_cast<f32x2*>(&sl.gam[ch]) = f32x2{gam[0], gam[1]};
+  }
   const int st = 64 * sw + lane;
   if (st < 8 * CS) {
     // V^T: this lane holds row st/8, columns 4(st%8)..+3
@@ -322,8 +372,13 @@ __device__ void scan4_body(Smem4<C>& sm, const Raw4<C>& raw, const Item& it, int
   }
   if (st < CS) sl.beta[st] = (FULL || (st >= lo && st < hi)) ? raw.beta : 0.0f;
   // regroup when some channel decays below e^{-10} or KC would leave fp16 range
-  const float rgm = fmaxf(rg[0], rg[1]);
-  const bool steep = !(fminf(gam[0], gam[1]) >= STEEP) || !(kmax * rgm < 32768.0f);
+  float gmin = gam[0], rgm = rg[0];
+#pragma unroll
+  for (int e = 1; e < L; ++e) {
+    gmin = fminf(gmin, gam[e]);
+    rgm = fmaxf(rgm, rg[e]);
+  }
+  const bool steep = !(gmin >= STEEP) || !(kmax * rgm < 32768.0f);
   const bool any = __builtin_amdgcn_ballot_w64(steep) != 0;
   if (lane == 0) sm.flags[par][sw] = (it.size > 2 && any) ? 1 : 0;
 }
@@ -684,6 +739,13 @@ __device__ void run_role(Smem4<C>& sm, const Ctx4& cx, int lane, int sw) {
       KDA_STEP_MARK(2, kstep);
       if (stI.seq >= 0) out_qs<C>(sm, O, usc, stI, lane);
     }
+    // Both possible successors of the scan item are formed before the barrier,
+    // so after it only the regroup vote remains to be read.
+    Item nI = none, spI = none;
+    if (sI.seq >= 0) {
+      nI = next_item(sI, p.T, cx.nchunks);
+      spI = split_item(sI, p.T);
+    }
     KDA_STEP_MARK(1, kstep);
     block_sync_lds();
     KDA_STEP_MARK(4, kstep);
@@ -701,7 +763,7 @@ __device__ void run_role(Smem4<C>& sm, const Ctx4& cx, int lane, int sw) {
     opI = stI;
     stI = bI;
     bI = (sI.seq >= 0 && !steep) ? sI : none;
-    if (sI.seq >= 0) sI = steep ? split_item(sI, p.T) : next_item(sI, p.T, cx.nchunks);
+    if (sI.seq >= 0) sI = steep ? spI : nI;
     par ^= 1;
   }
 
