@@ -164,6 +164,31 @@ def main():
     log(f"prefill: {ms_per_step:.3f} ms/step (kernel {kern_ms:.3f} ms), {tokens_per_s:.4g} tok/s, "
         f"{achieved_gbs:.0f} GB/s, {tflops:.1f} TFLOP/s")
 
+    # ------- the same prefill recording the state every 4096 tokens (prefix caching) -------
+    snap_pos = list(range(4096, T + 1, 4096))
+    snaps = torch.empty(B, H, len(snap_pos), dk, dv, device=dev, dtype=torch.float32)
+
+    def sstep():
+        kda.kda_chunk_fwd_snapshots(x["q"], x["k"], x["v"], x["alpha"], x["beta"], x["S0"], snap_tokens=snap_pos,
+                                    chunk=C, o=o, S_T=S_T, snaps=snaps)
+
+    sstep()
+    torch.cuda.synchronize()
+    snap_heads = [0, B * H // 2 + 5]
+    hs = {k: (v[:, :snap_pos[0]].cpu() if k != "S0" else v.cpu()) for k, v in x.items()}
+    _, rsn = oracle.forward(hs["q"], hs["k"], hs["v"], hs["alpha"], hs["beta"], hs["S0"], heads=snap_heads,
+                            want_o=False)
+    e_snap = rel_err_heads(snaps[:, :, 0].reshape(B * H, dk, dv)[snap_heads].cpu().double().numpy(), rsn)
+    snap_last_is_state = bool(torch.equal(snaps[:, :, -1], S_T))
+    del hs, rsn
+    for _ in range(args.warmup):
+        sstep()
+    s_wall_ms, s_kern_ms, _ = timed_launches(sstep, args.steps, torch)
+    snap_bytes = B * H * len(snap_pos) * dk * dv * 4
+    log(f"prefill + {len(snap_pos)} snapshots: {s_wall_ms / args.steps:.3f} ms/step (kernel {s_kern_ms:.3f} ms, "
+        f"{100 * (s_kern_ms / kern_ms - 1):+.1f}%); snapshot@{snap_pos[0]} err {e_snap:.3e}, "
+        f"last == S_T: {snap_last_is_state}")
+
     # ---------------- decode: B=256, H=32, d=128, 100 in-place steps ----------------
     wd = ki.WORKLOADS[4]
     DB, DH = wd.B, wd.H
@@ -233,7 +258,7 @@ def main():
                          f"({len(heads) * T} token-heads, {cpu_s:.1f} s wall); tokens/s = "
                          f"token-heads/s / H", "cpu": _cpu_model()}
 
-    parity_ok = max(e_o, e_s, e_do, e_ds) <= TOL_REL
+    parity_ok = max(e_o, e_s, e_do, e_ds, e_snap) <= TOL_REL and snap_last_is_state
     out = {
         "metric": METRIC,
         "value": tokens_per_s,
@@ -265,6 +290,11 @@ def main():
                                 "frac": d_gbs_kernel / HBM_PEAK_GBS,
                                 "traffic": measured_traffic("kda_decode"),
                                 "kernel_us": d_kern_ms * 1e3, "algorithmic_bytes": state_bytes + io_bytes}},
+        "snapshots": {"workload": f"the prefill above, also recording the state after every {snap_pos[0]} "
+                                  f"tokens ({len(snap_pos)} per sequence, kda_chunk_fwd_snapshots)",
+                      "ms_per_step": s_wall_ms / args.steps, "kernel_ms": s_kern_ms,
+                      "overhead_vs_prefill": s_kern_ms / kern_ms - 1, "snapshot_bytes": snap_bytes,
+                      "parity_first_snapshot": e_snap, "last_snapshot_equals_S_T": snap_last_is_state},
         "parity": {"pass": parity_ok, "tol_rel_rms": TOL_REL, "prefill_o": e_o, "prefill_S_T": e_s,
                    "prefill_heads": heads, "decode_o": e_do, "decode_S": e_ds, "decode_states": dheads},
         "cpu_baseline": cpu,

@@ -13,11 +13,12 @@ from pathlib import Path
 
 import torch
 
-__all__ = ["kda_chunk_fwd", "kda_decode_step", "kda_status_string", "kda_version",
+__all__ = ["kda_chunk_fwd", "kda_chunk_fwd_snapshots", "kda_decode_step", "kda_status_string", "kda_version",
            "kda_last_hip_error", "library_path", "load_library", "KdaError",
-           "KDA_F32", "KDA_BF16"]
+           "KDA_F32", "KDA_BF16", "KDA_MAX_SNAPSHOTS"]
 
 KDA_F32, KDA_BF16 = 0, 1
+KDA_MAX_SNAPSHOTS = 128
 _PKG = Path(__file__).resolve().parent
 _LIB_PATH = _PKG / "libkda.so"
 _lib = None
@@ -48,6 +49,9 @@ def load_library():
     lib.kda_chunk_fwd.restype = i32
     lib.kda_chunk_fwd.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, i32, vp,
                                   i32, i32, i32, i32, i32, i32, vp]
+    lib.kda_chunk_fwd_snapshots.restype = i32
+    lib.kda_chunk_fwd_snapshots.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, i32, vp, vp, i32, vp,
+                                            i32, i32, i32, i32, i32, i32, vp]
     lib.kda_decode_step.restype = i32
     lib.kda_decode_step.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
     lib.kda_status_string.restype = ctypes.c_char_p
@@ -102,16 +106,7 @@ def _stream(device, stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def kda_chunk_fwd(q, k, v, alpha, beta, S0=None, *, chunk: int = 64, o=None, S_T=None,
-                  o_dtype=torch.float32, want_state: bool = True, stream=None):
-    """Prefill: returns ``(o, S_T)`` (``S_T`` is None when ``want_state`` is False).
-
-    q, k: [B,T,H,d_k]; v: [B,T,H,d_v] (bf16 or fp32, same dtype); alpha: [B,T,H,d_k]
-    fp32; beta: [B,T,H] fp32; S0: [B,H,d_k,d_v] fp32 or None (zeros).  ``o`` is
-    float32 (default) or bfloat16 (``o_dtype``, or the dtype of a preallocated
-    ``o``).  ``S_T`` may be preallocated (it may be ``S0`` for an in-place update).
-    """
-    lib = load_library()
+def _prefill_prep(q, k, v, alpha, beta, S0, o, S_T, o_dtype, want_state):
     _check(q, "q")
     dev = q.device
     for t, n in ((k, "k"), (v, "v")):
@@ -140,12 +135,56 @@ def kda_chunk_fwd(q, k, v, alpha, beta, S0=None, *, chunk: int = 64, o=None, S_T
         _check(S_T, "S_T", torch.float32, dev)
         if S_T.shape != (B, H, dk, dv):
             raise ValueError("libkda: S_T must be [B,H,d_k,d_v]")
+    return dev, (B, T, H, dk, dv), o, S_T
+
+
+def kda_chunk_fwd(q, k, v, alpha, beta, S0=None, *, chunk: int = 64, o=None, S_T=None,
+                  o_dtype=torch.float32, want_state: bool = True, stream=None):
+    """Prefill: returns ``(o, S_T)`` (``S_T`` is None when ``want_state`` is False).
+
+    q, k: [B,T,H,d_k]; v: [B,T,H,d_v] (bf16 or fp32, same dtype); alpha: [B,T,H,d_k]
+    fp32; beta: [B,T,H] fp32; S0: [B,H,d_k,d_v] fp32 or None (zeros).  ``o`` is
+    float32 (default) or bfloat16 (``o_dtype``, or the dtype of a preallocated
+    ``o``).  ``S_T`` may be preallocated (it may be ``S0`` for an in-place update).
+    """
+    lib = load_library()
+    dev, (B, T, H, dk, dv), o, S_T = _prefill_prep(q, k, v, alpha, beta, S0, o, S_T, o_dtype, want_state)
     st = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(alpha), _ptr(beta),
                            _ptr(S0), _ptr(o), _dtype_code(o), _ptr(S_T), B, T, H, dk, dv, int(chunk),
                            _stream(dev, stream))
     if st != 0:
         raise KdaError(st, "kda_chunk_fwd")
     return o, S_T
+
+
+def kda_chunk_fwd_snapshots(q, k, v, alpha, beta, S0=None, *, snap_tokens, chunk: int = 64, o=None,
+                            S_T=None, snaps=None, o_dtype=torch.float32, want_state: bool = True,
+                            stream=None):
+    """Prefill that also records the state after each count in ``snap_tokens``.
+
+    Returns ``(o, S_T, snaps)`` with ``snaps`` [B,H,len(snap_tokens),d_k,d_v] fp32:
+    ``snaps[:, :, j]`` is the state after the first ``snap_tokens[j]`` tokens.  The
+    counts must be strictly increasing, in [1, T], and multiples of ``chunk`` (or T);
+    at most ``KDA_MAX_SNAPSHOTS`` of them.  Other arguments as ``kda_chunk_fwd``.
+    """
+    lib = load_library()
+    dev, (B, T, H, dk, dv), o, S_T = _prefill_prep(q, k, v, alpha, beta, S0, o, S_T, o_dtype, want_state)
+    pos = [int(t) for t in snap_tokens]
+    n = len(pos)
+    if snaps is None:
+        snaps = torch.empty(B, H, n, dk, dv, device=dev, dtype=torch.float32)
+    else:
+        _check(snaps, "snaps", torch.float32, dev)
+        if snaps.shape != (B, H, n, dk, dv):
+            raise ValueError("libkda: snaps must be [B,H,n_snap,d_k,d_v]")
+    arr = (ctypes.c_int * max(n, 1))(*pos)
+    st = lib.kda_chunk_fwd_snapshots(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(alpha), _ptr(beta),
+                                     _ptr(S0), _ptr(o), _dtype_code(o), _ptr(S_T), arr, n,
+                                     _ptr(snaps) if n > 0 else None, B, T, H, dk, dv, int(chunk),
+                                     _stream(dev, stream))
+    if st != 0:
+        raise KdaError(st, "kda_chunk_fwd_snapshots")
+    return o, S_T, snaps
 
 
 def kda_decode_step(q, k, v, alpha, beta, S, *, o=None, o_dtype=torch.float32, stream=None):

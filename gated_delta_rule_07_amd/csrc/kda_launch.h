@@ -16,6 +16,15 @@ struct PrefillParams {
   float* S_T;       // may be null (not written)
   int B, T, H, dk, dv;
   int o_f32;        // 1: o is fp32, 0: o is bf16
+  float* snaps;     // [B][H][nsnap][dk][dv], written when nsnap > 0
+  int nsnap;
+};
+
+// Token counts after which the state is recorded (ascending; a separate kernel
+// argument, read in place by the state waves).
+constexpr int kMaxSnapshots = 128;
+struct SnapList {
+  int pos[kMaxSnapshots];
 };
 
 struct DecodeParams {
@@ -34,12 +43,13 @@ struct DecodeParams {
 // workgroup owns (16, 32 or 64).  Returns hipErrorInvalidValue when no kernel is
 // built for the combination.
 bool prefill_supported(int io_dtype, int dk, int chunk, int slab);
-hipError_t launch_prefill(const PrefillParams& p, int io_dtype, int chunk, int slab, hipStream_t s);
+hipError_t launch_prefill(const PrefillParams& p, const SnapList& snap, int io_dtype, int chunk, int slab,
+                          hipStream_t s);
 
 // Warp-specialised pipeline prefill (bf16 q/k/v, d_k in {64,128}, d_v % 32 == 0,
 // requested chunk 32 or 64; runs 32-token chunks).
 bool prefill_pipe_supported(int io_dtype, int dk, int dv, int chunk, int H);
-hipError_t launch_prefill_pipe(const PrefillParams& p, hipStream_t s);
+hipError_t launch_prefill_pipe(const PrefillParams& p, const SnapList& snap, hipStream_t s);
 
 bool decode_supported(int io_dtype, int dk, int dv);
 hipError_t launch_decode(const DecodeParams& p, int io_dtype, hipStream_t s);

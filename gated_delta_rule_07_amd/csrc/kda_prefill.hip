@@ -564,8 +564,30 @@ __device__ bool process_chunk(Smem<C>& sm, Raw<C>& raw, f32x4 (&S)[C::NKT], cons
   return true;
 }
 
+// Writes this state wave's 16 columns of S (rows 16 it + 4 g + r, column col)
+// to the [d_k][d_v] matrix at dst, with buffer stores (a per-lane offset and a
+// scalar row offset; the stride is pinned here so no address is hoisted into
+// the chunk loop around a call).
 template <class C>
-__global__ __launch_bounds__(256, 1) void kda_prefill_kernel(PrefillParams p) {
+__device__ void store_state16(float* dst, const f32x4 (&S)[C::NKT], int dv_, int col, int g) {
+  int dvv = dv_;
+  asm volatile("" : "+v"(dvv));
+  const int dv = __builtin_amdgcn_readfirstlane(dvv);
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(static_cast<void*>(dst), (short)0, C::DK * dv * 4, 0x00020000);
+  const int voff = (4 * g * dv + col) * 4;
+#pragma unroll
+  for (int it = 0; it < C::NKT; ++it) {
+    // Reinterpret the tile as a whole: reinterpreting single elements of a
+    // vector is miscompiled by this toolchain (every element reads element 0).
+    const u32x4 w = __builtin_bit_cast(u32x4, S[it]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) __builtin_amdgcn_raw_buffer_store_b32(w[r], rs, voff, (16 * it + r) * dv * 4, 0);
+  }
+}
+
+template <class C>
+__global__ __launch_bounds__(256, 1) void kda_prefill_kernel(PrefillParams p, SnapList snap) {
   __shared__ Smem<C> sm;
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const int nslab = p.dv / C::J;
@@ -595,6 +617,8 @@ __global__ __launch_bounds__(256, 1) void kda_prefill_kernel(PrefillParams p) {
   const int nchunks = (p.T + C::CS - 1) / C::CS;
   Raw<C> raw;
   if (nchunks > 0) load_raw<C>(raw, cx, 0, tid);
+  const size_t mat = (size_t)C::DK * p.dv;  // elements of one state
+  int ns = 0;                               // next recorded position
   for (int c = 0; c < nchunks; ++c) {
     const int t0 = c * C::CS;
     const int next = (c + 1 < nchunks) ? t0 + C::CS : -1;
@@ -604,26 +628,25 @@ __global__ __launch_bounds__(256, 1) void kda_prefill_kernel(PrefillParams p) {
         process_chunk<C>(sm, raw, S, cx, t0, 16 * sq, 16 * sq + 16, false,
                          sq == C::NCT - 1 ? next : -1, tid, wave, lane);
     }
+    if (ns < p.nsnap && snap.pos[ns] == min(t0 + C::CS, p.T)) {
+      if (wave < C::NSW)
+        store_state16<C>(p.snaps + ((size_t)cx.bh * p.nsnap + ns) * mat, S, p.dv, cx.col0 + 16 * wave + m, g);
+      ++ns;
+    }
   }
 
-  if (wave < C::NSW && p.S_T) {
-#pragma unroll
-    for (int it = 0; it < C::NKT; ++it)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        p.S_T[((size_t)cx.bh * C::DK + 16 * it + 4 * g + r) * p.dv + cx.col0 + 16 * wave + m] = S[it][r];
-  }
+  if (wave < C::NSW && p.S_T) store_state16<C>(p.S_T + (size_t)cx.bh * mat, S, p.dv, cx.col0 + 16 * wave + m, g);
 }
 
 template <typename IO, int DK, int J, int CS>
-hipError_t launch_one(const PrefillParams& p, hipStream_t s) {
+hipError_t launch_one(const PrefillParams& p, const SnapList& snap, hipStream_t s) {
   using C = Cfg<IO, DK, J, CS>;
   const unsigned grid = (unsigned)(p.B * p.H * (p.dv / J));
-  hipLaunchKernelGGL((kda_prefill_kernel<C>), dim3(grid), dim3(C::NT), 0, s, p);
+  hipLaunchKernelGGL((kda_prefill_kernel<C>), dim3(grid), dim3(C::NT), 0, s, p, snap);
   return hipGetLastError();
 }
 
-typedef hipError_t (*launch_fn)(const PrefillParams&, hipStream_t);
+typedef hipError_t (*launch_fn)(const PrefillParams&, const SnapList&, hipStream_t);
 
 // Instantiated kernels: bf16 for d_k in {16,32,64,128}, fp32 for d_k in {16,32};
 // slabs of 16 or 32 columns; chunks of 16, 32 or 64 tokens.
@@ -672,10 +695,11 @@ bool prefill_supported(int io_dtype, int dk, int chunk, int slab) {
   return pick(io_dtype, dk, chunk, slab) != nullptr;
 }
 
-hipError_t launch_prefill(const PrefillParams& p, int io_dtype, int chunk, int slab, hipStream_t s) {
+hipError_t launch_prefill(const PrefillParams& p, const SnapList& snap, int io_dtype, int chunk, int slab,
+                          hipStream_t s) {
   const launch_fn f = pick(io_dtype, p.dk, chunk, slab);
   if (!f || p.dv % slab != 0) return hipErrorInvalidValue;
-  return f(p, s);
+  return f(p, snap, s);
 }
 
 }  // namespace kda

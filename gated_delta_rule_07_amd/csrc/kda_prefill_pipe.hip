@@ -54,6 +54,7 @@ typedef _Float16 h16;
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int CS = 32;  // tokens per chunk
 constexpr int J = 32;   // state columns per workgroup
@@ -676,8 +677,30 @@ enum Role { SCAN, SOLVE, PMAT, STATE, OUT };
 // One wave's whole life: its own copy of the item sequence and its own
 // registers (each role is a separate loop, so no role pays for another's live
 // values).  Every role executes exactly one barrier per step.
+// Writes the state wave's S (32 columns; S = R.S / R.sc) to the [d_k][d_v]
+// matrix whose slab starts at dst.  Buffer stores with a per-lane offset and a
+// scalar row offset: no 64-bit address per element, and the stride is pinned
+// here so nothing of it is hoisted into the step loop around a call.
+template <class C>
+__device__ void store_state(float* dst, const StateRegs<C>& R, int dv_, int lane) {
+  const int dv = __builtin_amdgcn_readfirstlane(opaque(dv_));
+  const int h = lane / 32, n = lane % 32;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(dst, C::DK * dv * 4);
+  const int voff = (4 * h * dv + n) * 4;
+  const float usc = __builtin_amdgcn_rcpf(R.sc);
+#pragma unroll
+  for (int ct = 0; ct < C::NKT; ++ct) {
+    // Reinterpret the scaled tile as a whole: reinterpreting single elements of
+    // a vector is miscompiled by this toolchain (every element reads element 0).
+    const u32x16 w = __builtin_bit_cast(u32x16, R.S[ct] * usc);
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      __builtin_amdgcn_raw_buffer_store_b32(w[i], rs, voff, (32 * ct + 8 * (i / 4) + (i % 4)) * dv * 4, 0);
+  }
+}
+
 template <class C, Role ROLE>
-__device__ void run_role(Smem4<C>& sm, const Ctx4& cx, int lane, int sw) {
+__device__ void run_role(Smem4<C>& sm, const Ctx4& cx, const SnapList& snap, int lane, int sw) {
   const PrefillParams& p = cx.p;
   StateRegs<C> R;
   Raw4<C> raw;
@@ -709,6 +732,7 @@ __device__ void run_role(Smem4<C>& sm, const Ctx4& cx, int lane, int sw) {
   Item sI = none, bI = none, stI = none, opI = none;
   if (cx.nchunks > 0) sI = Item{0, 0, 0, chunk_end(0, p.T), CS};
   int par = 0, kstep = 0;
+  int ns = 0;  // state role: next recorded position
   while (sI.seq >= 0 || bI.seq >= 0 || stI.seq >= 0 || opI.seq >= 0) {
     KDA_STEP_MARK(0, kstep);
     if constexpr (ROLE == SCAN) {
@@ -731,7 +755,14 @@ __device__ void run_role(Smem4<C>& sm, const Ctx4& cx, int lane, int sw) {
     } else if constexpr (ROLE == PMAT) {
       if (bI.seq >= 0) pmat4<C>(sm, bI, lane);
     } else if constexpr (ROLE == STATE) {
-      if (stI.seq >= 0) state_step<C>(sm, R, stI, lane);
+      if (stI.seq >= 0) {
+        state_step<C>(sm, R, stI, lane);
+        // record the state after a listed number of tokens
+        if (ns < p.nsnap && stI.hi == chunk_end(stI.c, p.T) && snap.pos[ns] == stI.c * CS + stI.hi) {
+          store_state<C>(p.snaps + ((size_t)cx.bh * p.nsnap + ns) * C::DK * p.dv + cx.col0, R, p.dv, lane);
+          ++ns;
+        }
+      }
       KDA_STEP_MARK(2, kstep);
       if (bI.seq >= 0) state_prepare<C>(sm, R, bI, lane);
     } else {
@@ -768,21 +799,12 @@ __device__ void run_role(Smem4<C>& sm, const Ctx4& cx, int lane, int sw) {
   }
 
   if constexpr (ROLE == STATE) {
-    if (p.S_T) {
-      const int h = lane / 32, n = lane % 32;
-      const size_t sbase = (size_t)cx.bh * C::DK * p.dv + cx.col0;
-      const float usc0 = __builtin_amdgcn_rcpf(R.sc);
-#pragma unroll
-      for (int ct = 0; ct < C::NKT; ++ct)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          p.S_T[sbase + (32 * ct + 8 * (i / 4) + 4 * h + (i % 4)) * p.dv + n] = R.S[ct][i] * usc0;
-    }
+    if (p.S_T) store_state<C>(p.S_T + (size_t)cx.bh * C::DK * p.dv + cx.col0, R, p.dv, lane);
   }
 }
 
 template <class C>
-__global__ __launch_bounds__(C::NT, 1) void kda_prefill_pipe_kernel(PrefillParams p) {
+__global__ __launch_bounds__(C::NT, 1) void kda_prefill_pipe_kernel(PrefillParams p, SnapList snap) {
   __shared__ Smem4<C> sm;
   const int tid = threadIdx.x, lane = tid % 64;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
@@ -799,18 +821,18 @@ __global__ __launch_bounds__(C::NT, 1) void kda_prefill_pipe_kernel(PrefillParam
   cx.nchunks = (p.T + CS - 1) / CS;
   // T's upper-right 16x16 block is read as zeros and never written
   for (int i = tid; i < 2 * CS * C::LDC; i += C::NT) (&sm.t[0][0])[i] = (h16)0.0f;
-  if (wave >= 4) run_role<C, SCAN>(sm, cx, lane, wave - 4);
-  else if (wave == 0) run_role<C, STATE>(sm, cx, lane, 0);
-  else if (wave == 1) run_role<C, SOLVE>(sm, cx, lane, 0);
-  else if (wave == 2) run_role<C, PMAT>(sm, cx, lane, 0);
-  else run_role<C, OUT>(sm, cx, lane, 0);
+  if (wave >= 4) run_role<C, SCAN>(sm, cx, snap, lane, wave - 4);
+  else if (wave == 0) run_role<C, STATE>(sm, cx, snap, lane, 0);
+  else if (wave == 1) run_role<C, SOLVE>(sm, cx, snap, lane, 0);
+  else if (wave == 2) run_role<C, PMAT>(sm, cx, snap, lane, 0);
+  else run_role<C, OUT>(sm, cx, snap, lane, 0);
 }
 
 template <int DK>
-hipError_t launch_pipe(const PrefillParams& p, hipStream_t s) {
+hipError_t launch_pipe(const PrefillParams& p, const SnapList& snap, hipStream_t s) {
   using C = Cfg4<DK>;
   const unsigned grid = (unsigned)(p.B * p.H * (p.dv / J));
-  hipLaunchKernelGGL((kda_prefill_pipe_kernel<C>), dim3(grid), dim3(C::NT), 0, s, p);
+  hipLaunchKernelGGL((kda_prefill_pipe_kernel<C>), dim3(grid), dim3(C::NT), 0, s, p, snap);
   return hipGetLastError();
 }
 
@@ -823,9 +845,9 @@ bool prefill_pipe_supported(int io_dtype, int dk, int dv, int chunk, int H) {
          chunk_bytes < (1LL << 31);
 }
 
-hipError_t launch_prefill_pipe(const PrefillParams& p, hipStream_t s) {
-  if (p.dk == 128) return launch_pipe<128>(p, s);
-  if (p.dk == 64) return launch_pipe<64>(p, s);
+hipError_t launch_prefill_pipe(const PrefillParams& p, const SnapList& snap, hipStream_t s) {
+  if (p.dk == 128) return launch_pipe<128>(p, snap, s);
+  if (p.dk == 64) return launch_pipe<64>(p, snap, s);
   return hipErrorInvalidValue;
 }
 

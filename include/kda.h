@@ -96,6 +96,40 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, kda_dtype 
                          void* o, kda_dtype o_dtype, float* S_T,
                          int B, int T, int H, int d_k, int d_v, int chunk, void* stream);
 
+/* Most positions one kda_chunk_fwd_snapshots call records. */
+#define KDA_MAX_SNAPSHOTS 128
+
+/*
+ * kda_chunk_fwd that also records the state at caller-chosen positions, for
+ * prefix caching.  A KDA layer keeps no per-token keys and values: resuming a
+ * shared prompt prefix needs the state at exactly that position, and saving it
+ * at every token is too costly, so a server saves it at positions it selects --
+ * at a fixed interval, or where a prompt ends (the second page, "Kimi 모델
+ * 분석", section on prefix caching breaking and its parts on separating block
+ * size from caching granularity and on where to store the summaries).
+ *
+ * Every argument of kda_chunk_fwd keeps its meaning; in addition:
+ *   snap_tokens: HOST array of n_snap token counts, strictly increasing, each
+ *                in [1, T] and a multiple of `chunk` or equal to T.  Entry j
+ *                asks for the state after the first snap_tokens[j] tokens of
+ *                every sequence, S_{snap_tokens[j]} (read during the call only).
+ *   n_snap     : 0 .. KDA_MAX_SNAPSHOTS (0: identical to kda_chunk_fwd).
+ *   snaps      : [B][H][n_snap][d_k][d_v] fp32, device (written).  Snapshot j
+ *                of (b, h) is the same value kda_chunk_fwd's S_T would hold for
+ *                the first snap_tokens[j] tokens with the same S0 (bit for bit:
+ *                the chunks before it are computed identically).
+ *
+ * Errors, in addition to kda_chunk_fwd's: KDA_ERR_SHAPE for n_snap outside
+ * [0, KDA_MAX_SNAPSHOTS] or a position list that breaks the rules above;
+ * KDA_ERR_NULL for a NULL snap_tokens or snaps with n_snap > 0;
+ * KDA_ERR_MISALIGNED / KDA_ERR_ALIAS for snaps as for the other outputs.
+ */
+kda_status kda_chunk_fwd_snapshots(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
+                                   const float* alpha, const float* beta, const float* S0,
+                                   void* o, kda_dtype o_dtype, float* S_T,
+                                   const int* snap_tokens, int n_snap, float* snaps,
+                                   int B, int T, int H, int d_k, int d_v, int chunk, void* stream);
+
 /*
  * One batched decode step: one new token for each of B sequences and H heads,
  * i.e. exactly one step of the recurrence, applied to the state in place.

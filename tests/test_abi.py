@@ -104,6 +104,48 @@ def test_decode_validation(over, code):
     assert _decode(_lib(), **over) == code
 
 
+def _snap(lib, pos, n=None, snaps=_addr(8), **over):
+    a = dict(q=_addr(0), k=_addr(1), v=_addr(2), dtype=1, alpha=_addr(3), beta=_addr(4), S0=_addr(5),
+             o=_addr(6), odt=0, S_T=_addr(7), B=1, T=300, H=2, dk=128, dv=128, chunk=64)
+    a.update(over)
+    arr = None if pos is None else (ctypes.c_int * max(1, len(pos)))(*pos)
+    n = (len(pos) if pos is not None else 1) if n is None else n
+    return lib.kda_chunk_fwd_snapshots(a["q"], a["k"], a["v"], a["dtype"], a["alpha"], a["beta"], a["S0"],
+                                       a["o"], a["odt"], a["S_T"], arr, n, snaps, a["B"], a["T"], a["H"],
+                                       a["dk"], a["dv"], a["chunk"], None)
+
+
+@pytest.mark.parametrize("pos,over,code", [
+    ([64, 64], {}, 2),             # not strictly increasing
+    ([128, 64], {}, 2),            # decreasing
+    ([0], {}, 2),                  # before the first token
+    ([320], {}, 2),                # past T
+    ([100], {}, 2),                # not a multiple of the chunk, not T
+    ([32], {}, 2),                 # multiple of 32 but chunk is 64
+    (list(range(64, 64 * 130, 64)), dict(T=64 * 130), 2),  # more than KDA_MAX_SNAPSHOTS
+    (None, {}, 1),                 # n_snap > 0 without a list
+    ([64], dict(snaps=None), 1),   # no snapshot buffer
+    ([64], dict(snaps=ctypes.c_void_p(BASE + (8 << 32) + 8)), 5),
+    ([64], dict(snaps=_addr(6)), 6),   # snapshots alias o
+    ([64], dict(snaps=_addr(7)), 6),   # snapshots alias S_T
+    ([64], dict(snaps=_addr(3)), 6),   # snapshots alias alpha
+    ([64], dict(snaps=_addr(5)), 6),   # snapshots alias S0
+    ([64], dict(dtype=5), 3),          # the checks of kda_chunk_fwd still apply
+])
+def test_snapshot_validation(pos, over, code):
+    lib = _lib()
+    snaps = over.pop("snaps", _addr(8))
+    assert _snap(lib, pos, snaps=snaps, **over) == code
+
+
+def test_snapshot_negative_count_and_empty_list():
+    lib = _lib()
+    assert _snap(lib, [64], n=-1) == 2
+    # n_snap = 0 with no list and no buffer is a plain prefill call: validation passes up
+    # to the launch, which needs a device, so only the argument checks are exercised here
+    assert _snap(lib, None, n=0, snaps=None, dtype=9) == 3
+
+
 def test_python_binding_rejects_cpu_tensors():
     torch = pytest.importorskip("torch")
     import gated_delta_rule_07_amd as kda
