@@ -243,6 +243,34 @@ def main():
     log(f"decode: {d_step_ms * 1e3:.1f} us/step (kernel {d_kern_ms * 1e3:.1f} us), "
         f"state {d_gbs_state:.0f} GB/s, kernel {d_gbs_kernel:.0f} GB/s")
 
+    # ------- speculative decoding: 4 drafts per sequence, verify then commit -------
+    SK = 4
+    dr = ki.make_prefill(DB, SK, DH, dk, dv, wd.qkv_dtype, wd.alpha_mu, 0.0, seed=5, device=dev)
+    o_sp = torch.empty(DB, SK, DH, dv, device=dev, dtype=torch.float32)
+    u_sp = torch.empty(DB, DH, SK, dv, device=dev, dtype=torch.float32)
+    acc = torch.arange(DB, device=dev, dtype=torch.int32) % (SK + 1)  # 0..4 drafts accepted
+    sp_seq = 4 * (SK + 1) - 1  # a sequence that accepts all 4 drafts; parity on its heads
+    S_sp0 = S[sp_seq].clone()
+    kda.kda_decode_verify(dr["q"], dr["k"], dr["v"], dr["alpha"], dr["beta"], S, o=o_sp, u=u_sp)
+    kda.kda_decode_commit(dr["k"], dr["alpha"], u_sp, acc, S)
+    torch.cuda.synchronize()
+    hs = {n: v[sp_seq:sp_seq + 1].cpu() for n, v in dr.items() if n != "S0"}
+    rso, rss = oracle.forward(hs["q"], hs["k"], hs["v"], hs["alpha"], hs["beta"], S_sp0[None].cpu())
+    e_spo = rel_err_heads(o_sp[sp_seq:sp_seq + 1].permute(0, 2, 1, 3).reshape(DH, SK, dv).cpu().double().numpy(),
+                          rso)
+    e_sps = rel_err_heads(S[sp_seq].cpu().double().numpy(), rss)
+    del hs, rso, rss
+    _, v_kern_ms, _ = timed_launches(
+        lambda: kda.kda_decode_verify(dr["q"], dr["k"], dr["v"], dr["alpha"], dr["beta"], S, o=o_sp, u=u_sp),
+        20, torch)
+    _, c_kern_ms, _ = timed_launches(lambda: kda.kda_decode_commit(dr["k"], dr["alpha"], u_sp, acc, S), 20, torch)
+    n_commit = int((acc > 0).sum().item())
+    v_bytes = DB * DH * dk * dv * 4 + DB * SK * DH * (2 * (2 * dk + dv) + 4 * dk + 4 + 4 * dv) + DB * DH * SK * dv * 4
+    c_bytes = 2 * n_commit * DH * dk * dv * 4
+    log(f"spec decode ({SK} drafts): verify {v_kern_ms * 1e3:.1f} us ({v_bytes / v_kern_ms / 1e6:.0f} GB/s), "
+        f"commit {c_kern_ms * 1e3:.1f} us ({c_bytes / c_kern_ms / 1e6:.0f} GB/s); {SK} decode steps "
+        f"{SK * d_kern_ms * 1e3:.1f} us; parity o {e_spo:.2e} S {e_sps:.2e}")
+
     if args.copy_probe:
         a = torch.empty(1 << 28, device=dev, dtype=torch.float32)
         b = torch.empty_like(a)
@@ -258,7 +286,7 @@ def main():
                          f"({len(heads) * T} token-heads, {cpu_s:.1f} s wall); tokens/s = "
                          f"token-heads/s / H", "cpu": _cpu_model()}
 
-    parity_ok = max(e_o, e_s, e_do, e_ds, e_snap) <= TOL_REL and snap_last_is_state
+    parity_ok = max(e_o, e_s, e_do, e_ds, e_snap, e_spo, e_sps) <= TOL_REL and snap_last_is_state
     out = {
         "metric": METRIC,
         "value": tokens_per_s,
@@ -295,6 +323,13 @@ def main():
                       "ms_per_step": s_wall_ms / args.steps, "kernel_ms": s_kern_ms,
                       "overhead_vs_prefill": s_kern_ms / kern_ms - 1, "snapshot_bytes": snap_bytes,
                       "parity_first_snapshot": e_snap, "last_snapshot_equals_S_T": snap_last_is_state},
+        "spec_decode": {"workload": f"decode B={DB} H={DH} d={dk} with {SK} draft tokens per sequence: "
+                                    f"kda_decode_verify, then kda_decode_commit with 0..{SK} accepted "
+                                    f"({n_commit} of {DB} sequences commit)",
+                        "verify_us": v_kern_ms * 1e3, "commit_us": c_kern_ms * 1e3,
+                        "verify_gbps": v_bytes / v_kern_ms / 1e6, "commit_gbps": c_bytes / c_kern_ms / 1e6,
+                        "sequential_decode_us": SK * d_kern_ms * 1e3,
+                        "parity_o": e_spo, "parity_S": e_sps},
         "parity": {"pass": parity_ok, "tol_rel_rms": TOL_REL, "prefill_o": e_o, "prefill_S_T": e_s,
                    "prefill_heads": heads, "decode_o": e_do, "decode_S": e_ds, "decode_states": dheads},
         "cpu_baseline": cpu,

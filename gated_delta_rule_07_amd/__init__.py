@@ -13,12 +13,14 @@ from pathlib import Path
 
 import torch
 
-__all__ = ["kda_chunk_fwd", "kda_chunk_fwd_snapshots", "kda_decode_step", "kda_status_string", "kda_version",
+__all__ = ["kda_chunk_fwd", "kda_chunk_fwd_snapshots", "kda_decode_step", "kda_decode_verify",
+           "kda_decode_commit", "kda_status_string", "kda_version",
            "kda_last_hip_error", "library_path", "load_library", "KdaError",
-           "KDA_F32", "KDA_BF16", "KDA_MAX_SNAPSHOTS"]
+           "KDA_F32", "KDA_BF16", "KDA_MAX_SNAPSHOTS", "KDA_MAX_DRAFT"]
 
 KDA_F32, KDA_BF16 = 0, 1
 KDA_MAX_SNAPSHOTS = 128
+KDA_MAX_DRAFT = 16
 _PKG = Path(__file__).resolve().parent
 _LIB_PATH = _PKG / "libkda.so"
 _lib = None
@@ -54,6 +56,10 @@ def load_library():
                                             i32, i32, i32, i32, i32, i32, vp]
     lib.kda_decode_step.restype = i32
     lib.kda_decode_step.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
+    lib.kda_decode_verify.restype = i32
+    lib.kda_decode_verify.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, vp]
+    lib.kda_decode_commit.restype = i32
+    lib.kda_decode_commit.argtypes = [vp, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_status_string.argtypes = [i32]
     lib.kda_last_hip_error.restype = i32
@@ -218,3 +224,69 @@ def kda_decode_step(q, k, v, alpha, beta, S, *, o=None, o_dtype=torch.float32, s
     if st != 0:
         raise KdaError(st, "kda_decode_step")
     return o
+
+
+def kda_decode_verify(q, k, v, alpha, beta, S, *, o=None, u=None, o_dtype=torch.float32, stream=None):
+    """Speculative decoding, pass 1: apply K draft tokens per (sequence, head)
+    without changing ``S``.  q, k: [B,K,H,d_k]; v: [B,K,H,d_v]; alpha: [B,K,H,d_k];
+    beta: [B,K,H]; S: [B,H,d_k,d_v] fp32 (read only).  Returns ``(o, u)``: o
+    [B,K,H,d_v] (o_t as if the first t drafts were accepted) and u [B,H,K,d_v]
+    fp32, the write vectors ``kda_decode_commit`` needs."""
+    lib = load_library()
+    _check(q, "q")
+    dev = q.device
+    for t, n in ((k, "k"), (v, "v")):
+        _check(t, n, q.dtype, dev)
+    _check(alpha, "alpha", torch.float32, dev)
+    _check(beta, "beta", torch.float32, dev)
+    _check(S, "S", torch.float32, dev)
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("libkda: draft q/k/v must be [B,K,H,d]")
+    B, K, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or alpha.shape != q.shape or v.shape[:3] != q.shape[:3] or beta.shape != (B, K, H):
+        raise ValueError("libkda: inconsistent shapes")
+    if S.shape != (B, H, dk, dv):
+        raise ValueError("libkda: S must be [B,H,d_k,d_v]")
+    if o is None:
+        o = torch.empty(B, K, H, dv, device=dev, dtype=o_dtype)
+    else:
+        _check(o, "o", None, dev)
+        if o.shape != (B, K, H, dv):
+            raise ValueError("libkda: o must be [B,K,H,d_v]")
+    if u is None:
+        u = torch.empty(B, H, K, dv, device=dev, dtype=torch.float32)
+    else:
+        _check(u, "u", torch.float32, dev)
+        if u.shape != (B, H, K, dv):
+            raise ValueError("libkda: u must be [B,H,K,d_v]")
+    st = lib.kda_decode_verify(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(alpha), _ptr(beta), _ptr(S),
+                               _ptr(o), _dtype_code(o), _ptr(u), B, K, H, dk, dv, _stream(dev, stream))
+    if st != 0:
+        raise KdaError(st, "kda_decode_verify")
+    return o, u
+
+
+def kda_decode_commit(k, alpha, u, n_accept, S, *, stream=None):
+    """Speculative decoding, pass 2: advance ``S`` in place over the accepted
+    drafts, ``n_accept[b]`` of them for sequence b (int32 [B] on the device,
+    clamped to [0, K]).  k, alpha: the drafts' [B,K,H,d_k] inputs of
+    ``kda_decode_verify``; u: its [B,H,K,d_v] output.  Returns ``S``."""
+    lib = load_library()
+    _check(k, "k")
+    dev = k.device
+    _check(alpha, "alpha", torch.float32, dev)
+    _check(u, "u", torch.float32, dev)
+    _check(n_accept, "n_accept", torch.int32, dev)
+    _check(S, "S", torch.float32, dev)
+    if k.dim() != 4:
+        raise ValueError("libkda: draft k must be [B,K,H,d_k]")
+    B, K, H, dk = k.shape
+    dv = S.shape[-1]
+    if alpha.shape != k.shape or S.shape != (B, H, dk, dv) or u.shape != (B, H, K, dv) or n_accept.shape != (B,):
+        raise ValueError("libkda: inconsistent shapes")
+    st = lib.kda_decode_commit(_ptr(k), _dtype_code(k), _ptr(alpha), _ptr(u), _ptr(n_accept), _ptr(S),
+                               B, K, H, dk, dv, _stream(dev, stream))
+    if st != 0:
+        raise KdaError(st, "kda_decode_commit")
+    return S

@@ -208,4 +208,70 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, kda_dtyp
   return KDA_OK;
 }
 
+kda_status kda_decode_verify(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
+                             const float* alpha, const float* beta, const float* S,
+                             void* o, kda_dtype o_dtype, float* u,
+                             int B, int K, int H, int d_k, int d_v, void* stream) {
+  if (qkv_dtype != KDA_F32 && qkv_dtype != KDA_BF16) return KDA_ERR_DTYPE;
+  if (o_dtype != KDA_F32 && o_dtype != KDA_BF16) return KDA_ERR_DTYPE;
+  if (B < 1 || H < 1 || K < 1 || K > KDA_MAX_DRAFT) return KDA_ERR_SHAPE;
+  if (!dim_ok(d_k) || !dim_ok(d_v)) return KDA_ERR_UNSUPPORTED;
+  if (!sizes_ok(B, K, H, d_k, d_v)) return KDA_ERR_SHAPE;
+  if (!q || !k || !v || !alpha || !beta || !S || !o || !u) return KDA_ERR_NULL;
+  const void* ptrs[] = {q, k, v, alpha, beta, S, o, u};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return KDA_ERR_MISALIGNED;
+  const int io = (qkv_dtype == KDA_BF16) ? 1 : 0;
+  if (!kda::spec_supported(io, d_k, d_v)) return KDA_ERR_UNSUPPORTED;
+
+  const size_t esz = (qkv_dtype == KDA_BF16) ? 2 : 4;
+  const size_t osz = (o_dtype == KDA_BF16) ? 2 : 4;
+  const size_t ntok = (size_t)B * K * H;
+  const Span ins[] = {span(q, ntok * d_k * esz), span(k, ntok * d_k * esz), span(v, ntok * d_v * esz),
+                      span(alpha, ntok * d_k * 4), span(beta, ntok * 4), span(S, (size_t)B * H * d_k * d_v * 4)};
+  const Span so = span(o, ntok * d_v * osz), su = span(u, ntok * d_v * 4);
+  if (overlap(so, su)) return KDA_ERR_ALIAS;
+  for (const Span& s : ins)
+    if (overlap(so, s) || overlap(su, s)) return KDA_ERR_ALIAS;
+
+  kda::VerifyParams p{q, k, v, alpha, beta, S, o, u, B, K, H, d_k, d_v, o_dtype == KDA_F32 ? 1 : 0};
+  const hipError_t e = kda::launch_verify(p, io, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return KDA_ERR_HIP;
+  }
+  return KDA_OK;
+}
+
+kda_status kda_decode_commit(const void* k, kda_dtype qkv_dtype, const float* alpha, const float* u,
+                             const int* n_accept, float* S,
+                             int B, int K, int H, int d_k, int d_v, void* stream) {
+  if (qkv_dtype != KDA_F32 && qkv_dtype != KDA_BF16) return KDA_ERR_DTYPE;
+  if (B < 1 || H < 1 || K < 1 || K > KDA_MAX_DRAFT) return KDA_ERR_SHAPE;
+  if (!dim_ok(d_k) || !dim_ok(d_v)) return KDA_ERR_UNSUPPORTED;
+  if (!sizes_ok(B, K, H, d_k, d_v)) return KDA_ERR_SHAPE;
+  if (!k || !alpha || !u || !n_accept || !S) return KDA_ERR_NULL;
+  const void* ptrs[] = {k, alpha, u, n_accept, S};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return KDA_ERR_MISALIGNED;
+  const int io = (qkv_dtype == KDA_BF16) ? 1 : 0;
+  if (!kda::spec_supported(io, d_k, d_v)) return KDA_ERR_UNSUPPORTED;
+
+  const size_t esz = (qkv_dtype == KDA_BF16) ? 2 : 4;
+  const size_t ntok = (size_t)B * K * H;
+  const Span ss = span(S, (size_t)B * H * d_k * d_v * 4);
+  const Span ins[] = {span(k, ntok * d_k * esz), span(alpha, ntok * d_k * 4), span(u, ntok * d_v * 4),
+                      span(n_accept, (size_t)B * 4)};
+  for (const Span& s : ins)
+    if (overlap(ss, s)) return KDA_ERR_ALIAS;
+
+  kda::CommitParams p{k, alpha, u, n_accept, S, B, K, H, d_k, d_v};
+  const hipError_t e = kda::launch_commit(p, io, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return KDA_ERR_HIP;
+  }
+  return KDA_OK;
+}
+
 }  // extern "C"

@@ -51,6 +51,32 @@ hipError_t launch_prefill(const PrefillParams& p, const SnapList& snap, int io_d
 bool prefill_pipe_supported(int io_dtype, int dk, int dv, int chunk, int H);
 hipError_t launch_prefill_pipe(const PrefillParams& p, const SnapList& snap, hipStream_t s);
 
+// Speculative decoding: K draft tokens per (sequence, head).
+constexpr int kMaxDraft = 16;
+struct VerifyParams {
+  const void* q;  // [B][K][H][dk]
+  const void* k;
+  const void* v;  // [B][K][H][dv]
+  const float* alpha;
+  const float* beta;  // [B][K][H]
+  const float* S;     // [B][H][dk][dv], read only
+  void* o;            // [B][K][H][dv]
+  float* u;           // [B][H][K][dv]
+  int B, K, H, dk, dv;
+  int o_f32;
+};
+struct CommitParams {
+  const void* k;  // [B][K][H][dk]
+  const float* alpha;
+  const float* u;         // [B][H][K][dv]
+  const int* n_accept;    // [B], clamped to [0, K]
+  float* S;               // [B][H][dk][dv], updated in place
+  int B, K, H, dk, dv;
+};
+bool spec_supported(int io_dtype, int dk, int dv);
+hipError_t launch_verify(const VerifyParams& p, int io_dtype, hipStream_t s);
+hipError_t launch_commit(const CommitParams& p, int io_dtype, hipStream_t s);
+
 bool decode_supported(int io_dtype, int dk, int dv);
 hipError_t launch_decode(const DecodeParams& p, int io_dtype, hipStream_t s);
 

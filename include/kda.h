@@ -146,6 +146,54 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, kda_dtyp
                            const float* alpha, const float* beta, float* S, void* o, kda_dtype o_dtype,
                            int B, int H, int d_k, int d_v, void* stream);
 
+/* Most draft tokens one speculative step may verify. */
+#define KDA_MAX_DRAFT 16
+
+/*
+ * Speculative decoding, pass 1 of 2: verify K draft tokens of each of B
+ * sequences without changing the state.  Each decode step overwrites the state
+ * in place, so a rejected draft token could not be taken back afterwards (the
+ * second page, "Kimi 모델 분석", serving section on speculative decoding; the
+ * first page, section 13, on restoring the state after rejected draft tokens).
+ * This call reads S once and applies the K tokens in registers, exactly as K
+ * kda_decode_step calls would (same recurrence, fp32), and stores what the
+ * commit pass needs instead of the state.
+ *
+ *   q, k   : [B][K][H][d_k] qkv_dtype     v: [B][K][H][d_v] qkv_dtype   (read)
+ *   alpha  : [B][K][H][d_k] fp32          beta: [B][K][H] fp32          (read)
+ *   S      : [B][H][d_k][d_v] fp32, the state before the drafts (read only)
+ *   o      : [B][K][H][d_v] o_dtype: o_t as if tokens 1..t were accepted (written)
+ *   u      : [B][H][K][d_v] fp32: the write vectors u_t = beta_t (v_t - Sbar^T k_t)
+ *            of the K updates S_t = Diag(alpha_t) S_{t-1} + k_t u_t^T   (written)
+ *   K      : 1 .. KDA_MAX_DRAFT
+ *
+ * o and u may overlap nothing else (KDA_ERR_ALIAS).  Other rules as for
+ * kda_decode_step.
+ */
+kda_status kda_decode_verify(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
+                             const float* alpha, const float* beta, const float* S,
+                             void* o, kda_dtype o_dtype, float* u,
+                             int B, int K, int H, int d_k, int d_v, void* stream);
+
+/*
+ * Speculative decoding, pass 2 of 2: advance the state over the accepted
+ * prefix.  For sequence b, j = n_accept[b] (clamped to [0, K]) tokens were
+ * accepted; S becomes the state after them,
+ *     S_j = Diag(P_j) S + sum_{t<j} Diag(P_j / P_{t+1}) k_t u_t^T,
+ *     P_m = prod_{s<m} alpha_s   (per key channel; products only, no division),
+ * the closed form of j steps of the recurrence, in one read and one write of
+ * each state (none when j = 0).  k, alpha and u are the arguments and output
+ * of the kda_decode_verify call for the same drafts.
+ *
+ *   n_accept: [B] int32, DEVICE memory (read)
+ *   S       : [B][H][d_k][d_v] fp32, updated in place
+ *
+ * S may overlap none of the inputs (KDA_ERR_ALIAS).
+ */
+kda_status kda_decode_commit(const void* k, kda_dtype qkv_dtype, const float* alpha, const float* u,
+                             const int* n_accept, float* S,
+                             int B, int K, int H, int d_k, int d_v, void* stream);
+
 /* Human-readable text for a status code (static storage; never NULL). */
 const char* kda_status_string(kda_status s);
 

@@ -146,6 +146,47 @@ def test_snapshot_negative_count_and_empty_list():
     assert _snap(lib, None, n=0, snaps=None, dtype=9) == 3
 
 
+def _verify(lib, **over):
+    a = dict(q=_addr(0), k=_addr(1), v=_addr(2), dtype=1, alpha=_addr(3), beta=_addr(4), S=_addr(5),
+             o=_addr(6), odt=0, u=_addr(7), B=4, K=4, H=2, dk=128, dv=128)
+    a.update(over)
+    return lib.kda_decode_verify(a["q"], a["k"], a["v"], a["dtype"], a["alpha"], a["beta"], a["S"], a["o"],
+                                 a["odt"], a["u"], a["B"], a["K"], a["H"], a["dk"], a["dv"], None)
+
+
+def _commit(lib, **over):
+    a = dict(k=_addr(1), dtype=1, alpha=_addr(3), u=_addr(7), n=_addr(8), S=_addr(5), B=4, K=4, H=2, dk=128, dv=128)
+    a.update(over)
+    return lib.kda_decode_commit(a["k"], a["dtype"], a["alpha"], a["u"], a["n"], a["S"], a["B"], a["K"], a["H"],
+                                 a["dk"], a["dv"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(dtype=3), 3), (dict(odt=2), 3),
+    (dict(K=0), 2), (dict(K=17), 2), (dict(B=0), 2),
+    (dict(dk=24), 4), (dict(dv=512), 4),
+    (dict(u=None), 1), (dict(S=None), 1), (dict(beta=None), 1),
+    (dict(u=ctypes.c_void_p(BASE + (7 << 32) + 4)), 5),
+    (dict(o=_addr(5)), 6),   # o aliases the state
+    (dict(u=_addr(0)), 6),   # u aliases q
+    (dict(u=_addr(6)), 6),   # u aliases o
+])
+def test_verify_validation(over, code):
+    assert _verify(_lib(), **over) == code
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(dtype=-1), 3), (dict(K=0), 2), (dict(K=99), 2), (dict(H=0), 2), (dict(dk=100), 4),
+    (dict(n=None), 1), (dict(S=None), 1), (dict(u=None), 1),
+    (dict(n=ctypes.c_void_p(BASE + (8 << 32) + 4)), 5),
+    (dict(S=_addr(7)), 6),   # state aliases u
+    (dict(S=_addr(8)), 6),   # state aliases the accepted counts
+    (dict(S=_addr(1)), 6),   # state aliases k
+])
+def test_commit_validation(over, code):
+    assert _commit(_lib(), **over) == code
+
+
 def test_python_binding_rejects_cpu_tensors():
     torch = pytest.importorskip("torch")
     import gated_delta_rule_07_amd as kda
