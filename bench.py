@@ -189,6 +189,39 @@ def main():
         f"{100 * (s_kern_ms / kern_ms - 1):+.1f}%); snapshot@{snap_pos[0]} err {e_snap:.3e}, "
         f"last == S_T: {snap_last_is_state}")
 
+    # ------- a packed batch of 16 sequences of mixed lengths (kda_chunk_fwd_varlen) -------
+    gl = torch.Generator().manual_seed(17)
+    v_lens = [int(1024 * 2 ** (4 * r)) for r in torch.rand(16, generator=gl).tolist()]  # 1K .. 16K tokens
+    v_total = sum(v_lens)
+    vx = ki.make_prefill(1, v_total, H, dk, dv, w.qkv_dtype, w.alpha_mu, w.s0_std, seed=3, device=dev)
+    vflat = {n: vx[n][0] for n in ("q", "k", "v", "alpha", "beta")}
+    v_S0 = torch.cat([vx["S0"]] * len(v_lens), 0).contiguous()
+    v_cu = torch.tensor([0] + torch.cumsum(torch.tensor(v_lens), 0).tolist(), dtype=torch.int32, device=dev)
+    v_o = torch.empty(v_total, H, dv, device=dev, dtype=torch.float32)
+    v_ST = torch.empty(len(v_lens), H, dk, dv, device=dev, dtype=torch.float32)
+
+    def vstep():
+        kda.kda_chunk_fwd_varlen(vflat["q"], vflat["k"], vflat["v"], vflat["alpha"], vflat["beta"], v_cu, v_S0,
+                                 chunk=C, o=v_o, S_T=v_ST)
+
+    vstep()
+    torch.cuda.synchronize()
+    vb = int(min(range(len(v_lens)), key=lambda i: v_lens[i]))  # the shortest sequence, against the oracle
+    vs0 = int(v_cu[vb])
+    hv = {n: vflat[n][vs0:vs0 + v_lens[vb]][None].cpu() for n in vflat}
+    rvo, rvs = oracle.forward(hv["q"], hv["k"], hv["v"], hv["alpha"], hv["beta"], v_S0[vb:vb + 1].cpu(),
+                              heads=[0, H - 1], threads=threads)
+    e_vo = rel_err_heads(v_o[vs0:vs0 + v_lens[vb]].permute(1, 0, 2)[[0, H - 1]].cpu().double().numpy(), rvo)
+    e_vs = rel_err_heads(v_ST[vb][[0, H - 1]].cpu().double().numpy(), rvs)
+    del hv, rvo, rvs
+    for _ in range(args.warmup):
+        vstep()
+    v_wall_ms, v_kern_ms, _ = timed_launches(vstep, args.steps, torch)
+    v_tok_s = v_total / (v_kern_ms / 1e3)
+    log(f"varlen: {len(v_lens)} sequences, {v_total} tokens ({min(v_lens)}..{max(v_lens)}): "
+        f"{v_kern_ms:.3f} ms, {v_tok_s:.4g} tok/s; parity o {e_vo:.2e} S_T {e_vs:.2e}")
+    del vx, vflat
+
     # ---------------- decode: B=256, H=32, d=128, 100 in-place steps ----------------
     wd = ki.WORKLOADS[4]
     DB, DH = wd.B, wd.H
@@ -286,7 +319,7 @@ def main():
                          f"({len(heads) * T} token-heads, {cpu_s:.1f} s wall); tokens/s = "
                          f"token-heads/s / H", "cpu": _cpu_model()}
 
-    parity_ok = max(e_o, e_s, e_do, e_ds, e_snap, e_spo, e_sps) <= TOL_REL and snap_last_is_state
+    parity_ok = max(e_o, e_s, e_do, e_ds, e_snap, e_spo, e_sps, e_vo, e_vs) <= TOL_REL and snap_last_is_state
     out = {
         "metric": METRIC,
         "value": tokens_per_s,
@@ -323,6 +356,10 @@ def main():
                       "ms_per_step": s_wall_ms / args.steps, "kernel_ms": s_kern_ms,
                       "overhead_vs_prefill": s_kern_ms / kern_ms - 1, "snapshot_bytes": snap_bytes,
                       "parity_first_snapshot": e_snap, "last_snapshot_equals_S_T": snap_last_is_state},
+        "varlen": {"workload": f"packed batch of {len(v_lens)} sequences, {v_total} tokens "
+                               f"(lengths {min(v_lens)}..{max(v_lens)}), H={H} d={dk}, kda_chunk_fwd_varlen",
+                   "kernel_ms": v_kern_ms, "tokens_per_s": v_tok_s, "lengths": v_lens,
+                   "parity_o": e_vo, "parity_S_T": e_vs},
         "spec_decode": {"workload": f"decode B={DB} H={DH} d={dk} with {SK} draft tokens per sequence: "
                                     f"kda_decode_verify, then kda_decode_commit with 0..{SK} accepted "
                                     f"({n_commit} of {DB} sequences commit)",

@@ -13,7 +13,8 @@ from pathlib import Path
 
 import torch
 
-__all__ = ["kda_chunk_fwd", "kda_chunk_fwd_snapshots", "kda_decode_step", "kda_decode_verify",
+__all__ = ["kda_chunk_fwd", "kda_chunk_fwd_snapshots", "kda_chunk_fwd_varlen", "kda_decode_step",
+           "kda_decode_verify",
            "kda_decode_commit", "kda_status_string", "kda_version",
            "kda_last_hip_error", "library_path", "load_library", "KdaError",
            "KDA_F32", "KDA_BF16", "KDA_MAX_SNAPSHOTS", "KDA_MAX_DRAFT"]
@@ -56,6 +57,9 @@ def load_library():
                                             i32, i32, i32, i32, i32, i32, vp]
     lib.kda_decode_step.restype = i32
     lib.kda_decode_step.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
+    lib.kda_chunk_fwd_varlen.restype = i32
+    lib.kda_chunk_fwd_varlen.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, i32, vp, vp, i32, i32,
+                                         i32, i32, i32, i32, vp]
     lib.kda_decode_verify.restype = i32
     lib.kda_decode_verify.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, vp]
     lib.kda_decode_commit.restype = i32
@@ -191,6 +195,46 @@ def kda_chunk_fwd_snapshots(q, k, v, alpha, beta, S0=None, *, snap_tokens, chunk
     if st != 0:
         raise KdaError(st, "kda_chunk_fwd_snapshots")
     return o, S_T, snaps
+
+
+def kda_chunk_fwd_varlen(q, k, v, alpha, beta, cu_seqlens, S0=None, *, chunk: int = 64, o=None, S_T=None,
+                         o_dtype=torch.float32, want_state: bool = True, stream=None):
+    """Prefill over a packed batch: returns ``(o, S_T)``.
+
+    q, k, alpha: [total_T,H,d_k]; v: [total_T,H,d_v]; beta: [total_T,H];
+    cu_seqlens: int32 [N+1] on the device (sequence b is rows cu[b]..cu[b+1]);
+    S0: [N,H,d_k,d_v] fp32 or None.  o: [total_T,H,d_v]; S_T: [N,H,d_k,d_v].
+    """
+    lib = load_library()
+    _check(cu_seqlens, "cu_seqlens", torch.int32, q.device if isinstance(q, torch.Tensor) else None)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("libkda: cu_seqlens must be [N+1] with N >= 1")
+    N = cu_seqlens.numel() - 1
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("libkda: packed q/k/v must be [total_T,H,d]")
+    if S0 is not None and S0.shape[0] != N:
+        raise ValueError("libkda: S0 must be [N,H,d_k,d_v]")
+    if S_T is not None and S_T.shape[0] != N:
+        raise ValueError("libkda: S_T must be [N,H,d_k,d_v]")
+    # the packed rows are one [1,total_T,...] batch for the shared checks
+    dev, (_, T, H, dk, dv), o4, _ = _prefill_prep(q[None], k[None], v[None], alpha[None], beta[None], None,
+                                                  None if o is None else o[None], None, o_dtype, False)
+    if S0 is not None:
+        _check(S0, "S0", torch.float32, dev)
+        if S0.shape != (N, H, dk, dv):
+            raise ValueError("libkda: S0 must be [N,H,d_k,d_v]")
+    if want_state and S_T is None:
+        S_T = torch.empty(N, H, dk, dv, device=dev, dtype=torch.float32)
+    elif S_T is not None:
+        _check(S_T, "S_T", torch.float32, dev)
+        if S_T.shape != (N, H, dk, dv):
+            raise ValueError("libkda: S_T must be [N,H,d_k,d_v]")
+    st = lib.kda_chunk_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(alpha), _ptr(beta), _ptr(S0),
+                                  _ptr(o4), _dtype_code(o4), _ptr(S_T), _ptr(cu_seqlens), N, T, H, dk, dv,
+                                  int(chunk), _stream(dev, stream))
+    if st != 0:
+        raise KdaError(st, "kda_chunk_fwd_varlen")
+    return o4[0], S_T
 
 
 def kda_decode_step(q, k, v, alpha, beta, S, *, o=None, o_dtype=torch.float32, stream=None):

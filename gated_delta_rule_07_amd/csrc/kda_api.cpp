@@ -93,16 +93,18 @@ int kda_version(void) { return kVersion; }
 namespace {
 
 // Shared body of kda_chunk_fwd and kda_chunk_fwd_snapshots (n_snap == 0: none).
+// cu != NULL: a packed batch of B sequences over T token rows (T = the packed
+// length); otherwise B sequences of T tokens each.
 kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, kda_dtype qkv_dtype, const float* alpha,
                           const float* beta, const float* S0, void* o, kda_dtype o_dtype, float* S_T,
-                          const int* snap_tokens, int n_snap, float* snaps, int B, int T, int H, int d_k, int d_v,
-                          int chunk, void* stream) {
+                          const int* snap_tokens, int n_snap, float* snaps, const int* cu, int B, int T, int H,
+                          int d_k, int d_v, int chunk, void* stream) {
   if (qkv_dtype != KDA_F32 && qkv_dtype != KDA_BF16) return KDA_ERR_DTYPE;
   if (o_dtype != KDA_F32 && o_dtype != KDA_BF16) return KDA_ERR_DTYPE;
   if (B < 1 || H < 1 || T < 0) return KDA_ERR_SHAPE;
   if (!dim_ok(d_k) || !dim_ok(d_v)) return KDA_ERR_UNSUPPORTED;
   if (chunk != 16 && chunk != 32 && chunk != 64) return KDA_ERR_UNSUPPORTED;
-  if (!sizes_ok(B, T, H, d_k, d_v)) return KDA_ERR_SHAPE;
+  if (!sizes_ok(cu ? 1 : B, T, H, d_k, d_v) || (long long)B * H > (1LL << 26)) return KDA_ERR_SHAPE;
   if (n_snap < 0 || n_snap > KDA_MAX_SNAPSHOTS) return KDA_ERR_SHAPE;
   if (T > 0 && (!q || !k || !v || !alpha || !beta || !o)) return KDA_ERR_NULL;
   if (n_snap > 0 && (!snap_tokens || !snaps)) return KDA_ERR_NULL;
@@ -113,7 +115,8 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, kda_dtype
     if (j > 0 && t <= snap_tokens[j - 1]) return KDA_ERR_SHAPE;
     snap.pos[j] = t;
   }
-  const void* ptrs[] = {q, k, v, alpha, beta, S0, o, S_T, n_snap > 0 ? snaps : nullptr};
+  if (cu && n_snap > 0) return KDA_ERR_UNSUPPORTED;
+  const void* ptrs[] = {q, k, v, alpha, beta, S0, o, S_T, n_snap > 0 ? snaps : nullptr, cu};
   for (const void* ptr : ptrs)
     if (ptr && !aligned16(ptr)) return KDA_ERR_MISALIGNED;
   const int io = (qkv_dtype == KDA_BF16) ? 1 : 0;
@@ -122,12 +125,13 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, kda_dtype
 
   const size_t esz = (qkv_dtype == KDA_BF16) ? 2 : 4;
   const size_t osz = (o_dtype == KDA_BF16) ? 2 : 4;
-  const size_t ntok = (size_t)B * T * H;
+  const size_t ntok = (size_t)(cu ? 1 : B) * T * H;
   const size_t sbytes = (size_t)B * H * d_k * d_v * 4;
   const Span none{0, 0};
   const Span in_spans[] = {T > 0 ? span(q, ntok * d_k * esz) : none, T > 0 ? span(k, ntok * d_k * esz) : none,
                            T > 0 ? span(v, ntok * d_v * esz) : none, T > 0 ? span(alpha, ntok * d_k * 4) : none,
-                           T > 0 ? span(beta, ntok * 4) : none, S0 ? span(S0, sbytes) : none};
+                           T > 0 ? span(beta, ntok * 4) : none, S0 ? span(S0, sbytes) : none,
+                           cu ? span(cu, (size_t)(B + 1) * 4) : none};
   const Span so = T > 0 ? span(o, ntok * d_v * osz) : none;
   const Span st = S_T ? span(S_T, sbytes) : none;
   const Span sn = n_snap > 0 ? span(snaps, sbytes * n_snap) : none;
@@ -135,13 +139,13 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, kda_dtype
   // no other input
   for (const Span& s : in_spans) {
     if (overlap(so, s) || overlap(sn, s)) return KDA_ERR_ALIAS;
-    if (&s != &in_spans[5] && overlap(st, s)) return KDA_ERR_ALIAS;
+    if (&s != &in_spans[5] && overlap(st, s)) return KDA_ERR_ALIAS;  // S_T may be S0 itself
   }
   if (S0 && S_T && S0 != S_T && overlap(st, in_spans[5])) return KDA_ERR_ALIAS;
   if (overlap(so, st) || overlap(so, sn) || overlap(st, sn)) return KDA_ERR_ALIAS;
 
   kda::PrefillParams p{q, k, v, alpha, beta, S0, o, S_T, B, T, H, d_k, d_v, o_dtype == KDA_F32 ? 1 : 0,
-                       n_snap > 0 ? snaps : nullptr, n_snap};
+                       n_snap > 0 ? snaps : nullptr, n_snap, cu};
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   const hipError_t e = plan.impl == IMPL_PIPE ? kda::launch_prefill_pipe(p, snap, hs)
                                               : kda::launch_prefill(p, snap, io, chunk, plan.slab, hs);
@@ -160,8 +164,8 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, kda_dtype 
                          const float* alpha, const float* beta, const float* S0,
                          void* o, kda_dtype o_dtype, float* S_T,
                          int B, int T, int H, int d_k, int d_v, int chunk, void* stream) {
-  return chunk_fwd_impl(q, k, v, qkv_dtype, alpha, beta, S0, o, o_dtype, S_T, nullptr, 0, nullptr, B, T, H, d_k,
-                        d_v, chunk, stream);
+  return chunk_fwd_impl(q, k, v, qkv_dtype, alpha, beta, S0, o, o_dtype, S_T, nullptr, 0, nullptr, nullptr, B, T,
+                        H, d_k, d_v, chunk, stream);
 }
 
 kda_status kda_chunk_fwd_snapshots(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
@@ -169,8 +173,18 @@ kda_status kda_chunk_fwd_snapshots(const void* q, const void* k, const void* v, 
                                    void* o, kda_dtype o_dtype, float* S_T,
                                    const int* snap_tokens, int n_snap, float* snaps,
                                    int B, int T, int H, int d_k, int d_v, int chunk, void* stream) {
-  return chunk_fwd_impl(q, k, v, qkv_dtype, alpha, beta, S0, o, o_dtype, S_T, snap_tokens, n_snap, snaps, B, T,
-                        H, d_k, d_v, chunk, stream);
+  return chunk_fwd_impl(q, k, v, qkv_dtype, alpha, beta, S0, o, o_dtype, S_T, snap_tokens, n_snap, snaps, nullptr,
+                        B, T, H, d_k, d_v, chunk, stream);
+}
+
+kda_status kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
+                                const float* alpha, const float* beta, const float* S0,
+                                void* o, kda_dtype o_dtype, float* S_T,
+                                const int* cu_seqlens, int N, int total_T,
+                                int H, int d_k, int d_v, int chunk, void* stream) {
+  if (!cu_seqlens) return KDA_ERR_NULL;
+  return chunk_fwd_impl(q, k, v, qkv_dtype, alpha, beta, S0, o, o_dtype, S_T, nullptr, 0, nullptr, cu_seqlens, N,
+                        total_T, H, d_k, d_v, chunk, stream);
 }
 
 kda_status kda_decode_step(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,

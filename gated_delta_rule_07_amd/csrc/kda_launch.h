@@ -18,7 +18,24 @@ struct PrefillParams {
   int o_f32;        // 1: o is fp32, 0: o is bf16
   float* snaps;     // [B][H][nsnap][dk][dv], written when nsnap > 0
   int nsnap;
+  // Packed variable-length batch: sequence b covers tokens [cu[b], cu[b+1]) of
+  // a [T][H][d] tensor (T = the packed length; values clamped to [0, T]).
+  // Null: B sequences of T tokens each.
+  const int* cu;
 };
+
+// Token range of sequence b: first packed token and length.
+__device__ __forceinline__ void seq_range(const PrefillParams& p, int b, long long& tok0, int& len) {
+  if (p.cu) {
+    const int s = min(max(p.cu[b], 0), p.T);
+    const int e = min(max(p.cu[b + 1], s), p.T);
+    tok0 = s;
+    len = e - s;
+  } else {
+    tok0 = (long long)b * p.T;
+    len = p.T;
+  }
+}
 
 // Token counts after which the state is recorded (ascending; a separate kernel
 // argument, read in place by the state waves).

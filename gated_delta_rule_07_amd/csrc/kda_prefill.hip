@@ -154,6 +154,8 @@ struct Raw {
 struct Ctx {
   PrefillParams p;
   int bh, b, h, col0;  // col0: first state column of this slab
+  int T;               // this sequence's length
+  long long tok0;      // its first token in the [.][H][d] token rows
 };
 
 template <class C>
@@ -168,8 +170,8 @@ __device__ __forceinline__ void load_raw(Raw<C>& raw, const Ctx& cx, int t0, int
       for (int i = 0; i < C::TGS; ++i) {
         const int t = t0 + tg * C::TGS + i;
         const int c = hh * C::HC + 4 * cq;
-        if (t < p.T) {
-          const size_t row = ((size_t)cx.b * p.T + t) * p.H + cx.h;
+        if (t < cx.T) {
+          const size_t row = (size_t)(cx.tok0 + t) * p.H + cx.h;
           raw.a[hh][i] = *reinterpret_cast<const f32x4*>(p.alpha + row * C::DK + c);
           raw.k[hh][i].load(static_cast<const IO*>(p.k) + row * C::DK + c);
           raw.q[hh][i].load(static_cast<const IO*>(p.q) + row * C::DK + c);
@@ -184,8 +186,8 @@ __device__ __forceinline__ void load_raw(Raw<C>& raw, const Ctx& cx, int t0, int
   for (int ps = 0; ps < C::VPASS; ++ps) {
     const int r = ps * C::VRPP + tid / C::VTPR;
     const int t = t0 + r;
-    if (r < C::CS && t < p.T) {
-      const size_t row = ((size_t)cx.b * p.T + t) * p.H + cx.h;
+    if (r < C::CS && t < cx.T) {
+      const size_t row = (size_t)(cx.tok0 + t) * p.H + cx.h;
       raw.v[ps] = *reinterpret_cast<const u32x4*>(static_cast<const IO*>(p.v) + row * p.dv + cx.col0 +
                                                   (tid % C::VTPR) * C::VV);
     } else {
@@ -193,7 +195,7 @@ __device__ __forceinline__ void load_raw(Raw<C>& raw, const Ctx& cx, int t0, int
     }
   }
   raw.beta = 0.0f;
-  if (tid < C::CS && t0 + tid < p.T) raw.beta = p.beta[((size_t)cx.b * p.T + t0 + tid) * p.H + cx.h];
+  if (tid < C::CS && t0 + tid < cx.T) raw.beta = p.beta[(size_t)(cx.tok0 + t0 + tid) * p.H + cx.h];
 }
 
 // ---- phase 1: decay scan and decayed operands for one pass of HC channels ----
@@ -510,8 +512,8 @@ __device__ void phase_state(Smem<C>& sm, f32x4 (&S)[C::NKT], int w, int lane, co
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = 16 * a + 4 * g + r;
-      if (t >= lo && t < hi && t0 + t < cx.p.T) {
-        const size_t idx = (((size_t)cx.b * cx.p.T + t0 + t) * cx.p.H + cx.h) * cx.p.dv + cx.col0 + 16 * w + m;
+      if (t >= lo && t < hi && t0 + t < cx.T) {
+        const size_t idx = ((size_t)(cx.tok0 + t0 + t) * cx.p.H + cx.h) * cx.p.dv + cx.col0 + 16 * w + m;
         const float ov = acc[r] * unscale;
         if (cx.p.o_f32) static_cast<float*>(cx.p.o)[idx] = ov;
         else static_cast<__bf16*>(cx.p.o)[idx] = (__bf16)ov;
@@ -614,7 +616,8 @@ __global__ __launch_bounds__(256, 1) void kda_prefill_kernel(PrefillParams p, Sn
                         : 0.0f;
   }
 
-  const int nchunks = (p.T + C::CS - 1) / C::CS;
+  seq_range(p, cx.b, cx.tok0, cx.T);
+  const int nchunks = (cx.T + C::CS - 1) / C::CS;
   Raw<C> raw;
   if (nchunks > 0) load_raw<C>(raw, cx, 0, tid);
   const size_t mat = (size_t)C::DK * p.dv;  // elements of one state
@@ -628,7 +631,7 @@ __global__ __launch_bounds__(256, 1) void kda_prefill_kernel(PrefillParams p, Sn
         process_chunk<C>(sm, raw, S, cx, t0, 16 * sq, 16 * sq + 16, false,
                          sq == C::NCT - 1 ? next : -1, tid, wave, lane);
     }
-    if (ns < p.nsnap && snap.pos[ns] == min(t0 + C::CS, p.T)) {
+    if (ns < p.nsnap && snap.pos[ns] == min(t0 + C::CS, cx.T)) {
       if (wave < C::NSW)
         store_state16<C>(p.snaps + ((size_t)cx.bh * p.nsnap + ns) * mat, S, p.dv, cx.col0 + 16 * wave + m, g);
       ++ns;

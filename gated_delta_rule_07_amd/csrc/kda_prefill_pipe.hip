@@ -180,6 +180,8 @@ __device__ __forceinline__ Item split_item(const Item& it, int T) {
 struct Ctx4 {
   PrefillParams p;
   int bh, b, h, col0, nchunks;
+  int T;           // this sequence's length
+  long long tok0;  // its first token in the [.][H][d] token rows
 };
 
 // ---- scan waves --------------------------------------------------------------------
@@ -201,8 +203,8 @@ __device__ void load_raw4(Raw4<C>& raw, const Ctx4& cx, int c, int sw, int lane)
   const PrefillParams& p = cx.p;
   const int cp = opaque(lane % C::PPW), tq = opaque(lane / C::PPW);
   const int t0 = c * CS;
-  const int rows = min(CS, p.T - t0);
-  const size_t row0 = ((size_t)cx.b * p.T + t0) * p.H + cx.h;
+  const int rows = min(CS, cx.T - t0);
+  const size_t row0 = (size_t)(cx.tok0 + t0) * p.H + cx.h;
   const int ts = p.H * C::DK;  // elements between tokens
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.alpha + row0 * C::DK, rows * ts * 4);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(static_cast<const __bf16*>(p.k) + row0 * C::DK, rows * ts * 2);
@@ -633,10 +635,10 @@ __device__ void out_pu_store(Smem4<C>& sm, f32x16& O, float usc, const Item& it,
   O = mma32(ld8(&pp[n * C::LDC + 16 + 8 * h]), ld8(&uf[(64 + lane) * 8]), O);
   const PrefillParams& p = cx.p;
   const int t0 = it.c * CS;
-  const int rows = chunk_end(it.c, p.T);
+  const int rows = chunk_end(it.c, cx.T);
   const int esz = p.o_f32 ? 4 : 2;
   const int rs = p.H * p.dv * esz;
-  char* ob = static_cast<char*>(p.o) + ((((size_t)cx.b * p.T + t0) * p.H + cx.h) * p.dv + cx.col0) * esz;
+  char* ob = static_cast<char*>(p.o) + (((size_t)(cx.tok0 + t0) * p.H + cx.h) * p.dv + cx.col0) * esz;
   const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(ob, rows * rs);
   const int vbase = 4 * h * rs + n * esz;
   if (p.o_f32) {
@@ -730,7 +732,7 @@ __device__ void run_role(Smem4<C>& sm, const Ctx4& cx, const SnapList& snap, int
 
   const Item none = {-1, 0, 0, 0, 0};
   Item sI = none, bI = none, stI = none, opI = none;
-  if (cx.nchunks > 0) sI = Item{0, 0, 0, chunk_end(0, p.T), CS};
+  if (cx.nchunks > 0) sI = Item{0, 0, 0, chunk_end(0, cx.T), CS};
   int par = 0, kstep = 0;
   int ns = 0;  // state role: next recorded position
   while (sI.seq >= 0 || bI.seq >= 0 || stI.seq >= 0 || opI.seq >= 0) {
@@ -745,7 +747,7 @@ __device__ void run_role(Smem4<C>& sm, const Ctx4& cx, const SnapList& snap, int
         KDA_STEP_MARK(2, kstep);
         scan4<C>(sm, raw, sI, sw, lane, par);
         KDA_STEP_MARK(3, kstep);
-        if (sI.hi == chunk_end(sI.c, p.T) && sI.c + 1 < cx.nchunks) {
+        if (sI.hi == chunk_end(sI.c, cx.T) && sI.c + 1 < cx.nchunks) {
           load_raw4<C>(raw, cx, sI.c + 1, sw, lane);  // prefetch the next chunk
           rc = sI.c + 1;
         }
@@ -758,7 +760,7 @@ __device__ void run_role(Smem4<C>& sm, const Ctx4& cx, const SnapList& snap, int
       if (stI.seq >= 0) {
         state_step<C>(sm, R, stI, lane);
         // record the state after a listed number of tokens
-        if (ns < p.nsnap && stI.hi == chunk_end(stI.c, p.T) && snap.pos[ns] == stI.c * CS + stI.hi) {
+        if (ns < p.nsnap && stI.hi == chunk_end(stI.c, cx.T) && snap.pos[ns] == stI.c * CS + stI.hi) {
           store_state<C>(p.snaps + ((size_t)cx.bh * p.nsnap + ns) * C::DK * p.dv + cx.col0, R, p.dv, lane);
           ++ns;
         }
@@ -774,8 +776,8 @@ __device__ void run_role(Smem4<C>& sm, const Ctx4& cx, const SnapList& snap, int
     // so after it only the regroup vote remains to be read.
     Item nI = none, spI = none;
     if (sI.seq >= 0) {
-      nI = next_item(sI, p.T, cx.nchunks);
-      spI = split_item(sI, p.T);
+      nI = next_item(sI, cx.T, cx.nchunks);
+      spI = split_item(sI, cx.T);
     }
     KDA_STEP_MARK(1, kstep);
     block_sync_lds();
@@ -818,7 +820,8 @@ __global__ __launch_bounds__(C::NT, 1) void kda_prefill_pipe_kernel(PrefillParam
   cx.b = cx.bh / p.H;
   cx.h = cx.bh % p.H;
   cx.col0 = (lid % nslab) * J;
-  cx.nchunks = (p.T + CS - 1) / CS;
+  seq_range(p, cx.b, cx.tok0, cx.T);
+  cx.nchunks = (cx.T + CS - 1) / CS;
   // T's upper-right 16x16 block is read as zeros and never written
   for (int i = tid; i < 2 * CS * C::LDC; i += C::NT) (&sm.t[0][0])[i] = (h16)0.0f;
   if (wave >= 4) run_role<C, SCAN>(sm, cx, snap, lane, wave - 4);

@@ -146,6 +146,31 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, kda_dtyp
                            const float* alpha, const float* beta, float* S, void* o, kda_dtype o_dtype,
                            int B, int H, int d_k, int d_v, void* stream);
 
+/*
+ * kda_chunk_fwd over a packed batch of N sequences of different lengths (for
+ * serving: prompts of a batch are concatenated along the token axis).  Sequence
+ * b covers token rows [cu_seqlens[b], cu_seqlens[b+1]) and is an independent
+ * recurrence with its own initial and final state.
+ *
+ *   q, k, alpha: [total_T][H][d_k]   v, o: [total_T][H][d_v]   beta: [total_T][H]
+ *                (dtypes as in kda_chunk_fwd)
+ *   S0, S_T    : [N][H][d_k][d_v] fp32 (S0 may be NULL; S_T may be NULL or S0)
+ *   cu_seqlens : [N + 1] int32, DEVICE memory, non-decreasing from 0 to total_T.
+ *                The kernels clamp each offset to [0, total_T] and each length
+ *                to >= 0, so no offset can make them access memory out of
+ *                range; o rows not covered by any sequence are not written.
+ *   N          : >= 1 sequences;  total_T >= 0.
+ *
+ * Validation and errors as kda_chunk_fwd (cu_seqlens must be non-NULL and
+ * 16-byte aligned, and may not overlap an output).  A sequence's results equal
+ * kda_chunk_fwd run on that sequence alone up to rounding.
+ */
+kda_status kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
+                                const float* alpha, const float* beta, const float* S0,
+                                void* o, kda_dtype o_dtype, float* S_T,
+                                const int* cu_seqlens, int N, int total_T,
+                                int H, int d_k, int d_v, int chunk, void* stream);
+
 /* Most draft tokens one speculative step may verify. */
 #define KDA_MAX_DRAFT 16
 

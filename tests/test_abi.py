@@ -146,6 +146,28 @@ def test_snapshot_negative_count_and_empty_list():
     assert _snap(lib, None, n=0, snaps=None, dtype=9) == 3
 
 
+def _varlen(lib, **over):
+    a = dict(q=_addr(0), k=_addr(1), v=_addr(2), dtype=1, alpha=_addr(3), beta=_addr(4), S0=_addr(5),
+             o=_addr(6), odt=0, S_T=_addr(7), cu=_addr(8), N=3, T=300, H=2, dk=128, dv=128, chunk=64)
+    a.update(over)
+    return lib.kda_chunk_fwd_varlen(a["q"], a["k"], a["v"], a["dtype"], a["alpha"], a["beta"], a["S0"], a["o"],
+                                    a["odt"], a["S_T"], a["cu"], a["N"], a["T"], a["H"], a["dk"], a["dv"],
+                                    a["chunk"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(cu=None), 1), (dict(q=None), 1),
+    (dict(N=0), 2), (dict(T=-5), 2), (dict(H=0), 2),
+    (dict(dk=12), 4), (dict(chunk=8), 4), (dict(dtype=4), 3),
+    (dict(cu=ctypes.c_void_p(BASE + (8 << 32) + 4)), 5),
+    (dict(cu=_addr(6)), 6),   # offsets alias o
+    (dict(cu=_addr(7)), 6),   # offsets alias S_T
+    (dict(o=_addr(3)), 6),    # o aliases alpha
+])
+def test_varlen_validation(over, code):
+    assert _varlen(_lib(), **over) == code
+
+
 def _verify(lib, **over):
     a = dict(q=_addr(0), k=_addr(1), v=_addr(2), dtype=1, alpha=_addr(3), beta=_addr(4), S=_addr(5),
              o=_addr(6), odt=0, u=_addr(7), B=4, K=4, H=2, dk=128, dv=128)
