@@ -24,6 +24,49 @@ struct PrefillParams {
   const int* cu;
 };
 
+// Packed batches of at most this many sequences are scheduled longest first.
+constexpr int kMaxRankedSeqs = 256;
+
+// The sequence a workgroup serves in rank slot r: for a packed batch of at most
+// kMaxRankedSeqs sequences, the one of r-th largest length (ties by index), so
+// the first workgroups to start take the longest sequences and the short ones
+// fill in behind them; otherwise r itself.  Every thread of the workgroup
+// calls it; `lens` is LDS for kMaxRankedSeqs ints.
+__device__ __forceinline__ int seq_by_length_rank(const int* cu, int n, int T, int r, int* lens, int* pick) {
+  if (!cu || n > kMaxRankedSeqs) return r;
+  for (int j = threadIdx.x; j < n; j += blockDim.x) {
+    const int s = min(max(cu[j], 0), T);
+    lens[j] = min(max(cu[j + 1], s), T) - s;
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < n; j += blockDim.x) {
+    const int lj = lens[j];
+    int rank = 0;
+    for (int i = 0; i < n; ++i) rank += (lens[i] > lj) || (lens[i] == lj && i < j);
+    if (rank == r) *pick = j;  // ranks are a permutation: exactly one writer
+  }
+  __syncthreads();
+  return *pick;
+}
+
+// Workgroup -> (task, slab), a task being one (sequence rank, head) pair served
+// by nslab workgroups.  Workgroups are dispatched in index order, round-robin
+// over the 8 XCDs (each with its own L2): a task's slabs go to one XCD, so they
+// share its L2 for the task's keys, queries and decays, and consecutive tasks
+// go to consecutive XCDs, so the tasks dispatched first -- the longest
+// sequences of a packed batch -- are spread over all of them.
+__device__ __forceinline__ void task_of_block(int nslab, int& task, int& slab) {
+  const int G = gridDim.x, bi = blockIdx.x;
+  if ((G / nslab) % 8 == 0) {
+    const int x = bi % 8, q = bi / 8;
+    slab = q % nslab;
+    task = (q / nslab) * 8 + x;
+  } else {
+    task = bi / nslab;
+    slab = bi % nslab;
+  }
+}
+
 // Token range of sequence b: first packed token and length.
 __device__ __forceinline__ void seq_range(const PrefillParams& p, int b, long long& tok0, int& len) {
   if (p.cu) {

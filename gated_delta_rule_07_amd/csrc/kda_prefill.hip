@@ -592,18 +592,15 @@ template <class C>
 __global__ __launch_bounds__(256, 1) void kda_prefill_kernel(PrefillParams p, SnapList snap) {
   __shared__ Smem<C> sm;
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
-  const int nslab = p.dv / C::J;
-  // XCD-aware placement: consecutive workgroup ids go round-robin over the 8
-  // XCDs, so remap them so the slabs of one head share an XCD (and its L2).
-  const int G = gridDim.x;
-  int lid = blockIdx.x;
-  if (G % 8 == 0) lid = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
+  int task, slab;
+  task_of_block(p.dv / C::J, task, slab);
+  __shared__ int seq_lens[kMaxRankedSeqs], seq_pick;
   Ctx cx;
   cx.p = p;
-  cx.bh = lid / nslab;
-  cx.b = cx.bh / p.H;
-  cx.h = cx.bh % p.H;
-  cx.col0 = (lid % nslab) * C::J;
+  cx.h = task % p.H;
+  cx.b = __builtin_amdgcn_readfirstlane(seq_by_length_rank(p.cu, p.B, p.T, task / p.H, seq_lens, &seq_pick));
+  cx.bh = cx.b * p.H + cx.h;
+  cx.col0 = slab * C::J;
   const int g = lane / 16, m = lane % 16;
 
   f32x4 S[C::NKT];

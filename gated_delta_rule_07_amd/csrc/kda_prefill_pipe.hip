@@ -810,16 +810,15 @@ __global__ __launch_bounds__(C::NT, 1) void kda_prefill_pipe_kernel(PrefillParam
   __shared__ Smem4<C> sm;
   const int tid = threadIdx.x, lane = tid % 64;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
-  const int nslab = p.dv / J;
-  const int Gn = gridDim.x;
-  int lid = blockIdx.x;
-  if (Gn % 8 == 0) lid = (blockIdx.x % 8) * (Gn / 8) + blockIdx.x / 8;  // slabs of a head on one XCD
+  int task, slab;
+  task_of_block(p.dv / J, task, slab);
+  __shared__ int seq_lens[kMaxRankedSeqs], seq_pick;
   Ctx4 cx;
   cx.p = p;
-  cx.bh = lid / nslab;
-  cx.b = cx.bh / p.H;
-  cx.h = cx.bh % p.H;
-  cx.col0 = (lid % nslab) * J;
+  cx.h = task % p.H;
+  cx.b = __builtin_amdgcn_readfirstlane(seq_by_length_rank(p.cu, p.B, p.T, task / p.H, seq_lens, &seq_pick));
+  cx.bh = cx.b * p.H + cx.h;
+  cx.col0 = slab * J;
   seq_range(p, cx.b, cx.tok0, cx.T);
   cx.nchunks = (cx.T + CS - 1) / CS;
   // T's upper-right 16x16 block is read as zeros and never written
