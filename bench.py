@@ -35,7 +35,9 @@ def log(msg):
 
 
 def prefill_counts(B, T, H, dk, dv, chunk, o_bytes):
-    """Algorithmic bytes and FLOPs of one prefill call (roofline)."""
+    """Algorithmic bytes and FLOPs of one prefill call: the q/k/v/alpha/beta reads
+    and o writes each token-head needs, plus one S0 read and S_T write per chain;
+    FLOPs of the chunk form at chunk size `chunk`."""
     th = B * T * H
     per_th_bytes = 2 * (2 * dk + dv) + 4 * dk + 4 + o_bytes * dv
     state_bytes = 2 * 4 * dk * dv * B * H
@@ -106,7 +108,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py: this build measures one GPU only (asked for {max(args.gpus, world)}); "
-              "the operator's (sequence, head) work is independent, see DESIGN.md for how it shards",
+              "every (sequence, head) chain is independent, so a multi-GPU run shards batch and heads, "
+              "one process per GPU",
               file=sys.stderr)
         sys.exit(2)
 
@@ -188,6 +191,56 @@ def main():
     log(f"prefill + {len(snap_pos)} snapshots: {s_wall_ms / args.steps:.3f} ms/step (kernel {s_kern_ms:.3f} ms, "
         f"{100 * (s_kern_ms / kern_ms - 1):+.1f}%); snapshot@{snap_pos[0]} err {e_snap:.3e}, "
         f"last == S_T: {snap_last_is_state}")
+
+    # ------- the same prefill with the gate fused in (z and A instead of alpha) -------
+    gz, gA = ki.make_gate((B, T, H, dk), H, w.qkv_dtype, seed=0, device=dev)
+
+    def gstep():
+        kda.kda_chunk_fwd_gated(x["q"], x["k"], x["v"], gz, gA, x["beta"], x["S0"], chunk=C, o=o, S_T=S_T)
+
+    gstep()
+    torch.cuda.synchronize()
+    e_go = e_gs = 0.0
+    for hid in (0, B * H // 2 + 5):
+        b_, h_ = divmod(hid, H)
+        hg = {n: x[n][b_:b_ + 1, :, h_:h_ + 1].cpu() for n in ("q", "k", "v", "beta")}
+        ga = oracle.gate_alpha(gz[b_:b_ + 1, :, h_:h_ + 1].cpu(), gA[h_:h_ + 1].cpu())
+        rgo, rgs = oracle.forward(hg["q"], hg["k"], hg["v"], ga, hg["beta"], x["S0"][b_:b_ + 1, h_:h_ + 1].cpu(),
+                                  threads=threads)
+        e_go = max(e_go, rel_err_heads(o[b_, :, h_][None].cpu().double().numpy(), rgo))
+        e_gs = max(e_gs, rel_err_heads(S_T[b_, h_][None].cpu().double().numpy(), rgs))
+        del hg, ga, rgo, rgs
+    for _ in range(args.warmup):
+        gstep()
+    g_wall_ms, g_kern_ms, _ = timed_launches(gstep, args.steps, torch)
+    g_per_th = per_th_bytes - 4 * dk + 2 * dk  # bf16 z in place of fp32 alpha; A is H floats per call
+    g_bytes = g_per_th * B * T * H + 2 * B * H * dk * dv * 4
+    log(f"gated prefill: {g_wall_ms / args.steps:.3f} ms/step (kernel {g_kern_ms:.3f} ms), "
+        f"{g_bytes / g_kern_ms / 1e6:.0f} GB/s of {g_per_th} B/token-head; parity o {e_go:.2e} S_T {e_gs:.2e}")
+    del gz, gA
+
+    # fast-forgetting heads (z ~ N(-3, 1), A ~ N(0, 0.3)): most 32-token chunks decay
+    # below e^-10 in some channel and are split into shorter segments
+    fz, fA = ki.make_gate((B, T, H, dk), H, w.qkv_dtype, seed=1, device=dev, z_mu=-3.0, z_std=1.0, a_std=0.3)
+
+    def fstep():
+        kda.kda_chunk_fwd_gated(x["q"], x["k"], x["v"], fz, fA, x["beta"], x["S0"], chunk=C, o=o, S_T=S_T)
+
+    fstep()
+    torch.cuda.synchronize()
+    b_, h_ = 1, 7
+    hg = {n: x[n][b_:b_ + 1, :, h_:h_ + 1].cpu() for n in ("q", "k", "v", "beta")}
+    ga = oracle.gate_alpha(fz[b_:b_ + 1, :, h_:h_ + 1].cpu(), fA[h_:h_ + 1].cpu())
+    rgo, rgs = oracle.forward(hg["q"], hg["k"], hg["v"], ga, hg["beta"], x["S0"][b_:b_ + 1, h_:h_ + 1].cpu(),
+                              threads=threads)
+    e_fo = rel_err_heads(o[b_, :, h_][None].cpu().double().numpy(), rgo)
+    e_fs = rel_err_heads(S_T[b_, h_][None].cpu().double().numpy(), rgs)
+    del hg, ga, rgo, rgs
+    fstep()
+    f_wall_ms, f_kern_ms, _ = timed_launches(fstep, args.steps, torch)
+    log(f"gated prefill, fast-forgetting heads: kernel {f_kern_ms:.3f} ms ({f_kern_ms / g_kern_ms:.2f}x); "
+        f"parity (head {b_ * H + h_}) o {e_fo:.2e} S_T {e_fs:.2e}")
+    del fz, fA
 
     # ------- a packed batch of 16 sequences of mixed lengths (kda_chunk_fwd_varlen) -------
     gl = torch.Generator().manual_seed(17)
@@ -319,7 +372,8 @@ def main():
                          f"({len(heads) * T} token-heads, {cpu_s:.1f} s wall); tokens/s = "
                          f"token-heads/s / H", "cpu": _cpu_model()}
 
-    parity_ok = max(e_o, e_s, e_do, e_ds, e_snap, e_spo, e_sps, e_vo, e_vs) <= TOL_REL and snap_last_is_state
+    parity_ok = (max(e_o, e_s, e_do, e_ds, e_snap, e_spo, e_sps, e_vo, e_vs, e_go, e_gs, e_fo, e_fs) <= TOL_REL
+                 and snap_last_is_state)
     out = {
         "metric": METRIC,
         "value": tokens_per_s,
@@ -356,6 +410,14 @@ def main():
                       "ms_per_step": s_wall_ms / args.steps, "kernel_ms": s_kern_ms,
                       "overhead_vs_prefill": s_kern_ms / kern_ms - 1, "snapshot_bytes": snap_bytes,
                       "parity_first_snapshot": e_snap, "last_snapshot_equals_S_T": snap_last_is_state},
+        "gated": {"workload": "the prefill above with the gate fused in (kda_chunk_fwd_gated: bf16 z and "
+                              "per-head A in place of fp32 alpha)",
+                  "ms_per_step": g_wall_ms / args.steps, "kernel_ms": g_kern_ms,
+                  "bytes_per_token_head": g_per_th, "achieved_gbps": g_bytes / g_kern_ms / 1e6,
+                  "frac_hbm": g_bytes / g_kern_ms / 1e6 / HBM_PEAK_GBS, "parity_o": e_go, "parity_S_T": e_gs,
+                  "gate_recipe": "z ~ N(-4.5, 0.4) bf16, A ~ N(0, 0.1) per head",
+                  "fast_forgetting": {"gate_recipe": "z ~ N(-3, 1), A ~ N(0, 0.3)", "kernel_ms": f_kern_ms,
+                                      "vs_gated": f_kern_ms / g_kern_ms, "parity_o": e_fo, "parity_S_T": e_fs}},
         "varlen": {"workload": f"packed batch of {len(v_lens)} sequences, {v_total} tokens "
                                f"(lengths {min(v_lens)}..{max(v_lens)}), H={H} d={dk}, kda_chunk_fwd_varlen",
                    "kernel_ms": v_kern_ms, "tokens_per_s": v_tok_s, "lengths": v_lens,

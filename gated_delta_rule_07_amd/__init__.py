@@ -13,7 +13,8 @@ from pathlib import Path
 
 import torch
 
-__all__ = ["kda_chunk_fwd", "kda_chunk_fwd_snapshots", "kda_chunk_fwd_varlen", "kda_decode_step",
+__all__ = ["kda_chunk_fwd", "kda_chunk_fwd_snapshots", "kda_chunk_fwd_varlen", "kda_chunk_fwd_gated",
+           "kda_decode_step", "kda_decode_step_gated",
            "kda_decode_verify",
            "kda_decode_commit", "kda_status_string", "kda_version",
            "kda_last_hip_error", "library_path", "load_library", "KdaError",
@@ -60,6 +61,11 @@ def load_library():
     lib.kda_chunk_fwd_varlen.restype = i32
     lib.kda_chunk_fwd_varlen.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, i32, vp, vp, i32, i32,
                                          i32, i32, i32, i32, vp]
+    lib.kda_chunk_fwd_gated.restype = i32
+    lib.kda_chunk_fwd_gated.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, vp, i32, vp,
+                                        i32, i32, i32, i32, i32, i32, vp]
+    lib.kda_decode_step_gated.restype = i32
+    lib.kda_decode_step_gated.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
     lib.kda_decode_verify.restype = i32
     lib.kda_decode_verify.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, vp]
     lib.kda_decode_commit.restype = i32
@@ -121,13 +127,15 @@ def _prefill_prep(q, k, v, alpha, beta, S0, o, S_T, o_dtype, want_state):
     dev = q.device
     for t, n in ((k, "k"), (v, "v")):
         _check(t, n, q.dtype, dev)
-    _check(alpha, "alpha", torch.float32, dev)
+    if alpha is not None:  # None: the gated call, which checks z and A itself
+        _check(alpha, "alpha", torch.float32, dev)
     _check(beta, "beta", torch.float32, dev)
     if q.dim() != 4 or v.dim() != 4:
         raise ValueError("libkda: q/k/v must be [B,T,H,d]")
     B, T, H, dk = q.shape
     dv = v.shape[-1]
-    if k.shape != q.shape or alpha.shape != q.shape or v.shape[:3] != q.shape[:3] or beta.shape != (B, T, H):
+    if (k.shape != q.shape or (alpha is not None and alpha.shape != q.shape) or v.shape[:3] != q.shape[:3]
+            or beta.shape != (B, T, H)):
         raise ValueError("libkda: inconsistent shapes")
     if S0 is not None:
         _check(S0, "S0", torch.float32, dev)
@@ -235,6 +243,53 @@ def kda_chunk_fwd_varlen(q, k, v, alpha, beta, cu_seqlens, S0=None, *, chunk: in
     if st != 0:
         raise KdaError(st, "kda_chunk_fwd_varlen")
     return o4[0], S_T
+
+
+def kda_chunk_fwd_gated(q, k, v, z, A, beta, S0=None, *, chunk: int = 64, o=None, S_T=None,
+                        o_dtype=torch.float32, want_state: bool = True, stream=None):
+    """Prefill with the gate fused in: alpha = exp(-5 sigmoid(e^A z)) is formed in
+    the kernels.  z: [B,T,H,d_k] in q's dtype; A: [H] fp32.  Returns ``(o, S_T)``;
+    other arguments as ``kda_chunk_fwd``."""
+    lib = load_library()
+    dev, (B, T, H, dk, dv), o, S_T = _prefill_prep(q, k, v, None, beta, S0, o, S_T, o_dtype, want_state)
+    _check(z, "z", q.dtype, dev)
+    _check(A, "A", torch.float32, dev)
+    if z.shape != q.shape or A.shape != (H,):
+        raise ValueError("libkda: z must be shaped like q and A must be [H]")
+    st = lib.kda_chunk_fwd_gated(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(z), _ptr(A), _ptr(beta),
+                                 _ptr(S0), _ptr(o), _dtype_code(o), _ptr(S_T), B, T, H, dk, dv, int(chunk),
+                                 _stream(dev, stream))
+    if st != 0:
+        raise KdaError(st, "kda_chunk_fwd_gated")
+    return o, S_T
+
+
+def kda_decode_step_gated(q, k, v, z, A, beta, S, *, o=None, o_dtype=torch.float32, stream=None):
+    """Decode with the gate fused in.  z: [B,H,d_k] in q's dtype; A: [H] fp32; the
+    rest as ``kda_decode_step``.  Returns ``o``."""
+    lib = load_library()
+    _check(q, "q")
+    dev = q.device
+    for t, n in ((k, "k"), (v, "v"), (z, "z")):
+        _check(t, n, q.dtype, dev)
+    _check(A, "A", torch.float32, dev)
+    _check(beta, "beta", torch.float32, dev)
+    _check(S, "S", torch.float32, dev)
+    if q.dim() != 3:
+        raise ValueError("libkda: decode q/k/v must be [B,H,d]")
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or z.shape != q.shape or v.shape[:2] != (B, H) or beta.shape != (B, H) or A.shape != (H,):
+        raise ValueError("libkda: inconsistent shapes")
+    if S.shape != (B, H, dk, dv):
+        raise ValueError("libkda: S must be [B,H,d_k,d_v]")
+    if o is None:
+        o = torch.empty(B, H, dv, device=dev, dtype=o_dtype)
+    st = lib.kda_decode_step_gated(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(z), _ptr(A), _ptr(beta),
+                                   _ptr(S), _ptr(o), _dtype_code(o), B, H, dk, dv, _stream(dev, stream))
+    if st != 0:
+        raise KdaError(st, "kda_decode_step_gated")
+    return o
 
 
 def kda_decode_step(q, k, v, alpha, beta, S, *, o=None, o_dtype=torch.float32, stream=None):

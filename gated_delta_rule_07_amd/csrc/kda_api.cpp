@@ -95,10 +95,11 @@ namespace {
 // Shared body of kda_chunk_fwd and kda_chunk_fwd_snapshots (n_snap == 0: none).
 // cu != NULL: a packed batch of B sequences over T token rows (T = the packed
 // length); otherwise B sequences of T tokens each.
+// z != NULL: fused gate (alpha formed from z and A in the kernels; alpha unused).
 kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, kda_dtype qkv_dtype, const float* alpha,
                           const float* beta, const float* S0, void* o, kda_dtype o_dtype, float* S_T,
-                          const int* snap_tokens, int n_snap, float* snaps, const int* cu, int B, int T, int H,
-                          int d_k, int d_v, int chunk, void* stream) {
+                          const int* snap_tokens, int n_snap, float* snaps, const int* cu, const void* z,
+                          const float* A, int B, int T, int H, int d_k, int d_v, int chunk, void* stream) {
   if (qkv_dtype != KDA_F32 && qkv_dtype != KDA_BF16) return KDA_ERR_DTYPE;
   if (o_dtype != KDA_F32 && o_dtype != KDA_BF16) return KDA_ERR_DTYPE;
   if (B < 1 || H < 1 || T < 0) return KDA_ERR_SHAPE;
@@ -106,7 +107,7 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, kda_dtype
   if (chunk != 16 && chunk != 32 && chunk != 64) return KDA_ERR_UNSUPPORTED;
   if (!sizes_ok(cu ? 1 : B, T, H, d_k, d_v) || (long long)B * H > (1LL << 26)) return KDA_ERR_SHAPE;
   if (n_snap < 0 || n_snap > KDA_MAX_SNAPSHOTS) return KDA_ERR_SHAPE;
-  if (T > 0 && (!q || !k || !v || !alpha || !beta || !o)) return KDA_ERR_NULL;
+  if (T > 0 && (!q || !k || !v || !(z ? (const void*)A : (const void*)alpha) || !beta || !o)) return KDA_ERR_NULL;
   if (n_snap > 0 && (!snap_tokens || !snaps)) return KDA_ERR_NULL;
   kda::SnapList snap{};
   for (int j = 0; j < n_snap; ++j) {
@@ -116,7 +117,8 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, kda_dtype
     snap.pos[j] = t;
   }
   if (cu && n_snap > 0) return KDA_ERR_UNSUPPORTED;
-  const void* ptrs[] = {q, k, v, alpha, beta, S0, o, S_T, n_snap > 0 ? snaps : nullptr, cu};
+  if (z) alpha = nullptr;
+  const void* ptrs[] = {q, k, v, alpha, beta, S0, o, S_T, n_snap > 0 ? snaps : nullptr, cu, z, A};
   for (const void* ptr : ptrs)
     if (ptr && !aligned16(ptr)) return KDA_ERR_MISALIGNED;
   const int io = (qkv_dtype == KDA_BF16) ? 1 : 0;
@@ -129,9 +131,10 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, kda_dtype
   const size_t sbytes = (size_t)B * H * d_k * d_v * 4;
   const Span none{0, 0};
   const Span in_spans[] = {T > 0 ? span(q, ntok * d_k * esz) : none, T > 0 ? span(k, ntok * d_k * esz) : none,
-                           T > 0 ? span(v, ntok * d_v * esz) : none, T > 0 ? span(alpha, ntok * d_k * 4) : none,
+                           T > 0 ? span(v, ntok * d_v * esz) : none,
+                           T > 0 ? (z ? span(z, ntok * d_k * esz) : span(alpha, ntok * d_k * 4)) : none,
                            T > 0 ? span(beta, ntok * 4) : none, S0 ? span(S0, sbytes) : none,
-                           cu ? span(cu, (size_t)(B + 1) * 4) : none};
+                           cu ? span(cu, (size_t)(B + 1) * 4) : none, z && T > 0 ? span(A, (size_t)H * 4) : none};
   const Span so = T > 0 ? span(o, ntok * d_v * osz) : none;
   const Span st = S_T ? span(S_T, sbytes) : none;
   const Span sn = n_snap > 0 ? span(snaps, sbytes * n_snap) : none;
@@ -145,7 +148,7 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, kda_dtype
   if (overlap(so, st) || overlap(so, sn) || overlap(st, sn)) return KDA_ERR_ALIAS;
 
   kda::PrefillParams p{q, k, v, alpha, beta, S0, o, S_T, B, T, H, d_k, d_v, o_dtype == KDA_F32 ? 1 : 0,
-                       n_snap > 0 ? snaps : nullptr, n_snap, cu};
+                       n_snap > 0 ? snaps : nullptr, n_snap, cu, T > 0 ? z : nullptr, A};
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   const hipError_t e = plan.impl == IMPL_PIPE ? kda::launch_prefill_pipe(p, snap, hs)
                                               : kda::launch_prefill(p, snap, io, chunk, plan.slab, hs);
@@ -164,8 +167,8 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, kda_dtype 
                          const float* alpha, const float* beta, const float* S0,
                          void* o, kda_dtype o_dtype, float* S_T,
                          int B, int T, int H, int d_k, int d_v, int chunk, void* stream) {
-  return chunk_fwd_impl(q, k, v, qkv_dtype, alpha, beta, S0, o, o_dtype, S_T, nullptr, 0, nullptr, nullptr, B, T,
-                        H, d_k, d_v, chunk, stream);
+  return chunk_fwd_impl(q, k, v, qkv_dtype, alpha, beta, S0, o, o_dtype, S_T, nullptr, 0, nullptr, nullptr, nullptr,
+                        nullptr, B, T, H, d_k, d_v, chunk, stream);
 }
 
 kda_status kda_chunk_fwd_snapshots(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
@@ -174,7 +177,7 @@ kda_status kda_chunk_fwd_snapshots(const void* q, const void* k, const void* v, 
                                    const int* snap_tokens, int n_snap, float* snaps,
                                    int B, int T, int H, int d_k, int d_v, int chunk, void* stream) {
   return chunk_fwd_impl(q, k, v, qkv_dtype, alpha, beta, S0, o, o_dtype, S_T, snap_tokens, n_snap, snaps, nullptr,
-                        B, T, H, d_k, d_v, chunk, stream);
+                        nullptr, nullptr, B, T, H, d_k, d_v, chunk, stream);
 }
 
 kda_status kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
@@ -183,22 +186,37 @@ kda_status kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, kda
                                 const int* cu_seqlens, int N, int total_T,
                                 int H, int d_k, int d_v, int chunk, void* stream) {
   if (!cu_seqlens) return KDA_ERR_NULL;
-  return chunk_fwd_impl(q, k, v, qkv_dtype, alpha, beta, S0, o, o_dtype, S_T, nullptr, 0, nullptr, cu_seqlens, N,
-                        total_T, H, d_k, d_v, chunk, stream);
+  return chunk_fwd_impl(q, k, v, qkv_dtype, alpha, beta, S0, o, o_dtype, S_T, nullptr, 0, nullptr, cu_seqlens,
+                        nullptr, nullptr, N, total_T, H, d_k, d_v, chunk, stream);
 }
 
-kda_status kda_decode_step(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
-                           const float* alpha, const float* beta, float* S, void* o, kda_dtype o_dtype,
-                           int B, int H, int d_k, int d_v, void* stream) {
+kda_status kda_chunk_fwd_gated(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
+                               const void* z, const float* A, const float* beta, const float* S0,
+                               void* o, kda_dtype o_dtype, float* S_T,
+                               int B, int T, int H, int d_k, int d_v, int chunk, void* stream) {
+  if (T > 0 && !z) return KDA_ERR_NULL;
+  return chunk_fwd_impl(q, k, v, qkv_dtype, nullptr, beta, S0, o, o_dtype, S_T, nullptr, 0, nullptr, nullptr, z, A,
+                        B, T, H, d_k, d_v, chunk, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// z != NULL: fused gate, as chunk_fwd_impl.
+kda_status decode_impl(const void* q, const void* k, const void* v, kda_dtype qkv_dtype, const float* alpha,
+                       const void* z, const float* A, const float* beta, float* S, void* o, kda_dtype o_dtype,
+                       int B, int H, int d_k, int d_v, void* stream) {
   if (qkv_dtype != KDA_F32 && qkv_dtype != KDA_BF16) return KDA_ERR_DTYPE;
   if (o_dtype != KDA_F32 && o_dtype != KDA_BF16) return KDA_ERR_DTYPE;
   if (B < 1 || H < 1) return KDA_ERR_SHAPE;
   if (!dim_ok(d_k) || !dim_ok(d_v)) return KDA_ERR_UNSUPPORTED;
   if (!sizes_ok(B, 1, H, d_k, d_v)) return KDA_ERR_SHAPE;
-  if (!q || !k || !v || !alpha || !beta || !S || !o) return KDA_ERR_NULL;
-  const void* ptrs[] = {q, k, v, alpha, beta, S, o};
+  if (!q || !k || !v || !(z ? (const void*)A : (const void*)alpha) || !beta || !S || !o) return KDA_ERR_NULL;
+  if (z) alpha = nullptr;
+  const void* ptrs[] = {q, k, v, alpha, beta, S, o, z, A};
   for (const void* ptr : ptrs)
-    if (!aligned16(ptr)) return KDA_ERR_MISALIGNED;
+    if (ptr && !aligned16(ptr)) return KDA_ERR_MISALIGNED;
   const int io = (qkv_dtype == KDA_BF16) ? 1 : 0;
   if (!kda::decode_supported(io, d_k, d_v)) return KDA_ERR_UNSUPPORTED;
 
@@ -208,18 +226,36 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, kda_dtyp
   const Span so = span(o, nbh * d_v * osz);
   const Span ss = span(S, nbh * d_k * d_v * 4);
   const Span ins[] = {span(q, nbh * d_k * esz), span(k, nbh * d_k * esz), span(v, nbh * d_v * esz),
-                      span(alpha, nbh * d_k * 4), span(beta, nbh * 4)};
+                      z ? span(z, nbh * d_k * esz) : span(alpha, nbh * d_k * 4), span(beta, nbh * 4),
+                      z ? span(A, (size_t)H * 4) : Span{0, 0}};
   if (overlap(so, ss)) return KDA_ERR_ALIAS;
   for (const Span& s : ins)
     if (overlap(so, s) || overlap(ss, s)) return KDA_ERR_ALIAS;
 
-  kda::DecodeParams p{q, k, v, alpha, beta, S, o, B, H, d_k, d_v, o_dtype == KDA_F32 ? 1 : 0};
+  kda::DecodeParams p{q, k, v, alpha, beta, S, o, B, H, d_k, d_v, o_dtype == KDA_F32 ? 1 : 0, z, A};
   const hipError_t e = kda::launch_decode(p, io, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     g_last_hip_error = (int)e;
     return KDA_ERR_HIP;
   }
   return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_decode_step(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
+                           const float* alpha, const float* beta, float* S, void* o, kda_dtype o_dtype,
+                           int B, int H, int d_k, int d_v, void* stream) {
+  return decode_impl(q, k, v, qkv_dtype, alpha, nullptr, nullptr, beta, S, o, o_dtype, B, H, d_k, d_v, stream);
+}
+
+kda_status kda_decode_step_gated(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
+                                 const void* z, const float* A, const float* beta, float* S, void* o,
+                                 kda_dtype o_dtype, int B, int H, int d_k, int d_v, void* stream) {
+  if (!z) return KDA_ERR_NULL;
+  return decode_impl(q, k, v, qkv_dtype, nullptr, z, A, beta, S, o, o_dtype, B, H, d_k, d_v, stream);
 }
 
 kda_status kda_decode_verify(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,

@@ -86,7 +86,9 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(DecodeParams p) {
   if (tid < DK) {
     sk[tid] = to_f32(k[tid]);
     sq[tid] = to_f32(q[tid]);
-    sa[tid] = alpha[tid];
+    // fused gate: alpha = exp(-5 sigmoid(e^A z)) from z in the q/k/v dtype
+    sa[tid] = p.z ? gate_retention(__expf(p.A[bh % p.H]) * to_f32(static_cast<const IO*>(p.z)[(size_t)bh * DK + tid]))
+                  : alpha[tid];
   }
   float vv[4];
   load4<IO>(v + 4 * cg, vv);

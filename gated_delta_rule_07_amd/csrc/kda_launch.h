@@ -22,7 +22,18 @@ struct PrefillParams {
   // a [T][H][d] tensor (T = the packed length; values clamped to [0, T]).
   // Null: B sequences of T tokens each.
   const int* cu;
+  // Fused gate: when z is set, alpha = exp(-5 sigmoid(e^{A_h} z)) is formed in
+  // the kernel from z ([.][H][dk], q/k/v dtype) and A ([H] fp32); alpha is unused.
+  const void* z;
+  const float* A;
 };
+
+// The lower-bounded retention exp(-5 sigmoid(e^A z)) for x = e^A z.
+__device__ __forceinline__ float gate_retention(float x) {
+  const float log2e = 1.4426950408889634f;
+  const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * log2e));
+  return __builtin_amdgcn_exp2f(-5.0f * log2e * s);
+}
 
 // Packed batches of at most this many sequences are scheduled longest first.
 constexpr int kMaxRankedSeqs = 256;
@@ -97,6 +108,8 @@ struct DecodeParams {
   void* o;
   int B, H, dk, dv;
   int o_f32;
+  const void* z;  // fused gate (see PrefillParams); null: alpha is given
+  const float* A;
 };
 
 // io_dtype: 0 = fp32, 1 = bf16.  `slab` is the number of state columns one

@@ -156,6 +156,7 @@ struct Ctx {
   int bh, b, h, col0;  // col0: first state column of this slab
   int T;               // this sequence's length
   long long tok0;      // its first token in the [.][H][d] token rows
+  float eA;            // fused gate: e^{A_h}
 };
 
 template <class C>
@@ -172,11 +173,23 @@ __device__ __forceinline__ void load_raw(Raw<C>& raw, const Ctx& cx, int t0, int
         const int c = hh * C::HC + 4 * cq;
         if (t < cx.T) {
           const size_t row = (size_t)(cx.tok0 + t) * p.H + cx.h;
-          raw.a[hh][i] = *reinterpret_cast<const f32x4*>(p.alpha + row * C::DK + c);
+          if (p.z) {  // fused gate: keep z (its bits, for bf16) where alpha goes; phase_scan forms alpha
+            if constexpr (sizeof(IO) == 2) {
+              const u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const IO*>(p.z) + row * C::DK + c);
+              raw.a[hh][i] = __builtin_bit_cast(f32x4, u32x4{w.x, w.y, 0u, 0u});
+            } else {
+              raw.a[hh][i] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.z) + row * C::DK + c);
+            }
+          } else {
+            raw.a[hh][i] = *reinterpret_cast<const f32x4*>(p.alpha + row * C::DK + c);
+          }
           raw.k[hh][i].load(static_cast<const IO*>(p.k) + row * C::DK + c);
           raw.q[hh][i].load(static_cast<const IO*>(p.q) + row * C::DK + c);
         } else {
-          raw.a[hh][i] = (f32x4)1.0f;
+          // padding is an identity step: alpha = 1, or z = -inf, which the gate maps to 1
+          if (!p.z) raw.a[hh][i] = (f32x4)1.0f;
+          else if constexpr (sizeof(IO) == 2) raw.a[hh][i] = __builtin_bit_cast(f32x4, u32x4{0xFF80FF80u, 0xFF80FF80u, 0u, 0u});
+          else raw.a[hh][i] = (f32x4)(-__builtin_inff());
           raw.k[hh][i].clear();
           raw.q[hh][i].clear();
         }
@@ -203,7 +216,8 @@ __device__ __forceinline__ void load_raw(Raw<C>& raw, const Ctx& cx, int t0, int
 // Returns true (uniformly) if `check` is set and the chunk's total decay in some
 // channel of the pass is below e^{-80}; nothing is written in that case.
 template <class C>
-__device__ bool phase_scan(Smem<C>& sm, const Raw<C>& raw, int hh, int lo, int hi, bool check, int tid) {
+__device__ bool phase_scan(Smem<C>& sm, const Raw<C>& raw, int hh, int lo, int hi, bool check, float eA,
+                           bool gated, int tid) {
   using SOP = typename C::SOP;
   using LOP = typename C::LOP;
   const int cq = tid % C::NCQ, tg = tid / C::NCQ;
@@ -215,9 +229,28 @@ __device__ bool phase_scan(Smem<C>& sm, const Raw<C>& raw, int hh, int lo, int h
     for (int i = 0; i < C::TGS; ++i) {
       const int t = tg * C::TGS + i;
       const bool in = t >= lo && t < hi;
+      float av[4];
+      if (gated) {  // alpha = exp(-5 sigmoid(e^A z))
+        float zf[4];
+        if constexpr (sizeof(typename C::IO) == 2) {
+          const u32x4 zb = __builtin_bit_cast(u32x4, raw.a[hh][i]);
+          zf[0] = __builtin_bit_cast(float, zb.x << 16);
+          zf[1] = __builtin_bit_cast(float, zb.x & 0xffff0000u);
+          zf[2] = __builtin_bit_cast(float, zb.y << 16);
+          zf[3] = __builtin_bit_cast(float, zb.y & 0xffff0000u);
+        } else {
+          const f32x4 zv = raw.a[hh][i];
+          zf[0] = zv.x; zf[1] = zv.y; zf[2] = zv.z; zf[3] = zv.w;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) av[e] = gate_retention(eA * zf[e]);
+      } else {
+        const f32x4 a4 = raw.a[hh][i];
+        av[0] = a4.x; av[1] = a4.y; av[2] = a4.z; av[3] = a4.w;
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        run[e] *= in ? raw.a[hh][i][e] : 1.0f;
+        run[e] *= in ? av[e] : 1.0f;
         lp[i][e] = run[e];
       }
     }
@@ -549,7 +582,7 @@ __device__ bool process_chunk(Smem<C>& sm, Raw<C>& raw, f32x4 (&S)[C::NKT], cons
   for (int hh = 0; hh < C::NH; ++hh) {
     block_sync_lds();
     KDA_PHASE_MARK(0);
-    if (phase_scan<C>(sm, raw, hh, lo, hi, check, tid)) return false;
+    if (phase_scan<C>(sm, raw, hh, lo, hi, check, cx.eA, cx.p.z != nullptr, tid)) return false;
     if (hh == C::NH - 1 && prefetch_t0 >= 0) load_raw<C>(raw, cx, prefetch_t0, tid);
     block_sync_lds();
     KDA_PHASE_MARK(1);
@@ -601,6 +634,7 @@ __global__ __launch_bounds__(256, 1) void kda_prefill_kernel(PrefillParams p, Sn
   cx.b = __builtin_amdgcn_readfirstlane(seq_by_length_rank(p.cu, p.B, p.T, task / p.H, seq_lens, &seq_pick));
   cx.bh = cx.b * p.H + cx.h;
   cx.col0 = slab * C::J;
+  cx.eA = p.z ? __expf(p.A[cx.h]) : 1.0f;
   const int g = lane / 16, m = lane % 16;
 
   f32x4 S[C::NKT];

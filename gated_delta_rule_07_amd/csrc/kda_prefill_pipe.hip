@@ -26,10 +26,12 @@
 // 32x32x16 fp16 matrix cores with fp32 accumulation; the state itself stays
 // fp32 in registers and is rounded to fp16 (times a power-of-two scale per state
 // column) only as an operand.  KG, QG and KH are bounded by |k|, |q|; KC grows
-// as 1/pre, so an item whose decay falls below e^{-10} in some channel, or whose
-// KC would leave fp16 range, is redone as 16-token and then 2-token segments
-// (alpha >= e^{-5}, the lower bound in section 3.5 of the technical report
-// review, keeps any 2 tokens within range); this regrouping is exact.
+// as 1/pre, so an item in which some channel's decay falls below e^{-10}, or
+// whose KC would leave fp16 range, is redone as a shorter segment: the scan
+// votes the first token out of range, the segment ends before it, and the rest
+// of the chunk proceeds in segments of that length (alpha >= e^{-5}, the lower
+// bound in section 3.5 of the technical report review, keeps any 2 tokens
+// within range).  This regrouping is exact.
 //
 // Sign conventions that save negations: the scan stores -KH, the P wave stores
 // -P, and the state wave computes Xn = KG S - V = -(V - KG S), so Un = T Xn = -U,
@@ -154,6 +156,8 @@ struct Item {
 
 __device__ __forceinline__ int chunk_end(int c, int T) { return min(CS, T - c * CS); }
 
+// The item after `it`: the next segment of the same length (size), or the next
+// chunk whole.
 __device__ __forceinline__ Item next_item(const Item& it, int T, int nchunks) {
   Item n = it;
   n.seq = it.seq + 1;
@@ -163,17 +167,19 @@ __device__ __forceinline__ Item next_item(const Item& it, int T, int nchunks) {
     n.lo = 0;
     n.size = CS;
     if (n.c >= nchunks) n.seq = -1;
-  } else if (it.size == 2 && (n.lo & 15) == 0) {
-    n.size = 16;
   }
   n.hi = min(n.lo + n.size, chunk_end(n.c, T));
   return n;
 }
 
-__device__ __forceinline__ Item split_item(const Item& it, int T) {
+// `it` redone as the segment that ends before its first out-of-range token
+// `first` (a chunk position in [lo, hi)): between 2 tokens and one token fewer
+// than `it` (the scan votes only for items longer than 2 tokens), so every
+// split makes progress.
+__device__ __forceinline__ Item split_item(const Item& it, int first) {
   Item n = it;
-  n.size = (it.size == CS) ? 16 : 2;
-  n.hi = min(it.lo + n.size, chunk_end(it.c, T));
+  n.hi = it.lo + min(max(first - it.lo, 2), it.hi - it.lo - 1);
+  n.size = n.hi - n.lo;
   return n;
 }
 
@@ -182,6 +188,7 @@ struct Ctx4 {
   int bh, b, h, col0, nchunks;
   int T;           // this sequence's length
   long long tok0;  // its first token in the [.][H][d] token rows
+  float eA;        // fused gate: e^{A_h}
 };
 
 // ---- scan waves --------------------------------------------------------------------
@@ -190,6 +197,7 @@ struct Raw4 {
   float a[C::TPL][C::CPL];         // alpha of this lane's channels, per token
   uint32_t k[C::TPL][C::CPL / 2];  // bf16 pairs
   uint32_t q[C::TPL][C::CPL / 2];
+  uint32_t z[C::TPL][C::CPL / 2];  // fused gate: bf16 pairs of z in place of alpha
   u32x2 v;                         // 4 bf16 of the V slab
   float beta;
 };
@@ -198,7 +206,7 @@ struct Raw4 {
 // wave's slice, tokens tq*TPL ..  Rows past the sequence end read as zeros
 // (buffer range check).  One load per token and tensor: the load count, not
 // the byte count, sets what the scan waits for here.
-template <class C>
+template <class C, bool G>
 __device__ void load_raw4(Raw4<C>& raw, const Ctx4& cx, int c, int sw, int lane) {
   const PrefillParams& p = cx.p;
   const int cp = opaque(lane % C::PPW), tq = opaque(lane / C::PPW);
@@ -206,7 +214,8 @@ __device__ void load_raw4(Raw4<C>& raw, const Ctx4& cx, int c, int sw, int lane)
   const int rows = min(CS, cx.T - t0);
   const size_t row0 = (size_t)(cx.tok0 + t0) * p.H + cx.h;
   const int ts = p.H * C::DK;  // elements between tokens
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.alpha + row0 * C::DK, rows * ts * 4);
+  const __amdgpu_buffer_rsrc_t ra = G ? make_rsrc(static_cast<const __bf16*>(p.z) + row0 * C::DK, rows * ts * 2)
+                                      : make_rsrc(p.alpha + row0 * C::DK, rows * ts * 4);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(static_cast<const __bf16*>(p.k) + row0 * C::DK, rows * ts * 2);
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(static_cast<const __bf16*>(p.q) + row0 * C::DK, rows * ts * 2);
   const int e0 = tq * C::TPL * ts + C::CPW * sw + C::CPL * cp;
@@ -215,10 +224,21 @@ __device__ void load_raw4(Raw4<C>& raw, const Ctx4& cx, int c, int sw, int lane)
     // Reinterpret each loaded vector as a whole: taking single elements of the
     // integer vector a buffer load returns and reinterpreting them as float is
     // miscompiled by this toolchain (both read one narrowed dword).
+    if constexpr (G) {  // z as bf16, like k
+      if constexpr (C::CPL == 4) {
+        const u32x2 zw = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(ra, 2 * e0, 2 * i * ts, 0));
+        raw.z[i][0] = zw.x;
+        raw.z[i][1] = zw.y;
+      } else {
+        raw.z[i][0] = __builtin_amdgcn_raw_buffer_load_b32(ra, 2 * e0, 2 * i * ts, 0);
+      }
+    }
     if constexpr (C::CPL == 4) {
-      const f32x4 w = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, 4 * e0, 4 * i * ts, 0));
+      if constexpr (!G) {
+        const f32x4 w = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, 4 * e0, 4 * i * ts, 0));
 #pragma unroll
-      for (int e = 0; e < 4; ++e) raw.a[i][e] = w[e];
+        for (int e = 0; e < 4; ++e) raw.a[i][e] = w[e];
+      }
       const u32x2 kw = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rk, 2 * e0, 2 * i * ts, 0));
       const u32x2 qw = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rq, 2 * e0, 2 * i * ts, 0));
       raw.k[i][0] = kw.x;
@@ -226,9 +246,11 @@ __device__ void load_raw4(Raw4<C>& raw, const Ctx4& cx, int c, int sw, int lane)
       raw.q[i][0] = qw.x;
       raw.q[i][1] = qw.y;
     } else {
-      const f32x2 w = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(ra, 4 * e0, 4 * i * ts, 0));
-      raw.a[i][0] = w.x;
-      raw.a[i][1] = w.y;
+      if constexpr (!G) {
+        const f32x2 w = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(ra, 4 * e0, 4 * i * ts, 0));
+        raw.a[i][0] = w.x;
+        raw.a[i][1] = w.y;
+      }
       raw.k[i][0] = __builtin_amdgcn_raw_buffer_load_b32(rk, 2 * e0, 2 * i * ts, 0);
       raw.q[i][0] = __builtin_amdgcn_raw_buffer_load_b32(rq, 2 * e0, 2 * i * ts, 0);
     }
@@ -247,8 +269,8 @@ __device__ void load_raw4(Raw4<C>& raw, const Ctx4& cx, int c, int sw, int lane)
 // Scan of item `it` by scan wave sw (one channel pair and TPL consecutive tokens
 // per lane): writes ring slot it.seq % 3, KC slot it.seq % 2 and this wave's
 // regroup vote.  FULL: the item is the whole chunk (no token is masked).
-template <class C, bool FULL>
-__device__ void scan4_body(Smem4<C>& sm, const Raw4<C>& raw, const Item& it, int sw, int lane, int par) {
+template <class C, bool FULL, bool G>
+__device__ void scan4_body(Smem4<C>& sm, const Raw4<C>& raw, const Item& it, float eA, int sw, int lane, int par) {
   constexpr int L = C::CPL, TP = C::TPL;
   ScanSlot<C>& sl = sm.ss[it.seq % 3];
   h16* kc = sm.kc[it.seq % 2];
@@ -265,7 +287,14 @@ __device__ void scan4_body(Smem4<C>& sm, const Raw4<C>& raw, const Item& it, int
   for (int i = 0; i < TP; ++i)
 #pragma unroll
     for (int e = 0; e < L; ++e) {
-      a[i][e] = in(i) ? raw.a[i][e] : 1.0f;
+      float ai;
+      if constexpr (G) {  // alpha = exp(-5 sigmoid(e^A z)) from the bf16 gate input
+        const uint32_t zw = raw.z[i][e / 2];
+        ai = gate_retention(eA * ((e & 1) ? bf16_hi(zw) : bf16_lo(zw)));
+      } else {
+        ai = raw.a[i][e];
+      }
+      a[i][e] = in(i) ? ai : 1.0f;
       gt[e] *= a[i][e];
     }
   // Token-group products of every channel, exchanged within the wave.  Each
@@ -374,22 +403,45 @@ __device__ void scan4_body(Smem4<C>& sm, const Raw4<C>& raw, const Item& it, int
       sl.v[(vc + e) * C::LDV + vr] = __builtin_bit_cast(__bf16, (uint16_t)(w[e / 2] >> (16 * (e % 2))));
   }
   if (st < CS) sl.beta[st] = (FULL || (st >= lo && st < hi)) ? raw.beta : 0.0f;
-  // regroup when some channel decays below e^{-10} or KC would leave fp16 range
+  // Regroup vote: the first token (chunk position) at which some channel's
+  // prefix decay falls below e^{-10} or KC = k/pre would leave fp16 range; CS
+  // when there is none.  A bound over the whole item (smallest gamma, largest
+  // |k| times largest 1/gamma) clears almost every item, so only a wave that
+  // fails it looks at the tokens one by one.  Items of 2 tokens are never split.
   float gmin = gam[0], rgm = rg[0];
 #pragma unroll
   for (int e = 1; e < L; ++e) {
     gmin = fminf(gmin, gam[e]);
     rgm = fmaxf(rgm, rg[e]);
   }
-  const bool steep = !(gmin >= STEEP) || !(kmax * rgm < 32768.0f);
-  const bool any = __builtin_amdgcn_ballot_w64(steep) != 0;
-  if (lane == 0) sm.flags[par][sw] = (it.size > 2 && any) ? 1 : 0;
+  const bool rough = !(gmin >= STEEP) || !(kmax * rgm < 32768.0f);
+  int vote = CS;
+  if (hi - lo > 2 && __builtin_amdgcn_ballot_w64(rough) != 0) {
+#pragma unroll
+    for (int i = 0; i < TP; ++i) {
+      bool bad = false;
+#pragma unroll
+      for (int j = 0; j < L / 2; ++j) {
+        const float k0 = fabsf(bf16_lo(raw.k[i][j])), k1 = fabsf(bf16_hi(raw.k[i][j]));
+        const float p0 = pre[i][2 * j], p1 = pre[i][2 * j + 1];
+        bad = bad || !(p0 >= STEEP) || !(k0 < 32768.0f * p0) || !(p1 >= STEEP) || !(k1 < 32768.0f * p1);
+      }
+      // lanes are ordered by token group, so the lowest voting lane holds the
+      // earliest such token among this token slot's lanes
+      const uint64_t m = __builtin_amdgcn_ballot_w64(bad && in(i));
+      if (m != 0) vote = min(vote, (int)(__builtin_ctzll(m) / C::PPW) * TP + i);
+    }
+    // gamma, a product in another order, may round below the bound although
+    // no prefix does: drop the last token
+    if (vote >= hi && __builtin_amdgcn_ballot_w64(!(gmin >= STEEP)) != 0) vote = hi - 1;
+  }
+  if (lane == 0) sm.flags[par][sw] = vote;
 }
 
-template <class C>
-__device__ void scan4(Smem4<C>& sm, const Raw4<C>& raw, const Item& it, int sw, int lane, int par) {
-  if (it.lo == 0 && it.hi == CS) scan4_body<C, true>(sm, raw, it, sw, lane, par);
-  else scan4_body<C, false>(sm, raw, it, sw, lane, par);
+template <class C, bool G>
+__device__ void scan4(Smem4<C>& sm, const Raw4<C>& raw, const Item& it, float eA, int sw, int lane, int par) {
+  if (it.lo == 0 && it.hi == CS) scan4_body<C, true, G>(sm, raw, it, eA, sw, lane, par);
+  else scan4_body<C, false, G>(sm, raw, it, eA, sw, lane, par);
 }
 
 // ---- L, T wave -------------------------------------------------------------------------
@@ -701,7 +753,7 @@ __device__ void store_state(float* dst, const StateRegs<C>& R, int dv_, int lane
   }
 }
 
-template <class C, Role ROLE>
+template <class C, Role ROLE, bool G>
 __device__ void run_role(Smem4<C>& sm, const Ctx4& cx, const SnapList& snap, int lane, int sw) {
   const PrefillParams& p = cx.p;
   StateRegs<C> R;
@@ -724,7 +776,7 @@ __device__ void run_role(Smem4<C>& sm, const Ctx4& cx, const SnapList& snap, int
   }
   if constexpr (ROLE == SCAN) {
     if (cx.nchunks > 0) {
-      load_raw4<C>(raw, cx, 0, sw, lane);
+      load_raw4<C, G>(raw, cx, 0, sw, lane);
       rc = 0;
     }
   }
@@ -740,15 +792,15 @@ __device__ void run_role(Smem4<C>& sm, const Ctx4& cx, const SnapList& snap, int
     if constexpr (ROLE == SCAN) {
       if (sI.seq >= 0) {
         if (rc != sI.c) {
-          load_raw4<C>(raw, cx, sI.c, sw, lane);
+          load_raw4<C, G>(raw, cx, sI.c, sw, lane);
           rc = sI.c;
         }
         KDA_PROBE_VMWAIT();
         KDA_STEP_MARK(2, kstep);
-        scan4<C>(sm, raw, sI, sw, lane, par);
+        scan4<C, G>(sm, raw, sI, cx.eA, sw, lane, par);
         KDA_STEP_MARK(3, kstep);
         if (sI.hi == chunk_end(sI.c, cx.T) && sI.c + 1 < cx.nchunks) {
-          load_raw4<C>(raw, cx, sI.c + 1, sw, lane);  // prefetch the next chunk
+          load_raw4<C, G>(raw, cx, sI.c + 1, sw, lane);  // prefetch the next chunk
           rc = sI.c + 1;
         }
       }
@@ -772,31 +824,28 @@ __device__ void run_role(Smem4<C>& sm, const Ctx4& cx, const SnapList& snap, int
       KDA_STEP_MARK(2, kstep);
       if (stI.seq >= 0) out_qs<C>(sm, O, usc, stI, lane);
     }
-    // Both possible successors of the scan item are formed before the barrier,
-    // so after it only the regroup vote remains to be read.
-    Item nI = none, spI = none;
-    if (sI.seq >= 0) {
-      nI = next_item(sI, cx.T, cx.nchunks);
-      spI = split_item(sI, cx.T);
-    }
+    // The scan item's successor is formed before the barrier, so after it only
+    // the regroup vote remains to be read.
+    Item nI = none;
+    if (sI.seq >= 0) nI = next_item(sI, cx.T, cx.nchunks);
     KDA_STEP_MARK(1, kstep);
     block_sync_lds();
     KDA_STEP_MARK(4, kstep);
     ++kstep;
-    bool steep = false;
+    int first = CS;  // the scan waves' earliest out-of-range token, CS: none
     if (sI.seq >= 0) {
-      int any = 0;
 #pragma unroll
       for (int w4 = 0; w4 < C::NSW; w4 += 4) {
         const int4 f = *reinterpret_cast<const int4*>(&sm.flags[par][w4]);
-        any |= f.x | f.y | f.z | f.w;
+        first = min(first, min(min(f.x, f.y), min(f.z, f.w)));
       }
-      steep = __builtin_amdgcn_readfirstlane(any) != 0;
+      first = __builtin_amdgcn_readfirstlane(first);
     }
+    const bool steep = first < CS;
     opI = stI;
     stI = bI;
     bI = (sI.seq >= 0 && !steep) ? sI : none;
-    if (sI.seq >= 0) sI = steep ? spI : nI;
+    if (sI.seq >= 0) sI = steep ? split_item(sI, first) : nI;
     par ^= 1;
   }
 
@@ -805,7 +854,7 @@ __device__ void run_role(Smem4<C>& sm, const Ctx4& cx, const SnapList& snap, int
   }
 }
 
-template <class C>
+template <class C, bool G>
 __global__ __launch_bounds__(C::NT, 1) void kda_prefill_pipe_kernel(PrefillParams p, SnapList snap) {
   __shared__ Smem4<C> sm;
   const int tid = threadIdx.x, lane = tid % 64;
@@ -819,22 +868,24 @@ __global__ __launch_bounds__(C::NT, 1) void kda_prefill_pipe_kernel(PrefillParam
   cx.b = __builtin_amdgcn_readfirstlane(seq_by_length_rank(p.cu, p.B, p.T, task / p.H, seq_lens, &seq_pick));
   cx.bh = cx.b * p.H + cx.h;
   cx.col0 = slab * J;
+  cx.eA = G ? __expf(p.A[cx.h]) : 1.0f;
   seq_range(p, cx.b, cx.tok0, cx.T);
   cx.nchunks = (cx.T + CS - 1) / CS;
   // T's upper-right 16x16 block is read as zeros and never written
   for (int i = tid; i < 2 * CS * C::LDC; i += C::NT) (&sm.t[0][0])[i] = (h16)0.0f;
-  if (wave >= 4) run_role<C, SCAN>(sm, cx, snap, lane, wave - 4);
-  else if (wave == 0) run_role<C, STATE>(sm, cx, snap, lane, 0);
-  else if (wave == 1) run_role<C, SOLVE>(sm, cx, snap, lane, 0);
-  else if (wave == 2) run_role<C, PMAT>(sm, cx, snap, lane, 0);
-  else run_role<C, OUT>(sm, cx, snap, lane, 0);
+  if (wave >= 4) run_role<C, SCAN, G>(sm, cx, snap, lane, wave - 4);
+  else if (wave == 0) run_role<C, STATE, G>(sm, cx, snap, lane, 0);
+  else if (wave == 1) run_role<C, SOLVE, G>(sm, cx, snap, lane, 0);
+  else if (wave == 2) run_role<C, PMAT, G>(sm, cx, snap, lane, 0);
+  else run_role<C, OUT, G>(sm, cx, snap, lane, 0);
 }
 
 template <int DK>
 hipError_t launch_pipe(const PrefillParams& p, const SnapList& snap, hipStream_t s) {
   using C = Cfg4<DK>;
   const unsigned grid = (unsigned)(p.B * p.H * (p.dv / J));
-  hipLaunchKernelGGL((kda_prefill_pipe_kernel<C>), dim3(grid), dim3(C::NT), 0, s, p, snap);
+  if (p.z) hipLaunchKernelGGL((kda_prefill_pipe_kernel<C, true>), dim3(grid), dim3(C::NT), 0, s, p, snap);
+  else hipLaunchKernelGGL((kda_prefill_pipe_kernel<C, false>), dim3(grid), dim3(C::NT), 0, s, p, snap);
   return hipGetLastError();
 }
 

@@ -171,6 +171,32 @@ kda_status kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, kda
                                 const int* cu_seqlens, int N, int total_T,
                                 int H, int d_k, int d_v, int chunk, void* stream);
 
+/*
+ * kda_chunk_fwd with the gate fused in: instead of alpha, the caller passes the
+ * gate pre-activation z and a per-head log-scale A, and the kernels form the
+ * lower-bounded retention of section 3.5 of the first page,
+ *     alpha_t[i] = exp(-5 * sigmoid(exp(A_h) * z_t[i]))      (in (e^-5, 1)),
+ * in fp32 as they read z, so no fp32 alpha tensor is stored or read: the
+ * per-token-head input shrinks from 4*d_k to 2*d_k bytes with bf16 z.
+ *
+ *   z : [B][T][H][d_k] in qkv_dtype (read)        A : [H] fp32, device (read)
+ * Every other argument as kda_chunk_fwd.  The result equals kda_chunk_fwd with
+ * alpha = the formula above evaluated in fp32 (the exponentials and the
+ * reciprocal use the hardware's approximations, within a few fp32 ulps).
+ */
+kda_status kda_chunk_fwd_gated(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
+                               const void* z, const float* A, const float* beta, const float* S0,
+                               void* o, kda_dtype o_dtype, float* S_T,
+                               int B, int T, int H, int d_k, int d_v, int chunk, void* stream);
+
+/*
+ * kda_decode_step with the gate fused in (as kda_chunk_fwd_gated):
+ *   z : [B][H][d_k] in qkv_dtype (read)           A : [H] fp32, device (read)
+ */
+kda_status kda_decode_step_gated(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
+                                 const void* z, const float* A, const float* beta, float* S, void* o,
+                                 kda_dtype o_dtype, int B, int H, int d_k, int d_v, void* stream);
+
 /* Most draft tokens one speculative step may verify. */
 #define KDA_MAX_DRAFT 16
 

@@ -118,3 +118,16 @@ def make_workload_prefill(idx, seed=0, device="cpu"):
     w = WORKLOADS[idx]
     return make_prefill(w.B, w.T, w.H, w.dk, w.dv, w.qkv_dtype, w.alpha_mu, w.s0_std,
                         seed=seed, device=device)
+
+
+def make_gate(shape, H, qkv_dtype=torch.bfloat16, seed=0, device="cpu", z_mu=-4.5, z_std=0.4, a_std=0.1):
+    """Gate inputs for the fused-gate calls: z ~ N(z_mu, z_std) of the given shape
+    (its second-to-last axis is the head axis), rounded to qkv_dtype, and one
+    log-scale per head A ~ N(0, a_std) in fp32.  The defaults give a mean log
+    retention of about -0.074 per token (per-head means -0.18 .. -0.03), matching
+    alpha = sigmoid(N(3, 1)) of the other workloads (-0.075); a smaller z_mu or
+    a wider z_std gives faster-forgetting heads."""
+    g = _gen(device, seed * 7919 + 13)
+    z = (z_mu + z_std * torch.randn(*shape, generator=g, device=device, dtype=torch.float32)).to(qkv_dtype)
+    A = a_std * torch.randn(H, generator=g, device=device, dtype=torch.float32)
+    return z.contiguous(), A.contiguous()

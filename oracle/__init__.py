@@ -4,8 +4,9 @@ TEST INFRASTRUCTURE ONLY.  Only the tests, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import this package.  The product library
 (``gated_delta_rule_07_amd``) never imports it and shares no code with it.
 
-The arithmetic lives in ``kda_oracle.c`` (built with gcc into
-``libkda_oracle.so``); this module only marshals arrays.  What the recurrence
+The recurrence lives in ``kda_oracle.c`` (built with gcc into
+``libkda_oracle.so``); this module marshals arrays, and ``gate_alpha`` forms
+the retention from a gate pre-activation in numpy fp64.  What the recurrence
 computes, with its citations, is documented at the top of the C file:
 the "Kimi K3 Technical Report review" (jw9603.github.io), sections 3.2-3.3.
 
@@ -158,6 +159,30 @@ def forward(q, k, v, alpha, beta, S0=None, *, heads=None, order="page1",
     if rc != 0:
         raise ValueError("oracle: kda_oracle_forward rejected its arguments")
     return o, st
+
+
+def _widen(x):
+    """Exact fp64 values of a bf16 (uint16 bits), fp32 or fp64 array or tensor."""
+    a, code = _as_array(x)
+    if code == BF16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def gate_alpha(z, A):
+    """Per-channel retention from a gate pre-activation, the lower-bounded decay
+    of section 3.5 of the "Kimi K3 Technical Report review" (jw9603.github.io):
+    the log-decay is g = g_min * Sigmoid(e^A z) with g_min = -5, and alpha = e^g,
+    so alpha lies in (e^-5, 1).
+
+    z: [..., H, d_k] (bf16, fp32 or fp64; bf16 widened exactly); A: [H], one
+    log-scale per head.  Returns float64 alpha with z's shape.
+    """
+    zz = _widen(z)
+    aa = _widen(A)
+    x = np.exp(aa)[:, None] * zz          # e^A z, A broadcast over the head axis
+    s = 1.0 / (1.0 + np.exp(-x))          # Sigmoid
+    return np.exp(-5.0 * s)
 
 
 def decode_step(q, k, v, alpha, beta, S, *, threads=None, col_block=None):

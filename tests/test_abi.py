@@ -168,6 +168,43 @@ def test_varlen_validation(over, code):
     assert _varlen(_lib(), **over) == code
 
 
+def _gated(lib, **over):
+    a = dict(q=_addr(0), k=_addr(1), v=_addr(2), dtype=1, z=_addr(3), A=_addr(9), beta=_addr(4), S0=_addr(5),
+             o=_addr(6), odt=0, S_T=_addr(7), B=1, T=64, H=2, dk=128, dv=128, chunk=64)
+    a.update(over)
+    return lib.kda_chunk_fwd_gated(a["q"], a["k"], a["v"], a["dtype"], a["z"], a["A"], a["beta"], a["S0"], a["o"],
+                                   a["odt"], a["S_T"], a["B"], a["T"], a["H"], a["dk"], a["dv"], a["chunk"], None)
+
+
+def _dgated(lib, **over):
+    a = dict(q=_addr(0), k=_addr(1), v=_addr(2), dtype=1, z=_addr(3), A=_addr(9), beta=_addr(4), S=_addr(5),
+             o=_addr(6), odt=0, B=4, H=2, dk=128, dv=128)
+    a.update(over)
+    return lib.kda_decode_step_gated(a["q"], a["k"], a["v"], a["dtype"], a["z"], a["A"], a["beta"], a["S"],
+                                     a["o"], a["odt"], a["B"], a["H"], a["dk"], a["dv"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(z=None), 1), (dict(A=None), 1), (dict(q=None), 1),
+    (dict(dtype=7), 3), (dict(B=0), 2), (dict(dk=40), 4),
+    (dict(z=ctypes.c_void_p(BASE + (3 << 32) + 2)), 5), (dict(A=ctypes.c_void_p(BASE + (9 << 32) + 4)), 5),
+    (dict(o=_addr(3)), 6),     # o aliases z
+    (dict(S_T=_addr(9)), 6),   # S_T aliases A
+])
+def test_gated_prefill_validation(over, code):
+    assert _gated(_lib(), **over) == code
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(z=None), 1), (dict(A=None), 1), (dict(dtype=2), 3), (dict(H=0), 2), (dict(dv=24), 4),
+    (dict(z=ctypes.c_void_p(BASE + (3 << 32) + 8)), 5),
+    (dict(o=_addr(9)), 6),     # o aliases A
+    (dict(S=_addr(3)), 6),     # state aliases z
+])
+def test_gated_decode_validation(over, code):
+    assert _dgated(_lib(), **over) == code
+
+
 def _verify(lib, **over):
     a = dict(q=_addr(0), k=_addr(1), v=_addr(2), dtype=1, alpha=_addr(3), beta=_addr(4), S=_addr(5),
              o=_addr(6), odt=0, u=_addr(7), B=4, K=4, H=2, dk=128, dv=128)

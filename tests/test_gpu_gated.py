@@ -1,0 +1,124 @@
+"""GPU checks of the fused-gate calls, kda_chunk_fwd_gated and
+kda_decode_step_gated: the kernels form alpha = exp(-5 sigmoid(e^A z)) from z
+and A themselves.  Each result must match the oracle fed the oracle's own fp64
+alpha from the same z and A (oracle.gate_alpha), to the operator's tolerance,
+on both prefill kernels (ragged tails, a regrouping steep gate) and on decode;
+and a gated call must agree closely with the plain call given alpha formed on
+the host side of the test.
+"""
+import numpy as np
+import pytest
+import torch
+
+import kda_inputs as ki
+import oracle
+from kda_check import TOL_BF16_REL, TOL_F32_ABS, assert_close, gpu_o_heads, gpu_s_heads, log, rel_err_per_head
+
+pytestmark = pytest.mark.gpu
+
+
+def _kda():
+    import gated_delta_rule_07_amd as kda
+    return kda
+
+
+def _oracle_gated(inp, z, A):
+    h = {n: x.cpu() for n, x in inp.items()}
+    alpha = oracle.gate_alpha(z.cpu(), A.cpu())
+    return oracle.forward(h["q"], h["k"], h["v"], alpha, h["beta"], h["S0"])
+
+
+CASES = [
+    ("pipe bf16 d128", 2, 300, 2, 128, 128, torch.bfloat16, 64),
+    ("pipe bf16 d64 chunk32", 1, 150, 3, 64, 64, torch.bfloat16, 32),
+    ("generic f32 d32 chunk16", 1, 100, 2, 32, 32, torch.float32, 16),
+    ("generic bf16 d32", 2, 130, 2, 32, 64, torch.bfloat16, 64),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_gated_prefill_matches_oracle(gpu, case):
+    name, B, T, H, dk, dv, dtype, chunk = case
+    kda = _kda()
+    log(f"gated prefill {name}")
+    inp = ki.make_prefill(B, T, H, dk, dv, dtype, 3.0, 0.1, seed=T + dk, device=gpu)
+    z, A = ki.make_gate((B, T, H, dk), H, dtype, seed=T, device=gpu)
+    o, st = kda.kda_chunk_fwd_gated(inp["q"], inp["k"], inp["v"], z, A, inp["beta"], inp["S0"], chunk=chunk)
+    torch.cuda.synchronize()
+    ro, rs = _oracle_gated(inp, z, A)
+    bf = dtype == torch.bfloat16
+    assert_close(gpu_o_heads(o), ro, bf, f"{name} o")
+    assert_close(gpu_s_heads(st), rs, bf, f"{name} S_T")
+
+
+def test_gated_prefill_steep_gate_regroups(gpu):
+    """z far above 0 drives alpha to its e^-5 bound: chunks regroup into short segments."""
+    kda = _kda()
+    inp = ki.make_prefill(1, 256, 2, 128, 128, torch.bfloat16, 3.0, 0.1, seed=4, device=gpu)
+    z, A = ki.make_gate((1, 256, 2, 128), 2, torch.bfloat16, seed=4, device=gpu)
+    z[:, 40:150] = 30.0
+    o, st = kda.kda_chunk_fwd_gated(inp["q"], inp["k"], inp["v"], z, A, inp["beta"], inp["S0"])
+    torch.cuda.synchronize()
+    ro, rs = _oracle_gated(inp, z, A)
+    assert_close(gpu_o_heads(o), ro, True, "steep gate o")
+    assert_close(gpu_s_heads(st), rs, True, "steep gate S_T")
+
+
+@pytest.mark.parametrize("dk", [128, 64])
+def test_gated_prefill_fast_forgetting_heads(gpu, dk):
+    """z ~ N(-3, 1) with A ~ N(0, 0.3): most 32-token chunks decay below e^-10 in
+    some channel, so the pipelined kernel splits them at varying tokens."""
+    kda = _kda()
+    B, T, H = 1, 300, 4
+    log(f"gated fast-forgetting d={dk}")
+    inp = ki.make_prefill(B, T, H, dk, dk, torch.bfloat16, 3.0, 0.1, seed=40 + dk, device=gpu)
+    z, A = ki.make_gate((B, T, H, dk), H, torch.bfloat16, seed=41 + dk, device=gpu, z_mu=-3.0, z_std=1.0, a_std=0.3)
+    o, st = kda.kda_chunk_fwd_gated(inp["q"], inp["k"], inp["v"], z, A, inp["beta"], inp["S0"], chunk=32)
+    torch.cuda.synchronize()
+    ro, rs = _oracle_gated(inp, z, A)
+    assert_close(gpu_o_heads(o), ro, True, f"fast-forgetting d={dk} o")
+    assert_close(gpu_s_heads(st), rs, True, f"fast-forgetting d={dk} S_T")
+
+
+def test_gated_prefill_agrees_with_plain_call(gpu):
+    """The in-kernel gate against alpha formed by torch on the device, then kda_chunk_fwd."""
+    kda = _kda()
+    inp = ki.make_prefill(2, 257, 2, 128, 128, torch.bfloat16, 3.0, 0.1, seed=8, device=gpu)
+    z, A = ki.make_gate((2, 257, 2, 128), 2, torch.bfloat16, seed=8, device=gpu)
+    alpha = torch.exp(-5.0 * torch.sigmoid(torch.exp(A)[:, None] * z.float())).contiguous()
+    o1, s1 = kda.kda_chunk_fwd_gated(inp["q"], inp["k"], inp["v"], z, A, inp["beta"], inp["S0"])
+    o2, s2 = kda.kda_chunk_fwd(inp["q"], inp["k"], inp["v"], alpha, inp["beta"], inp["S0"])
+    torch.cuda.synchronize()
+    eo = (o1 - o2).abs().max().item() / o2.pow(2).mean().sqrt().item()
+    es = (s1 - s2).abs().max().item() / s2.pow(2).mean().sqrt().item()
+    log(f"  gated vs plain: o {eo:.2e}, S_T {es:.2e}")
+    # The two alphas differ by a few fp32 ulps (hardware exp/rcp vs torch's); through
+    # the fp16 matrix-core operands that becomes a difference of the same order as
+    # either call's own error against exact arithmetic (up to ~1e-2 of the RMS), so
+    # the bar is half the operator's bf16 tolerance.
+    assert eo < TOL_BF16_REL / 2 and es < TOL_BF16_REL / 2
+
+
+@pytest.mark.parametrize("dk,dv,dtype", [(128, 128, torch.bfloat16), (32, 64, torch.float32), (64, 16, torch.bfloat16)])
+def test_gated_decode_matches_oracle(gpu, dk, dv, dtype):
+    kda = _kda()
+    B, H, steps = 3, 4, 5
+    S = ki.make_state(B, H, dk, dv, 0.1, 2, gpu)
+    S_ref = S.cpu().double().numpy().copy()
+    worst = 0.0
+    for step in range(steps):
+        tok = ki.make_decode_token(B, H, dk, dv, dtype, 3.0, seed=1, step=step, device=gpu)
+        z, A = ki.make_gate((B, H, dk), H, dtype, seed=100 + step, device=gpu)
+        o = kda.kda_decode_step_gated(tok["q"], tok["k"], tok["v"], z, A, tok["beta"], S)
+        h = {n: x.cpu() for n, x in tok.items()}
+        ro = oracle.decode_step(h["q"], h["k"], h["v"], oracle.gate_alpha(z.cpu(), A.cpu()), h["beta"], S_ref)
+        got = o.float().cpu().double().numpy().reshape(1, -1)
+        worst = max(worst, rel_err_per_head(got, ro.reshape(1, -1)) if dtype == torch.bfloat16
+                    else float(np.abs(got - ro.reshape(1, -1)).max()))
+    torch.cuda.synchronize()
+    gs = S.cpu().double().numpy().reshape(B * H, dk, dv)
+    rs = S_ref.reshape(B * H, dk, dv)
+    es = rel_err_per_head(gs, rs) if dtype == torch.bfloat16 else float(np.abs(gs - rs).max())
+    tol = TOL_BF16_REL if dtype == torch.bfloat16 else TOL_F32_ABS
+    log(f"  gated decode d={dk}x{dv}: o {worst:.2e}  S {es:.2e} (tol {tol})")
+    assert worst <= tol and es <= tol

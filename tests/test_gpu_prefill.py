@@ -2,7 +2,7 @@
 
 Small and medium shapes that span several chunks and a ragged tail, plus the
 edge cases of the method: empty and one-token sequences, chunk sizes 16/32/64,
-steep decay at the lower bound (exercises the 16-token sub-chunk path), beta
+steep decay at the lower bound and splits at the first out-of-range token, beta
 outside [0, 1], several head sizes, and the decay/write order.
 """
 import math
@@ -84,8 +84,8 @@ def test_chunk_size_invariance(gpu):
 
 @pytest.mark.parametrize("chunk", [32, 64])
 def test_steep_decay_at_lower_bound(gpu, chunk):
-    """alpha = e^{-5} in every channel: the chunk's total decay underflows, so the
-    kernel must regroup into 16-token sub-chunks; results still match the oracle."""
+    """alpha = e^{-5} in every channel: the chunk's total decay leaves range, so the
+    kernels must regroup into shorter segments; results still match the oracle."""
     log(f"steep chunk={chunk}")
     inp = _inp(gpu, 1, 300, 2, 64, 64, seed=7)
     inp["alpha"].fill_(math.exp(-5.0))
@@ -99,6 +99,24 @@ def test_steep_decay_mixed_channels(gpu):
     a[..., ::2] = math.exp(-5.0)
     a[:, 200:264] = 0.999  # one chunk that is not steep in any channel
     check_prefill(inp, what="mixed steep")
+
+
+@pytest.mark.parametrize("dk", [128, 64])
+def test_steep_splits_at_first_out_of_range_token(gpu, dk):
+    """Segments end before the first token whose decay or KC leaves range, at any
+    offset: short bursts at odd tokens, a slow decay that crosses e^-10 late in
+    every chunk, and a split forced by a large key alone (decay still above e^-10)."""
+    inp = _inp(gpu, 2, 330, 2, dk, dk, seed=30 + dk)
+    a, k = inp["alpha"], inp["k"]
+    a[0, 37:45, :, 3] = math.exp(-3.0)          # 8 tokens at e^-3 in one channel
+    a[0, 101:103, :, 7] = math.exp(-5.0)        # two tokens at the bound, odd start
+    a[0, 150:190, 1, ::5] = math.exp(-4.9)      # a run across a chunk boundary
+    a[1, 0:128] = math.exp(-0.42)               # e^-10 crossed at the 24th token of each chunk
+    a[1, 192:224, :, 5] = 1.0                   # chunk 6, channel 5: no decay but ...
+    a[1, 200:202, :, 5] = math.exp(-4.8)        # ... e^-9.6 over tokens 200, 201, and then
+    k[1, 210, :, 5] = 3.0                       # |k| / pre = 3 e^9.6 > 2^15 at token 210
+    log(f"steep splits d={dk}")
+    check_prefill(inp, chunk=32, what="first-token splits")
 
 
 @pytest.mark.parametrize("beta_val", [0.0, 0.5, 1.0, 2.0])

@@ -85,7 +85,7 @@ def test_snapshots_leave_outputs_unchanged(gpu):
 
 
 def test_snapshots_through_regrouped_chunks(gpu):
-    """Decay at the lower bound forces 16- and 2-token segments; snapshots around them stay exact."""
+    """Decay at the lower bound forces short segments; snapshots around them stay exact."""
     inp = ki.make_prefill(1, 256, 2, 128, 128, torch.bfloat16, 3.0, 0.1, seed=5, device=gpu)
     a = inp["alpha"].clone()
     a[:, 40:140] = 0.0067379470  # e^-5

@@ -389,3 +389,44 @@ def test_empty_sequence_returns_initial_state():
     z = np.zeros((1, 0, 2, 4))
     o, st = oracle.forward(z, z, z, z, np.zeros((1, 0, 2)), S0)
     assert o.shape == (2, 0, 4) and np.array_equal(st, S0.reshape(2, 4, 4))
+
+
+# ---- the fused gate (lower-bounded decay of P1 section 3.5) ----
+# Pinned by properties, not by restating the formula: each catches a different
+# plausible slip (the sign of z, the -5 factor, a missing sigmoid, the e^A scale).
+
+def test_gate_at_zero_is_half_the_bound_for_any_scale():
+    z = np.zeros((1, 3, 4, 8))
+    for A in (np.zeros(4), np.array([-3.0, 0.0, 1.5, 4.0])):
+        assert np.allclose(oracle.gate_alpha(z, A), np.exp(-2.5), rtol=0, atol=1e-15)
+
+
+def test_gate_sigmoid_symmetry_sums_to_the_bound():
+    rng = np.random.default_rng(30)
+    z = rng.standard_normal((2, 5, 3, 16)) * 3
+    A = rng.standard_normal(3)
+    s = np.log(oracle.gate_alpha(z, A)) + np.log(oracle.gate_alpha(-z, A))
+    assert np.allclose(s, -5.0, rtol=0, atol=1e-12)
+
+
+def test_gate_scale_is_exp_A():
+    rng = np.random.default_rng(31)
+    z = rng.standard_normal((1, 4, 3, 8))
+    A = np.array([0.7, -1.2, 2.0])
+    scaled = z * np.exp(A)[:, None]
+    assert np.allclose(oracle.gate_alpha(z, A), oracle.gate_alpha(scaled, np.zeros(3)), rtol=1e-14, atol=0)
+
+
+def test_gate_range_and_monotonicity():
+    z = np.linspace(-40, 40, 801).reshape(1, 801, 1, 1)
+    a = oracle.gate_alpha(z, np.zeros(1)).ravel()
+    assert np.all(a > np.exp(-5) - 1e-15) and np.all(a <= 1.0)
+    assert np.all(np.diff(a) <= 0)                          # more gate input, faster forgetting
+    assert abs(a[0] - 1.0) < 1e-12 and abs(a[-1] - np.exp(-5)) < 1e-12
+
+
+def test_gate_widens_bf16_exactly():
+    torch = pytest.importorskip("torch")
+    zt = torch.randn(1, 3, 2, 8).to(torch.bfloat16)
+    A = np.array([0.3, -0.4])
+    assert np.array_equal(oracle.gate_alpha(zt, A), oracle.gate_alpha(zt.double().numpy(), A))
