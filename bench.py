@@ -415,6 +415,7 @@ def main():
                   "ms_per_step": g_wall_ms / args.steps, "kernel_ms": g_kern_ms,
                   "bytes_per_token_head": g_per_th, "achieved_gbps": g_bytes / g_kern_ms / 1e6,
                   "frac_hbm": g_bytes / g_kern_ms / 1e6 / HBM_PEAK_GBS, "parity_o": e_go, "parity_S_T": e_gs,
+                  "traffic": measured_traffic("kda_prefill_gated"),
                   "gate_recipe": "z ~ N(-4.5, 0.4) bf16, A ~ N(0, 0.1) per head",
                   "fast_forgetting": {"gate_recipe": "z ~ N(-3, 1), A ~ N(0, 0.3)", "kernel_ms": f_kern_ms,
                                       "vs_gated": f_kern_ms / g_kern_ms, "parity_o": e_fo, "parity_S_T": e_fs}},
