@@ -86,9 +86,12 @@ def timed_launches(fn, n, torch):
 
 
 def rel_err_heads(got, ref):
+    """Worst head's max|got - ref| / RMS(ref); inf when anything is not finite."""
     import numpy as np
     worst = 0.0
     for g, r in zip(got, ref):
+        if not (np.isfinite(g).all() and np.isfinite(r).all()):
+            return float("inf")
         rms = float(np.sqrt(np.mean(r * r)))
         worst = max(worst, float(np.abs(g - r).max()) / max(rms, 1e-30))
     return worst
@@ -275,6 +278,47 @@ def main():
         f"{v_kern_ms:.3f} ms, {v_tok_s:.4g} tok/s; parity o {e_vo:.2e} S_T {e_vs:.2e}")
     del vx, vflat
 
+    # ------- few long chains: the split prefill (kda_chunk_fwd_split) against the single pass -------
+    split_res = []
+    e_so = e_ss = 0.0
+    for sB, sT, sH, sseed in ((1, 4096, 8, 5), (1, 65536, 2, 6)):
+        sx = ki.make_prefill(sB, sT, sH, dk, dv, w.qkv_dtype, w.alpha_mu, w.s0_std, seed=sseed, device=dev)
+        n_parts, ws_bytes = kda.kda_chunk_fwd_split_plan(w.qkv_dtype, sB, sT, sH, dk, dv, chunk=C)
+        s_ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+        s_o = torch.empty(sB, sT, sH, dv, device=dev, dtype=torch.float32)
+        s_S = torch.empty(sB, sH, dk, dv, device=dev, dtype=torch.float32)
+
+        def one(sx=sx, s_o=s_o, s_S=s_S):
+            kda.kda_chunk_fwd(sx["q"], sx["k"], sx["v"], sx["alpha"], sx["beta"], sx["S0"], chunk=C, o=s_o, S_T=s_S)
+
+        def spl(sx=sx, s_o=s_o, s_S=s_S, n_parts=n_parts, s_ws=s_ws):
+            kda.kda_chunk_fwd_split(sx["q"], sx["k"], sx["v"], sx["alpha"], sx["beta"], sx["S0"], parts=n_parts,
+                                    chunk=C, o=s_o, S_T=s_S, workspace=s_ws)
+
+        spl()
+        torch.cuda.synchronize()
+        sheads = [0, sB * sH - 1]
+        hs = {n: sx[n].cpu() for n in ("q", "k", "v", "alpha", "beta", "S0")}
+        rso, rss = oracle.forward(hs["q"], hs["k"], hs["v"], hs["alpha"], hs["beta"], hs["S0"], heads=sheads,
+                                  threads=threads)
+        got_o = s_o.permute(0, 2, 1, 3).reshape(sB * sH, sT, dv)[sheads].cpu().double().numpy()
+        got_s = s_S.reshape(sB * sH, dk, dv)[sheads].cpu().double().numpy()
+        eo_, es_ = rel_err_heads(got_o, rso), rel_err_heads(got_s, rss)
+        e_so, e_ss = max(e_so, eo_), max(e_ss, es_)
+        del hs, rso, rss
+        for _ in range(args.warmup):
+            one()
+            spl()
+        _, one_ms, _ = timed_launches(one, args.steps, torch)
+        _, spl_ms, _ = timed_launches(spl, args.steps, torch)
+        log(f"split prefill B={sB} T={sT} H={sH}: {n_parts} parts, {spl_ms:.3f} ms vs single pass "
+            f"{one_ms:.3f} ms ({one_ms / spl_ms:.2f}x); parity o {eo_:.2e} S_T {es_:.2e}")
+        split_res.append({"workload": f"prefill B={sB} T={sT} H={sH} d={dk} (kda_chunk_fwd_split, library's "
+                                      f"part count)", "parts": n_parts, "workspace_bytes": ws_bytes,
+                          "ms": spl_ms, "single_pass_ms": one_ms, "speedup": one_ms / spl_ms,
+                          "tokens_per_s": sB * sT / (spl_ms / 1e3), "parity_o": eo_, "parity_S_T": es_})
+        del sx, s_ws, s_o, s_S
+
     # ---------------- decode: B=256, H=32, d=128, 100 in-place steps ----------------
     wd = ki.WORKLOADS[4]
     DB, DH = wd.B, wd.H
@@ -300,8 +344,7 @@ def main():
                               S_init[None], threads=threads)
     gdo = od.reshape(nsteps, DB * DH, dv)[:, dheads].permute(1, 0, 2).cpu().double().numpy()
     gds = S.reshape(DB * DH, dk, dv)[dheads].cpu().double().numpy()
-    e_do = max(float(np.abs(gdo[:, s] - rdo[:, s]).max()) / float(np.sqrt(np.mean(rdo[:, s] ** 2)))
-               for s in range(nsteps))
+    e_do = max(rel_err_heads(gdo[:, s].reshape(1, -1), rdo[:, s].reshape(1, -1)) for s in range(nsteps))
     e_ds = rel_err_heads(gds, rds)
     log(f"decode parity: o {e_do:.3e}  S {e_ds:.3e}")
 
@@ -372,7 +415,7 @@ def main():
                          f"({len(heads) * T} token-heads, {cpu_s:.1f} s wall); tokens/s = "
                          f"token-heads/s / H", "cpu": _cpu_model()}
 
-    parity_ok = (max(e_o, e_s, e_do, e_ds, e_snap, e_spo, e_sps, e_vo, e_vs, e_go, e_gs, e_fo, e_fs) <= TOL_REL
+    parity_ok = (max(e_o, e_s, e_do, e_ds, e_snap, e_spo, e_sps, e_vo, e_vs, e_go, e_gs, e_fo, e_fs, e_so, e_ss) <= TOL_REL
                  and snap_last_is_state)
     out = {
         "metric": METRIC,
@@ -419,6 +462,7 @@ def main():
                   "gate_recipe": "z ~ N(-4.5, 0.4) bf16, A ~ N(0, 0.1) per head",
                   "fast_forgetting": {"gate_recipe": "z ~ N(-3, 1), A ~ N(0, 0.3)", "kernel_ms": f_kern_ms,
                                       "vs_gated": f_kern_ms / g_kern_ms, "parity_o": e_fo, "parity_S_T": e_fs}},
+        "split": split_res,
         "varlen": {"workload": f"packed batch of {len(v_lens)} sequences, {v_total} tokens "
                                f"(lengths {min(v_lens)}..{max(v_lens)}), H={H} d={dk}, kda_chunk_fwd_varlen",
                    "kernel_ms": v_kern_ms, "tokens_per_s": v_tok_s, "lengths": v_lens,

@@ -14,6 +14,7 @@ from pathlib import Path
 import torch
 
 __all__ = ["kda_chunk_fwd", "kda_chunk_fwd_snapshots", "kda_chunk_fwd_varlen", "kda_chunk_fwd_gated",
+           "kda_chunk_fwd_split", "kda_chunk_fwd_split_plan",
            "kda_decode_step", "kda_decode_step_gated",
            "kda_decode_verify",
            "kda_decode_commit", "kda_status_string", "kda_version",
@@ -64,6 +65,13 @@ def load_library():
     lib.kda_chunk_fwd_gated.restype = i32
     lib.kda_chunk_fwd_gated.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, vp, i32, vp,
                                         i32, i32, i32, i32, i32, i32, vp]
+    sz = ctypes.c_size_t
+    lib.kda_chunk_fwd_split_plan.restype = i32
+    lib.kda_chunk_fwd_split_plan.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                             ctypes.POINTER(i32), ctypes.POINTER(sz)]
+    lib.kda_chunk_fwd_split.restype = i32
+    lib.kda_chunk_fwd_split.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, i32, vp,
+                                        i32, i32, i32, i32, i32, i32, i32, i32, vp, sz, vp]
     lib.kda_decode_step_gated.restype = i32
     lib.kda_decode_step_gated.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
     lib.kda_decode_verify.restype = i32
@@ -261,6 +269,44 @@ def kda_chunk_fwd_gated(q, k, v, z, A, beta, S0=None, *, chunk: int = 64, o=None
                                  _stream(dev, stream))
     if st != 0:
         raise KdaError(st, "kda_chunk_fwd_gated")
+    return o, S_T
+
+
+def kda_chunk_fwd_split_plan(qkv_dtype, B, T, H, d_k, d_v, *, chunk: int = 64, parts: int = 0,
+                             num_cus: int = 0):
+    """``(parts, workspace_bytes)`` a split prefill of this shape would use
+    (``parts`` 0: the library's choice for ``num_cus`` compute units, 0: the
+    current device's)."""
+    lib = load_library()
+    code = KDA_BF16 if qkv_dtype == torch.bfloat16 else KDA_F32 if qkv_dtype == torch.float32 else -1
+    n, ws = ctypes.c_int(0), ctypes.c_size_t(0)
+    st = lib.kda_chunk_fwd_split_plan(code, B, T, H, d_k, d_v, int(chunk), int(parts), int(num_cus),
+                                      ctypes.byref(n), ctypes.byref(ws))
+    if st != 0:
+        raise KdaError(st, "kda_chunk_fwd_split_plan")
+    return n.value, ws.value
+
+
+def kda_chunk_fwd_split(q, k, v, alpha, beta, S0=None, *, parts: int = 0, num_cus: int = 0, chunk: int = 64,
+                        o=None, S_T=None, workspace=None, o_dtype=torch.float32, want_state: bool = True,
+                        stream=None):
+    """Prefill with every sequence split into parts that run side by side (a
+    two-level scan over the parts).  ``parts`` 0: the library's choice; the
+    workspace (a uint8 device tensor) is allocated here when not given.  Returns
+    ``(o, S_T)``; other arguments as ``kda_chunk_fwd``."""
+    lib = load_library()
+    dev, (B, T, H, dk, dv), o, S_T = _prefill_prep(q, k, v, alpha, beta, S0, o, S_T, o_dtype, want_state)
+    n, need = kda_chunk_fwd_split_plan(q.dtype, B, T, H, dk, dv, chunk=chunk, parts=parts, num_cus=num_cus)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _check(workspace, "workspace", torch.uint8, dev)
+    st = lib.kda_chunk_fwd_split(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(alpha), _ptr(beta),
+                                 _ptr(S0), _ptr(o), _dtype_code(o), _ptr(S_T), B, T, H, dk, dv, int(chunk),
+                                 n, 0, _ptr(workspace), workspace.numel() if workspace is not None else 0,
+                                 _stream(dev, stream))
+    if st != 0:
+        raise KdaError(st, "kda_chunk_fwd_split")
     return o, S_T
 
 

@@ -19,7 +19,8 @@ INCLUDE = PKG.parent / "include"
 LIB = PKG / "libkda.so"
 OBJDIR = PKG / "_build"
 
-SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_prefill.hip", "kda_prefill_pipe.hip", "kda_spec.hip"]
+SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_prefill.hip", "kda_prefill_pipe.hip", "kda_spec.hip",
+           "kda_split.hip"]
 
 ARCH = "gfx950"
 # Packed-fp32 VALU forms are disabled: plain fp32 code only.

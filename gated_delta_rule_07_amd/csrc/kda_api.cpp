@@ -66,6 +66,72 @@ PrefillPlan plan_prefill(int B, int H, int dk, int dv, int chunk, int io) {
   return {IMPL_GENERIC, 16};
 }
 
+// ---- sequence split ----------------------------------------------------------------
+// The pipelined kernel serves one (b, h, 32-column slab) chain per workgroup and
+// keeps one workgroup per compute unit, so with few chains most of the GPU
+// idles.  A split prefill cuts every sequence into parts of whole 32-token
+// chunks: pass 1 runs parts 0..P-2 from a zero state over d_v + d_k columns
+// (their contributions and transitions), a combine kernel chains them into each
+// part's incoming state, and pass 2 reruns all P parts from those states.
+constexpr int kMaxParts = 1024;
+struct SplitShape {
+  int parts, part_len;  // part_len: tokens per part, a multiple of 32
+};
+
+SplitShape split_shape_for(int T, int P) {
+  const int nch = (T + 31) / 32;
+  if (nch <= 1 || P <= 1) return {1, T};
+  const int pc = (nch + P - 1) / P;  // chunks per part
+  return {(nch + pc - 1) / pc, 32 * pc};
+}
+
+// The part count with the smallest modelled time.  The model counts pipeline
+// steps: a launch of G workgroups on `cus` compute units runs ceil(G / cus)
+// rounds of (chunks per part + 3) steps; the combine costs about half a step per
+// part and the two extra launches about two steps.  A split is taken only when
+// it models at least 10% faster than the single pass.
+SplitShape split_shape_auto(int B, int T, int H, int dk, int dv, int cus) {
+  const int nch = (T + 31) / 32;
+  const long long bh = (long long)B * H, ns = dv / 32, nsa = (dv + dk) / 32;
+  auto rounds = [&](long long g) { return (double)((g + cus - 1) / cus); };
+  const double single = rounds(bh * ns) * (nch + 3);
+  SplitShape best{1, T};
+  double best_cost = 0.9 * single;
+  for (int P = 2; P <= nch && P <= kMaxParts; ++P) {
+    const SplitShape sh = split_shape_for(T, P);
+    if (sh.parts != P) continue;
+    const double cost = (rounds(bh * (P - 1) * nsa) + rounds(bh * P * ns)) * (sh.part_len / 32 + 3) +
+                        0.5 * (P - 1) + 2.0;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = sh;
+    }
+  }
+  return best;
+}
+
+size_t split_ws_bytes(int B, int H, int dk, int dv, int P) {
+  if (P <= 1) return 0;
+  return (size_t)4 * B * H * dk * ((size_t)(P - 1) * (dv + dk) + (size_t)P * dv);
+}
+
+// Compute units of the current device (0 on failure).
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return n;
+}
+
+// A split request: parts == 0 lets the library choose (num_cus == 0: the current
+// device's compute units).
+struct SplitReq {
+  int parts;
+  int num_cus;
+  void* ws;
+  size_t ws_bytes;
+};
+
 }  // namespace
 
 extern "C" {
@@ -99,7 +165,8 @@ namespace {
 kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, kda_dtype qkv_dtype, const float* alpha,
                           const float* beta, const float* S0, void* o, kda_dtype o_dtype, float* S_T,
                           const int* snap_tokens, int n_snap, float* snaps, const int* cu, const void* z,
-                          const float* A, int B, int T, int H, int d_k, int d_v, int chunk, void* stream) {
+                          const float* A, int B, int T, int H, int d_k, int d_v, int chunk, void* stream,
+                          const SplitReq* split = nullptr) {
   if (qkv_dtype != KDA_F32 && qkv_dtype != KDA_BF16) return KDA_ERR_DTYPE;
   if (o_dtype != KDA_F32 && o_dtype != KDA_BF16) return KDA_ERR_DTYPE;
   if (B < 1 || H < 1 || T < 0) return KDA_ERR_SHAPE;
@@ -147,11 +214,57 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, kda_dtype
   if (S0 && S_T && S0 != S_T && overlap(st, in_spans[5])) return KDA_ERR_ALIAS;
   if (overlap(so, st) || overlap(so, sn) || overlap(st, sn)) return KDA_ERR_ALIAS;
 
+  SplitShape sh{1, T};
+  if (split) {
+    if (split->parts < 0 || split->num_cus < 0) return KDA_ERR_SHAPE;
+    if (split->parts != 1 && (cu || n_snap > 0)) return KDA_ERR_UNSUPPORTED;
+    if (plan.impl != IMPL_PIPE) {
+      if (split->parts > 1) return KDA_ERR_UNSUPPORTED;
+    } else if (split->parts > 1) {
+      sh = split_shape_for(T, split->parts);
+    } else if (split->parts == 0) {
+      const int cus = split->num_cus ? split->num_cus : device_cus();
+      if (cus <= 0) {
+        g_last_hip_error = (int)hipErrorNoDevice;
+        return KDA_ERR_HIP;
+      }
+      sh = split_shape_auto(B, T, H, d_k, d_v, cus);
+    }
+  }
+  char* ws = nullptr;
+  if (sh.parts > 1) {
+    const size_t need = split_ws_bytes(B, H, d_k, d_v, sh.parts);
+    if (!split->ws) return KDA_ERR_NULL;
+    if (!aligned16(split->ws)) return KDA_ERR_MISALIGNED;
+    if (split->ws_bytes < need) return KDA_ERR_SHAPE;
+    const Span sw = span(split->ws, need);
+    for (const Span& s : in_spans)
+      if (overlap(sw, s)) return KDA_ERR_ALIAS;
+    if (overlap(sw, so) || overlap(sw, st)) return KDA_ERR_ALIAS;
+    ws = static_cast<char*>(split->ws);
+  }
+
   kda::PrefillParams p{q, k, v, alpha, beta, S0, o, S_T, B, T, H, d_k, d_v, o_dtype == KDA_F32 ? 1 : 0,
                        n_snap > 0 ? snaps : nullptr, n_snap, cu, T > 0 ? z : nullptr, A};
   const hipStream_t hs = static_cast<hipStream_t>(stream);
-  const hipError_t e = plan.impl == IMPL_PIPE ? kda::launch_prefill_pipe(p, snap, hs)
-                                              : kda::launch_prefill(p, snap, io, chunk, plan.slab, hs);
+  hipError_t e;
+  if (sh.parts > 1) {
+    // pass 1: (N | M) of parts 0..P-2; combine: the state entering each part;
+    // pass 2: every part from its state (S0 is read only by the combine, so
+    // S_T may alias it)
+    p.nparts = sh.parts;
+    p.part_len = sh.part_len;
+    p.ws_trans = reinterpret_cast<float*>(ws);
+    p.ws_in = reinterpret_cast<float*>(ws + (size_t)4 * B * H * d_k * (size_t)(sh.parts - 1) * (d_v + d_k));
+    p.split = 1;
+    e = kda::launch_prefill_pipe(p, snap, hs);
+    if (e == hipSuccess) e = kda::launch_split_combine(p, hs);
+    p.split = 2;
+    if (e == hipSuccess) e = kda::launch_prefill_pipe(p, snap, hs);
+  } else {
+    e = plan.impl == IMPL_PIPE ? kda::launch_prefill_pipe(p, snap, hs)
+                               : kda::launch_prefill(p, snap, io, chunk, plan.slab, hs);
+  }
   if (e != hipSuccess) {
     g_last_hip_error = (int)e;
     return KDA_ERR_HIP;
@@ -197,6 +310,43 @@ kda_status kda_chunk_fwd_gated(const void* q, const void* k, const void* v, kda_
   if (T > 0 && !z) return KDA_ERR_NULL;
   return chunk_fwd_impl(q, k, v, qkv_dtype, nullptr, beta, S0, o, o_dtype, S_T, nullptr, 0, nullptr, nullptr, z, A,
                         B, T, H, d_k, d_v, chunk, stream);
+}
+
+kda_status kda_chunk_fwd_split_plan(kda_dtype qkv_dtype, int B, int T, int H, int d_k, int d_v, int chunk,
+                                    int parts, int num_cus, int* parts_out, size_t* workspace_bytes) {
+  if (qkv_dtype != KDA_F32 && qkv_dtype != KDA_BF16) return KDA_ERR_DTYPE;
+  if (B < 1 || H < 1 || T < 0 || parts < 0 || num_cus < 0) return KDA_ERR_SHAPE;
+  if (!dim_ok(d_k) || !dim_ok(d_v)) return KDA_ERR_UNSUPPORTED;
+  if (chunk != 16 && chunk != 32 && chunk != 64) return KDA_ERR_UNSUPPORTED;
+  if (!sizes_ok(B, T, H, d_k, d_v)) return KDA_ERR_SHAPE;
+  if (!parts_out || !workspace_bytes) return KDA_ERR_NULL;
+  const int io = (qkv_dtype == KDA_BF16) ? 1 : 0;
+  SplitShape sh{1, T};
+  if (plan_prefill(B, H, d_k, d_v, chunk, io).impl != IMPL_PIPE) {
+    if (parts > 1) return KDA_ERR_UNSUPPORTED;
+  } else if (parts > 1) {
+    sh = split_shape_for(T, parts);
+  } else if (parts == 0) {
+    const int cus = num_cus ? num_cus : device_cus();
+    if (cus <= 0) {
+      g_last_hip_error = (int)hipErrorNoDevice;
+      return KDA_ERR_HIP;
+    }
+    sh = split_shape_auto(B, T, H, d_k, d_v, cus);
+  }
+  *parts_out = sh.parts;
+  *workspace_bytes = split_ws_bytes(B, H, d_k, d_v, sh.parts);
+  return KDA_OK;
+}
+
+kda_status kda_chunk_fwd_split(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
+                               const float* alpha, const float* beta, const float* S0,
+                               void* o, kda_dtype o_dtype, float* S_T,
+                               int B, int T, int H, int d_k, int d_v, int chunk,
+                               int parts, int num_cus, void* workspace, size_t workspace_bytes, void* stream) {
+  const SplitReq req{parts, num_cus, workspace, workspace_bytes};
+  return chunk_fwd_impl(q, k, v, qkv_dtype, alpha, beta, S0, o, o_dtype, S_T, nullptr, 0, nullptr, nullptr,
+                        nullptr, nullptr, B, T, H, d_k, d_v, chunk, stream, &req);
 }
 
 }  // extern "C"

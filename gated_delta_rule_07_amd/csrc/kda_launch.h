@@ -26,6 +26,19 @@ struct PrefillParams {
   // the kernel from z ([.][H][dk], q/k/v dtype) and A ([H] fp32); alpha is unused.
   const void* z;
   const float* A;
+  // Sequence split (a two-level scan over parts of each sequence).  split = 0:
+  // off.  Otherwise every sequence is cut into nparts parts of part_len tokens
+  // (a multiple of 32; the last part may be shorter).
+  //   split = 1: parts 0 .. nparts-2, each from a zero state over d_v + d_k
+  //     state columns: the d_v value columns give the part's own contribution N,
+  //     the d_k extra columns start as the identity with V = 0 and give the
+  //     part's transition M (state after the part = M S_in + N).  Both go to
+  //     ws_trans [B][nparts-1][H][dk][dv+dk]; o is not written.
+  //   split = 2: parts 0 .. nparts-1, each from the state entering it, ws_in
+  //     [B][nparts][H][dk][dv]; o is written, and S_T by the last part.
+  int split, nparts, part_len;
+  float* ws_trans;
+  float* ws_in;
 };
 
 // The lower-bounded retention exp(-5 sigmoid(e^A z)) for x = e^A z.
@@ -123,6 +136,10 @@ hipError_t launch_prefill(const PrefillParams& p, const SnapList& snap, int io_d
 // requested chunk 32 or 64; runs 32-token chunks).
 bool prefill_pipe_supported(int io_dtype, int dk, int dv, int chunk, int H);
 hipError_t launch_prefill_pipe(const PrefillParams& p, const SnapList& snap, hipStream_t s);
+
+// Between the two split passes: ws_in[b][0] = S0 (zeros when null) and
+// ws_in[b][j+1] = M_j ws_in[b][j] + N_j from ws_trans, for every (b, h).
+hipError_t launch_split_combine(const PrefillParams& p, hipStream_t s);
 
 // Speculative decoding: K draft tokens per (sequence, head).
 constexpr int kMaxDraft = 16;

@@ -490,7 +490,9 @@ __device__ void phase_state(Smem<C>& sm, f32x4 (&S)[C::NKT], int w, int lane, co
     }
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const int ex = (mx > 0.0f) ? __builtin_amdgcn_frexp_expf(mx) : 0;
+  // scale at most 2^64: a column below 2^-68 (decayed, with no value input) is
+  // negligible, and a larger scale could overflow to infinity
+  const int ex = (mx > 0.0f) ? max(__builtin_amdgcn_frexp_expf(mx), -64) : 0;
   const float scale = __builtin_amdgcn_ldexpf(1.0f, -ex);
   const float unscale = __builtin_amdgcn_ldexpf(1.0f, ex);
 

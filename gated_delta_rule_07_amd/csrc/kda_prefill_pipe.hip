@@ -186,9 +186,16 @@ __device__ __forceinline__ Item split_item(const Item& it, int first) {
 struct Ctx4 {
   PrefillParams p;
   int bh, b, h, col0, nchunks;
-  int T;           // this sequence's length
+  int T;           // this sequence's (or part's) length
   long long tok0;  // its first token in the [.][H][d] token rows
   float eA;        // fused gate: e^{A_h}
+  bool v_on;       // false: V reads as zeros (transition columns)
+  bool o_on;       // false: o is not written
+  int ident;       // >= 0: the state starts as columns ident.. of the identity
+  const float* s0; // else: this slab's initial state (null: zeros), row stride s0_ld
+  int s0_ld;
+  float* st;       // this slab's final state (null: not written), row stride st_ld
+  int st_ld;
 };
 
 // ---- scan waves --------------------------------------------------------------------
@@ -257,7 +264,9 @@ __device__ void load_raw4(Raw4<C>& raw, const Ctx4& cx, int c, int sw, int lane)
   }
   const int st = opaque(64 * sw + lane);  // scan lanes 0-255: V row st/8, columns 4(st%8)..+3
   const int vs = p.H * p.dv;
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(static_cast<const __bf16*>(p.v) + row0 * p.dv + cx.col0, rows * vs * 2);
+  // a zero-length range reads as zeros: the transition columns have V = 0
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(static_cast<const __bf16*>(p.v) + row0 * p.dv + (cx.v_on ? cx.col0 : 0),
+                                              cx.v_on ? rows * vs * 2 : 0);
   raw.v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, 2 * (((st / 8) % CS) * vs + 4 * (st % 8)), 0, 0));
   raw.beta = 0.0f;
   if (sw == 0) {  // beta is kept by the first CS scan lanes only
@@ -652,14 +661,17 @@ __device__ void state_prepare(Smem4<C>& sm, StateRegs<C>& R, const Item& it, int
   for (int i = 0; i < 16; ++i) mv = fmaxf(mv, fabsf(vf[i]));
   ms = fmaxf(ms, __shfl_xor(ms, 32));
   mv = fmaxf(mv, __shfl_xor(mv, 32));
-  // keep the scaled column maximum within [2^-4, 2^4]; rescale rarely
+  // Keep the scaled column maximum within [2^-4, 2^4]; rescale rarely.  The
+  // scale is capped at 2^64: a column whose values have decayed below 2^-68
+  // with no value input (a transition column, or an all-zero V column) stays
+  // there, so the scale never overflows to infinity (0 * inf would be NaN).
   const float m = fmaxf(ms, mv * R.sc);
-  const bool bad = m > 16.0f || (m > 0.0f && m < 0.0625f);
+  const bool bad = m > 16.0f || (m > 0.0f && m < 0.0625f && R.sc < 0x1p64f);
   if (__builtin_amdgcn_ballot_w64(bad) != 0) {
     float f = 1.0f;
     if (bad) {
       const int ex = __builtin_amdgcn_frexp_expf(m);  // m = frac * 2^ex, frac in [0.5, 1)
-      f = __builtin_amdgcn_ldexpf(1.0f, -ex);
+      f = fminf(__builtin_amdgcn_ldexpf(1.0f, -ex), 0x1p64f / R.sc);  // powers of two: exact
     }
 #pragma unroll
     for (int ct = 0; ct < C::NKT; ++ct) R.S[ct] *= f;
@@ -690,8 +702,8 @@ __device__ void out_pu_store(Smem4<C>& sm, f32x16& O, float usc, const Item& it,
   const int rows = chunk_end(it.c, cx.T);
   const int esz = p.o_f32 ? 4 : 2;
   const int rs = p.H * p.dv * esz;
-  char* ob = static_cast<char*>(p.o) + (((size_t)(cx.tok0 + t0) * p.H + cx.h) * p.dv + cx.col0) * esz;
-  const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(ob, rows * rs);
+  char* ob = static_cast<char*>(p.o) + (((size_t)(cx.tok0 + t0) * p.H + cx.h) * p.dv + (cx.o_on ? cx.col0 : 0)) * esz;
+  const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(ob, cx.o_on ? rows * rs : 0);  // zero-length: stores dropped
   const int vbase = 4 * h * rs + n * esz;
   if (p.o_f32) {
 #pragma unroll
@@ -763,14 +775,18 @@ __device__ void run_role(Smem4<C>& sm, const Ctx4& cx, const SnapList& snap, int
   float usc = 1.0f;
   if constexpr (ROLE == STATE) {
     const int h = lane / 32, n = lane % 32;
-    const size_t sbase = (size_t)cx.bh * C::DK * p.dv + cx.col0;
 #pragma unroll
     for (int ct = 0; ct < C::NKT; ++ct) R.S[ct] = (f32x16)0.0f;
-    if (p.S0) {
+    if (cx.ident >= 0) {
 #pragma unroll
       for (int ct = 0; ct < C::NKT; ++ct)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) R.S[ct][i] = p.S0[sbase + (32 * ct + 8 * (i / 4) + 4 * h + (i % 4)) * p.dv + n];
+        for (int i = 0; i < 16; ++i) R.S[ct][i] = (32 * ct + 8 * (i / 4) + 4 * h + (i % 4) == cx.ident + n) ? 1.0f : 0.0f;
+    } else if (cx.s0) {
+#pragma unroll
+      for (int ct = 0; ct < C::NKT; ++ct)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) R.S[ct][i] = cx.s0[(size_t)(32 * ct + 8 * (i / 4) + 4 * h + (i % 4)) * cx.s0_ld + n];
     }
     R.sc = 1.0f;
   }
@@ -850,7 +866,7 @@ __device__ void run_role(Smem4<C>& sm, const Ctx4& cx, const SnapList& snap, int
   }
 
   if constexpr (ROLE == STATE) {
-    if (p.S_T) store_state<C>(p.S_T + (size_t)cx.bh * C::DK * p.dv + cx.col0, R, p.dv, lane);
+    if (cx.st) store_state<C>(cx.st, R, cx.st_ld, lane);
   }
 }
 
@@ -860,16 +876,48 @@ __global__ __launch_bounds__(C::NT, 1) void kda_prefill_pipe_kernel(PrefillParam
   const int tid = threadIdx.x, lane = tid % 64;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   int task, slab;
-  task_of_block(p.dv / J, task, slab);
+  task_of_block((p.split == 1 ? p.dv + C::DK : p.dv) / J, task, slab);
   __shared__ int seq_lens[kMaxRankedSeqs], seq_pick;
   Ctx4 cx;
   cx.p = p;
   cx.h = task % p.H;
-  cx.b = __builtin_amdgcn_readfirstlane(seq_by_length_rank(p.cu, p.B, p.T, task / p.H, seq_lens, &seq_pick));
-  cx.bh = cx.b * p.H + cx.h;
   cx.col0 = slab * J;
   cx.eA = G ? __expf(p.A[cx.h]) : 1.0f;
-  seq_range(p, cx.b, cx.tok0, cx.T);
+  const size_t mat = (size_t)C::DK * p.dv;  // elements of one state
+  if (p.split) {
+    // task = (b, part, h); part j covers tokens [j part_len, (j+1) part_len) of sequence b
+    const int np = p.split == 1 ? p.nparts - 1 : p.nparts;
+    const int part = (task / p.H) % np;
+    cx.b = task / p.H / np;
+    cx.bh = cx.b * p.H + cx.h;
+    const long long start = (long long)part * p.part_len;
+    cx.tok0 = (long long)cx.b * p.T + start;
+    cx.T = (int)max(0LL, min((long long)p.part_len, (long long)p.T - start));
+    if (p.split == 1) {
+      cx.v_on = cx.col0 < p.dv;
+      cx.o_on = false;
+      cx.ident = cx.col0 < p.dv ? -1 : cx.col0 - p.dv;
+      cx.s0 = nullptr;
+      cx.s0_ld = 0;
+      cx.st_ld = p.dv + C::DK;
+      cx.st = p.ws_trans + ((size_t)(cx.b * (p.nparts - 1) + part) * p.H + cx.h) * C::DK * cx.st_ld + cx.col0;
+    } else {
+      cx.v_on = cx.o_on = true;
+      cx.ident = -1;
+      cx.s0_ld = cx.st_ld = p.dv;
+      cx.s0 = p.ws_in + ((size_t)(cx.b * p.nparts + part) * p.H + cx.h) * mat + cx.col0;
+      cx.st = (part == p.nparts - 1 && p.S_T) ? p.S_T + (size_t)cx.bh * mat + cx.col0 : nullptr;
+    }
+  } else {
+    cx.b = __builtin_amdgcn_readfirstlane(seq_by_length_rank(p.cu, p.B, p.T, task / p.H, seq_lens, &seq_pick));
+    cx.bh = cx.b * p.H + cx.h;
+    seq_range(p, cx.b, cx.tok0, cx.T);
+    cx.v_on = cx.o_on = true;
+    cx.ident = -1;
+    cx.s0_ld = cx.st_ld = p.dv;
+    cx.s0 = p.S0 ? p.S0 + (size_t)cx.bh * mat + cx.col0 : nullptr;
+    cx.st = p.S_T ? p.S_T + (size_t)cx.bh * mat + cx.col0 : nullptr;
+  }
   cx.nchunks = (cx.T + CS - 1) / CS;
   // T's upper-right 16x16 block is read as zeros and never written
   for (int i = tid; i < 2 * CS * C::LDC; i += C::NT) (&sm.t[0][0])[i] = (h16)0.0f;
@@ -883,7 +931,8 @@ __global__ __launch_bounds__(C::NT, 1) void kda_prefill_pipe_kernel(PrefillParam
 template <int DK>
 hipError_t launch_pipe(const PrefillParams& p, const SnapList& snap, hipStream_t s) {
   using C = Cfg4<DK>;
-  const unsigned grid = (unsigned)(p.B * p.H * (p.dv / J));
+  const int tasks = p.B * p.H * (p.split == 1 ? p.nparts - 1 : p.split == 2 ? p.nparts : 1);
+  const unsigned grid = (unsigned)(tasks * ((p.split == 1 ? p.dv + DK : p.dv) / J));
   if (p.z) hipLaunchKernelGGL((kda_prefill_pipe_kernel<C, true>), dim3(grid), dim3(C::NT), 0, s, p, snap);
   else hipLaunchKernelGGL((kda_prefill_pipe_kernel<C, false>), dim3(grid), dim3(C::NT), 0, s, p, snap);
   return hipGetLastError();

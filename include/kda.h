@@ -41,6 +41,8 @@
 #ifndef KDA_H
 #define KDA_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -188,6 +190,48 @@ kda_status kda_chunk_fwd_gated(const void* q, const void* k, const void* v, kda_
                                const void* z, const float* A, const float* beta, const float* S0,
                                void* o, kda_dtype o_dtype, float* S_T,
                                int B, int T, int H, int d_k, int d_v, int chunk, void* stream);
+
+/*
+ * Prefill with each sequence split into parts that run side by side: for few
+ * long sequences (small B*H) the single-pass kernel has one workgroup per
+ * (sequence, head, 32 state columns) and leaves most of the GPU idle.  Between
+ * chunks only the state is carried (the second page, on putting the recurrence
+ * on the GPU), and a run of tokens maps its incoming state S to M S + N with a
+ * d_k x d_k transition M (section 3.3 of the first page: each token applies
+ * (I - beta k k^T) Diag(alpha) to every state column and adds beta k v^T), so:
+ * pass 1 computes N and M of every part but the last, in parallel; a combine
+ * step chains S_in(j+1) = M_j S_in(j) + N_j in fp32; pass 2 reruns every part
+ * from its S_in and writes o and S_T.  Parts are whole 32-token chunks.
+ *
+ *   parts     : 0 = the library's choice (a step-count model of the launches
+ *               on num_cus compute units; 1 part when splitting does not pay);
+ *               1 = the single pass (kda_chunk_fwd); >= 2 = that many parts, or
+ *               fewer when T has fewer 32-token chunks.
+ *   num_cus   : compute units for the model; 0 = those of the current device.
+ *   workspace : device memory of workspace_bytes bytes, 16-byte aligned, used
+ *               for the transitions and incoming states; its contents on entry
+ *               do not matter and are overwritten.  May be NULL when the
+ *               resulting split has 1 part.  kda_chunk_fwd_split_plan gives the
+ *               part count and the bytes needed:
+ *               4 * B * H * d_k * ((P - 1) * (d_v + d_k) + P * d_v) for P parts.
+ * Every other argument as kda_chunk_fwd.  Splitting is built for the pipelined
+ * kernel's shapes (bf16 q/k/v, d_k in {64, 128}, d_v a multiple of 32, chunk 32
+ * or 64); parts >= 2 for another shape returns KDA_ERR_UNSUPPORTED.  Errors:
+ * as kda_chunk_fwd, plus KDA_ERR_NULL (workspace NULL when needed),
+ * KDA_ERR_SHAPE (workspace_bytes too small, parts or num_cus < 0),
+ * KDA_ERR_ALIAS (workspace overlaps an input or output), KDA_ERR_HIP (the
+ * device's compute units could not be queried).  The result equals
+ * kda_chunk_fwd up to rounding (the state entering each part goes through one
+ * fp32 product with M instead of the chunk recurrence).  Three kernels are
+ * enqueued on `stream`.
+ */
+kda_status kda_chunk_fwd_split_plan(kda_dtype qkv_dtype, int B, int T, int H, int d_k, int d_v, int chunk,
+                                    int parts, int num_cus, int* parts_out, size_t* workspace_bytes);
+kda_status kda_chunk_fwd_split(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
+                               const float* alpha, const float* beta, const float* S0,
+                               void* o, kda_dtype o_dtype, float* S_T,
+                               int B, int T, int H, int d_k, int d_v, int chunk,
+                               int parts, int num_cus, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * kda_decode_step with the gate fused in (as kda_chunk_fwd_gated):

@@ -53,13 +53,21 @@ def gpu_s_heads(S, heads=None):
 
 
 def abs_err(got, ref):
-    return float(np.abs(got - ref).max()) if got.size else 0.0
+    """max|got - ref|; inf when either side holds a value that is not finite."""
+    if got.size == 0:
+        return 0.0
+    if not (np.isfinite(got).all() and np.isfinite(ref).all()):
+        return float("inf")
+    return float(np.abs(got - ref).max())
 
 
 def rel_err_per_head(got, ref):
-    """max over heads of max|got-ref| / RMS(ref) (heads along axis 0)."""
+    """max over heads of max|got-ref| / RMS(ref) (heads along axis 0); inf when
+    either side holds a value that is not finite (so NaN never passes)."""
     if got.size == 0:
         return 0.0
+    if not (np.isfinite(got).all() and np.isfinite(ref).all()):
+        return float("inf")
     worst = 0.0
     for g, r in zip(got, ref):
         rms = float(np.sqrt(np.mean(r * r)))

@@ -263,3 +263,75 @@ def test_product_path_does_not_import_the_oracle():
         text = f.read_text()
         for bad in ("import oracle", "from oracle", "kda_oracle"):
             assert bad not in text, f"{f} mentions {bad}"
+
+
+def _plan(lib, dtype=1, B=1, T=4096, H=8, dk=128, dv=128, chunk=64, parts=0, cus=256):
+    n, ws = ctypes.c_int(-1), ctypes.c_size_t(0)
+    st = lib.kda_chunk_fwd_split_plan(dtype, B, T, H, dk, dv, chunk, parts, cus, ctypes.byref(n), ctypes.byref(ws))
+    return st, n.value, ws.value
+
+
+def _ws_bytes(P, B=1, H=8, dk=128, dv=128):
+    return 4 * B * H * dk * ((P - 1) * (dv + dk) + P * dv)
+
+
+def test_split_plan_choices():
+    """The part count the library picks for 256 compute units, and the workspace
+    it asks for (host logic only: an explicit compute-unit count makes no HIP call)."""
+    lib = _lib()
+    st, n, ws = _plan(lib, B=1, T=4096, H=8)      # 32 chains of 128 chunks: split
+    assert st == 0 and 2 <= n <= 16 and ws == _ws_bytes(n)
+    st, n, _ = _plan(lib, B=1, T=65536, H=2)      # 8 chains of 2048 chunks: many parts
+    assert st == 0 and n >= 16
+    assert _plan(lib, B=2, T=65536, H=32) == (0, 1, 0)   # 256 chains fill the GPU already
+    assert _plan(lib, T=32)[:2] == (0, 1) and _plan(lib, T=0)[:2] == (0, 1)
+    assert _plan(lib, dtype=0, dk=32, dv=32)[:2] == (0, 1)   # not a split shape: single pass
+    assert _plan(lib, dtype=0, dk=32, dv=32, parts=4)[0] == 4
+    assert _plan(lib, dk=32, parts=4)[0] == 4
+
+
+@pytest.mark.parametrize("T", [33, 100, 1000, 4096, 5000])
+def test_split_plan_explicit_counts(T):
+    """Explicit counts give at most that many parts of whole 32-token chunks, at
+    most one per chunk, and planning again with the result keeps it."""
+    lib = _lib()
+    nch = -(-T // 32)
+    for P in (1, 2, 3, 5, 7, 64, 1000):
+        st, n, ws = _plan(lib, T=T, parts=P)
+        assert st == 0 and 1 <= n <= min(P, nch)
+        assert ws == (_ws_bytes(n) if n > 1 else 0)
+        assert _plan(lib, T=T, parts=n)[1] == n
+
+
+def test_split_plan_invalid():
+    lib = _lib()
+    assert _plan(lib, parts=-1)[0] == 2
+    assert _plan(lib, cus=-1)[0] == 2
+    assert _plan(lib, dtype=5)[0] == 3
+    assert _plan(lib, dk=48)[0] == 4
+    assert lib.kda_chunk_fwd_split_plan(1, 1, 64, 1, 128, 128, 64, 0, 256, None, None) == 1
+
+
+def _split(lib, parts=4, cus=256, ws=_addr(10), wsb=1 << 30, **over):
+    a = dict(q=_addr(0), k=_addr(1), v=_addr(2), dtype=1, alpha=_addr(3), beta=_addr(4), S0=_addr(5),
+             o=_addr(6), odt=0, S_T=_addr(7), B=1, T=4096, H=8, dk=128, dv=128, chunk=64)
+    a.update(over)
+    return lib.kda_chunk_fwd_split(a["q"], a["k"], a["v"], a["dtype"], a["alpha"], a["beta"], a["S0"], a["o"],
+                                   a["odt"], a["S_T"], a["B"], a["T"], a["H"], a["dk"], a["dv"], a["chunk"],
+                                   parts, cus, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ws=None), 1),                                        # workspace needed
+    (dict(wsb=_ws_bytes(4) - 16), 2),                          # workspace too small
+    (dict(ws=ctypes.c_void_p(BASE + (10 << 32) + 8)), 5),      # misaligned workspace
+    (dict(ws=_addr(0)), 6), (dict(ws=_addr(3)), 6),            # workspace aliases q, alpha
+    (dict(ws=_addr(5)), 6),                                    # ... S0
+    (dict(ws=_addr(6)), 6), (dict(ws=_addr(7)), 6),            # ... o, S_T
+    (dict(parts=-1), 2), (dict(cus=-1), 2),
+    (dict(dtype=0, dk=32, dv=32), 4),                          # fp32: no split kernel
+    (dict(dk=32, parts=3), 4),                                 # bf16 d_k = 32: generic kernel
+    (dict(q=None), 1), (dict(B=0), 2),
+])
+def test_split_validation(kw, code):
+    assert _split(_lib(), **kw) == code

@@ -5,7 +5,7 @@ import torch
 
 import kda_inputs as ki
 import oracle
-from kda_check import TOL_BF16_REL, TOL_F32_ABS, log, rel_err_per_head
+from kda_check import TOL_BF16_REL, TOL_F32_ABS, abs_err, log, rel_err_per_head
 
 pytestmark = pytest.mark.gpu
 
@@ -32,7 +32,7 @@ def _run_steps(gpu, B, H, dk, dv, dtype, steps, seed=0, check_every=1):
                 # one token per head: normalise by the RMS of the whole step's output
                 worst_o = max(worst_o, rel_err_per_head(got.reshape(1, -1), ref.reshape(1, -1)))
             else:
-                worst_o = max(worst_o, float(np.abs(got - ref).max()))
+                worst_o = max(worst_o, abs_err(got, ref))
     torch.cuda.synchronize()
     gs = S.cpu().double().numpy().reshape(B * H, dk, dv)
     rs = S_ref.reshape(B * H, dk, dv)
@@ -41,7 +41,7 @@ def _run_steps(gpu, B, H, dk, dv, dtype, steps, seed=0, check_every=1):
         log(f"  o err {worst_o:.2e}  S err {es:.2e}")
         assert worst_o <= TOL_BF16_REL and es <= TOL_BF16_REL
     else:
-        es = float(np.abs(gs - rs).max())
+        es = abs_err(gs, rs)
         log(f"  o err {worst_o:.2e}  S err {es:.2e}")
         assert worst_o <= TOL_F32_ABS and es <= TOL_F32_ABS
 

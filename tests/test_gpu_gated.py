@@ -12,7 +12,8 @@ import torch
 
 import kda_inputs as ki
 import oracle
-from kda_check import TOL_BF16_REL, TOL_F32_ABS, assert_close, gpu_o_heads, gpu_s_heads, log, rel_err_per_head
+from kda_check import (TOL_BF16_REL, TOL_F32_ABS, abs_err, assert_close, gpu_o_heads, gpu_s_heads, log,
+                       rel_err_per_head)
 
 pytestmark = pytest.mark.gpu
 
@@ -114,11 +115,11 @@ def test_gated_decode_matches_oracle(gpu, dk, dv, dtype):
         ro = oracle.decode_step(h["q"], h["k"], h["v"], oracle.gate_alpha(z.cpu(), A.cpu()), h["beta"], S_ref)
         got = o.float().cpu().double().numpy().reshape(1, -1)
         worst = max(worst, rel_err_per_head(got, ro.reshape(1, -1)) if dtype == torch.bfloat16
-                    else float(np.abs(got - ro.reshape(1, -1)).max()))
+                    else abs_err(got, ro.reshape(1, -1)))
     torch.cuda.synchronize()
     gs = S.cpu().double().numpy().reshape(B * H, dk, dv)
     rs = S_ref.reshape(B * H, dk, dv)
-    es = rel_err_per_head(gs, rs) if dtype == torch.bfloat16 else float(np.abs(gs - rs).max())
+    es = rel_err_per_head(gs, rs) if dtype == torch.bfloat16 else abs_err(gs, rs)
     tol = TOL_BF16_REL if dtype == torch.bfloat16 else TOL_F32_ABS
     log(f"  gated decode d={dk}x{dv}: o {worst:.2e}  S {es:.2e} (tol {tol})")
     assert worst <= tol and es <= tol

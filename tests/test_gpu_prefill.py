@@ -119,6 +119,19 @@ def test_steep_splits_at_first_out_of_range_token(gpu, dk):
     check_prefill(inp, chunk=32, what="first-token splits")
 
 
+@pytest.mark.parametrize("dtype,dk", [(torch.bfloat16, 128), (torch.float32, 32)])
+def test_zero_value_columns_with_long_decay(gpu, dtype, dk):
+    """State columns with no value input decay to zero over a long sequence; the
+    kernels' power-of-two operand scale for them must stay finite (an unbounded
+    scale would reach infinity and turn the zero V times it into NaN)."""
+    inp = _inp(gpu, 1, 8192, 1, dk, dk, dtype=dtype, seed=21)
+    inp["v"][..., : dk // 2] = 0
+    inp["alpha"].fill_(math.exp(-0.3))
+    log(f"zero V columns, decay e^-0.3, d={dk} {dtype}")
+    o, st, _, _ = check_prefill(inp, what="zero V columns")
+    assert torch.isfinite(o).all() and torch.isfinite(st).all()
+
+
 @pytest.mark.parametrize("beta_val", [0.0, 0.5, 1.0, 2.0])
 def test_beta_values(gpu, beta_val):
     """beta is not clamped: 0, 1/2, 1 and the Householder value 2."""

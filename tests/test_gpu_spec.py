@@ -15,7 +15,7 @@ import torch
 
 import kda_inputs as ki
 import oracle
-from kda_check import TOL_BF16_REL, TOL_F32_ABS, log, rel_err_per_head, to_host
+from kda_check import TOL_BF16_REL, TOL_F32_ABS, abs_err, log, rel_err_per_head, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -42,7 +42,7 @@ def _close(got, ref, bf, what):
         e = rel_err_per_head(got, ref)
         tol = TOL_BF16_REL
     else:
-        e = float(np.abs(got - ref).max())
+        e = abs_err(got, ref)
         tol = TOL_F32_ABS
     log(f"  {what}: {e:.3e} (tol {tol})")
     assert e <= tol, f"{what}: {e:.3e} > {tol}"
