@@ -86,10 +86,11 @@ SplitShape split_shape_for(int T, int P) {
 }
 
 // The part count with the smallest modelled time.  The model counts pipeline
-// steps: a launch of G workgroups on `cus` compute units runs ceil(G / cus)
-// rounds of (chunks per part + 3) steps; the combine costs about half a step per
-// part and the two extra launches about two steps.  A split is taken only when
-// it models at least 10% faster than the single pass.
+// steps (about 2 us each): a launch of G workgroups on `cus` compute units runs
+// ceil(G / cus) rounds of (chunks per part + 3) steps; the combine costs about
+// two steps per part (it is sequential over the parts, about 4 us each) and the
+// two extra launches about two steps.  A split is taken only when it models at
+// least 10% faster than the single pass.
 SplitShape split_shape_auto(int B, int T, int H, int dk, int dv, int cus) {
   const int nch = (T + 31) / 32;
   const long long bh = (long long)B * H, ns = dv / 32, nsa = (dv + dk) / 32;
@@ -101,7 +102,7 @@ SplitShape split_shape_auto(int B, int T, int H, int dk, int dv, int cus) {
     const SplitShape sh = split_shape_for(T, P);
     if (sh.parts != P) continue;
     const double cost = (rounds(bh * (P - 1) * nsa) + rounds(bh * P * ns)) * (sh.part_len / 32 + 3) +
-                        0.5 * (P - 1) + 2.0;
+                        2.0 * (P - 1) + 2.0;
     if (cost < best_cost) {
       best_cost = cost;
       best = sh;

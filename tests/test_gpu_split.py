@@ -52,6 +52,13 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("dk,dv", [(128, 64), (64, 128), (128, 32)])
+def test_split_unequal_head_sizes(gpu, dk, dv):
+    """d_k != d_v: pass 1 runs d_v value columns and d_k transition columns."""
+    inp = ki.make_prefill(2, 450, 2, dk, dv, torch.bfloat16, 3.0, 0.1, seed=dk + 3 * dv, device=gpu)
+    _check(inp, 3, f"d_k={dk} d_v={dv}")
+
+
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_split_matches_oracle(gpu, case):
     name, B, T, H, dk, parts = case
