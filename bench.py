@@ -3,11 +3,14 @@
 
 One timed step is one kda_chunk_fwd call over the 64K-token prefill workload
 (B=2, H=32, T=65536, d_k=d_v=128, bf16 q/k/v, fp32 alpha/beta/state, chunk 64,
-fp32 o), with inputs resident in HBM.  The same run also times the batched
-decode workload (B=256, H=32, d=128, 100 in-place steps) and reports it under
-"decode".  Before any timing, sampled heads of both workloads are checked
-against the fp64 oracle (the parity gate); the oracle's time on that sample,
-on this host's cores, is the CPU baseline.
+fp32 o), with inputs resident in HBM.  The same run times the other calls on
+their workloads (state snapshots, the fused gate, a packed batch, the split
+prefill, batched and speculative decode) and reports each under its own key.
+
+The GPU legs keep host copies of sampled heads' inputs and outputs; the last
+leg, the CPU baseline, runs the fp64 oracle on all of them.  Its time on the
+prefill sample, on this host's cores, is `cpu_baseline`; its comparisons are
+the parity fields (max|GPU - oracle| / RMS(oracle) per head, worst head).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -85,6 +88,20 @@ def timed_launches(fn, n, torch):
     return wall_ms, sum(per) / len(per), starts[0].elapsed_time(ends[-1])
 
 
+def back_to_back_ms(fn, n, torch):
+    """Mean ms per launch of n launches of fn() back to back, between one pair of
+    HIP events on the current stream (no markers between the launches, so short
+    kernels are not charged for them)."""
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
 def rel_err_heads(got, ref):
     """Worst head's max|got - ref| / RMS(ref); inf when anything is not finite."""
     import numpy as np
@@ -97,6 +114,49 @@ def rel_err_heads(got, ref):
     return worst
 
 
+class OracleChecks:
+    """Host copies of sampled heads' inputs and the GPU's outputs for them, filled
+    in by the GPU legs and compared in the CPU-baseline leg (the only leg that
+    runs the oracle)."""
+
+    def __init__(self):
+        self.items = {}
+
+    def add(self, name, inputs, got_o, got_s, heads=None, gate=None, per_step=False, timed=False):
+        """inputs: host q, k, v, alpha (or None with gate=(z, A)), beta, S0 as [B,T,H,.];
+        got_o [n, T, d_v] (None: not compared), got_s [n, d_k, d_v], both for `heads`
+        (ids b*H + h; None: all, in (b, h) order).  per_step: normalise o per token
+        over the heads (decode, where each head has one token per step)."""
+        self.items[name] = dict(inputs=inputs, got_o=got_o, got_s=got_s, heads=heads, gate=gate,
+                                per_step=per_step, timed=timed)
+
+
+def cpu_baseline_leg(checks, threads, log):
+    """Runs the oracle on every check: returns {name: (err_o, err_s)} and the wall
+    time of the timed check (the prefill sample), which is the CPU baseline."""
+    import oracle
+    errs, timed_s = {}, None
+    for name, c in checks.items.items():
+        h = c["inputs"]
+        alpha = h["alpha"] if c["gate"] is None else oracle.gate_alpha(*c["gate"])
+        t0 = time.perf_counter()
+        ro, rs = oracle.forward(h["q"], h["k"], h["v"], alpha, h["beta"], h["S0"], heads=c["heads"],
+                                threads=threads, want_o=c["got_o"] is not None)
+        if c["timed"]:
+            timed_s = time.perf_counter() - t0
+        eo = None
+        if c["got_o"] is not None:
+            if c["per_step"]:
+                eo = max(rel_err_heads(c["got_o"][:, t].reshape(1, -1), ro[:, t].reshape(1, -1))
+                         for t in range(ro.shape[1]))
+            else:
+                eo = max(rel_err_heads(g[None].astype("float64"), r[None]) for g, r in zip(c["got_o"], ro))
+        es = rel_err_heads(c["got_s"].astype("float64"), rs)
+        errs[name] = (eo, es)
+        log(f"parity {name}: o {eo if eo is None else f'{eo:.3e}'}  S {es:.3e}")
+    return errs, timed_s
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -104,7 +164,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=100)
     ap.add_argument("--sample-heads", type=int, default=64, help="heads checked by the oracle (all 64 by default)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="do not report the oracle's time")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
     args = ap.parse_args()
@@ -126,12 +186,22 @@ def main():
     torch.cuda.set_device(dev)
     kda.load_library()
     props = torch.cuda.get_device_properties(dev)
+    checks = OracleChecks()
+
+    def heads_of(t, heads):
+        """[B,T,H,d] device tensor -> float32 numpy [n, T, d] for head ids b*H + h."""
+        Bt, Tt, Ht, dt = t.shape
+        return t.permute(0, 2, 1, 3).reshape(Bt * Ht, Tt, dt)[heads].float().cpu().numpy()
+
+    def states_of(t, heads):
+        return t.reshape(-1, t.shape[-2], t.shape[-1])[heads].float().cpu().numpy()
 
     # ---------------- prefill: 64K tokens, B=2, H=32, d=128 ----------------
     w = ki.WORKLOADS[2]
     B, T, H, dk, dv, C = w.B, w.T, w.H, w.dk, w.dv, w.chunk
     log(f"generating prefill inputs B={B} T={T} H={H} d={dk}")
     x = ki.make_workload_prefill(2, seed=0, device=dev)
+    hx = {n: t.cpu() for n, t in x.items()}  # host copy for the oracle leg
     o = torch.empty(B, T, H, dv, device=dev, dtype=torch.float32)
     S_T = torch.empty(B, H, dk, dv, device=dev, dtype=torch.float32)
 
@@ -140,23 +210,9 @@ def main():
 
     step()
     torch.cuda.synchronize()
-
-    # parity gate on sampled heads; the oracle's time on that sample is the CPU baseline
-    import oracle
     nh = min(args.sample_heads, B * H)
     heads = sorted(set(int(v) for v in np.linspace(0, B * H - 1, nh)))
-    log(f"parity gate: oracle on heads {heads} (full T)")
-    hq = {k: v.cpu() for k, v in x.items()}
-    threads = oracle.default_threads()
-    t0 = time.perf_counter()
-    ro, rs = oracle.forward(hq["q"], hq["k"], hq["v"], hq["alpha"], hq["beta"], hq["S0"], heads=heads,
-                            threads=threads)
-    cpu_s = time.perf_counter() - t0
-    go = o.permute(0, 2, 1, 3).reshape(B * H, T, dv)[heads].cpu().double().numpy()
-    gs = S_T.reshape(B * H, dk, dv)[heads].cpu().double().numpy()
-    e_o, e_s = rel_err_heads(go, ro), rel_err_heads(gs, rs)
-    del hq, ro, rs, go, gs
-    log(f"parity: o {e_o:.3e}  S_T {e_s:.3e} (tol {TOL_REL}); oracle {cpu_s:.1f} s on {threads} threads")
+    checks.add("prefill", hx, heads_of(o, heads), states_of(S_T, heads), heads=heads, timed=True)
 
     for _ in range(args.warmup):
         step()
@@ -181,21 +237,25 @@ def main():
     sstep()
     torch.cuda.synchronize()
     snap_heads = [0, B * H // 2 + 5]
-    hs = {k: (v[:, :snap_pos[0]].cpu() if k != "S0" else v.cpu()) for k, v in x.items()}
-    _, rsn = oracle.forward(hs["q"], hs["k"], hs["v"], hs["alpha"], hs["beta"], hs["S0"], heads=snap_heads,
-                            want_o=False)
-    e_snap = rel_err_heads(snaps[:, :, 0].reshape(B * H, dk, dv)[snap_heads].cpu().double().numpy(), rsn)
+    checks.add("snapshot", {n: (t[:, :snap_pos[0]] if n != "S0" else t) for n, t in hx.items()}, None,
+               states_of(snaps[:, :, 0].contiguous(), snap_heads), heads=snap_heads)
     snap_last_is_state = bool(torch.equal(snaps[:, :, -1], S_T))
-    del hs, rsn
     for _ in range(args.warmup):
         sstep()
     s_wall_ms, s_kern_ms, _ = timed_launches(sstep, args.steps, torch)
     snap_bytes = B * H * len(snap_pos) * dk * dv * 4
     log(f"prefill + {len(snap_pos)} snapshots: {s_wall_ms / args.steps:.3f} ms/step (kernel {s_kern_ms:.3f} ms, "
-        f"{100 * (s_kern_ms / kern_ms - 1):+.1f}%); snapshot@{snap_pos[0]} err {e_snap:.3e}, "
-        f"last == S_T: {snap_last_is_state}")
+        f"{100 * (s_kern_ms / kern_ms - 1):+.1f}%); last == S_T: {snap_last_is_state}")
 
     # ------- the same prefill with the gate fused in (z and A instead of alpha) -------
+    def gate_check(name, z, A, hid):
+        b_, h_ = divmod(hid, H)
+        hin = {n: hx[n][b_:b_ + 1, :, h_:h_ + 1] for n in ("q", "k", "v", "beta")}
+        hin["S0"] = hx["S0"][b_:b_ + 1, h_:h_ + 1]
+        hin["alpha"] = None
+        checks.add(name, hin, heads_of(o, [hid]), states_of(S_T, [hid]),
+                   gate=(z[b_:b_ + 1, :, h_:h_ + 1].cpu(), A[h_:h_ + 1].cpu()))
+
     gz, gA = ki.make_gate((B, T, H, dk), H, w.qkv_dtype, seed=0, device=dev)
 
     def gstep():
@@ -203,23 +263,15 @@ def main():
 
     gstep()
     torch.cuda.synchronize()
-    e_go = e_gs = 0.0
     for hid in (0, B * H // 2 + 5):
-        b_, h_ = divmod(hid, H)
-        hg = {n: x[n][b_:b_ + 1, :, h_:h_ + 1].cpu() for n in ("q", "k", "v", "beta")}
-        ga = oracle.gate_alpha(gz[b_:b_ + 1, :, h_:h_ + 1].cpu(), gA[h_:h_ + 1].cpu())
-        rgo, rgs = oracle.forward(hg["q"], hg["k"], hg["v"], ga, hg["beta"], x["S0"][b_:b_ + 1, h_:h_ + 1].cpu(),
-                                  threads=threads)
-        e_go = max(e_go, rel_err_heads(o[b_, :, h_][None].cpu().double().numpy(), rgo))
-        e_gs = max(e_gs, rel_err_heads(S_T[b_, h_][None].cpu().double().numpy(), rgs))
-        del hg, ga, rgo, rgs
+        gate_check(f"gated head {hid}", gz, gA, hid)
     for _ in range(args.warmup):
         gstep()
     g_wall_ms, g_kern_ms, _ = timed_launches(gstep, args.steps, torch)
     g_per_th = per_th_bytes - 4 * dk + 2 * dk  # bf16 z in place of fp32 alpha; A is H floats per call
     g_bytes = g_per_th * B * T * H + 2 * B * H * dk * dv * 4
     log(f"gated prefill: {g_wall_ms / args.steps:.3f} ms/step (kernel {g_kern_ms:.3f} ms), "
-        f"{g_bytes / g_kern_ms / 1e6:.0f} GB/s of {g_per_th} B/token-head; parity o {e_go:.2e} S_T {e_gs:.2e}")
+        f"{g_bytes / g_kern_ms / 1e6:.0f} GB/s of {g_per_th} B/token-head")
     del gz, gA
 
     # fast-forgetting heads (z ~ N(-3, 1), A ~ N(0, 0.3)): most 32-token chunks decay
@@ -231,18 +283,11 @@ def main():
 
     fstep()
     torch.cuda.synchronize()
-    b_, h_ = 1, 7
-    hg = {n: x[n][b_:b_ + 1, :, h_:h_ + 1].cpu() for n in ("q", "k", "v", "beta")}
-    ga = oracle.gate_alpha(fz[b_:b_ + 1, :, h_:h_ + 1].cpu(), fA[h_:h_ + 1].cpu())
-    rgo, rgs = oracle.forward(hg["q"], hg["k"], hg["v"], ga, hg["beta"], x["S0"][b_:b_ + 1, h_:h_ + 1].cpu(),
-                              threads=threads)
-    e_fo = rel_err_heads(o[b_, :, h_][None].cpu().double().numpy(), rgo)
-    e_fs = rel_err_heads(S_T[b_, h_][None].cpu().double().numpy(), rgs)
-    del hg, ga, rgo, rgs
+    f_head = 1 * H + 7
+    gate_check("fast-forgetting", fz, fA, f_head)
     fstep()
     f_wall_ms, f_kern_ms, _ = timed_launches(fstep, args.steps, torch)
-    log(f"gated prefill, fast-forgetting heads: kernel {f_kern_ms:.3f} ms ({f_kern_ms / g_kern_ms:.2f}x); "
-        f"parity (head {b_ * H + h_}) o {e_fo:.2e} S_T {e_fs:.2e}")
+    log(f"gated prefill, fast-forgetting heads: kernel {f_kern_ms:.3f} ms ({f_kern_ms / g_kern_ms:.2f}x)")
     del fz, fA
 
     # ------- a packed batch of 16 sequences of mixed lengths (kda_chunk_fwd_varlen) -------
@@ -264,23 +309,20 @@ def main():
     torch.cuda.synchronize()
     vb = int(min(range(len(v_lens)), key=lambda i: v_lens[i]))  # the shortest sequence, against the oracle
     vs0 = int(v_cu[vb])
-    hv = {n: vflat[n][vs0:vs0 + v_lens[vb]][None].cpu() for n in vflat}
-    rvo, rvs = oracle.forward(hv["q"], hv["k"], hv["v"], hv["alpha"], hv["beta"], v_S0[vb:vb + 1].cpu(),
-                              heads=[0, H - 1], threads=threads)
-    e_vo = rel_err_heads(v_o[vs0:vs0 + v_lens[vb]].permute(1, 0, 2)[[0, H - 1]].cpu().double().numpy(), rvo)
-    e_vs = rel_err_heads(v_ST[vb][[0, H - 1]].cpu().double().numpy(), rvs)
-    del hv, rvo, rvs
+    vhin = {n: vflat[n][vs0:vs0 + v_lens[vb]][None].cpu() for n in vflat}
+    vhin["S0"] = v_S0[vb:vb + 1].cpu()
+    checks.add("varlen", vhin, heads_of(v_o[vs0:vs0 + v_lens[vb]][None], [0, H - 1]),
+               states_of(v_ST[vb:vb + 1], [0, H - 1]), heads=[0, H - 1])
     for _ in range(args.warmup):
         vstep()
     v_wall_ms, v_kern_ms, _ = timed_launches(vstep, args.steps, torch)
     v_tok_s = v_total / (v_kern_ms / 1e3)
     log(f"varlen: {len(v_lens)} sequences, {v_total} tokens ({min(v_lens)}..{max(v_lens)}): "
-        f"{v_kern_ms:.3f} ms, {v_tok_s:.4g} tok/s; parity o {e_vo:.2e} S_T {e_vs:.2e}")
+        f"{v_kern_ms:.3f} ms, {v_tok_s:.4g} tok/s")
     del vx, vflat
 
     # ------- few long chains: the split prefill (kda_chunk_fwd_split) against the single pass -------
     split_res = []
-    e_so = e_ss = 0.0
     for sB, sT, sH, sseed in ((1, 4096, 8, 5), (1, 65536, 2, 6)):
         sx = ki.make_prefill(sB, sT, sH, dk, dv, w.qkv_dtype, w.alpha_mu, w.s0_std, seed=sseed, device=dev)
         n_parts, ws_bytes = kda.kda_chunk_fwd_split_plan(w.qkv_dtype, sB, sT, sH, dk, dv, chunk=C)
@@ -298,25 +340,20 @@ def main():
         spl()
         torch.cuda.synchronize()
         sheads = [0, sB * sH - 1]
-        hs = {n: sx[n].cpu() for n in ("q", "k", "v", "alpha", "beta", "S0")}
-        rso, rss = oracle.forward(hs["q"], hs["k"], hs["v"], hs["alpha"], hs["beta"], hs["S0"], heads=sheads,
-                                  threads=threads)
-        got_o = s_o.permute(0, 2, 1, 3).reshape(sB * sH, sT, dv)[sheads].cpu().double().numpy()
-        got_s = s_S.reshape(sB * sH, dk, dv)[sheads].cpu().double().numpy()
-        eo_, es_ = rel_err_heads(got_o, rso), rel_err_heads(got_s, rss)
-        e_so, e_ss = max(e_so, eo_), max(e_ss, es_)
-        del hs, rso, rss
+        name = f"split B={sB} T={sT} H={sH}"
+        checks.add(name, {n: t.cpu() for n, t in sx.items()}, heads_of(s_o, sheads), states_of(s_S, sheads),
+                   heads=sheads)
         for _ in range(args.warmup):
             one()
             spl()
         _, one_ms, _ = timed_launches(one, args.steps, torch)
         _, spl_ms, _ = timed_launches(spl, args.steps, torch)
         log(f"split prefill B={sB} T={sT} H={sH}: {n_parts} parts, {spl_ms:.3f} ms vs single pass "
-            f"{one_ms:.3f} ms ({one_ms / spl_ms:.2f}x); parity o {eo_:.2e} S_T {es_:.2e}")
+            f"{one_ms:.3f} ms ({one_ms / spl_ms:.2f}x)")
         split_res.append({"workload": f"prefill B={sB} T={sT} H={sH} d={dk} (kda_chunk_fwd_split, library's "
                                       f"part count)", "parts": n_parts, "workspace_bytes": ws_bytes,
                           "ms": spl_ms, "single_pass_ms": one_ms, "speedup": one_ms / spl_ms,
-                          "tokens_per_s": sB * sT / (spl_ms / 1e3), "parity_o": eo_, "parity_S_T": es_})
+                          "tokens_per_s": sB * sT / (spl_ms / 1e3), "check": name})
         del sx, s_ws, s_o, s_S
 
     # ---------------- decode: B=256, H=32, d=128, 100 in-place steps ----------------
@@ -328,7 +365,7 @@ def main():
     toks = [ki.make_decode_token(DB, DH, dk, dv, wd.qkv_dtype, wd.alpha_mu, seed=0, step=s, device=dev)
             for s in range(nsteps)]
     od = torch.empty(nsteps, DB, DH, dv, device=dev, dtype=torch.float32)
-    # decode parity on sampled states: the 100 tokens of one state are a sequence
+    # sampled states: the 100 tokens of one state are a sequence of 100 tokens
     dheads = sorted(set(int(v) for v in np.linspace(0, DB * DH - 1, 8)))
     S_init = S.reshape(DB * DH, dk, dv)[dheads].cpu()
     for s, tk in enumerate(toks):
@@ -340,13 +377,9 @@ def main():
 
     seq = {n: gather(n) for n in ("q", "k", "v", "alpha")}
     seq["beta"] = torch.stack([tk["beta"].reshape(DB * DH)[dheads] for tk in toks], 0)[None].cpu()
-    rdo, rds = oracle.forward(seq["q"], seq["k"], seq["v"], seq["alpha"], seq["beta"],
-                              S_init[None], threads=threads)
-    gdo = od.reshape(nsteps, DB * DH, dv)[:, dheads].permute(1, 0, 2).cpu().double().numpy()
-    gds = S.reshape(DB * DH, dk, dv)[dheads].cpu().double().numpy()
-    e_do = max(rel_err_heads(gdo[:, s].reshape(1, -1), rdo[:, s].reshape(1, -1)) for s in range(nsteps))
-    e_ds = rel_err_heads(gds, rds)
-    log(f"decode parity: o {e_do:.3e}  S {e_ds:.3e}")
+    seq["S0"] = S_init[None]
+    checks.add("decode", seq, od.reshape(nsteps, DB * DH, dv)[:, dheads].permute(1, 0, 2).cpu().numpy(),
+               states_of(S, dheads), per_step=True)
 
     def dstep_all():
         for s, tk in enumerate(toks):
@@ -360,8 +393,8 @@ def main():
     ev1.record()
     torch.cuda.synchronize()
     d_total_ms = ev0.elapsed_time(ev1)
-    # per-launch durations on the same stream
-    _, d_kern_ms, _ = timed_launches(
+    # per-launch duration on the same stream: 20 launches back to back
+    d_kern_ms = back_to_back_ms(
         lambda: kda.kda_decode_step(toks[0]["q"], toks[0]["k"], toks[0]["v"], toks[0]["alpha"],
                                     toks[0]["beta"], S, o=od[0]), 20, torch)
     d_step_ms = d_total_ms / nsteps
@@ -383,22 +416,20 @@ def main():
     kda.kda_decode_verify(dr["q"], dr["k"], dr["v"], dr["alpha"], dr["beta"], S, o=o_sp, u=u_sp)
     kda.kda_decode_commit(dr["k"], dr["alpha"], u_sp, acc, S)
     torch.cuda.synchronize()
-    hs = {n: v[sp_seq:sp_seq + 1].cpu() for n, v in dr.items() if n != "S0"}
-    rso, rss = oracle.forward(hs["q"], hs["k"], hs["v"], hs["alpha"], hs["beta"], S_sp0[None].cpu())
-    e_spo = rel_err_heads(o_sp[sp_seq:sp_seq + 1].permute(0, 2, 1, 3).reshape(DH, SK, dv).cpu().double().numpy(),
-                          rso)
-    e_sps = rel_err_heads(S[sp_seq].cpu().double().numpy(), rss)
-    del hs, rso, rss
-    _, v_kern_ms, _ = timed_launches(
+    sphin = {n: t[sp_seq:sp_seq + 1].cpu() for n, t in dr.items() if n != "S0"}
+    sphin["S0"] = S_sp0[None].cpu()
+    checks.add("spec decode", sphin, heads_of(o_sp[sp_seq:sp_seq + 1], list(range(DH))),
+               states_of(S[sp_seq:sp_seq + 1], list(range(DH))))
+    v_kern_ms = back_to_back_ms(
         lambda: kda.kda_decode_verify(dr["q"], dr["k"], dr["v"], dr["alpha"], dr["beta"], S, o=o_sp, u=u_sp),
         20, torch)
-    _, c_kern_ms, _ = timed_launches(lambda: kda.kda_decode_commit(dr["k"], dr["alpha"], u_sp, acc, S), 20, torch)
+    c_kern_ms = back_to_back_ms(lambda: kda.kda_decode_commit(dr["k"], dr["alpha"], u_sp, acc, S), 20, torch)
     n_commit = int((acc > 0).sum().item())
     v_bytes = DB * DH * dk * dv * 4 + DB * SK * DH * (2 * (2 * dk + dv) + 4 * dk + 4 + 4 * dv) + DB * DH * SK * dv * 4
     c_bytes = 2 * n_commit * DH * dk * dv * 4
     log(f"spec decode ({SK} drafts): verify {v_kern_ms * 1e3:.1f} us ({v_bytes / v_kern_ms / 1e6:.0f} GB/s), "
         f"commit {c_kern_ms * 1e3:.1f} us ({c_bytes / c_kern_ms / 1e6:.0f} GB/s); {SK} decode steps "
-        f"{SK * d_kern_ms * 1e3:.1f} us; parity o {e_spo:.2e} S {e_sps:.2e}")
+        f"{SK * d_kern_ms * 1e3:.1f} us")
 
     if args.copy_probe:
         a = torch.empty(1 << 28, device=dev, dtype=torch.float32)
@@ -406,7 +437,14 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
         log("copy probe: 1 GiB read + 1 GiB written")
+        del a, b
 
+    # ---------------- the CPU baseline: the oracle on every sample above ----------------
+    import oracle
+    threads = oracle.default_threads()
+    log(f"CPU baseline: the oracle on the sampled heads ({threads} threads); prefill heads {heads}")
+    errs, cpu_s = cpu_baseline_leg(checks, threads, log)
+    e_o, e_s = errs["prefill"]
     cpu = None
     if not args.no_cpu_baseline:
         rate = len(heads) * T / cpu_s  # token-heads per second on this host
@@ -414,9 +452,12 @@ def main():
                "sample": f"{len(heads)} of {B * H} heads of the same workload, full T={T} "
                          f"({len(heads) * T} token-heads, {cpu_s:.1f} s wall); tokens/s = "
                          f"token-heads/s / H", "cpu": _cpu_model()}
-
-    parity_ok = (max(e_o, e_s, e_do, e_ds, e_snap, e_spo, e_sps, e_vo, e_vs, e_go, e_gs, e_fo, e_fs, e_so, e_ss) <= TOL_REL
-                 and snap_last_is_state)
+    gated_err = [errs[f"gated head {hid}"] for hid in (0, B * H // 2 + 5)]
+    e_go, e_gs = max(e[0] for e in gated_err), max(e[1] for e in gated_err)
+    for r in split_res:
+        r["parity_o"], r["parity_S_T"] = errs[r.pop("check")]
+    all_errs = [v for pair in errs.values() for v in pair if v is not None]
+    parity_ok = max(all_errs) <= TOL_REL and snap_last_is_state
     out = {
         "metric": METRIC,
         "value": tokens_per_s,
@@ -452,7 +493,7 @@ def main():
                                   f"tokens ({len(snap_pos)} per sequence, kda_chunk_fwd_snapshots)",
                       "ms_per_step": s_wall_ms / args.steps, "kernel_ms": s_kern_ms,
                       "overhead_vs_prefill": s_kern_ms / kern_ms - 1, "snapshot_bytes": snap_bytes,
-                      "parity_first_snapshot": e_snap, "last_snapshot_equals_S_T": snap_last_is_state},
+                      "parity_first_snapshot": errs["snapshot"][1], "last_snapshot_equals_S_T": snap_last_is_state},
         "gated": {"workload": "the prefill above with the gate fused in (kda_chunk_fwd_gated: bf16 z and "
                               "per-head A in place of fp32 alpha)",
                   "ms_per_step": g_wall_ms / args.steps, "kernel_ms": g_kern_ms,
@@ -461,21 +502,23 @@ def main():
                   "traffic": measured_traffic("kda_prefill_gated"),
                   "gate_recipe": "z ~ N(-4.5, 0.4) bf16, A ~ N(0, 0.1) per head",
                   "fast_forgetting": {"gate_recipe": "z ~ N(-3, 1), A ~ N(0, 0.3)", "kernel_ms": f_kern_ms,
-                                      "vs_gated": f_kern_ms / g_kern_ms, "parity_o": e_fo, "parity_S_T": e_fs}},
+                                      "vs_gated": f_kern_ms / g_kern_ms, "parity_o": errs["fast-forgetting"][0],
+                                      "parity_S_T": errs["fast-forgetting"][1]}},
         "split": split_res,
         "varlen": {"workload": f"packed batch of {len(v_lens)} sequences, {v_total} tokens "
                                f"(lengths {min(v_lens)}..{max(v_lens)}), H={H} d={dk}, kda_chunk_fwd_varlen",
                    "kernel_ms": v_kern_ms, "tokens_per_s": v_tok_s, "lengths": v_lens,
-                   "parity_o": e_vo, "parity_S_T": e_vs},
+                   "parity_o": errs["varlen"][0], "parity_S_T": errs["varlen"][1]},
         "spec_decode": {"workload": f"decode B={DB} H={DH} d={dk} with {SK} draft tokens per sequence: "
                                     f"kda_decode_verify, then kda_decode_commit with 0..{SK} accepted "
                                     f"({n_commit} of {DB} sequences commit)",
                         "verify_us": v_kern_ms * 1e3, "commit_us": c_kern_ms * 1e3,
                         "verify_gbps": v_bytes / v_kern_ms / 1e6, "commit_gbps": c_bytes / c_kern_ms / 1e6,
                         "sequential_decode_us": SK * d_kern_ms * 1e3,
-                        "parity_o": e_spo, "parity_S": e_sps},
+                        "parity_o": errs["spec decode"][0], "parity_S": errs["spec decode"][1]},
         "parity": {"pass": parity_ok, "tol_rel_rms": TOL_REL, "prefill_o": e_o, "prefill_S_T": e_s,
-                   "prefill_heads": heads, "decode_o": e_do, "decode_S": e_ds, "decode_states": dheads},
+                   "prefill_heads": heads, "decode_o": errs["decode"][0], "decode_S": errs["decode"][1],
+                   "decode_states": dheads, "checks": {k: list(v) for k, v in errs.items()}},
         "cpu_baseline": cpu,
         "device": props.name,
         "source_hash": source_hash(),

@@ -145,10 +145,10 @@ __global__ __launch_bounds__(256) void kda_commit_kernel(CommitParams p) {
   if (j == 0) return;  // nothing accepted: the state stays as it is
 
   float* S = p.S + (size_t)bh * DK * DV;
+  // plain loads with the non-temporal stores below: faster than non-temporal both ways
   f32x4 s[C::RPT];
 #pragma unroll
-  for (int r = 0; r < C::RPT; ++r)
-    s[r] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + (size_t)(rg + C::RG * r) * DV + 4 * cg));
+  for (int r = 0; r < C::RPT; ++r) s[r] = *reinterpret_cast<const f32x4*>(S + (size_t)(rg + C::RG * r) * DV + 4 * cg);
   for (int i = tid; i < DK; i += C::NT) {
     float run = 1.0f;  // product of the decays after token t
     for (int t = j - 1; t >= 0; --t) {
