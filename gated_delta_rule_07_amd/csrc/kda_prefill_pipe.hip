@@ -921,8 +921,17 @@ __global__ __launch_bounds__(C::NT, 1) void kda_prefill_pipe_kernel(PrefillParam
   cx.nchunks = (cx.T + CS - 1) / CS;
   // T's upper-right 16x16 block is read as zeros and never written
   for (int i = tid; i < 2 * CS * C::LDC; i += C::NT) (&sm.t[0][0])[i] = (h16)0.0f;
-  if (wave >= 4) run_role<C, SCAN, G>(sm, cx, snap, lane, wave - 4);
-  else if (wave == 0) run_role<C, STATE, G>(sm, cx, snap, lane, 0);
+  // Waves w and w + 4 share a SIMD.  The scan waves and the state wave carry the
+  // step's critical path, while the L/T, P and output waves wait at the barrier
+  // for a good part of each step, so the former issue first (measured: a 5%
+  // shorter step; raising the scan waves alone starved the state wave).
+  if (wave >= 4) {
+    __builtin_amdgcn_s_setprio(3);
+    run_role<C, SCAN, G>(sm, cx, snap, lane, wave - 4);
+  } else if (wave == 0) {
+    __builtin_amdgcn_s_setprio(3);
+    run_role<C, STATE, G>(sm, cx, snap, lane, 0);
+  }
   else if (wave == 1) run_role<C, SOLVE, G>(sm, cx, snap, lane, 0);
   else if (wave == 2) run_role<C, PMAT, G>(sm, cx, snap, lane, 0);
   else run_role<C, OUT, G>(sm, cx, snap, lane, 0);
