@@ -81,6 +81,20 @@ def test_split_without_initial_state_and_bf16_output(gpu):
     assert torch.equal(o16, o32.to(torch.bfloat16)) and torch.equal(s16, s32)
 
 
+def test_split_edge_lengths(gpu):
+    """A last part of one token (T = 33, 2 parts) and an empty sequence (T = 0:
+    S_T = S0, the single pass)."""
+    kda = _kda()
+    inp = ki.make_prefill(1, 33, 2, 128, 128, torch.bfloat16, 3.0, 0.1, seed=16, device=gpu)
+    assert _check(inp, 2, "T=33, 2 parts") == 2
+    x0 = ki.make_prefill(1, 1, 2, 128, 128, torch.bfloat16, 3.0, 0.1, seed=17, device=gpu)
+    empty = {n: t[:, :0].contiguous() if n != "S0" else t for n, t in x0.items()}
+    o, st = kda.kda_chunk_fwd_split(empty["q"], empty["k"], empty["v"], empty["alpha"], empty["beta"],
+                                    empty["S0"], parts=4)
+    torch.cuda.synchronize()
+    assert o.shape[1] == 0 and torch.equal(st, x0["S0"])
+
+
 def test_split_in_place_state(gpu):
     """S0 == S_T: the last part writes the state while earlier parts still run;
     only the combine reads S0, so the result is the single pass's."""
