@@ -246,7 +246,8 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, kda_dtype
   }
 
   kda::PrefillParams p{q, k, v, alpha, beta, S0, o, S_T, B, T, H, d_k, d_v, o_dtype == KDA_F32 ? 1 : 0,
-                       n_snap > 0 ? snaps : nullptr, n_snap, cu, T > 0 ? z : nullptr, A};
+                       n_snap > 0 ? snaps : nullptr, n_snap, cu, T > 0 ? z : nullptr, A,
+                       /*split*/ 0, /*nparts*/ 0, /*part_len*/ 0, nullptr, nullptr};
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (sh.parts > 1) {

@@ -469,7 +469,6 @@ template <class C>
 __device__ void phase_state(Smem<C>& sm, f32x4 (&S)[C::NKT], int w, int lane, const Ctx& cx,
                             int t0, int lo, int hi) {
   using SOP = typename C::SOP;
-  using IO = typename C::IO;
   const int g = lane / 16, m = lane % 16;
   const f32x4 zero4 = (f32x4)0.0f;
 

@@ -801,8 +801,9 @@ __device__ void run_role(Smem4<C>& sm, const Ctx4& cx, const SnapList& snap, int
   const Item none = {-1, 0, 0, 0, 0};
   Item sI = none, bI = none, stI = none, opI = none;
   if (cx.nchunks > 0) sI = Item{0, 0, 0, chunk_end(0, cx.T), CS};
-  int par = 0, kstep = 0;
-  int ns = 0;  // state role: next recorded position
+  int par = 0;
+  [[maybe_unused]] int kstep = 0;  // step count, for step timestamps in instrumented builds
+  int ns = 0;                      // state role: next recorded position
   while (sI.seq >= 0 || bI.seq >= 0 || stI.seq >= 0 || opI.seq >= 0) {
     KDA_STEP_MARK(0, kstep);
     if constexpr (ROLE == SCAN) {
