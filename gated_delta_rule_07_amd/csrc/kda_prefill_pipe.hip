@@ -115,6 +115,10 @@ struct Smem4 {
   alignas(16) int flags[2][C::NSW];        // scan: regroup votes per wave
 };
 
+// s_waitcnt immediate for "vector memory counter at 0" (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+constexpr int kVmcnt0 = 0x0F70;
+
 __device__ __forceinline__ void block_sync_lds() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
@@ -199,79 +203,115 @@ struct Ctx4 {
 };
 
 // ---- scan waves --------------------------------------------------------------------
+constexpr int VW0 = 2;  // scan waves VW0.. load the V slab (CS x J bf16: 64 lanes x 16 B each)
+constexpr int BW = 1;   // the scan wave that loads beta
+static_assert(CS * J * 2 == (4 - VW0) * 64 * 16, "V slab split");
+// Each load's result is kept as the vector it arrives in: the step loop then
+// carries whole register tuples from one step's prefetch to the next step's
+// scan.  (Kept as separate words, the tuples were reassembled by register
+// copies right after the prefetch, which waited for the loads to land.)
 template <class C>
 struct Raw4 {
-  float a[C::TPL][C::CPL];         // alpha of this lane's channels, per token
-  uint32_t k[C::TPL][C::CPL / 2];  // bf16 pairs
-  uint32_t q[C::TPL][C::CPL / 2];
-  uint32_t z[C::TPL][C::CPL / 2];  // fused gate: bf16 pairs of z in place of alpha
-  u32x2 v;                         // 4 bf16 of the V slab
+  typedef float AV __attribute__((ext_vector_type(C::CPL)));         // CPL fp32
+  typedef uint32_t WV __attribute__((ext_vector_type(C::CPL / 2)));  // CPL bf16
+  AV a[C::TPL];  // alpha of this lane's channels, per token
+  WV k[C::TPL];
+  WV q[C::TPL];
+  WV z[C::TPL];  // fused gate: z in place of alpha
+  u32x4 v;       // 8 bf16 of the V slab (scan waves VW0.. only)
   float beta;
 };
+
+// Where a scan lane's inputs lie: the byte address of chunk 0 of this
+// (sequence, head) in each tensor, the bytes per chunk and per token row, and
+// the lane's own offsets.  Formed once per wave, so a chunk's addresses cost one
+// 64-bit product (chunk index x bytes per chunk) per tensor family rather than
+// the whole (token x heads + head) x width arithmetic per tensor, which a scan
+// wave otherwise issues as ~60 scalar instructions every step (a wave issues
+// at most one instruction per turn of its SIMD, scalar or vector).
+struct ScanSrc {
+  const char* a;  // alpha (fp32) or the gate's z (bf16)
+  const char* k;
+  const char* q;
+  const char* v;  // this slab's first column (or any address when V is off)
+  const char* b;  // beta
+  int kc;         // bytes per chunk of k and q (alpha: kc << ash)
+  int ash;        // 1: alpha is fp32, 0: z is bf16
+  int vc, bc;     // bytes per chunk of v and beta
+  int kr, vr, br; // bytes per token row of k, v (0: V off) and beta
+  int ts2;        // bytes between a lane's consecutive tokens in k (alpha: ts2 << ash)
+  int vo_k, vo_v, vo_b;  // this lane's byte offsets in k, v and beta
+};
+
+template <class C, bool G>
+__device__ ScanSrc scan_src(const Ctx4& cx, int sw, int lane) {
+  const PrefillParams& p = cx.p;
+  const int cp = lane % C::PPW, tq = lane / C::PPW;
+  const size_t row0 = (size_t)cx.tok0 * p.H + cx.h;
+  const int ts = p.H * C::DK;  // elements between tokens
+  ScanSrc r;
+  r.ash = G ? 0 : 1;
+  r.a = G ? reinterpret_cast<const char*>(static_cast<const __bf16*>(p.z) + row0 * C::DK)
+          : reinterpret_cast<const char*>(p.alpha + row0 * C::DK);
+  r.k = reinterpret_cast<const char*>(static_cast<const __bf16*>(p.k) + row0 * C::DK);
+  r.q = reinterpret_cast<const char*>(static_cast<const __bf16*>(p.q) + row0 * C::DK);
+  r.v = reinterpret_cast<const char*>(static_cast<const __bf16*>(p.v) + row0 * p.dv + (cx.v_on ? cx.col0 : 0));
+  r.b = reinterpret_cast<const char*>(p.beta + row0);
+  r.kr = ts * 2;
+  r.kc = CS * r.kr;
+  r.vr = cx.v_on ? p.H * p.dv * 2 : 0;  // a zero-length range reads as zeros: the transition columns have V = 0
+  r.vc = CS * p.H * p.dv * 2;
+  r.br = p.H * 4;
+  r.bc = CS * r.br;
+  r.ts2 = ts * 2;
+  r.vo_k = 2 * (tq * C::TPL * ts + C::CPW * sw + C::CPL * cp);
+  const int vt = 64 * (sw - VW0) + lane;  // V row vt/4, columns 8(vt%4)..+7 (scan waves VW0.. only)
+  r.vo_v = 2 * ((vt / 4) * p.H * p.dv + 8 * (vt % 4));
+  r.vo_b = 4 * (lane % CS) * p.H;  // beta of token l is kept by lane l
+  return r;
+}
 
 // Loads chunk c's inputs for scan lane (sw, lane): channels CPL*cp .. of the
 // wave's slice, tokens tq*TPL ..  Rows past the sequence end read as zeros
 // (buffer range check).  One load per token and tensor: the load count, not
-// the byte count, sets what the scan waits for here.
+// the byte count, sets what the scan waits for here.  The V slab and beta are
+// loaded by the last scan waves, so the first one, which shares its SIMD with
+// the state wave, does none of that work.
 template <class C, bool G>
-__device__ void load_raw4(Raw4<C>& raw, const Ctx4& cx, int c, int sw, int lane) {
-  const PrefillParams& p = cx.p;
-  const int cp = opaque(lane % C::PPW), tq = opaque(lane / C::PPW);
-  const int t0 = c * CS;
-  const int rows = min(CS, cx.T - t0);
-  const size_t row0 = (size_t)(cx.tok0 + t0) * p.H + cx.h;
-  const int ts = p.H * C::DK;  // elements between tokens
-  const __amdgpu_buffer_rsrc_t ra = G ? make_rsrc(static_cast<const __bf16*>(p.z) + row0 * C::DK, rows * ts * 2)
-                                      : make_rsrc(p.alpha + row0 * C::DK, rows * ts * 4);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(static_cast<const __bf16*>(p.k) + row0 * C::DK, rows * ts * 2);
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(static_cast<const __bf16*>(p.q) + row0 * C::DK, rows * ts * 2);
-  const int e0 = tq * C::TPL * ts + C::CPW * sw + C::CPL * cp;
+__device__ void load_raw4(Raw4<C>& raw, const Ctx4& cx, const ScanSrc& src, int c, int sw) {
+  const int rows = min(CS, cx.T - c * CS);
+  const size_t ok = (size_t)(unsigned)c * (unsigned)src.kc;  // chunk offset in k and q
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(src.a + (ok << src.ash), (rows * src.kr) << src.ash);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(src.k + ok, rows * src.kr);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(src.q + ok, rows * src.kr);
+  const int vk = src.vo_k, va = src.vo_k << src.ash;
+  typedef typename Raw4<C>::AV AV;
+  typedef typename Raw4<C>::WV WV;
 #pragma unroll
   for (int i = 0; i < C::TPL; ++i) {
     // Reinterpret each loaded vector as a whole: taking single elements of the
     // integer vector a buffer load returns and reinterpreting them as float is
     // miscompiled by this toolchain (both read one narrowed dword).
-    if constexpr (G) {  // z as bf16, like k
-      if constexpr (C::CPL == 4) {
-        const u32x2 zw = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(ra, 2 * e0, 2 * i * ts, 0));
-        raw.z[i][0] = zw.x;
-        raw.z[i][1] = zw.y;
-      } else {
-        raw.z[i][0] = __builtin_amdgcn_raw_buffer_load_b32(ra, 2 * e0, 2 * i * ts, 0);
-      }
-    }
+    const int sk = i * src.ts2, sa = sk << src.ash;
     if constexpr (C::CPL == 4) {
-      if constexpr (!G) {
-        const f32x4 w = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, 4 * e0, 4 * i * ts, 0));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) raw.a[i][e] = w[e];
-      }
-      const u32x2 kw = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rk, 2 * e0, 2 * i * ts, 0));
-      const u32x2 qw = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rq, 2 * e0, 2 * i * ts, 0));
-      raw.k[i][0] = kw.x;
-      raw.k[i][1] = kw.y;
-      raw.q[i][0] = qw.x;
-      raw.q[i][1] = qw.y;
+      if constexpr (G) raw.z[i] = __builtin_bit_cast(WV, __builtin_amdgcn_raw_buffer_load_b64(ra, va, sa, 0));
+      else raw.a[i] = __builtin_bit_cast(AV, __builtin_amdgcn_raw_buffer_load_b128(ra, va, sa, 0));
+      raw.k[i] = __builtin_bit_cast(WV, __builtin_amdgcn_raw_buffer_load_b64(rk, vk, sk, 0));
+      raw.q[i] = __builtin_bit_cast(WV, __builtin_amdgcn_raw_buffer_load_b64(rq, vk, sk, 0));
     } else {
-      if constexpr (!G) {
-        const f32x2 w = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(ra, 4 * e0, 4 * i * ts, 0));
-        raw.a[i][0] = w.x;
-        raw.a[i][1] = w.y;
-      }
-      raw.k[i][0] = __builtin_amdgcn_raw_buffer_load_b32(rk, 2 * e0, 2 * i * ts, 0);
-      raw.q[i][0] = __builtin_amdgcn_raw_buffer_load_b32(rq, 2 * e0, 2 * i * ts, 0);
+      if constexpr (G) raw.z[i] = __builtin_bit_cast(WV, __builtin_amdgcn_raw_buffer_load_b32(ra, va, sa, 0));
+      else raw.a[i] = __builtin_bit_cast(AV, __builtin_amdgcn_raw_buffer_load_b64(ra, va, sa, 0));
+      raw.k[i] = __builtin_bit_cast(WV, __builtin_amdgcn_raw_buffer_load_b32(rk, vk, sk, 0));
+      raw.q[i] = __builtin_bit_cast(WV, __builtin_amdgcn_raw_buffer_load_b32(rq, vk, sk, 0));
     }
   }
-  const int st = opaque(64 * sw + lane);  // scan lanes 0-255: V row st/8, columns 4(st%8)..+3
-  const int vs = p.H * p.dv;
-  // a zero-length range reads as zeros: the transition columns have V = 0
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(static_cast<const __bf16*>(p.v) + row0 * p.dv + (cx.v_on ? cx.col0 : 0),
-                                              cx.v_on ? rows * vs * 2 : 0);
-  raw.v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, 2 * (((st / 8) % CS) * vs + 4 * (st % 8)), 0, 0));
-  raw.beta = 0.0f;
-  if (sw == 0) {  // beta is kept by the first CS scan lanes only
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.beta + row0, rows * p.H * 4);
-    raw.beta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, 4 * (st % CS) * p.H, 0, 0));
+  if (sw >= VW0) {
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(src.v + (size_t)(unsigned)c * (unsigned)src.vc, rows * src.vr);
+    raw.v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, src.vo_v, 0, 0));
+  }
+  if (sw == BW) {
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(src.b + (size_t)(unsigned)c * (unsigned)src.bc, rows * src.br);
+    raw.beta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, src.vo_b, 0, 0));
   }
 }
 
@@ -378,11 +418,13 @@ __device__ void scan4_body(Smem4<C>& sm, const Raw4<C>& raw, const Item& it, flo
 #pragma unroll
     for (int e = 0; e < L; ++e) {
       kmax = fmaxf(kmax, fabsf(kf[e]));
-      kg[e] = (h16)(kf[e] * pre[i][e]);
-      qg[e] = (h16)(qf[e] * pre[i][e]);
+      // fused multiply rounded once to fp16 (a mixed-precision fma): one
+      // instruction per element instead of a multiply and half a conversion
+      kg[e] = (h16)__builtin_fmaf(kf[e], pre[i][e], 0.0f);
+      qg[e] = (h16)__builtin_fmaf(qf[e], pre[i][e], 0.0f);
       const float kh = kf[e] * ns[i][e];  // -KH
       khv[e][i] = (h16)kh;
-      kcv[e] = (h16)(kh * -rg[e]);        // KC = KH / gamma
+      kcv[e] = (h16)__builtin_fmaf(kh, -rg[e], 0.0f);  // KC = KH / gamma
     }
     const int r = (tb + i) * C::LDK + col;  // CPL adjacent channels keep adjacent positions
     if constexpr (L == 4) {
@@ -402,16 +444,16 @@ __device__ void scan4_body(Smem4<C>& sm, const Raw4<C>& raw, const Item& it, flo
     if constexpr (L == 4) *reinterpret_cast<f32x4*>(&sl.gam[ch]) = f32x4{gam[0], gam[1], gam[2], gam[3]};
     else *reinterpret_cast<f32x2*>(&sl.gam[ch]) = f32x2{gam[0], gam[1]};
   }
-  const int st = 64 * sw + lane;
-  if (st < 8 * CS) {
-    // V^T: this lane holds row st/8, columns 4(st%8)..+3
-    const int vr = st / 8, vc = 4 * (st % 8);
-    const uint32_t w[2] = {raw.v.x, raw.v.y};
+  if (sw >= VW0) {
+    // V^T: this lane holds row vt/4, columns 8(vt%4)..+7
+    const int vt = 64 * (sw - VW0) + lane;
+    const int vr = vt / 4, vc = 8 * (vt % 4);
+    const uint32_t w[4] = {raw.v.x, raw.v.y, raw.v.z, raw.v.w};
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
+    for (int e = 0; e < 8; ++e)
       sl.v[(vc + e) * C::LDV + vr] = __builtin_bit_cast(__bf16, (uint16_t)(w[e / 2] >> (16 * (e % 2))));
   }
-  if (st < CS) sl.beta[st] = (FULL || (st >= lo && st < hi)) ? raw.beta : 0.0f;
+  if (sw == BW && lane < CS) sl.beta[lane] = (FULL || (lane >= lo && lane < hi)) ? raw.beta : 0.0f;
   // Regroup vote: the first token (chunk position) at which some channel's
   // prefix decay falls below e^{-10} or KC = k/pre would leave fp16 range; CS
   // when there is none.  A bound over the whole item (smallest gamma, largest
@@ -690,13 +732,18 @@ __device__ void state_prepare(Smem4<C>& sm, StateRegs<C>& R, const Item& it, int
 }
 
 // ---- output wave -------------------------------------------------------------------------
+// The output tile is carried transposed (both products take their operands in
+// swapped order): lane (n, h) holds token n, columns 8g + 4h .. +3 for g = 0..3,
+// so a lane writes four runs of 4 adjacent columns.  Four stores per step
+// instead of one per element: every vector memory instruction costs the
+// workgroup's shared texture addresser about as much whatever its width.
 template <class C>
-__device__ void out_pu_store(Smem4<C>& sm, f32x16& O, float usc, const Item& it, const Ctx4& cx, int lane) {
+__device__ void out_pu_store(Smem4<C>& sm, f32x16& O, const f32x16& usc, const Item& it, const Ctx4& cx, int lane) {
   const h16* pp = sm.p[it.seq % 3];
   const h16* uf = sm.uf[it.seq % 2];
   const int h = opaque(lane / 32), n = opaque(lane % 32);
-  O = mma32(ld8(&pp[n * C::LDC + 8 * h]), ld8(&uf[lane * 8]), O);
-  O = mma32(ld8(&pp[n * C::LDC + 16 + 8 * h]), ld8(&uf[(64 + lane) * 8]), O);
+  O = mma32(ld8(&uf[lane * 8]), ld8(&pp[n * C::LDC + 8 * h]), O);
+  O = mma32(ld8(&uf[(64 + lane) * 8]), ld8(&pp[n * C::LDC + 16 + 8 * h]), O);
   const PrefillParams& p = cx.p;
   const int t0 = it.c * CS;
   const int rows = chunk_end(it.c, cx.T);
@@ -704,37 +751,40 @@ __device__ void out_pu_store(Smem4<C>& sm, f32x16& O, float usc, const Item& it,
   const int rs = p.H * p.dv * esz;
   char* ob = static_cast<char*>(p.o) + (((size_t)(cx.tok0 + t0) * p.H + cx.h) * p.dv + (cx.o_on ? cx.col0 : 0)) * esz;
   const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(ob, cx.o_on ? rows * rs : 0);  // zero-length: stores dropped
-  const int vbase = 4 * h * rs + n * esz;
+  // tokens outside the item are pushed past the range, so their stores are dropped
+  const int voff = n * rs + 4 * h * esz + ((unsigned)(n - it.lo) < (unsigned)(it.hi - it.lo) ? 0 : 0x40000000);
+  const f32x16 y = O * usc;
   if (p.o_f32) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int tr = 8 * (i / 4) + (i % 4);
-      const int t = tr + 4 * h;
-      const int voff = vbase + ((unsigned)(t - it.lo) < (unsigned)(it.hi - it.lo) ? 0 : 0x40000000);
-      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, O[i] * usc), rsrc, voff, tr * rs, 0);
-    }
+    for (int g = 0; g < 4; ++g)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{y[4 * g], y[4 * g + 1], y[4 * g + 2], y[4 * g + 3]}),
+                                             rsrc, voff, 8 * g * 4, 0);
   } else {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int tr = 8 * (i / 4) + (i % 4);
-      const int t = tr + 4 * h;
-      const int voff = vbase + ((unsigned)(t - it.lo) < (unsigned)(it.hi - it.lo) ? 0 : 0x40000000);
-      __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (__bf16)(O[i] * usc)), rsrc, voff,
-                                            tr * rs, 0);
+    for (int g = 0; g < 4; ++g) {
+      // reinterpret the whole vector (single elements are miscompiled)
+      const bf16x4 b = {(__bf16)y[4 * g], (__bf16)y[4 * g + 1], (__bf16)y[4 * g + 2], (__bf16)y[4 * g + 3]};
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, b), rsrc, voff, 8 * g * 2, 0);
     }
   }
 }
 
+// Q_G S for the output wave (transposed), and the scale of each column it holds.
 template <class C>
-__device__ void out_qs(Smem4<C>& sm, f32x16& O, float& usc, const Item& it, int lane) {
+__device__ void out_qs(Smem4<C>& sm, f32x16& O, f32x16& usc, const Item& it, int lane) {
   const ScanSlot<C>& sl = sm.ss[it.seq % 3];
   const h16* sf = sm.sf[it.seq % 2];
   const int h = opaque(lane / 32), n = opaque(lane % 32);
   O = (f32x16)0.0f;
 #pragma unroll
   for (int s = 0; s < C::NKS; ++s)
-    O = mma32(ld8(&sl.qg[n * C::LDK + 16 * s + 8 * h]), ld8(&sf[(s * 64 + lane) * 8]), O);
-  usc = sm.sexp[it.seq % 2][n];
+    O = mma32(ld8(&sf[(s * 64 + lane) * 8]), ld8(&sl.qg[n * C::LDK + 16 * s + 8 * h]), O);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const f32x4 w = *reinterpret_cast<const f32x4*>(&sm.sexp[it.seq % 2][8 * g + 4 * h]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) usc[4 * g + e] = w[e];
+  }
 }
 
 // ---- kernel ---------------------------------------------------------------------------------
@@ -772,7 +822,7 @@ __device__ void run_role(Smem4<C>& sm, const Ctx4& cx, const SnapList& snap, int
   Raw4<C> raw;
   int rc = -1;  // chunk held in raw
   f32x16 O = (f32x16)0.0f;
-  float usc = 1.0f;
+  f32x16 usc = (f32x16)1.0f;
   if constexpr (ROLE == STATE) {
     const int h = lane / 32, n = lane % 32;
 #pragma unroll
@@ -788,11 +838,17 @@ __device__ void run_role(Smem4<C>& sm, const Ctx4& cx, const SnapList& snap, int
 #pragma unroll
         for (int i = 0; i < 16; ++i) R.S[ct][i] = cx.s0[(size_t)(32 * ct + 8 * (i / 4) + 4 * h + (i % 4)) * cx.s0_ld + n];
     }
+    // Wait for the state loads once, here: otherwise the step loop carries a
+    // wait before each write to a state register (dozens of no-op waits per
+    // step on the state wave, which is on the step's critical path).
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
     R.sc = 1.0f;
   }
+  ScanSrc src{};
   if constexpr (ROLE == SCAN) {
+    src = scan_src<C, G>(cx, sw, lane);
     if (cx.nchunks > 0) {
-      load_raw4<C, G>(raw, cx, 0, sw, lane);
+      load_raw4<C, G>(raw, cx, src, 0, sw);
       rc = 0;
     }
   }
@@ -809,7 +865,7 @@ __device__ void run_role(Smem4<C>& sm, const Ctx4& cx, const SnapList& snap, int
     if constexpr (ROLE == SCAN) {
       if (sI.seq >= 0) {
         if (rc != sI.c) {
-          load_raw4<C, G>(raw, cx, sI.c, sw, lane);
+          load_raw4<C, G>(raw, cx, src, sI.c, sw);
           rc = sI.c;
         }
         KDA_PROBE_VMWAIT();
@@ -817,7 +873,7 @@ __device__ void run_role(Smem4<C>& sm, const Ctx4& cx, const SnapList& snap, int
         scan4<C, G>(sm, raw, sI, cx.eA, sw, lane, par);
         KDA_STEP_MARK(3, kstep);
         if (sI.hi == chunk_end(sI.c, cx.T) && sI.c + 1 < cx.nchunks) {
-          load_raw4<C, G>(raw, cx, sI.c + 1, sw, lane);  // prefetch the next chunk
+          load_raw4<C, G>(raw, cx, src, sI.c + 1, sw);  // prefetch the next chunk
           rc = sI.c + 1;
         }
       }
@@ -832,6 +888,10 @@ __device__ void run_role(Smem4<C>& sm, const Ctx4& cx, const SnapList& snap, int
         if (ns < p.nsnap && stI.hi == chunk_end(stI.c, cx.T) && snap.pos[ns] == stI.c * CS + stI.hi) {
           store_state<C>(p.snaps + ((size_t)cx.bh * p.nsnap + ns) * C::DK * p.dv + cx.col0, R, p.dv, lane);
           ++ns;
+          // Drain the stores here, on this rare path: otherwise the next steps
+          // carry a wait for them before every write to a register they might
+          // still read (dozens of no-op waits per step on the state wave).
+          __builtin_amdgcn_s_waitcnt(kVmcnt0);
         }
       }
       KDA_STEP_MARK(2, kstep);
