@@ -52,17 +52,13 @@ SHAPES = [(128, 128, torch.bfloat16), (64, 32, torch.bfloat16), (32, 32, torch.f
           (128, 16, torch.bfloat16)]
 
 
-@pytest.mark.parametrize("dk,dv,dtype", SHAPES)
-@pytest.mark.parametrize("K", [1, 4, 16])
-def test_verify_matches_oracle_and_leaves_state(gpu, dk, dv, dtype, K):
+def _check_verify(d, S, B, H, K, dk, dv, dtype):
     kda = _kda()
-    B, H = 2, 3
-    log(f"verify d={dk}x{dv} {dtype} K={K}")
-    d, S = _drafts(gpu, B, K, H, dk, dv, dtype, seed=dk + dv + K)
     S_before = S.clone()
     o, u = kda.kda_decode_verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], S)
     torch.cuda.synchronize()
     assert torch.equal(S, S_before), "verify wrote the state"
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(u).all()), "verify produced a non-finite value"
     bf = dtype == torch.bfloat16
     ro, _ = _oracle_after(d, S, K)
     got_o = o.float().permute(0, 2, 1, 3).reshape(B * H, K, dv).cpu().double().numpy()
@@ -82,6 +78,34 @@ def test_verify_matches_oracle_and_leaves_state(gpu, dk, dv, dtype, K):
             x = (a[:, None] * prev[bh]).T @ hs["k"][b, t, h]
             ref_u[bh, t] = hs["beta"][b, t, h] * (hs["v"][b, t, h] - x)
     _close(got_u, ref_u, bf, "u")
+
+
+@pytest.mark.parametrize("dk,dv,dtype", SHAPES)
+@pytest.mark.parametrize("K", [1, 4, 16])
+def test_verify_matches_oracle_and_leaves_state(gpu, dk, dv, dtype, K):
+    B, H = 2, 3
+    log(f"verify d={dk}x{dv} {dtype} K={K}")
+    d, S = _drafts(gpu, B, K, H, dk, dv, dtype, seed=dk + dv + K)
+    _check_verify(d, S, B, H, K, dk, dv, dtype)
+
+
+@pytest.mark.parametrize("dk,dv,dtype", [(128, 128, torch.bfloat16), (32, 32, torch.float32)])
+def test_verify_steep_decay(gpu, dk, dv, dtype):
+    """Channels whose decay over the drafts leaves fp32's comfortable range:
+    alpha = 0 (the channel is wiped), alpha = 1e-30, and alpha = 2^-20 on every
+    draft (the running product passes 2^-64 at the fourth), beside ordinary
+    channels; the state is carried undecayed inside the kernel, so these take
+    the path that folds the decay into the state row."""
+    B, H, K = 2, 3, 8
+    log(f"verify steep decay d={dk}x{dv} {dtype} K={K}")
+    d, S = _drafts(gpu, B, K, H, dk, dv, dtype, seed=dk + 5)
+    a = d["alpha"].clone()
+    a[:, 2, :, 0::7] = 0.0
+    a[:, 5, :, 1::5] = 1e-30
+    a[:, :, :, 3::4] = 2.0 ** -20
+    a[1, :, 2, :] = 2.0 ** -20  # every channel of one head
+    d["alpha"] = a.contiguous()
+    _check_verify(d, S, B, H, K, dk, dv, dtype)
 
 
 @pytest.mark.parametrize("dk,dv,dtype", SHAPES[:3])
