@@ -85,11 +85,19 @@ SplitShape split_shape_for(int T, int P) {
   return {(nch + pc - 1) / pc, 32 * pc};
 }
 
+// Combine cost in pipeline steps (about 2 us each): the chain costs about two
+// per part (about 4 us each); the tree about three per level plus the apply.
+double combine_steps(int P) {
+  if (P < kda::kTreeParts) return 2.0 * (P - 1);
+  int levels = 0;
+  for (int d = 1; d < P - 1; d *= 2) ++levels;
+  return 3.0 * (levels + 1);
+}
+
 // The part count with the smallest modelled time.  The model counts pipeline
-// steps (about 2 us each): a launch of G workgroups on `cus` compute units runs
-// ceil(G / cus) rounds of (chunks per part + 3) steps; the combine costs about
-// two steps per part (it is sequential over the parts, about 4 us each) and the
-// two extra launches about two steps.  A split is taken only when it models at
+// steps: a launch of G workgroups on `cus` compute units runs ceil(G / cus)
+// rounds of (chunks per part + 3) steps; the combine as above, and the two
+// extra launches about two steps.  A split is taken only when it models at
 // least 10% faster than the single pass.
 SplitShape split_shape_auto(int B, int T, int H, int dk, int dv, int cus) {
   const int nch = (T + 31) / 32;
@@ -102,7 +110,7 @@ SplitShape split_shape_auto(int B, int T, int H, int dk, int dv, int cus) {
     const SplitShape sh = split_shape_for(T, P);
     if (sh.parts != P) continue;
     const double cost = (rounds(bh * (P - 1) * nsa) + rounds(bh * P * ns)) * (sh.part_len / 32 + 3) +
-                        2.0 * (P - 1) + 2.0;
+                        combine_steps(P) + 2.0;
     if (cost < best_cost) {
       best_cost = cost;
       best = sh;
@@ -111,9 +119,11 @@ SplitShape split_shape_auto(int B, int T, int H, int dk, int dv, int cus) {
   return best;
 }
 
+// (N | M) of parts 0..P-2 (twice when the combine is a tree) and S_in of every part
 size_t split_ws_bytes(int B, int H, int dk, int dv, int P) {
   if (P <= 1) return 0;
-  return (size_t)4 * B * H * dk * ((size_t)(P - 1) * (dv + dk) + (size_t)P * dv);
+  const size_t trans = (size_t)(P - 1) * (dv + dk) * (P >= kda::kTreeParts ? 2 : 1);
+  return (size_t)4 * B * H * dk * (trans + (size_t)P * dv);
 }
 
 // Compute units of the current device (0 on failure).
@@ -247,7 +257,7 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, kda_dtype
 
   kda::PrefillParams p{q, k, v, alpha, beta, S0, o, S_T, B, T, H, d_k, d_v, o_dtype == KDA_F32 ? 1 : 0,
                        n_snap > 0 ? snaps : nullptr, n_snap, cu, T > 0 ? z : nullptr, A,
-                       /*split*/ 0, /*nparts*/ 0, /*part_len*/ 0, nullptr, nullptr};
+                       /*split*/ 0, /*nparts*/ 0, /*part_len*/ 0, nullptr, nullptr, nullptr};
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (sh.parts > 1) {
@@ -256,8 +266,10 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, kda_dtype
     // S_T may alias it)
     p.nparts = sh.parts;
     p.part_len = sh.part_len;
+    const size_t trans_bytes = (size_t)4 * B * H * d_k * (size_t)(sh.parts - 1) * (d_v + d_k);
     p.ws_trans = reinterpret_cast<float*>(ws);
-    p.ws_in = reinterpret_cast<float*>(ws + (size_t)4 * B * H * d_k * (size_t)(sh.parts - 1) * (d_v + d_k));
+    p.ws_tree = sh.parts >= kda::kTreeParts ? reinterpret_cast<float*>(ws + trans_bytes) : nullptr;
+    p.ws_in = reinterpret_cast<float*>(ws + trans_bytes * (p.ws_tree ? 2 : 1));
     p.split = 1;
     e = kda::launch_prefill_pipe(p, snap, hs);
     if (e == hipSuccess) e = kda::launch_split_combine(p, hs);

@@ -39,7 +39,12 @@ struct PrefillParams {
   int split, nparts, part_len;
   float* ws_trans;
   float* ws_in;
+  float* ws_tree;  // nparts >= kTreeParts: a second [B][nparts-1][H][dk][dv+dk] buffer
 };
+
+// Part counts from which the combine runs as a tree over the parts (log2 levels)
+// instead of a sequential chain.
+constexpr int kTreeParts = 9;
 
 // The lower-bounded retention exp(-5 sigmoid(e^A z)) for x = e^A z.
 __device__ __forceinline__ float gate_retention(float x) {
@@ -138,7 +143,9 @@ bool prefill_pipe_supported(int io_dtype, int dk, int dv, int chunk, int H);
 hipError_t launch_prefill_pipe(const PrefillParams& p, const SnapList& snap, hipStream_t s);
 
 // Between the two split passes: ws_in[b][0] = S0 (zeros when null) and
-// ws_in[b][j+1] = M_j ws_in[b][j] + N_j from ws_trans, for every (b, h).
+// ws_in[b][j+1] = M_j ws_in[b][j] + N_j from ws_trans, for every (b, h): a
+// sequential chain below kTreeParts parts, else a tree (ws_trans and ws_tree
+// are both overwritten).
 hipError_t launch_split_combine(const PrefillParams& p, hipStream_t s);
 
 // Speculative decoding: K draft tokens per (sequence, head).

@@ -27,6 +27,10 @@ namespace {
 
 constexpr int KQ = 8;  // key ranges per row
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
 template <int DK>
 __global__ __launch_bounds__(KQ * DK) void kda_split_combine_kernel(PrefillParams p) {
   constexpr int KR = DK / KQ;  // keys per thread
@@ -41,19 +45,26 @@ __global__ __launch_bounds__(KQ * DK) void kda_split_combine_kernel(PrefillParam
   const int P = p.nparts;
   const size_t mat = (size_t)DK * p.dv;
   const int ld = p.dv + DK;  // row stride of (N | M)
-  auto trans = [&](int j) {  // row r of (N_j | M_j)
-    return p.ws_trans + ((size_t)(b * (P - 1) + j) * p.H + h) * DK * ld + (size_t)r * ld;
+  // Part addresses are uniform (a buffer resource per part) and each thread's
+  // offsets are fixed, so a part needs no vector address arithmetic: computed
+  // per part, it landed in registers still awaiting the previous prefetch, and
+  // the compiler waited for that prefetch at the start of every part.
+  const int vo_m = 4 * (r * ld + p.dv + kq * KR);  // this thread's keys of row r of M_j
+  const int vo_n = 4 * (r * ld + col);             // row r, this slab's columns, of N_j
+  const int vo_s = 4 * (r * p.dv + col);           // the same in S_in(j)
+  auto trans = [&](int j) {  // (N_j | M_j)
+    return make_rsrc(p.ws_trans + ((size_t)(b * (P - 1) + j) * p.H + h) * DK * ld, DK * ld * 4);
   };
-  auto slot = [&](int j) { return p.ws_in + ((size_t)(b * P + j) * p.H + h) * mat + (size_t)r * p.dv + col; };
+  auto slot = [&](int j) { return make_rsrc(p.ws_in + ((size_t)(b * P + j) * p.H + h) * mat, (int)(mat * 4)); };
   // Rows of M_j (this thread's keys) and of N_j.  Loads, stores and LDS writes
   // are unconditional (part indices clamped, every lane of a row storing the
   // same value), so the compiler can count the loads still in flight and wait
   // only for the oldest buffer instead of for all of them.
   auto load = [&](int j, f32x4 (&m)[NL], f32x4& n) {
-    const float* tr = trans(min(j, P - 2));
+    const __amdgpu_buffer_rsrc_t tr = trans(min(j, P - 2));
 #pragma unroll
-    for (int i = 0; i < NL; ++i) m[i] = *reinterpret_cast<const f32x4*>(tr + p.dv + kq * KR + 4 * i);
-    n = *reinterpret_cast<const f32x4*>(tr + col);
+    for (int i = 0; i < NL; ++i) m[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(tr, vo_m, 16 * i, 0));
+    n = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(tr, vo_n, 0, 0));
   };
   // S_in(j+1) = M_j S_in(j) + N_j, prefetching part j + 2 into (mp, np)
   auto part = [&](int j, const f32x4 (&m)[NL], const f32x4& n, f32x4 (&mp)[NL], f32x4& np) {
@@ -73,13 +84,13 @@ __global__ __launch_bounds__(KQ * DK) void kda_split_combine_kernel(PrefillParam
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], off);
     s[(j + 1) & 1][r] = acc;  // the same value from every lane of row r
-    *reinterpret_cast<f32x4*>(slot(j + 1)) = acc;
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), slot(j + 1), vo_s, 0, 0);
     __syncthreads();  // S_in(j+1) visible; every read of the other buffer is done
   };
 
   f32x4 cur = (f32x4)0.0f;
   if (p.S0) cur = *reinterpret_cast<const f32x4*>(p.S0 + (size_t)bh * mat + (size_t)r * p.dv + col);
-  *reinterpret_cast<f32x4*>(slot(0)) = cur;
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, cur), slot(0), vo_s, 0, 0);
   s[0][r] = cur;
   f32x4 m0[NL], m1[NL], m2[NL], n0, n1, n2;
   load(0, m0, n0);
@@ -94,9 +105,155 @@ __global__ __launch_bounds__(KQ * DK) void kda_split_combine_kernel(PrefillParam
   }
 }
 
+
+// ---- tree combine ----------------------------------------------------------
+// For many parts the chain above is a long sequence of dependent steps.  The
+// part maps compose associatively, (M_a, N_a) o (M_b, N_b) = (M_a M_b,
+// M_a N_b + N_a), so an inclusive scan over them takes log2(P - 1) levels: at
+// level d every part j >= d becomes its composition with part j - d (both from
+// the previous level), parts j < d are carried over.  Afterwards part j holds
+// the map of parts 0..j together, and S_in(j + 1) = M*_j S0 + N*_j.
+//
+// Both kernels compute DK x 32 tiles of M X in fp32: one 256-thread workgroup
+// per (b, h, part, 32-column block); M and X's column block are staged in LDS
+// 64 keys at a time (row-major, 16-byte writes and reads; 43 KB, three
+// workgroups per CU), and each thread accumulates a 4 x 4 block.
+constexpr int TC = 32;  // output columns per workgroup
+constexpr int TNT = 256;
+constexpr int TK = 64;  // keys staged per phase
+
+// acc[i] += row 4 rg + i of M (row stride ldm) times columns 4 cgi.. of X (row
+// stride ldx).  LDS is reusable on return.
+template <int DK>
+__device__ __forceinline__ void tile_rows(float (&am)[DK][TK + 4], f32x4 (&xs)[TK][TC / 4], const float* M, int ldm,
+                                          const float* X, int ldx, int tid, int rg, int cgi, f32x4 (&acc)[4]) {
+  for (int kb = 0; kb < DK; kb += TK) {
+    for (int e = tid; e < DK * TK / 4; e += TNT) {
+      const int row = e / (TK / 4), k4 = 4 * (e % (TK / 4));
+      *reinterpret_cast<f32x4*>(&am[row][k4]) = *reinterpret_cast<const f32x4*>(M + (size_t)row * ldm + kb + k4);
+    }
+    for (int e = tid; e < TK * TC / 4; e += TNT) {
+      const int k = e / (TC / 4), c4 = e % (TC / 4);
+      xs[k][c4] = *reinterpret_cast<const f32x4*>(X + (size_t)(kb + k) * ldx + 4 * c4);
+    }
+    __syncthreads();
+    if (rg < DK / 4) {
+#pragma unroll 2
+      for (int k = 0; k < TK; k += 4) {
+        f32x4 a[4], x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const f32x4*>(&am[4 * rg + i][k]);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) x[kk] = xs[k + kk][cgi];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) acc[i] += a[i][kk] * x[kk];
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// One level: dst_j = src_j o src_{j-d} for j >= d, dst_j = src_j for j < d, on
+// (N | M) blocks of ld = dv + DK columns.
+template <int DK>
+__global__ __launch_bounds__(TNT) void kda_split_level_kernel(PrefillParams p, const float* src, float* dst, int d) {
+  __shared__ float am[DK][TK + 4];
+  __shared__ f32x4 xs[TK][TC / 4];
+  const int ld = p.dv + DK, ncb = ld / TC, np = p.nparts - 1;
+  const int cb = blockIdx.x % ncb, j = (blockIdx.x / ncb) % np, bh = blockIdx.x / ncb / np;
+  const int b = bh / p.H, h = bh % p.H;
+  const size_t blk = (size_t)DK * ld;
+  auto part = [&](const float* base, int jj) { return base + ((size_t)(b * np + jj) * p.H + h) * blk; };
+  const int tid = threadIdx.x, rg = tid / (TC / 4), cgi = tid % (TC / 4);
+  const float* sj = part(src, j);
+  float* dj = const_cast<float*>(part(dst, j));
+  const int col = cb * TC;
+  if (j < d) {  // carried over
+    for (int e = tid; e < DK * TC / 4; e += TNT) {
+      const int r = e / (TC / 4), c4 = e % (TC / 4);
+      *reinterpret_cast<f32x4*>(dj + (size_t)r * ld + col + 4 * c4) =
+          *reinterpret_cast<const f32x4*>(sj + (size_t)r * ld + col + 4 * c4);
+    }
+    return;
+  }
+  f32x4 acc[4] = {(f32x4)0.0f, (f32x4)0.0f, (f32x4)0.0f, (f32x4)0.0f};
+  // M_j X_{j-d} over this column block, plus N_j in the N columns
+  tile_rows<DK>(am, xs, sj + p.dv, ld, part(src, j - d) + col, ld, tid, rg, cgi, acc);
+  if (rg < DK / 4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const size_t o = (size_t)(4 * rg + i) * ld + col + 4 * cgi;
+      f32x4 v = acc[i];
+      if (col < p.dv) v += *reinterpret_cast<const f32x4*>(sj + o);
+      *reinterpret_cast<f32x4*>(dj + o) = v;
+    }
+  }
+}
+
+// S_in(0) = S0 (zeros when null), S_in(j+1) = M*_j S0 + N*_j.
+template <int DK>
+__global__ __launch_bounds__(TNT) void kda_split_apply_kernel(PrefillParams p, const float* comp) {
+  __shared__ float am[DK][TK + 4];
+  __shared__ f32x4 xs[TK][TC / 4];
+  const int ld = p.dv + DK, ncb = p.dv / TC, P = p.nparts;
+  const int cb = blockIdx.x % ncb, j = (blockIdx.x / ncb) % P, bh = blockIdx.x / ncb / P;
+  const int b = bh / p.H, h = bh % p.H;
+  const int tid = threadIdx.x, rg = tid / (TC / 4), cgi = tid % (TC / 4);
+  const size_t mat = (size_t)DK * p.dv;
+  const int col = cb * TC;
+  float* out = p.ws_in + ((size_t)(b * P + j) * p.H + h) * mat + col;
+  const float* s0 = p.S0 ? p.S0 + (size_t)bh * mat + col : nullptr;
+  const float* cj = j > 0 ? comp + ((size_t)(b * (P - 1) + j - 1) * p.H + h) * DK * ld : nullptr;
+  if (j == 0 || !s0) {  // S0 itself, or N*_{j-1} alone
+    for (int e = tid; e < DK * TC / 4; e += TNT) {
+      const int r = e / (TC / 4), c4 = e % (TC / 4);
+      f32x4 v = (f32x4)0.0f;
+      if (j == 0 && s0) v = *reinterpret_cast<const f32x4*>(s0 + (size_t)r * p.dv + 4 * c4);
+      if (j > 0) v = *reinterpret_cast<const f32x4*>(cj + (size_t)r * ld + col + 4 * c4);
+      *reinterpret_cast<f32x4*>(out + (size_t)r * p.dv + 4 * c4) = v;
+    }
+    return;
+  }
+  f32x4 acc[4] = {(f32x4)0.0f, (f32x4)0.0f, (f32x4)0.0f, (f32x4)0.0f};
+  tile_rows<DK>(am, xs, cj + p.dv, ld, s0, p.dv, tid, rg, cgi, acc);
+  if (rg < DK / 4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const size_t r = 4 * rg + i;
+      *reinterpret_cast<f32x4*>(out + r * p.dv + 4 * cgi) =
+          acc[i] + *reinterpret_cast<const f32x4*>(cj + r * ld + col + 4 * cgi);
+    }
+  }
+}
+
+template <int DK>
+hipError_t launch_tree(const PrefillParams& p, hipStream_t s) {
+  const int np = p.nparts - 1, ld = p.dv + DK;
+  const unsigned lgrid = (unsigned)(p.B * p.H * np * (ld / TC));
+  float* src = p.ws_trans;
+  float* dst = p.ws_tree;
+  for (int d = 1; d < np; d *= 2) {
+    hipLaunchKernelGGL(kda_split_level_kernel<DK>, dim3(lgrid), dim3(TNT), 0, s, p, (const float*)src, dst, d);
+    float* t = src;
+    src = dst;
+    dst = t;
+  }
+  const unsigned agrid = (unsigned)(p.B * p.H * p.nparts * (p.dv / TC));
+  hipLaunchKernelGGL(kda_split_apply_kernel<DK>, dim3(agrid), dim3(TNT), 0, s, p, (const float*)src);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_split_combine(const PrefillParams& p, hipStream_t s) {
+  if (p.nparts >= kTreeParts) {
+    if (!p.ws_tree) return hipErrorInvalidValue;
+    if (p.dk == 128) return launch_tree<128>(p, s);
+    if (p.dk == 64) return launch_tree<64>(p, s);
+    return hipErrorInvalidValue;
+  }
   const unsigned grid = (unsigned)(p.B * p.H * (p.dv / 4));
   if (p.dk == 128) hipLaunchKernelGGL(kda_split_combine_kernel<128>, dim3(grid), dim3(KQ * 128), 0, s, p);
   else if (p.dk == 64) hipLaunchKernelGGL(kda_split_combine_kernel<64>, dim3(grid), dim3(KQ * 64), 0, s, p);

@@ -200,8 +200,10 @@ kda_status kda_chunk_fwd_gated(const void* q, const void* k, const void* v, kda_
  * d_k x d_k transition M (section 3.3 of the first page: each token applies
  * (I - beta k k^T) Diag(alpha) to every state column and adds beta k v^T), so:
  * pass 1 computes N and M of every part but the last, in parallel; a combine
- * step chains S_in(j+1) = M_j S_in(j) + N_j in fp32; pass 2 reruns every part
- * from its S_in and writes o and S_T.  Parts are whole 32-token chunks.
+ * step chains S_in(j+1) = M_j S_in(j) + N_j in fp32 (from 9 parts on, as a tree
+ * over the part maps: log2 levels of pairwise compositions, then one product
+ * with S0); pass 2 reruns every part from its S_in and writes o and S_T.  Parts
+ * are whole 32-token chunks.
  *
  *   parts     : 0 = the library's choice (a step-count model of the launches
  *               on num_cus compute units; 1 part when splitting does not pay);
@@ -213,7 +215,8 @@ kda_status kda_chunk_fwd_gated(const void* q, const void* k, const void* v, kda_
  *               do not matter and are overwritten.  May be NULL when the
  *               resulting split has 1 part.  kda_chunk_fwd_split_plan gives the
  *               part count and the bytes needed:
- *               4 * B * H * d_k * ((P - 1) * (d_v + d_k) + P * d_v) for P parts.
+ *               4 * B * H * d_k * (c * (P - 1) * (d_v + d_k) + P * d_v) for P
+ *               parts, with c = 1 below 9 parts and c = 2 from 9 parts on.
  * Every other argument as kda_chunk_fwd.  Splitting is built for the pipelined
  * kernel's shapes (bf16 q/k/v, d_k in {64, 128}, d_v a multiple of 32, chunk 32
  * or 64); parts >= 2 for another shape returns KDA_ERR_UNSUPPORTED.  Errors:
@@ -223,7 +226,7 @@ kda_status kda_chunk_fwd_gated(const void* q, const void* k, const void* v, kda_
  * device's compute units could not be queried).  The result equals
  * kda_chunk_fwd up to rounding (the state entering each part goes through one
  * fp32 product with M instead of the chunk recurrence).  Three kernels are
- * enqueued on `stream`.
+ * enqueued on `stream` below 9 parts; from 9 parts on, 3 + ceil(log2(P - 1)).
  */
 kda_status kda_chunk_fwd_split_plan(kda_dtype qkv_dtype, int B, int T, int H, int d_k, int d_v, int chunk,
                                     int parts, int num_cus, int* parts_out, size_t* workspace_bytes);

@@ -271,8 +271,12 @@ def _plan(lib, dtype=1, B=1, T=4096, H=8, dk=128, dv=128, chunk=64, parts=0, cus
     return st, n.value, ws.value
 
 
+TREE_PARTS = 9  # part counts from which the combine is a tree (a second (N | M) buffer)
+
+
 def _ws_bytes(P, B=1, H=8, dk=128, dv=128):
-    return 4 * B * H * dk * ((P - 1) * (dv + dk) + P * dv)
+    trans = (P - 1) * (dv + dk) * (2 if P >= TREE_PARTS else 1)
+    return 4 * B * H * dk * (trans + P * dv)
 
 
 def test_split_plan_choices():

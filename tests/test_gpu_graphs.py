@@ -72,9 +72,10 @@ def test_decode_steps_in_a_graph(gpu):
         assert torch.equal(S_g, S_e) and torch.equal(o_g, o_e), f"replay {rep} differs from the eager steps"
 
 
-@pytest.mark.parametrize("parts", [1, 4])
+@pytest.mark.parametrize("parts", [1, 4, 12])
 def test_prefill_in_a_graph(gpu, parts):
-    """The prefill (one kernel) and the split prefill (three kernels and a workspace) in a graph."""
+    """The prefill (one kernel) and the split prefill (three kernels and a workspace; with 12
+    parts, a tree of combine launches) in a graph."""
     kda = _kda()
     B, T, H, d = 1, 640, 2, 128
     x = ki.make_prefill(B, T, H, d, d, torch.bfloat16, 3.0, 0.1, seed=63, device=gpu)

@@ -67,6 +67,28 @@ def test_split_matches_oracle(gpu, case):
     assert 1 < n <= min(parts, -(-T // 32))
 
 
+TREE_CASES = [
+    # (name, B, T, H, dk, dv, parts, S0): part counts >= 9 run the combine as a tree
+    ("d128 10 parts", 1, 1200, 2, 128, 128, 12, True),
+    ("d128 16 parts ragged", 2, 1500, 2, 128, 128, 16, True),
+    ("d64 33 parts", 1, 2100, 3, 64, 64, 33, True),
+    ("d128 10 parts no S0", 1, 1200, 2, 128, 128, 12, False),
+    ("d128x64 10 parts", 1, 1200, 2, 128, 64, 12, True),
+]
+
+
+@pytest.mark.parametrize("case", TREE_CASES, ids=[c[0] for c in TREE_CASES])
+def test_split_tree_combine(gpu, case):
+    """Enough parts that the states entering them are formed by a tree over the
+    part maps (log2 levels of pairwise compositions, then one product with S0).
+    Slow decay (alpha = sigmoid(N(8, 1)), about 0.9997) keeps S0 and the early
+    parts visible at the end, so the composed transitions are what is tested."""
+    name, B, T, H, dk, dv, parts, s0 = case
+    inp = ki.make_prefill(B, T, H, dk, dv, torch.bfloat16, 8.0, 0.1, seed=T + parts + dv, device=gpu)
+    n = _check(inp, parts, name, S0=s0)
+    assert n >= 9, f"{name}: {n} parts do not reach the tree"
+
+
 def test_split_without_initial_state_and_bf16_output(gpu):
     """No S0 against the oracle; a bf16 o is the fp32 o rounded to nearest even,
     bit for bit (the rounding of a bf16 o alone can spend the whole tolerance)."""

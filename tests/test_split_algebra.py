@@ -64,6 +64,53 @@ def test_two_level_scan_reproduces_the_single_pass(cuts):
     assert np.abs(ss - rs).max() < 1e-12 * max(1.0, np.abs(rs).max())
 
 
+def _part_maps(q, k, v, alpha, beta, cuts):
+    """(M_j, N_j) of every part but the last, from the oracle."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    bounds = [0] + list(cuts) + [T]
+    maps = []
+    for lo, hi in list(zip(bounds[:-1], bounds[1:]))[:-1]:
+        vaug = np.concatenate([v[:, lo:hi], np.zeros((B, hi - lo, H, dk))], axis=-1)
+        s_aug = np.zeros((B, H, dk, dv + dk))
+        s_aug[..., dv:] = np.eye(dk)
+        _, st = oracle.forward(q[:, lo:hi], k[:, lo:hi], vaug, alpha[:, lo:hi], beta[:, lo:hi], s_aug,
+                               want_o=False)
+        st = st.reshape(B, H, dk, dv + dk)
+        maps.append((st[..., dv:], st[..., :dv]))
+    return maps
+
+
+@pytest.mark.parametrize("nparts", [2, 3, 9, 10, 17, 33])
+def test_tree_of_part_maps_equals_the_chain(nparts):
+    """The tree the GPU path takes from 9 parts on: an inclusive scan over the
+    part maps with (M_a, N_a) o (M_b, N_b) = (M_a M_b, M_a N_b + N_a), in levels
+    d = 1, 2, 4, ... where part j >= d is composed with part j - d of the
+    previous level, then S_in(j + 1) = M*_j S0 + N*_j.  It must give the chain's
+    incoming states to fp64 rounding (associativity), for part counts around
+    the powers of two."""
+    rng = np.random.default_rng(nparts)
+    B, H, dk, dv = 1, 2, 6, 3
+    T = 3 * nparts
+    q, k, v, alpha, beta, S0 = _inputs(rng, B, T, H, dk, dv)
+    maps = _part_maps(q, k, v, alpha, beta, [3 * j for j in range(1, nparts)])
+    chain = [S0]
+    for M, N in maps:
+        chain.append(np.einsum("bhij,bhjc->bhic", M, chain[-1]) + N)
+    cur = list(maps)
+    d = 1
+    while d < len(cur):
+        nxt = list(cur)
+        for j in range(d, len(cur)):
+            (Ma, Na), (Mb, Nb) = cur[j], cur[j - d]
+            nxt[j] = (np.einsum("bhij,bhjk->bhik", Ma, Mb), np.einsum("bhij,bhjc->bhic", Ma, Nb) + Na)
+        cur = nxt
+        d *= 2
+    tree = [S0] + [np.einsum("bhij,bhjc->bhic", M, S0) + N for M, N in cur]
+    for j, (a, b) in enumerate(zip(tree, chain)):
+        assert np.abs(a - b).max() < 1e-12 * max(1.0, np.abs(b).max()), f"S_in({j})"
+
+
 def test_transition_is_the_product_of_token_maps():
     """M over a few tokens equals the product of the dense per-token matrices
     (I - beta k k^T) Diag(alpha), built independently here."""
