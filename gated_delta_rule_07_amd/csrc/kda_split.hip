@@ -115,28 +115,58 @@ __global__ __launch_bounds__(KQ * DK) void kda_split_combine_kernel(PrefillParam
 // the map of parts 0..j together, and S_in(j + 1) = M*_j S0 + N*_j.
 //
 // Both kernels compute DK x 32 tiles of M X in fp32: one 256-thread workgroup
-// per (b, h, part, 32-column block); M and X's column block are staged in LDS
-// 64 keys at a time (row-major, 16-byte writes and reads; 43 KB, three
-// workgroups per CU), and each thread accumulates a 4 x 4 block.
+// per (b, h, part, 32-column block).  M and X's column block pass through LDS
+// TK keys at a time (row-major, 16-byte writes and reads); the next phase's
+// values are loaded into registers while the current phase is multiplied, so
+// only the first phase's loads are waited for.  Each thread accumulates a
+// 4 x 4 block.
 constexpr int TC = 32;  // output columns per workgroup
 constexpr int TNT = 256;
-constexpr int TK = 64;  // keys staged per phase
+constexpr int TK = 32;  // keys per phase
+
+template <int DK>
+struct TilePhase {
+  static constexpr int NA = DK * TK / 4 / TNT;  // f32x4 of M per thread and phase
+  static constexpr int NX = TK * TC / 4 / TNT;  // f32x4 of X per thread and phase (1)
+  static_assert(NA >= 1 && NX == 1, "tile phase shape");
+  f32x4 a[NA];
+  f32x4 x;
+};
+
+template <int DK>
+__device__ __forceinline__ void tile_load(TilePhase<DK>& t, const float* M, int ldm, const float* X, int ldx, int kb,
+                                          int tid) {
+#pragma unroll
+  for (int n = 0; n < TilePhase<DK>::NA; ++n) {
+    const int e = tid + n * TNT, row = e / (TK / 4), k4 = 4 * (e % (TK / 4));
+    t.a[n] = *reinterpret_cast<const f32x4*>(M + (size_t)row * ldm + kb + k4);
+  }
+  const int k = tid / (TC / 4), c4 = tid % (TC / 4);
+  t.x = *reinterpret_cast<const f32x4*>(X + (size_t)(kb + k) * ldx + 4 * c4);
+}
+
+template <int DK>
+__device__ __forceinline__ void tile_store(const TilePhase<DK>& t, float (&am)[DK][TK + 4], f32x4 (&xs)[TK][TC / 4],
+                                           int tid) {
+#pragma unroll
+  for (int n = 0; n < TilePhase<DK>::NA; ++n) {
+    const int e = tid + n * TNT, row = e / (TK / 4), k4 = 4 * (e % (TK / 4));
+    *reinterpret_cast<f32x4*>(&am[row][k4]) = t.a[n];
+  }
+  xs[tid / (TC / 4)][tid % (TC / 4)] = t.x;
+}
 
 // acc[i] += row 4 rg + i of M (row stride ldm) times columns 4 cgi.. of X (row
 // stride ldx).  LDS is reusable on return.
 template <int DK>
 __device__ __forceinline__ void tile_rows(float (&am)[DK][TK + 4], f32x4 (&xs)[TK][TC / 4], const float* M, int ldm,
                                           const float* X, int ldx, int tid, int rg, int cgi, f32x4 (&acc)[4]) {
+  TilePhase<DK> t;
+  tile_load<DK>(t, M, ldm, X, ldx, 0, tid);
   for (int kb = 0; kb < DK; kb += TK) {
-    for (int e = tid; e < DK * TK / 4; e += TNT) {
-      const int row = e / (TK / 4), k4 = 4 * (e % (TK / 4));
-      *reinterpret_cast<f32x4*>(&am[row][k4]) = *reinterpret_cast<const f32x4*>(M + (size_t)row * ldm + kb + k4);
-    }
-    for (int e = tid; e < TK * TC / 4; e += TNT) {
-      const int k = e / (TC / 4), c4 = e % (TC / 4);
-      xs[k][c4] = *reinterpret_cast<const f32x4*>(X + (size_t)(kb + k) * ldx + 4 * c4);
-    }
+    tile_store<DK>(t, am, xs, tid);
     __syncthreads();
+    if (kb + TK < DK) tile_load<DK>(t, M, ldm, X, ldx, kb + TK, tid);  // in flight during the products
     if (rg < DK / 4) {
 #pragma unroll 2
       for (int k = 0; k < TK; k += 4) {
