@@ -8,12 +8,14 @@
 // is any run of tokens: the state after part j of a sequence is
 // M_j S_in + N_j, with M_j the part's transition and N_j its state from zero.
 // The first prefill pass computes (N_j | M_j) for every part but the last, the
-// parts in parallel; this kernel chains them,
+// parts in parallel; the kernels here form
 //     S_in(0) = S0,   S_in(j+1) = M_j S_in(j) + N_j,
-// in fp32; the second pass reruns every part from S_in(j) (section 13 of the
-// technical report review lists this kind of context parallelism).
+// in fp32, as a chain below kTreeParts parts and as a tree over the part maps
+// from there on (below); the second pass reruns every part from S_in(j)
+// (section 13 of the technical report review lists this kind of context
+// parallelism).
 //
-// One workgroup per (b, h, 4 state columns), KQ * DK threads: thread (r, kq)
+// The chain: one workgroup per (b, h, 4 state columns), KQ * DK threads: thread (r, kq)
 // owns row r and the kq-th of KQ key ranges of the product (the ranges are
 // summed with lane shuffles).  The parts are sequential, so the latency of each
 // part is what counts: the rows of M and N for part j + 2 are loaded while part
@@ -116,10 +118,10 @@ __global__ __launch_bounds__(KQ * DK) void kda_split_combine_kernel(PrefillParam
 //
 // Both kernels compute DK x 32 tiles of M X in fp32: one 256-thread workgroup
 // per (b, h, part, 32-column block).  M and X's column block pass through LDS
-// TK keys at a time (row-major, 16-byte writes and reads); the next phase's
-// values are loaded into registers while the current phase is multiplied, so
-// only the first phase's loads are waited for.  Each thread accumulates a
-// 4 x 4 block.
+// TK keys at a time (row-major, 16-byte writes); the next phase's values are
+// loaded into registers while the current phase is multiplied, so only the
+// first phase's loads are waited for.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int TC = 32;  // output columns per workgroup
 constexpr int TNT = 256;
 constexpr int TK = 32;  // keys per phase
@@ -156,33 +158,35 @@ __device__ __forceinline__ void tile_store(const TilePhase<DK>& t, float (&am)[D
   xs[tid / (TC / 4)][tid % (TC / 4)] = t.x;
 }
 
-// acc[i] += row 4 rg + i of M (row stride ldm) times columns 4 cgi.. of X (row
-// stride ldx).  LDS is reusable on return.
+// The 32-row block 32 w.. of M X for wave w (row stride ldm of M, ldx of X, X
+// offset to the tile's columns) on fp32 matrix cores: 32 x 32 x 2 steps, lane
+// l supplying M[32 w + l % 32][k + l / 32] and X[k + l / 32][l % 32]; the
+// result holds rows 8 (e / 4) + 4 (l / 32) + e % 4 of column l % 32 in element
+// e.  fp32 products and sums throughout, at twice the unpacked vector rate.
+// Waves whose block lies past DK return zeros.  LDS is reusable on return.
 template <int DK>
-__device__ __forceinline__ void tile_rows(float (&am)[DK][TK + 4], f32x4 (&xs)[TK][TC / 4], const float* M, int ldm,
-                                          const float* X, int ldx, int tid, int rg, int cgi, f32x4 (&acc)[4]) {
+__device__ __forceinline__ f32x16 tile_mfma(float (&am)[DK][TK + 4], f32x4 (&xs)[TK][TC / 4], const float* M, int ldm,
+                                            const float* X, int ldx, int tid) {
+  const int wave = tid / 64, lane = tid % 64, i = lane % 32, hk = lane / 32;
+  const int row = 32 * wave + i;
+  f32x16 d = (f32x16)0.0f;
   TilePhase<DK> t;
   tile_load<DK>(t, M, ldm, X, ldx, 0, tid);
   for (int kb = 0; kb < DK; kb += TK) {
     tile_store<DK>(t, am, xs, tid);
     __syncthreads();
     if (kb + TK < DK) tile_load<DK>(t, M, ldm, X, ldx, kb + TK, tid);  // in flight during the products
-    if (rg < DK / 4) {
-#pragma unroll 2
-      for (int k = 0; k < TK; k += 4) {
-        f32x4 a[4], x[4];
+    if (32 * wave < DK) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const f32x4*>(&am[4 * rg + i][k]);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) x[kk] = xs[k + kk][cgi];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk) acc[i] += a[i][kk] * x[kk];
+      for (int k = 0; k < TK; k += 2) {
+        const float av = am[row][k + hk];
+        const float bv = reinterpret_cast<const float*>(&xs[k + hk][0])[i];
+        d = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, d, 0, 0, 0);
       }
     }
     __syncthreads();
   }
+  return d;
 }
 
 // One level: dst_j = src_j o src_{j-d} for j >= d, dst_j = src_j for j < d, on
@@ -196,7 +200,7 @@ __global__ __launch_bounds__(TNT) void kda_split_level_kernel(PrefillParams p, c
   const int b = bh / p.H, h = bh % p.H;
   const size_t blk = (size_t)DK * ld;
   auto part = [&](const float* base, int jj) { return base + ((size_t)(b * np + jj) * p.H + h) * blk; };
-  const int tid = threadIdx.x, rg = tid / (TC / 4), cgi = tid % (TC / 4);
+  const int tid = threadIdx.x;
   const float* sj = part(src, j);
   float* dj = const_cast<float*>(part(dst, j));
   const int col = cb * TC;
@@ -208,16 +212,15 @@ __global__ __launch_bounds__(TNT) void kda_split_level_kernel(PrefillParams p, c
     }
     return;
   }
-  f32x4 acc[4] = {(f32x4)0.0f, (f32x4)0.0f, (f32x4)0.0f, (f32x4)0.0f};
   // M_j X_{j-d} over this column block, plus N_j in the N columns
-  tile_rows<DK>(am, xs, sj + p.dv, ld, part(src, j - d) + col, ld, tid, rg, cgi, acc);
-  if (rg < DK / 4) {
+  const f32x16 acc = tile_mfma<DK>(am, xs, sj + p.dv, ld, part(src, j - d) + col, ld, tid);
+  const int wave = tid / 64, lane = tid % 64;
+  if (32 * wave < DK) {
+    const int c = col + lane % 32;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const size_t o = (size_t)(4 * rg + i) * ld + col + 4 * cgi;
-      f32x4 v = acc[i];
-      if (col < p.dv) v += *reinterpret_cast<const f32x4*>(sj + o);
-      *reinterpret_cast<f32x4*>(dj + o) = v;
+    for (int e = 0; e < 16; ++e) {
+      const size_t o = (size_t)(32 * wave + 8 * (e / 4) + 4 * (lane / 32) + e % 4) * ld + c;
+      dj[o] = acc[e] + (col < p.dv ? sj[o] : 0.0f);
     }
   }
 }
@@ -230,7 +233,7 @@ __global__ __launch_bounds__(TNT) void kda_split_apply_kernel(PrefillParams p, c
   const int ld = p.dv + DK, ncb = p.dv / TC, P = p.nparts;
   const int cb = blockIdx.x % ncb, j = (blockIdx.x / ncb) % P, bh = blockIdx.x / ncb / P;
   const int b = bh / p.H, h = bh % p.H;
-  const int tid = threadIdx.x, rg = tid / (TC / 4), cgi = tid % (TC / 4);
+  const int tid = threadIdx.x;
   const size_t mat = (size_t)DK * p.dv;
   const int col = cb * TC;
   float* out = p.ws_in + ((size_t)(b * P + j) * p.H + h) * mat + col;
@@ -246,14 +249,13 @@ __global__ __launch_bounds__(TNT) void kda_split_apply_kernel(PrefillParams p, c
     }
     return;
   }
-  f32x4 acc[4] = {(f32x4)0.0f, (f32x4)0.0f, (f32x4)0.0f, (f32x4)0.0f};
-  tile_rows<DK>(am, xs, cj + p.dv, ld, s0, p.dv, tid, rg, cgi, acc);
-  if (rg < DK / 4) {
+  const f32x16 acc = tile_mfma<DK>(am, xs, cj + p.dv, ld, s0, p.dv, tid);
+  const int wave = tid / 64, lane = tid % 64;
+  if (32 * wave < DK) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const size_t r = 4 * rg + i;
-      *reinterpret_cast<f32x4*>(out + r * p.dv + 4 * cgi) =
-          acc[i] + *reinterpret_cast<const f32x4*>(cj + r * ld + col + 4 * cgi);
+    for (int e = 0; e < 16; ++e) {
+      const size_t r = 32 * wave + 8 * (e / 4) + 4 * (lane / 32) + e % 4;
+      out[r * p.dv + lane % 32] = acc[e] + cj[r * ld + col + lane % 32];
     }
   }
 }
