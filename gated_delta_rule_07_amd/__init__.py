@@ -14,11 +14,11 @@ from pathlib import Path
 import torch
 
 __all__ = ["kda_chunk_fwd", "kda_chunk_fwd_snapshots", "kda_chunk_fwd_varlen", "kda_chunk_fwd_gated",
-           "kda_chunk_fwd_split", "kda_chunk_fwd_split_plan",
+           "kda_chunk_fwd_split", "kda_chunk_fwd_split_plan", "kda_chunk_fwd_run_chunk",
            "kda_decode_step", "kda_decode_step_gated",
            "kda_decode_verify",
            "kda_decode_commit", "kda_status_string", "kda_version",
-           "kda_last_hip_error", "library_path", "load_library", "KdaError",
+           "kda_last_hip_error", "library_path", "load_library", "bind", "KdaError",
            "KDA_F32", "KDA_BF16", "KDA_MAX_SNAPSHOTS", "KDA_MAX_DRAFT"]
 
 KDA_F32, KDA_BF16 = 0, 1
@@ -49,7 +49,13 @@ def load_library():
     if not _LIB_PATH.exists():
         raise RuntimeError(f"libkda is not built ({_LIB_PATH} missing); run "
                            "`python -m gated_delta_rule_07_amd.build` first")
-    lib = ctypes.CDLL(str(_LIB_PATH))
+    _lib = bind(_LIB_PATH)
+    return _lib
+
+
+def bind(path) -> ctypes.CDLL:
+    """Open a build of the C ABI at `path` and declare its argument types."""
+    lib = ctypes.CDLL(str(path))
     vp, i32 = ctypes.c_void_p, ctypes.c_int
     lib.kda_chunk_fwd.restype = i32
     lib.kda_chunk_fwd.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, i32, vp,
@@ -84,8 +90,19 @@ def load_library():
     lib.kda_last_hip_error.argtypes = []
     lib.kda_version.restype = i32
     lib.kda_version.argtypes = []
-    _lib = lib
+    lib.kda_chunk_fwd_run_chunk.restype = i32
+    lib.kda_chunk_fwd_run_chunk.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(i32)]
     return lib
+
+
+def kda_chunk_fwd_run_chunk(qkv_dtype, H, d_k, d_v, chunk: int = 64) -> int:
+    """Tokens per chunk a ``kda_chunk_fwd`` call with these sizes runs."""
+    code = KDA_BF16 if qkv_dtype == torch.bfloat16 else KDA_F32 if qkv_dtype == torch.float32 else -1
+    run = ctypes.c_int(0)
+    st = load_library().kda_chunk_fwd_run_chunk(code, int(H), int(d_k), int(d_v), int(chunk), ctypes.byref(run))
+    if st != 0:
+        raise KdaError(st, "kda_chunk_fwd_run_chunk")
+    return run.value
 
 
 def kda_status_string(status: int) -> str:
@@ -331,6 +348,10 @@ def kda_decode_step_gated(q, k, v, z, A, beta, S, *, o=None, o_dtype=torch.float
         raise ValueError("libkda: S must be [B,H,d_k,d_v]")
     if o is None:
         o = torch.empty(B, H, dv, device=dev, dtype=o_dtype)
+    else:
+        _check(o, "o", None, dev)
+        if o.shape != (B, H, dv):
+            raise ValueError("libkda: o must be [B,H,d_v]")
     st = lib.kda_decode_step_gated(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(z), _ptr(A), _ptr(beta),
                                    _ptr(S), _ptr(o), _dtype_code(o), B, H, dk, dv, _stream(dev, stream))
     if st != 0:

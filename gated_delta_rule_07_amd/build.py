@@ -17,6 +17,7 @@ PKG = Path(__file__).resolve().parent
 CSRC = PKG / "csrc"
 INCLUDE = PKG.parent / "include"
 LIB = PKG / "libkda.so"
+TEST_LIB = PKG / "libkda_testhooks.so"
 OBJDIR = PKG / "_build"
 
 SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_prefill.hip", "kda_prefill_pipe.hip", "kda_spec.hip",
@@ -35,9 +36,9 @@ def hipcc() -> str:
     return path
 
 
-def _compile(src: str, verbose: bool) -> Path:
-    out = OBJDIR / (Path(src).stem + ".o")
-    cmd = [hipcc(), *COMMON, *DEVICE_FLAGS, "-c", str(CSRC / src), "-o", str(out)]
+def _compile(src: str, verbose: bool, defines=()) -> Path:
+    out = OBJDIR / (Path(src).stem + ("_hooks" if defines else "") + ".o")
+    cmd = [hipcc(), *COMMON, *DEVICE_FLAGS, *defines, "-c", str(CSRC / src), "-o", str(out)]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     if verbose:
@@ -48,20 +49,31 @@ def _compile(src: str, verbose: bool) -> Path:
     return out
 
 
-def build(verbose: bool = False, jobs: int | None = None) -> Path:
-    """Compile every source and link libkda.so; always rebuilds."""
-    OBJDIR.mkdir(exist_ok=True)
-    jobs = jobs or min(len(SOURCES), max(1, os.cpu_count() or 1))
-    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB.with_suffix(".so.tmp%d" % os.getpid())
+def _link(objs, lib: Path, verbose: bool) -> None:
+    tmp = lib.with_suffix(".so.tmp%d" % os.getpid())
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *map(str, objs), "-o", str(tmp)]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False, jobs: int | None = None) -> Path:
+    """Compile every source and link libkda.so; always rebuilds.
+
+    Also links libkda_testhooks.so: the same kernels with the C ABI compiled
+    with KDA_TEST_HOOKS, which adds kda_test_force_prefill (the tests use it to
+    run the generic kernel on shapes the pipelined kernel would serve).  The
+    product library carries no such switch."""
+    OBJDIR.mkdir(exist_ok=True)
+    jobs = jobs or min(len(SOURCES) + 1, max(1, os.cpu_count() or 1))
+    units = [(s, ()) for s in SOURCES] + [("kda_api.cpp", ("-DKDA_TEST_HOOKS",))]
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda u: _compile(u[0], verbose, u[1]), units))
+    _link(objs[:len(SOURCES)], LIB, verbose)
+    _link([objs[-1]] + objs[1:len(SOURCES)], TEST_LIB, verbose)
     return LIB
 
 

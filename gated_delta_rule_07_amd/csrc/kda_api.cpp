@@ -5,7 +5,6 @@
 // the calls return without synchronising.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
-#include <stdlib.h>
 #include <string.h>
 
 #include "../../include/kda.h"
@@ -15,9 +14,23 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
-constexpr int kVersion = 100;  // 0.1.0
+constexpr int kVersion = 200;  // 0.2.0
 
 bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+// A C caller may pass any int where the header says kda_dtype or kda_status;
+// reading such a value as the C++ enum type is undefined, so it is read as the
+// integer it is.
+// (Taken by reference: passing it by value would already read it as the enum.)
+template <typename E>
+int raw_enum(const E& e) {
+  static_assert(sizeof(E) == sizeof(int), "enum size");
+  int v;
+  memcpy(&v, &e, sizeof v);
+  return v;
+}
+bool dtype_ok(int d) { return d == KDA_F32 || d == KDA_BF16; }
+int io_of(int d) { return d == KDA_BF16 ? 1 : 0; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 struct Span {
@@ -44,23 +57,27 @@ bool sizes_ok(long long B, long long T, long long H, long long dk, long long dv)
 // {64,128}, d_v % 32 == 0 and chunk 32 or 64 (it runs 32-token chunks); the
 // generic 16x16-tile kernel serves everything else, with 16 state columns per
 // workgroup unless 32-column slabs still give one workgroup per compute unit.
-// KDA_PREFILL_IMPL=generic selects the generic kernel where the pipeline one
-// would apply, and KDA_PREFILL_SLAB=16 or 32 the generic kernel's slab width
-// (both for tests and measurements).
 enum PrefillImpl { IMPL_GENERIC, IMPL_PIPE };
 struct PrefillPlan {
   PrefillImpl impl;
   int slab;
 };
+
+#ifdef KDA_TEST_HOOKS
+// Test builds only (libkda_testhooks.so): a process-wide override of the kernel
+// choice, so tests can run the generic kernel on shapes the pipeline kernel
+// would take and pick its slab width.  The product library has no such state.
+int g_force_impl = -1;  // -1: the library's choice; 0: generic; 1: pipeline
+int g_force_slab = 0;   // 0: the library's choice; 16 or 32
+#endif
+
 PrefillPlan plan_prefill(int B, int H, int dk, int dv, int chunk, int io) {
-  int forced = 0;
-  if (const char* env = getenv("KDA_PREFILL_SLAB")) {
-    const int s = atoi(env);
-    if ((s == 16 || s == 32) && dv % s == 0) forced = s;
-  }
-  const char* impl = getenv("KDA_PREFILL_IMPL");
-  const bool want_generic = impl && strcmp(impl, "generic") == 0;
-  if (!want_generic && !forced && kda::prefill_pipe_supported(io, dk, dv, chunk, H)) return {IMPL_PIPE, 32};
+  int impl = -1, forced = 0;
+#ifdef KDA_TEST_HOOKS
+  impl = g_force_impl;
+  if ((g_force_slab == 16 || g_force_slab == 32) && dv % g_force_slab == 0) forced = g_force_slab;
+#endif
+  if (impl != 0 && !forced && kda::prefill_pipe_supported(io, dk, dv, chunk, H)) return {IMPL_PIPE, 32};
   if (forced) return {IMPL_GENERIC, forced};
   if (io == 1 && dv % 32 == 0 && (long long)B * H * (dv / 32) >= 256) return {IMPL_GENERIC, 32};
   return {IMPL_GENERIC, 16};
@@ -148,7 +165,7 @@ struct SplitReq {
 extern "C" {
 
 const char* kda_status_string(kda_status s) {
-  switch (s) {
+  switch (raw_enum(s)) {
     case KDA_OK: return "KDA_OK: success";
     case KDA_ERR_NULL: return "KDA_ERR_NULL: a required pointer is NULL";
     case KDA_ERR_SHAPE: return "KDA_ERR_SHAPE: invalid B/T/H or sizes too large";
@@ -165,6 +182,16 @@ int kda_last_hip_error(void) { return g_last_hip_error; }
 
 int kda_version(void) { return kVersion; }
 
+#ifdef KDA_TEST_HOOKS
+// Test builds only: force the prefill kernel (impl -1: the library's choice, 0:
+// the generic kernel, 1: the pipeline kernel where it applies) and the generic
+// kernel's slab width (0: the library's choice, 16 or 32).  Not thread-safe.
+void kda_test_force_prefill(int impl, int slab) {
+  g_force_impl = impl;
+  g_force_slab = slab;
+}
+#endif
+
 }  // extern "C"
 
 namespace {
@@ -173,13 +200,13 @@ namespace {
 // cu != NULL: a packed batch of B sequences over T token rows (T = the packed
 // length); otherwise B sequences of T tokens each.
 // z != NULL: fused gate (alpha formed from z and A in the kernels; alpha unused).
-kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, kda_dtype qkv_dtype, const float* alpha,
-                          const float* beta, const float* S0, void* o, kda_dtype o_dtype, float* S_T,
+kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, int qkv_dtype, const float* alpha,
+                          const float* beta, const float* S0, void* o, int o_dtype, float* S_T,
                           const int* snap_tokens, int n_snap, float* snaps, const int* cu, const void* z,
-                          const float* A, int B, int T, int H, int d_k, int d_v, int chunk, void* stream,
+                          const float* A, int B, int T, int H, int d_k, int d_v, int chunk, hipStream_t stream,
                           const SplitReq* split = nullptr) {
-  if (qkv_dtype != KDA_F32 && qkv_dtype != KDA_BF16) return KDA_ERR_DTYPE;
-  if (o_dtype != KDA_F32 && o_dtype != KDA_BF16) return KDA_ERR_DTYPE;
+  if (!dtype_ok(qkv_dtype)) return KDA_ERR_DTYPE;
+  if (!dtype_ok(o_dtype)) return KDA_ERR_DTYPE;
   if (B < 1 || H < 1 || T < 0) return KDA_ERR_SHAPE;
   if (!dim_ok(d_k) || !dim_ok(d_v)) return KDA_ERR_UNSUPPORTED;
   if (chunk != 16 && chunk != 32 && chunk != 64) return KDA_ERR_UNSUPPORTED;
@@ -199,12 +226,12 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, kda_dtype
   const void* ptrs[] = {q, k, v, alpha, beta, S0, o, S_T, n_snap > 0 ? snaps : nullptr, cu, z, A};
   for (const void* ptr : ptrs)
     if (ptr && !aligned16(ptr)) return KDA_ERR_MISALIGNED;
-  const int io = (qkv_dtype == KDA_BF16) ? 1 : 0;
+  const int io = io_of(qkv_dtype);
   const PrefillPlan plan = plan_prefill(B, H, d_k, d_v, chunk, io);
   if (plan.impl == IMPL_GENERIC && !kda::prefill_supported(io, d_k, chunk, plan.slab)) return KDA_ERR_UNSUPPORTED;
 
-  const size_t esz = (qkv_dtype == KDA_BF16) ? 2 : 4;
-  const size_t osz = (o_dtype == KDA_BF16) ? 2 : 4;
+  const size_t esz = io_of(qkv_dtype) ? 2 : 4;
+  const size_t osz = io_of(o_dtype) ? 2 : 4;
   const size_t ntok = (size_t)(cu ? 1 : B) * T * H;
   const size_t sbytes = (size_t)B * H * d_k * d_v * 4;
   const Span none{0, 0};
@@ -255,10 +282,10 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, kda_dtype
     ws = static_cast<char*>(split->ws);
   }
 
-  kda::PrefillParams p{q, k, v, alpha, beta, S0, o, S_T, B, T, H, d_k, d_v, o_dtype == KDA_F32 ? 1 : 0,
+  kda::PrefillParams p{q, k, v, alpha, beta, S0, o, S_T, B, T, H, d_k, d_v, io_of(o_dtype) ? 0 : 1,
                        n_snap > 0 ? snaps : nullptr, n_snap, cu, T > 0 ? z : nullptr, A,
                        /*split*/ 0, /*nparts*/ 0, /*part_len*/ 0, nullptr, nullptr, nullptr};
-  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  const hipStream_t hs = stream;
   hipError_t e;
   if (sh.parts > 1) {
     // pass 1: (N | M) of parts 0..P-2; combine: the state entering each part;
@@ -293,8 +320,8 @@ extern "C" {
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
                          const float* alpha, const float* beta, const float* S0,
                          void* o, kda_dtype o_dtype, float* S_T,
-                         int B, int T, int H, int d_k, int d_v, int chunk, void* stream) {
-  return chunk_fwd_impl(q, k, v, qkv_dtype, alpha, beta, S0, o, o_dtype, S_T, nullptr, 0, nullptr, nullptr, nullptr,
+                         int B, int T, int H, int d_k, int d_v, int chunk, hipStream_t stream) {
+  return chunk_fwd_impl(q, k, v, raw_enum(qkv_dtype), alpha, beta, S0, o, raw_enum(o_dtype), S_T, nullptr, 0, nullptr, nullptr, nullptr,
                         nullptr, B, T, H, d_k, d_v, chunk, stream);
 }
 
@@ -302,8 +329,8 @@ kda_status kda_chunk_fwd_snapshots(const void* q, const void* k, const void* v, 
                                    const float* alpha, const float* beta, const float* S0,
                                    void* o, kda_dtype o_dtype, float* S_T,
                                    const int* snap_tokens, int n_snap, float* snaps,
-                                   int B, int T, int H, int d_k, int d_v, int chunk, void* stream) {
-  return chunk_fwd_impl(q, k, v, qkv_dtype, alpha, beta, S0, o, o_dtype, S_T, snap_tokens, n_snap, snaps, nullptr,
+                                   int B, int T, int H, int d_k, int d_v, int chunk, hipStream_t stream) {
+  return chunk_fwd_impl(q, k, v, raw_enum(qkv_dtype), alpha, beta, S0, o, raw_enum(o_dtype), S_T, snap_tokens, n_snap, snaps, nullptr,
                         nullptr, nullptr, B, T, H, d_k, d_v, chunk, stream);
 }
 
@@ -311,30 +338,48 @@ kda_status kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, kda
                                 const float* alpha, const float* beta, const float* S0,
                                 void* o, kda_dtype o_dtype, float* S_T,
                                 const int* cu_seqlens, int N, int total_T,
-                                int H, int d_k, int d_v, int chunk, void* stream) {
+                                int H, int d_k, int d_v, int chunk, hipStream_t stream) {
   if (!cu_seqlens) return KDA_ERR_NULL;
-  return chunk_fwd_impl(q, k, v, qkv_dtype, alpha, beta, S0, o, o_dtype, S_T, nullptr, 0, nullptr, cu_seqlens,
+  return chunk_fwd_impl(q, k, v, raw_enum(qkv_dtype), alpha, beta, S0, o, raw_enum(o_dtype), S_T, nullptr, 0, nullptr, cu_seqlens,
                         nullptr, nullptr, N, total_T, H, d_k, d_v, chunk, stream);
 }
 
 kda_status kda_chunk_fwd_gated(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
                                const void* z, const float* A, const float* beta, const float* S0,
                                void* o, kda_dtype o_dtype, float* S_T,
-                               int B, int T, int H, int d_k, int d_v, int chunk, void* stream) {
+                               int B, int T, int H, int d_k, int d_v, int chunk, hipStream_t stream) {
   if (T > 0 && !z) return KDA_ERR_NULL;
-  return chunk_fwd_impl(q, k, v, qkv_dtype, nullptr, beta, S0, o, o_dtype, S_T, nullptr, 0, nullptr, nullptr, z, A,
+  return chunk_fwd_impl(q, k, v, raw_enum(qkv_dtype), nullptr, beta, S0, o, raw_enum(o_dtype), S_T, nullptr, 0, nullptr, nullptr, z, A,
                         B, T, H, d_k, d_v, chunk, stream);
+}
+
+kda_status kda_chunk_fwd_run_chunk(kda_dtype qkv_dtype, int H, int d_k, int d_v, int chunk, int* run_chunk) {
+  if (!dtype_ok(raw_enum(qkv_dtype))) return KDA_ERR_DTYPE;
+  if (H < 1) return KDA_ERR_SHAPE;
+  if (!dim_ok(d_k) || !dim_ok(d_v)) return KDA_ERR_UNSUPPORTED;
+  if (chunk != 16 && chunk != 32 && chunk != 64) return KDA_ERR_UNSUPPORTED;
+  if (!run_chunk) return KDA_ERR_NULL;
+  const int io = io_of(raw_enum(qkv_dtype));
+  const PrefillPlan plan = plan_prefill(1, H, d_k, d_v, chunk, io);
+  if (plan.impl == IMPL_PIPE) {
+    *run_chunk = kda::kPipeChunk;
+    return KDA_OK;
+  }
+  const int run = kda::prefill_run_chunk(io, d_k, chunk, plan.slab);
+  if (run <= 0) return KDA_ERR_UNSUPPORTED;
+  *run_chunk = run;
+  return KDA_OK;
 }
 
 kda_status kda_chunk_fwd_split_plan(kda_dtype qkv_dtype, int B, int T, int H, int d_k, int d_v, int chunk,
                                     int parts, int num_cus, int* parts_out, size_t* workspace_bytes) {
-  if (qkv_dtype != KDA_F32 && qkv_dtype != KDA_BF16) return KDA_ERR_DTYPE;
+  if (!dtype_ok(raw_enum(qkv_dtype))) return KDA_ERR_DTYPE;
   if (B < 1 || H < 1 || T < 0 || parts < 0 || num_cus < 0) return KDA_ERR_SHAPE;
   if (!dim_ok(d_k) || !dim_ok(d_v)) return KDA_ERR_UNSUPPORTED;
   if (chunk != 16 && chunk != 32 && chunk != 64) return KDA_ERR_UNSUPPORTED;
   if (!sizes_ok(B, T, H, d_k, d_v)) return KDA_ERR_SHAPE;
   if (!parts_out || !workspace_bytes) return KDA_ERR_NULL;
-  const int io = (qkv_dtype == KDA_BF16) ? 1 : 0;
+  const int io = io_of(raw_enum(qkv_dtype));
   SplitShape sh{1, T};
   if (plan_prefill(B, H, d_k, d_v, chunk, io).impl != IMPL_PIPE) {
     if (parts > 1) return KDA_ERR_UNSUPPORTED;
@@ -357,9 +402,9 @@ kda_status kda_chunk_fwd_split(const void* q, const void* k, const void* v, kda_
                                const float* alpha, const float* beta, const float* S0,
                                void* o, kda_dtype o_dtype, float* S_T,
                                int B, int T, int H, int d_k, int d_v, int chunk,
-                               int parts, int num_cus, void* workspace, size_t workspace_bytes, void* stream) {
+                               int parts, int num_cus, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   const SplitReq req{parts, num_cus, workspace, workspace_bytes};
-  return chunk_fwd_impl(q, k, v, qkv_dtype, alpha, beta, S0, o, o_dtype, S_T, nullptr, 0, nullptr, nullptr,
+  return chunk_fwd_impl(q, k, v, raw_enum(qkv_dtype), alpha, beta, S0, o, raw_enum(o_dtype), S_T, nullptr, 0, nullptr, nullptr,
                         nullptr, nullptr, B, T, H, d_k, d_v, chunk, stream, &req);
 }
 
@@ -368,11 +413,11 @@ kda_status kda_chunk_fwd_split(const void* q, const void* k, const void* v, kda_
 namespace {
 
 // z != NULL: fused gate, as chunk_fwd_impl.
-kda_status decode_impl(const void* q, const void* k, const void* v, kda_dtype qkv_dtype, const float* alpha,
-                       const void* z, const float* A, const float* beta, float* S, void* o, kda_dtype o_dtype,
-                       int B, int H, int d_k, int d_v, void* stream) {
-  if (qkv_dtype != KDA_F32 && qkv_dtype != KDA_BF16) return KDA_ERR_DTYPE;
-  if (o_dtype != KDA_F32 && o_dtype != KDA_BF16) return KDA_ERR_DTYPE;
+kda_status decode_impl(const void* q, const void* k, const void* v, int qkv_dtype, const float* alpha,
+                       const void* z, const float* A, const float* beta, float* S, void* o, int o_dtype,
+                       int B, int H, int d_k, int d_v, hipStream_t stream) {
+  if (!dtype_ok(qkv_dtype)) return KDA_ERR_DTYPE;
+  if (!dtype_ok(o_dtype)) return KDA_ERR_DTYPE;
   if (B < 1 || H < 1) return KDA_ERR_SHAPE;
   if (!dim_ok(d_k) || !dim_ok(d_v)) return KDA_ERR_UNSUPPORTED;
   if (!sizes_ok(B, 1, H, d_k, d_v)) return KDA_ERR_SHAPE;
@@ -381,11 +426,11 @@ kda_status decode_impl(const void* q, const void* k, const void* v, kda_dtype qk
   const void* ptrs[] = {q, k, v, alpha, beta, S, o, z, A};
   for (const void* ptr : ptrs)
     if (ptr && !aligned16(ptr)) return KDA_ERR_MISALIGNED;
-  const int io = (qkv_dtype == KDA_BF16) ? 1 : 0;
+  const int io = io_of(qkv_dtype);
   if (!kda::decode_supported(io, d_k, d_v)) return KDA_ERR_UNSUPPORTED;
 
-  const size_t esz = (qkv_dtype == KDA_BF16) ? 2 : 4;
-  const size_t osz = (o_dtype == KDA_BF16) ? 2 : 4;
+  const size_t esz = io_of(qkv_dtype) ? 2 : 4;
+  const size_t osz = io_of(o_dtype) ? 2 : 4;
   const size_t nbh = (size_t)B * H;
   const Span so = span(o, nbh * d_v * osz);
   const Span ss = span(S, nbh * d_k * d_v * 4);
@@ -396,8 +441,8 @@ kda_status decode_impl(const void* q, const void* k, const void* v, kda_dtype qk
   for (const Span& s : ins)
     if (overlap(so, s) || overlap(ss, s)) return KDA_ERR_ALIAS;
 
-  kda::DecodeParams p{q, k, v, alpha, beta, S, o, B, H, d_k, d_v, o_dtype == KDA_F32 ? 1 : 0, z, A};
-  const hipError_t e = kda::launch_decode(p, io, static_cast<hipStream_t>(stream));
+  kda::DecodeParams p{q, k, v, alpha, beta, S, o, B, H, d_k, d_v, io_of(o_dtype) ? 0 : 1, z, A};
+  const hipError_t e = kda::launch_decode(p, io, stream);
   if (e != hipSuccess) {
     g_last_hip_error = (int)e;
     return KDA_ERR_HIP;
@@ -411,23 +456,23 @@ extern "C" {
 
 kda_status kda_decode_step(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
                            const float* alpha, const float* beta, float* S, void* o, kda_dtype o_dtype,
-                           int B, int H, int d_k, int d_v, void* stream) {
-  return decode_impl(q, k, v, qkv_dtype, alpha, nullptr, nullptr, beta, S, o, o_dtype, B, H, d_k, d_v, stream);
+                           int B, int H, int d_k, int d_v, hipStream_t stream) {
+  return decode_impl(q, k, v, raw_enum(qkv_dtype), alpha, nullptr, nullptr, beta, S, o, raw_enum(o_dtype), B, H, d_k, d_v, stream);
 }
 
 kda_status kda_decode_step_gated(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
                                  const void* z, const float* A, const float* beta, float* S, void* o,
-                                 kda_dtype o_dtype, int B, int H, int d_k, int d_v, void* stream) {
+                                 kda_dtype o_dtype, int B, int H, int d_k, int d_v, hipStream_t stream) {
   if (!z) return KDA_ERR_NULL;
-  return decode_impl(q, k, v, qkv_dtype, nullptr, z, A, beta, S, o, o_dtype, B, H, d_k, d_v, stream);
+  return decode_impl(q, k, v, raw_enum(qkv_dtype), nullptr, z, A, beta, S, o, raw_enum(o_dtype), B, H, d_k, d_v, stream);
 }
 
 kda_status kda_decode_verify(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
                              const float* alpha, const float* beta, const float* S,
                              void* o, kda_dtype o_dtype, float* u,
-                             int B, int K, int H, int d_k, int d_v, void* stream) {
-  if (qkv_dtype != KDA_F32 && qkv_dtype != KDA_BF16) return KDA_ERR_DTYPE;
-  if (o_dtype != KDA_F32 && o_dtype != KDA_BF16) return KDA_ERR_DTYPE;
+                             int B, int K, int H, int d_k, int d_v, hipStream_t stream) {
+  if (!dtype_ok(raw_enum(qkv_dtype))) return KDA_ERR_DTYPE;
+  if (!dtype_ok(raw_enum(o_dtype))) return KDA_ERR_DTYPE;
   if (B < 1 || H < 1 || K < 1 || K > KDA_MAX_DRAFT) return KDA_ERR_SHAPE;
   if (!dim_ok(d_k) || !dim_ok(d_v)) return KDA_ERR_UNSUPPORTED;
   if (!sizes_ok(B, K, H, d_k, d_v)) return KDA_ERR_SHAPE;
@@ -435,11 +480,11 @@ kda_status kda_decode_verify(const void* q, const void* k, const void* v, kda_dt
   const void* ptrs[] = {q, k, v, alpha, beta, S, o, u};
   for (const void* ptr : ptrs)
     if (!aligned16(ptr)) return KDA_ERR_MISALIGNED;
-  const int io = (qkv_dtype == KDA_BF16) ? 1 : 0;
+  const int io = io_of(raw_enum(qkv_dtype));
   if (!kda::spec_supported(io, d_k, d_v)) return KDA_ERR_UNSUPPORTED;
 
-  const size_t esz = (qkv_dtype == KDA_BF16) ? 2 : 4;
-  const size_t osz = (o_dtype == KDA_BF16) ? 2 : 4;
+  const size_t esz = io_of(raw_enum(qkv_dtype)) ? 2 : 4;
+  const size_t osz = io_of(raw_enum(o_dtype)) ? 2 : 4;
   const size_t ntok = (size_t)B * K * H;
   const Span ins[] = {span(q, ntok * d_k * esz), span(k, ntok * d_k * esz), span(v, ntok * d_v * esz),
                       span(alpha, ntok * d_k * 4), span(beta, ntok * 4), span(S, (size_t)B * H * d_k * d_v * 4)};
@@ -448,8 +493,8 @@ kda_status kda_decode_verify(const void* q, const void* k, const void* v, kda_dt
   for (const Span& s : ins)
     if (overlap(so, s) || overlap(su, s)) return KDA_ERR_ALIAS;
 
-  kda::VerifyParams p{q, k, v, alpha, beta, S, o, u, B, K, H, d_k, d_v, o_dtype == KDA_F32 ? 1 : 0};
-  const hipError_t e = kda::launch_verify(p, io, static_cast<hipStream_t>(stream));
+  kda::VerifyParams p{q, k, v, alpha, beta, S, o, u, B, K, H, d_k, d_v, io_of(raw_enum(o_dtype)) ? 0 : 1};
+  const hipError_t e = kda::launch_verify(p, io, stream);
   if (e != hipSuccess) {
     g_last_hip_error = (int)e;
     return KDA_ERR_HIP;
@@ -459,8 +504,8 @@ kda_status kda_decode_verify(const void* q, const void* k, const void* v, kda_dt
 
 kda_status kda_decode_commit(const void* k, kda_dtype qkv_dtype, const float* alpha, const float* u,
                              const int* n_accept, float* S,
-                             int B, int K, int H, int d_k, int d_v, void* stream) {
-  if (qkv_dtype != KDA_F32 && qkv_dtype != KDA_BF16) return KDA_ERR_DTYPE;
+                             int B, int K, int H, int d_k, int d_v, hipStream_t stream) {
+  if (!dtype_ok(raw_enum(qkv_dtype))) return KDA_ERR_DTYPE;
   if (B < 1 || H < 1 || K < 1 || K > KDA_MAX_DRAFT) return KDA_ERR_SHAPE;
   if (!dim_ok(d_k) || !dim_ok(d_v)) return KDA_ERR_UNSUPPORTED;
   if (!sizes_ok(B, K, H, d_k, d_v)) return KDA_ERR_SHAPE;
@@ -468,10 +513,10 @@ kda_status kda_decode_commit(const void* k, kda_dtype qkv_dtype, const float* al
   const void* ptrs[] = {k, alpha, u, n_accept, S};
   for (const void* ptr : ptrs)
     if (!aligned16(ptr)) return KDA_ERR_MISALIGNED;
-  const int io = (qkv_dtype == KDA_BF16) ? 1 : 0;
+  const int io = io_of(raw_enum(qkv_dtype));
   if (!kda::spec_supported(io, d_k, d_v)) return KDA_ERR_UNSUPPORTED;
 
-  const size_t esz = (qkv_dtype == KDA_BF16) ? 2 : 4;
+  const size_t esz = io_of(raw_enum(qkv_dtype)) ? 2 : 4;
   const size_t ntok = (size_t)B * K * H;
   const Span ss = span(S, (size_t)B * H * d_k * d_v * 4);
   const Span ins[] = {span(k, ntok * d_k * esz), span(alpha, ntok * d_k * 4), span(u, ntok * d_v * 4),
@@ -480,7 +525,7 @@ kda_status kda_decode_commit(const void* k, kda_dtype qkv_dtype, const float* al
     if (overlap(ss, s)) return KDA_ERR_ALIAS;
 
   kda::CommitParams p{k, alpha, u, n_accept, S, B, K, H, d_k, d_v};
-  const hipError_t e = kda::launch_commit(p, io, static_cast<hipStream_t>(stream));
+  const hipError_t e = kda::launch_commit(p, io, stream);
   if (e != hipSuccess) {
     g_last_hip_error = (int)e;
     return KDA_ERR_HIP;

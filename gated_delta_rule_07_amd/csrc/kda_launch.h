@@ -134,11 +134,14 @@ struct DecodeParams {
 // workgroup owns (16, 32 or 64).  Returns hipErrorInvalidValue when no kernel is
 // built for the combination.
 bool prefill_supported(int io_dtype, int dk, int chunk, int slab);
+// Tokens per chunk the generic kernel runs for a requested chunk size (0: not built).
+int prefill_run_chunk(int io_dtype, int dk, int chunk, int slab);
 hipError_t launch_prefill(const PrefillParams& p, const SnapList& snap, int io_dtype, int chunk, int slab,
                           hipStream_t s);
 
 // Warp-specialised pipeline prefill (bf16 q/k/v, d_k in {64,128}, d_v % 32 == 0,
-// requested chunk 32 or 64; runs 32-token chunks).
+// requested chunk 32 or 64; runs kPipeChunk-token chunks).
+constexpr int kPipeChunk = 32;
 bool prefill_pipe_supported(int io_dtype, int dk, int dv, int chunk, int H);
 hipError_t launch_prefill_pipe(const PrefillParams& p, const SnapList& snap, hipStream_t s);
 

@@ -39,10 +39,6 @@
 #include "kda_device.h"
 #include "kda_launch.h"
 
-// Phase boundary hook for external instrumentation builds; compiles to nothing here.
-#ifndef KDA_PHASE_MARK
-#define KDA_PHASE_MARK(i)
-#endif
 
 namespace kda {
 namespace {
@@ -582,21 +578,15 @@ __device__ bool process_chunk(Smem<C>& sm, Raw<C>& raw, f32x4 (&S)[C::NKT], cons
 #pragma unroll
   for (int hh = 0; hh < C::NH; ++hh) {
     block_sync_lds();
-    KDA_PHASE_MARK(0);
     if (phase_scan<C>(sm, raw, hh, lo, hi, check, cx.eA, cx.p.z != nullptr, tid)) return false;
     if (hh == C::NH - 1 && prefetch_t0 >= 0) load_raw<C>(raw, cx, prefetch_t0, tid);
     block_sync_lds();
-    KDA_PHASE_MARK(1);
     phase_lp<C>(sm, acc, wave, lane, blo, bhi);
-    KDA_PHASE_MARK(2);
   }
   lp_epilogue<C>(sm, acc, wave, lane);
   block_sync_lds();
-  KDA_PHASE_MARK(3);
   phase_solve<C>(sm, tid, wave, lane);
-  KDA_PHASE_MARK(4);
   if (wave < C::NSW) phase_state<C>(sm, S, wave, lane, cx, t0, lo, hi);
-  KDA_PHASE_MARK(5);
   return true;
 }
 
@@ -683,7 +673,7 @@ hipError_t launch_one(const PrefillParams& p, const SnapList& snap, hipStream_t 
 
 typedef hipError_t (*launch_fn)(const PrefillParams&, const SnapList&, hipStream_t);
 
-// Instantiated kernels: bf16 for d_k in {16,32,64,128}, fp32 for d_k in {16,32};
+// Instantiated kernels: bf16 and fp32 for d_k in {16,32,64,128} (fp32 with 16-column slabs);
 // slabs of 16 or 32 columns; chunks of 16, 32 or 64 tokens.
 template <typename IO, int DK, int J>
 launch_fn pick_chunk(int chunk) {
@@ -691,6 +681,16 @@ launch_fn pick_chunk(int chunk) {
     case 16: return &launch_one<IO, DK, J, 16>;
     case 32: return &launch_one<IO, DK, J, 32>;
     case 64: return &launch_one<IO, DK, J, 64>;
+    default: return nullptr;
+  }
+}
+
+template <typename IO, int DK, int J>
+launch_fn pick_chunk_upto32(int chunk) {
+  switch (chunk) {
+    case 16: return &launch_one<IO, DK, J, 16>;
+    case 32:
+    case 64: return &launch_one<IO, DK, J, 32>;
     default: return nullptr;
   }
 }
@@ -718,6 +718,11 @@ launch_fn pick(int io_dtype, int dk, int chunk, int slab) {
     switch (dk) {
       case 16: return pick_chunk<float, 16, 16>(chunk);
       case 32: return pick_chunk<float, 32, 16>(chunk);
+      // fp32 stages of 64-token chunks do not fit the 160 KB of LDS at these key
+      // sizes: chunk 64 runs as 32-token chunks (the result does not depend on
+      // the chunk size beyond rounding)
+      case 64: return pick_chunk_upto32<float, 64, 16>(chunk);
+      case 128: return pick_chunk_upto32<float, 128, 16>(chunk);
       default: return nullptr;
     }
   }
@@ -728,6 +733,11 @@ launch_fn pick(int io_dtype, int dk, int chunk, int slab) {
 
 bool prefill_supported(int io_dtype, int dk, int chunk, int slab) {
   return pick(io_dtype, dk, chunk, slab) != nullptr;
+}
+
+int prefill_run_chunk(int io_dtype, int dk, int chunk, int slab) {
+  if (!prefill_supported(io_dtype, dk, chunk, slab)) return 0;
+  return (io_dtype == 0 && dk >= 64 && chunk == 64) ? 32 : chunk;
 }
 
 hipError_t launch_prefill(const PrefillParams& p, const SnapList& snap, int io_dtype, int chunk, int slab,

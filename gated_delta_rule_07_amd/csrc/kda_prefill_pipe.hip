@@ -39,15 +39,6 @@
 #include "kda_device.h"
 #include "kda_launch.h"
 
-#ifndef KDA_PHASE_MARK
-#define KDA_PHASE_MARK(i)
-#endif
-#ifndef KDA_STEP_MARK
-#define KDA_STEP_MARK(i, step)
-#endif
-#ifndef KDA_PROBE_VMWAIT
-#define KDA_PROBE_VMWAIT()
-#endif
 
 namespace kda {
 namespace {
@@ -58,7 +49,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int CS = 32;  // tokens per chunk
+constexpr int CS = kPipeChunk;  // tokens per chunk
 constexpr int J = 32;   // state columns per workgroup
 constexpr float STEEP = 4.5399930e-05f;  // e^{-10}
 
@@ -630,7 +621,6 @@ __device__ void state_step(Smem4<C>& sm, StateRegs<C>& R, const Item& it, int la
   const ScanSlot<C>& sl = sm.ss[it.seq % 3];
   const h16* tt = sm.t[it.seq % 2];
   const int h = opaque(lane / 32), n = opaque(lane % 32);
-  KDA_PHASE_MARK(7);
   // operands first, so their reads overlap the products
   f16x8 A[C::NKS];
 #pragma unroll
@@ -658,7 +648,6 @@ __device__ void state_step(Smem4<C>& sm, StateRegs<C>& R, const Item& it, int la
     KH[ct][0] = ld8(&sl.kh[row]);
     KH[ct][1] = ld8(&sl.kh[row + 16]);
   }
-  KDA_PHASE_MARK(8);
   // Un = T Xn
   const f16x8 x0 = bfrag(X, 0), x1 = bfrag(X, 1);
   f32x16 U = (f32x16)0.0f;
@@ -668,14 +657,12 @@ __device__ void state_step(Smem4<C>& sm, StateRegs<C>& R, const Item& it, int la
   h16* uf = sm.uf[it.seq % 2];
   *reinterpret_cast<f16x8*>(&uf[lane * 8]) = u0;
   *reinterpret_cast<f16x8*>(&uf[(64 + lane) * 8]) = u1;
-  KDA_PHASE_MARK(9);
   // S' = gamma S + (-KH)^T Un
 #pragma unroll
   for (int ct = 0; ct < C::NKT; ++ct) {
     R.S[ct] = mma32(KH[ct][0], u0, R.S[ct]);
     R.S[ct] = mma32(KH[ct][1], u1, R.S[ct]);
   }
-  KDA_PHASE_MARK(10);
 }
 
 // Prepares item `it` (next for the state wave): column scale, fp16 fragments of
@@ -684,7 +671,6 @@ template <class C>
 __device__ void state_prepare(Smem4<C>& sm, StateRegs<C>& R, const Item& it, int lane) {
   const ScanSlot<C>& sl = sm.ss[it.seq % 3];
   const int h = opaque(lane / 32), n = opaque(lane % 32);
-  KDA_PHASE_MARK(11);
   float vf[16];
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {  // rows 8jj + 4h .. +3 of column n
@@ -728,7 +714,6 @@ __device__ void state_prepare(Smem4<C>& sm, StateRegs<C>& R, const Item& it, int
     *reinterpret_cast<f16x8*>(&sf[(s * 64 + lane) * 8]) = R.Sf[s];
   }
   if (h == 0) sm.sexp[it.seq % 2][n] = __builtin_amdgcn_rcpf(R.sc);
-  KDA_PHASE_MARK(12);
 }
 
 // ---- output wave -------------------------------------------------------------------------
@@ -858,20 +843,15 @@ __device__ void run_role(Smem4<C>& sm, const Ctx4& cx, const SnapList& snap, int
   Item sI = none, bI = none, stI = none, opI = none;
   if (cx.nchunks > 0) sI = Item{0, 0, 0, chunk_end(0, cx.T), CS};
   int par = 0;
-  [[maybe_unused]] int kstep = 0;  // step count, for step timestamps in instrumented builds
-  int ns = 0;                      // state role: next recorded position
+  int ns = 0;  // state role: next recorded position
   while (sI.seq >= 0 || bI.seq >= 0 || stI.seq >= 0 || opI.seq >= 0) {
-    KDA_STEP_MARK(0, kstep);
     if constexpr (ROLE == SCAN) {
       if (sI.seq >= 0) {
         if (rc != sI.c) {
           load_raw4<C, G>(raw, cx, src, sI.c, sw);
           rc = sI.c;
         }
-        KDA_PROBE_VMWAIT();
-        KDA_STEP_MARK(2, kstep);
         scan4<C, G>(sm, raw, sI, cx.eA, sw, lane, par);
-        KDA_STEP_MARK(3, kstep);
         if (sI.hi == chunk_end(sI.c, cx.T) && sI.c + 1 < cx.nchunks) {
           load_raw4<C, G>(raw, cx, src, sI.c + 1, sw);  // prefetch the next chunk
           rc = sI.c + 1;
@@ -894,21 +874,16 @@ __device__ void run_role(Smem4<C>& sm, const Ctx4& cx, const SnapList& snap, int
           __builtin_amdgcn_s_waitcnt(kVmcnt0);
         }
       }
-      KDA_STEP_MARK(2, kstep);
       if (bI.seq >= 0) state_prepare<C>(sm, R, bI, lane);
     } else {
       if (opI.seq >= 0) out_pu_store<C>(sm, O, usc, opI, cx, lane);
-      KDA_STEP_MARK(2, kstep);
       if (stI.seq >= 0) out_qs<C>(sm, O, usc, stI, lane);
     }
     // The scan item's successor is formed before the barrier, so after it only
     // the regroup vote remains to be read.
     Item nI = none;
     if (sI.seq >= 0) nI = next_item(sI, cx.T, cx.nchunks);
-    KDA_STEP_MARK(1, kstep);
     block_sync_lds();
-    KDA_STEP_MARK(4, kstep);
-    ++kstep;
     int first = CS;  // the scan waves' earliest out-of-range token, CS: none
     if (sI.seq >= 0) {
 #pragma unroll

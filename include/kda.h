@@ -15,16 +15,16 @@
  *  - All tensor pointers are DEVICE pointers (HIP global memory) owned by the
  *    caller.  The library allocates nothing and keeps no state beyond a
  *    thread-local copy of the last HIP error.  Calls are reentrant.
- *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Each
- *    call only enqueues work on that stream and returns without synchronising;
- *    a device-side fault surfaces at the caller's next synchronisation.
+ *  - `stream` is the hipStream_t the work is enqueued on (NULL = the default
+ *    stream).  Each call only enqueues work on that stream and returns without
+ *    synchronising; a device-side fault surfaces at the caller's next
+ *    synchronisation.
  *  - Layouts are dense, row-major, token-major: [B][T][H][d] for per-token
  *    tensors and [B][H][d_k][d_v] for states.
  *  - Every pointer must be 16-byte aligned.
  *  - Arguments are validated before any HIP call; on error nothing is enqueued
  *    and no output is touched.  Calls never abort and never throw.
- *  - Supported sizes: d_k, d_v in {16, 32, 64, 128}.  fp32 q/k/v are supported
- *    for d_k <= 32 (prefill) and any supported d_k (decode).
+ *  - Supported sizes: d_k, d_v in {16, 32, 64, 128}, for bf16 and fp32 q/k/v.
  *  - Arithmetic.  The state is carried in fp32 and every product accumulates in
  *    fp32.  With fp32 q/k/v all matrix-core operands are fp32.  With bf16 q/k/v
  *    the matrix-core operands are fp16: the decayed keys and queries (bounded by
@@ -43,6 +43,8 @@
 
 #include <stddef.h>
 
+#include <hip/hip_runtime_api.h> /* hipStream_t */
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -57,8 +59,7 @@ typedef enum {
   KDA_ERR_NULL = 1,        /* a required pointer is NULL */
   KDA_ERR_SHAPE = 2,       /* B, H < 1, T < 0, or a size overflows 2^31 elements per row index */
   KDA_ERR_DTYPE = 3,       /* qkv_dtype or o_dtype is not a kda_dtype */
-  KDA_ERR_UNSUPPORTED = 4, /* d_k/d_v not in {16,32,64,128}, chunk not in {16,32,64},
-                              or fp32 prefill with d_k > 32 */
+  KDA_ERR_UNSUPPORTED = 4, /* d_k/d_v not in {16,32,64,128} or chunk not in {16,32,64} */
   KDA_ERR_MISALIGNED = 5,  /* a pointer is not 16-byte aligned */
   KDA_ERR_ALIAS = 6,       /* an output overlaps an input it may not overlap */
   KDA_ERR_HIP = 7          /* the launch failed; kda_last_hip_error() holds the hipError_t */
@@ -79,14 +80,18 @@ typedef enum {
  *   beta   : [B][T][H]       fp32, write strength          (read)
  *   S0     : [B][H][d_k][d_v] fp32 initial state, or NULL for zeros   (read)
  *   o      : [B][T][H][d_v]  o_dtype, o_t for every token             (written)
- *   o_dtype: KDA_F32 or KDA_BF16.  With bf16 q/k/v, an fp32 o keeps the full
- *            accuracy; a bf16 o is that same fp32 value rounded to nearest even,
- *            and the rounding alone can reach 2^-9 of |o_t|.
+ *   o_dtype: KDA_F32 or KDA_BF16 (the q/k/v dtype is the usual choice).  A
+ *            bf16 o is exactly the fp32 result rounded to nearest even; that
+ *            rounding alone can reach 2^-8 of |o_t|, so an fp32 o keeps the full
+ *            accuracy of the fp32 state.
  *   S_T    : [B][H][d_k][d_v] fp32 final state, or NULL to skip       (written)
- *   chunk  : 16, 32 or 64 (64 is the intended size).  With bf16 q/k/v,
- *            d_k in {64, 128} and d_v a multiple of 32, chunk 32 and 64 both
- *            run the 32-token pipelined kernel; the result does not depend on
- *            the chunk size beyond rounding.
+ *   chunk  : 16, 32 or 64 (64 is the size the second page names).  The chunk
+ *            size a call actually runs: 32 for chunk 32 or 64 with bf16 q/k/v,
+ *            d_k in {64, 128} and d_v a multiple of 32 (the pipelined kernel,
+ *            whose stage rings of 64-token chunks would not fit the 160 KB of
+ *            LDS), and for chunk 64 with fp32 q/k/v and d_k in {64, 128} (same
+ *            reason); the requested size otherwise.  The result does not depend
+ *            on the chunk size beyond rounding.
  *
  * S0 == S_T (the same buffer) is allowed and updates the state in place; any
  * other overlap between an output and an input returns KDA_ERR_ALIAS.
@@ -96,7 +101,15 @@ typedef enum {
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
                          const float* alpha, const float* beta, const float* S0,
                          void* o, kda_dtype o_dtype, float* S_T,
-                         int B, int T, int H, int d_k, int d_v, int chunk, void* stream);
+                         int B, int T, int H, int d_k, int d_v, int chunk, hipStream_t stream);
+
+/*
+ * The chunk size a kda_chunk_fwd call with these arguments runs (see `chunk`
+ * above), written to *run_chunk.  Host only: enqueues nothing and touches no
+ * device.  Errors: KDA_ERR_DTYPE, KDA_ERR_SHAPE (H < 1), KDA_ERR_UNSUPPORTED
+ * (a size or chunk that kda_chunk_fwd would refuse), KDA_ERR_NULL.
+ */
+kda_status kda_chunk_fwd_run_chunk(kda_dtype qkv_dtype, int H, int d_k, int d_v, int chunk, int* run_chunk);
 
 /* Most positions one kda_chunk_fwd_snapshots call records. */
 #define KDA_MAX_SNAPSHOTS 128
@@ -130,7 +143,7 @@ kda_status kda_chunk_fwd_snapshots(const void* q, const void* k, const void* v, 
                                    const float* alpha, const float* beta, const float* S0,
                                    void* o, kda_dtype o_dtype, float* S_T,
                                    const int* snap_tokens, int n_snap, float* snaps,
-                                   int B, int T, int H, int d_k, int d_v, int chunk, void* stream);
+                                   int B, int T, int H, int d_k, int d_v, int chunk, hipStream_t stream);
 
 /*
  * One batched decode step: one new token for each of B sequences and H heads,
@@ -146,7 +159,7 @@ kda_status kda_chunk_fwd_snapshots(const void* q, const void* k, const void* v, 
  */
 kda_status kda_decode_step(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
                            const float* alpha, const float* beta, float* S, void* o, kda_dtype o_dtype,
-                           int B, int H, int d_k, int d_v, void* stream);
+                           int B, int H, int d_k, int d_v, hipStream_t stream);
 
 /*
  * kda_chunk_fwd over a packed batch of N sequences of different lengths (for
@@ -171,7 +184,7 @@ kda_status kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, kda
                                 const float* alpha, const float* beta, const float* S0,
                                 void* o, kda_dtype o_dtype, float* S_T,
                                 const int* cu_seqlens, int N, int total_T,
-                                int H, int d_k, int d_v, int chunk, void* stream);
+                                int H, int d_k, int d_v, int chunk, hipStream_t stream);
 
 /*
  * kda_chunk_fwd with the gate fused in: instead of alpha, the caller passes the
@@ -189,7 +202,7 @@ kda_status kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, kda
 kda_status kda_chunk_fwd_gated(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
                                const void* z, const float* A, const float* beta, const float* S0,
                                void* o, kda_dtype o_dtype, float* S_T,
-                               int B, int T, int H, int d_k, int d_v, int chunk, void* stream);
+                               int B, int T, int H, int d_k, int d_v, int chunk, hipStream_t stream);
 
 /*
  * Prefill with each sequence split into parts that run side by side: for few
@@ -234,7 +247,7 @@ kda_status kda_chunk_fwd_split(const void* q, const void* k, const void* v, kda_
                                const float* alpha, const float* beta, const float* S0,
                                void* o, kda_dtype o_dtype, float* S_T,
                                int B, int T, int H, int d_k, int d_v, int chunk,
-                               int parts, int num_cus, void* workspace, size_t workspace_bytes, void* stream);
+                               int parts, int num_cus, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * kda_decode_step with the gate fused in (as kda_chunk_fwd_gated):
@@ -242,7 +255,7 @@ kda_status kda_chunk_fwd_split(const void* q, const void* k, const void* v, kda_
  */
 kda_status kda_decode_step_gated(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
                                  const void* z, const float* A, const float* beta, float* S, void* o,
-                                 kda_dtype o_dtype, int B, int H, int d_k, int d_v, void* stream);
+                                 kda_dtype o_dtype, int B, int H, int d_k, int d_v, hipStream_t stream);
 
 /* Most draft tokens one speculative step may verify. */
 #define KDA_MAX_DRAFT 16
@@ -271,7 +284,7 @@ kda_status kda_decode_step_gated(const void* q, const void* k, const void* v, kd
 kda_status kda_decode_verify(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
                              const float* alpha, const float* beta, const float* S,
                              void* o, kda_dtype o_dtype, float* u,
-                             int B, int K, int H, int d_k, int d_v, void* stream);
+                             int B, int K, int H, int d_k, int d_v, hipStream_t stream);
 
 /*
  * Speculative decoding, pass 2 of 2: advance the state over the accepted
@@ -290,7 +303,7 @@ kda_status kda_decode_verify(const void* q, const void* k, const void* v, kda_dt
  */
 kda_status kda_decode_commit(const void* k, kda_dtype qkv_dtype, const float* alpha, const float* u,
                              const int* n_accept, float* S,
-                             int B, int K, int H, int d_k, int d_v, void* stream);
+                             int B, int K, int H, int d_k, int d_v, hipStream_t stream);
 
 /* Human-readable text for a status code (static storage; never NULL). */
 const char* kda_status_string(kda_status s);

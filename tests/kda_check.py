@@ -75,6 +75,70 @@ def rel_err_per_head(got, ref):
     return worst
 
 
+class PerHeadSeqErr:
+    """max|got - ref| / RMS(ref) per head over a sequence of decode steps, worst
+    head: each call adds one step's outputs ([n_heads, d_v]); a head's RMS is
+    taken over every output it produced, as for a prefill head over its T
+    tokens.  inf when a value is not finite."""
+
+    def __init__(self):
+        self.maxd = None
+        self.ss = None
+        self.count = 0
+        self.finite = True
+
+    def add(self, got, ref):
+        got = np.asarray(got, np.float64).reshape(ref.shape[0], -1)
+        ref = np.asarray(ref, np.float64).reshape(ref.shape[0], -1)
+        self.finite = self.finite and bool(np.isfinite(got).all() and np.isfinite(ref).all())
+        d = np.abs(got - ref).max(axis=1)
+        s = (ref * ref).sum(axis=1)
+        self.maxd = d if self.maxd is None else np.maximum(self.maxd, d)
+        self.ss = s if self.ss is None else self.ss + s
+        self.count += ref.shape[1]
+
+    def value(self):
+        if self.maxd is None:
+            return 0.0
+        if not self.finite:
+            return float("inf")
+        rms = np.sqrt(self.ss / self.count)
+        return float((self.maxd / np.maximum(rms, 1e-30)).max())
+
+
+def forced_prefill(impl, slab=0):
+    """Context manager: run the binding's calls through libkda_testhooks.so (the
+    same kernels, with a test switch in the C ABI) with the prefill kernel forced
+    (impl 0: the generic kernel, 1: the pipelined kernel where it applies; slab:
+    the generic kernel's columns per workgroup, 0: the library's choice)."""
+    import contextlib
+    import ctypes
+
+    import gated_delta_rule_07_amd as kda
+
+    @contextlib.contextmanager
+    def cm():
+        global _HOOKS
+        if _HOOKS is None:
+            path = kda.library_path().with_name("libkda_testhooks.so")
+            _HOOKS = kda.bind(path)
+            _HOOKS.kda_test_force_prefill.argtypes = [ctypes.c_int, ctypes.c_int]
+            _HOOKS.kda_test_force_prefill.restype = None
+        saved = kda._lib
+        kda._lib = _HOOKS
+        _HOOKS.kda_test_force_prefill(int(impl), int(slab))
+        try:
+            yield
+        finally:
+            _HOOKS.kda_test_force_prefill(-1, 0)
+            kda._lib = saved
+
+    return cm()
+
+
+_HOOKS = None
+
+
 def assert_close(got, ref, is_bf16, what):
     if is_bf16:
         e = rel_err_per_head(got, ref)

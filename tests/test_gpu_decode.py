@@ -5,7 +5,7 @@ import torch
 
 import kda_inputs as ki
 import oracle
-from kda_check import TOL_BF16_REL, TOL_F32_ABS, abs_err, log, rel_err_per_head
+from kda_check import TOL_BF16_REL, TOL_F32_ABS, PerHeadSeqErr, abs_err, log, rel_err_per_head
 
 pytestmark = pytest.mark.gpu
 
@@ -20,6 +20,7 @@ def _run_steps(gpu, B, H, dk, dv, dtype, steps, seed=0, check_every=1):
     S = ki.make_state(B, H, dk, dv, 0.1, seed + 1, gpu)
     S_ref = S.detach().cpu().double().numpy().copy()
     worst_o = 0.0
+    per_head = PerHeadSeqErr()  # bf16: each head's error over its own outputs' RMS
     for step in range(steps):
         tok = ki.make_decode_token(B, H, dk, dv, dtype, 3.0, seed=seed, step=step, device=gpu)
         o = kda.kda_decode_step(tok["q"], tok["k"], tok["v"], tok["alpha"], tok["beta"], S)
@@ -29,10 +30,11 @@ def _run_steps(gpu, B, H, dk, dv, dtype, steps, seed=0, check_every=1):
             got = o.float().cpu().double().numpy().reshape(B * H, dv)
             ref = o_ref.reshape(B * H, dv)
             if dtype == torch.bfloat16:
-                # one token per head: normalise by the RMS of the whole step's output
-                worst_o = max(worst_o, rel_err_per_head(got.reshape(1, -1), ref.reshape(1, -1)))
+                per_head.add(got, ref)
             else:
                 worst_o = max(worst_o, abs_err(got, ref))
+    if dtype == torch.bfloat16:
+        worst_o = per_head.value()
     torch.cuda.synchronize()
     gs = S.cpu().double().numpy().reshape(B * H, dk, dv)
     rs = S_ref.reshape(B * H, dk, dv)

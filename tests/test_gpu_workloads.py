@@ -7,7 +7,7 @@
 * decode:      B=256, H=32, d=128    - 100 in-place steps; o at every step and
                                        the final S for every state
 Tolerance: max |gpu - oracle| / RMS(oracle) <= 2e-2 per head (bf16 q/k/v, fp32
-state and output).  The oracle reads the exact device inputs.
+state and output); a decode head's RMS is over all of its outputs.  The oracle reads the exact device inputs.
 """
 import time
 
@@ -18,7 +18,7 @@ import torch
 import gated_delta_rule_07_amd as kda
 import kda_inputs as ki
 import oracle
-from kda_check import TOL_BF16_REL, gpu_o_heads, gpu_s_heads, log, rel_err_per_head
+from kda_check import TOL_BF16_REL, PerHeadSeqErr, gpu_o_heads, gpu_s_heads, log, rel_err_per_head
 
 pytestmark = pytest.mark.gpu
 
@@ -105,18 +105,18 @@ def test_decode_b256_100_steps(gpu):
     B, H, dk, dv = w.B, w.H, w.dk, w.dv
     S = ki.make_state(B, H, dk, dv, w.s0_std, 1, gpu)
     S_ref = S.cpu().double().numpy()
-    worst_o = 0.0
+    per_head = PerHeadSeqErr()  # each state's o over its 100 tokens, normalised by their RMS
     t0 = time.time()
     for step in range(w.decode_steps):
         tok = ki.make_decode_token(B, H, dk, dv, w.qkv_dtype, w.alpha_mu, seed=0, step=step, device=gpu)
         o = kda.kda_decode_step(tok["q"], tok["k"], tok["v"], tok["alpha"], tok["beta"], S)
         h = {k: v.cpu() for k, v in tok.items()}
         o_ref = oracle.decode_step(h["q"], h["k"], h["v"], h["alpha"], h["beta"], S_ref)
-        got = o.cpu().double().numpy().reshape(1, -1)
-        worst_o = max(worst_o, rel_err_per_head(got, o_ref.reshape(1, -1)))
+        per_head.add(o.cpu().double().numpy().reshape(B * H, dv), o_ref.reshape(B * H, dv))
         if step % 25 == 0:
-            log(f"  decode step {step}: worst o err so far {worst_o:.3e} ({time.time() - t0:.0f} s)")
-    log(f"  decode o over 100 steps: {worst_o:.3e}")
+            log(f"  decode step {step}: worst head's o err so far {per_head.value():.3e} ({time.time() - t0:.0f} s)")
+    worst_o = per_head.value()
+    log(f"  decode o over 100 steps, worst of {B * H} heads: {worst_o:.3e}")
     assert worst_o <= TOL_BF16_REL
     _check("decode S (all 8192 states)", S.cpu().double().numpy().reshape(B * H, dk, dv),
            S_ref.reshape(B * H, dk, dv))
