@@ -15,6 +15,7 @@ import torch
 
 __all__ = ["kda_chunk_fwd", "kda_chunk_fwd_snapshots", "kda_chunk_fwd_varlen", "kda_chunk_fwd_gated",
            "kda_chunk_fwd_split", "kda_chunk_fwd_split_plan", "kda_chunk_fwd_run_chunk",
+           "kda_chunk_fwd_split_noalloc", "KDA_SPLIT_SCRATCH_BYTES",
            "kda_decode_step", "kda_decode_step_gated",
            "kda_decode_verify",
            "kda_decode_commit", "kda_status_string", "kda_version",
@@ -24,6 +25,7 @@ __all__ = ["kda_chunk_fwd", "kda_chunk_fwd_snapshots", "kda_chunk_fwd_varlen", "
 KDA_F32, KDA_BF16 = 0, 1
 KDA_MAX_SNAPSHOTS = 128
 KDA_MAX_DRAFT = 16
+KDA_SPLIT_SCRATCH_BYTES = 64 << 20
 _PKG = Path(__file__).resolve().parent
 _LIB_PATH = _PKG / "libkda.so"
 _lib = None
@@ -78,6 +80,9 @@ def bind(path) -> ctypes.CDLL:
     lib.kda_chunk_fwd_split.restype = i32
     lib.kda_chunk_fwd_split.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, i32, vp,
                                         i32, i32, i32, i32, i32, i32, i32, i32, vp, sz, vp]
+    lib.kda_chunk_fwd_split_noalloc.restype = i32
+    lib.kda_chunk_fwd_split_noalloc.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, i32, vp,
+                                                i32, i32, i32, i32, i32, i32, i32, i32, vp]
     lib.kda_decode_step_gated.restype = i32
     lib.kda_decode_step_gated.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
     lib.kda_decode_verify.restype = i32
@@ -324,6 +329,24 @@ def kda_chunk_fwd_split(q, k, v, alpha, beta, S0=None, *, parts: int = 0, num_cu
                                  _stream(dev, stream))
     if st != 0:
         raise KdaError(st, "kda_chunk_fwd_split")
+    return o, S_T
+
+
+def kda_chunk_fwd_split_noalloc(q, k, v, alpha, beta, S0=None, *, parts: int = 0, num_cus: int = 0,
+                                chunk: int = 64, o=None, S_T=None, o_dtype=torch.float32, want_state: bool = True,
+                                stream=None):
+    """The split prefill with its workspace in the library's fixed per-GPU scratch
+    array (``KDA_SPLIT_SCRATCH_BYTES``): the C call allocates nothing.  Pass
+    preallocated ``o`` and ``S_T`` to keep this wrapper from allocating them.
+    Calls that overlap on one GPU race.  Returns ``(o, S_T)``; other arguments as
+    ``kda_chunk_fwd_split``."""
+    lib = load_library()
+    dev, (B, T, H, dk, dv), o, S_T = _prefill_prep(q, k, v, alpha, beta, S0, o, S_T, o_dtype, want_state)
+    st = lib.kda_chunk_fwd_split_noalloc(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(alpha), _ptr(beta),
+                                         _ptr(S0), _ptr(o), _dtype_code(o), _ptr(S_T), B, T, H, dk, dv, int(chunk),
+                                         int(parts), int(num_cus), _stream(dev, stream))
+    if st != 0:
+        raise KdaError(st, "kda_chunk_fwd_split_noalloc")
     return o, S_T
 
 

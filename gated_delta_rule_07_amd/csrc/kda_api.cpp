@@ -7,6 +7,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/kda.h"
 #include "kda_launch.h"
 
@@ -116,7 +118,9 @@ double combine_steps(int P) {
 // rounds of (chunks per part + 3) steps; the combine as above, and the two
 // extra launches about two steps.  A split is taken only when it models at
 // least 10% faster than the single pass.
-SplitShape split_shape_auto(int B, int T, int H, int dk, int dv, int cus) {
+size_t split_ws_bytes(int B, int H, int dk, int dv, int P);
+
+SplitShape split_shape_auto(int B, int T, int H, int dk, int dv, int cus, size_t max_ws = SIZE_MAX) {
   const int nch = (T + 31) / 32;
   const long long bh = (long long)B * H, ns = dv / 32, nsa = (dv + dk) / 32;
   auto rounds = [&](long long g) { return (double)((g + cus - 1) / cus); };
@@ -125,7 +129,7 @@ SplitShape split_shape_auto(int B, int T, int H, int dk, int dv, int cus) {
   double best_cost = 0.9 * single;
   for (int P = 2; P <= nch && P <= kMaxParts; ++P) {
     const SplitShape sh = split_shape_for(T, P);
-    if (sh.parts != P) continue;
+    if (sh.parts != P || split_ws_bytes(B, H, dk, dv, P) > max_ws) continue;
     const double cost = (rounds(bh * (P - 1) * nsa) + rounds(bh * P * ns)) * (sh.part_len / 32 + 3) +
                         combine_steps(P) + 2.0;
     if (cost < best_cost) {
@@ -158,7 +162,37 @@ struct SplitReq {
   int num_cus;
   void* ws;
   size_t ws_bytes;
+  bool scratch;  // the workspace is this GPU's scratch array (ws unused)
 };
+
+// ---- allocation-free split: a fixed scratch array per GPU --------------------------
+// kda_chunk_fwd_split_noalloc keeps its workspace in this array.  In host code
+// `scratch` names a host-side stand-in, not device memory: its device address
+// is looked up once per GPU (with that GPU current) and only that address is
+// passed to kernels.  Every call on one GPU shares the array.
+__device__ __align__(256) unsigned char scratch[KDA_SPLIT_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The device address of the current GPU's scratch array.
+hipError_t scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 }  // namespace
 
@@ -266,11 +300,20 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, int qkv_d
         g_last_hip_error = (int)hipErrorNoDevice;
         return KDA_ERR_HIP;
       }
-      sh = split_shape_auto(B, T, H, d_k, d_v, cus);
+      sh = split_shape_auto(B, T, H, d_k, d_v, cus, split->scratch ? KDA_SPLIT_SCRATCH_BYTES : SIZE_MAX);
     }
   }
   char* ws = nullptr;
-  if (sh.parts > 1) {
+  if (sh.parts > 1 && split->scratch) {
+    if (split_ws_bytes(B, H, d_k, d_v, sh.parts) > KDA_SPLIT_SCRATCH_BYTES) return KDA_ERR_SHAPE;
+    void* sp = nullptr;
+    const hipError_t se = scratch_of_current_device(&sp);
+    if (se != hipSuccess) {
+      g_last_hip_error = (int)se;
+      return KDA_ERR_HIP;
+    }
+    ws = static_cast<char*>(sp);
+  } else if (sh.parts > 1) {
     const size_t need = split_ws_bytes(B, H, d_k, d_v, sh.parts);
     if (!split->ws) return KDA_ERR_NULL;
     if (!aligned16(split->ws)) return KDA_ERR_MISALIGNED;
@@ -403,9 +446,19 @@ kda_status kda_chunk_fwd_split(const void* q, const void* k, const void* v, kda_
                                void* o, kda_dtype o_dtype, float* S_T,
                                int B, int T, int H, int d_k, int d_v, int chunk,
                                int parts, int num_cus, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  const SplitReq req{parts, num_cus, workspace, workspace_bytes};
+  const SplitReq req{parts, num_cus, workspace, workspace_bytes, false};
   return chunk_fwd_impl(q, k, v, raw_enum(qkv_dtype), alpha, beta, S0, o, raw_enum(o_dtype), S_T, nullptr, 0, nullptr, nullptr,
                         nullptr, nullptr, B, T, H, d_k, d_v, chunk, stream, &req);
+}
+
+kda_status kda_chunk_fwd_split_noalloc(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
+                                       const float* alpha, const float* beta, const float* S0,
+                                       void* o, kda_dtype o_dtype, float* S_T,
+                                       int B, int T, int H, int d_k, int d_v, int chunk,
+                                       int parts, int num_cus, hipStream_t stream) {
+  const SplitReq req{parts, num_cus, nullptr, 0, true};
+  return chunk_fwd_impl(q, k, v, raw_enum(qkv_dtype), alpha, beta, S0, o, raw_enum(o_dtype), S_T, nullptr, 0,
+                        nullptr, nullptr, nullptr, nullptr, B, T, H, d_k, d_v, chunk, stream, &req);
 }
 
 }  // extern "C"

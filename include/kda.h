@@ -249,6 +249,34 @@ kda_status kda_chunk_fwd_split(const void* q, const void* k, const void* v, kda_
                                int B, int T, int H, int d_k, int d_v, int chunk,
                                int parts, int num_cus, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Bytes of device scratch kda_chunk_fwd_split_noalloc holds on each GPU (64 MiB). */
+#define KDA_SPLIT_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * kda_chunk_fwd_split for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.  The
+ * same split prefill, with its workspace in a fixed device array of
+ * KDA_SPLIT_SCRATCH_BYTES that the library holds on each GPU it runs on (from
+ * when the library's code is loaded on that GPU until the process ends).  The
+ * call allocates nothing; the caller still passes every input and output.
+ *
+ *   parts : 0 = the library's choice among part counts whose workspace fits
+ *           the scratch (1, the single pass, needs none); >= 2 = that many
+ *           parts (or fewer, as kda_chunk_fwd_split), KDA_ERR_SHAPE when
+ *           their workspace (kda_chunk_fwd_split_plan) exceeds
+ *           KDA_SPLIT_SCRATCH_BYTES.
+ * Every call on one GPU uses that GPU's one array and overwrites what the last
+ * call left there: calls that overlap on one GPU (on other streams or from
+ * other threads) race and must be ordered by the caller.  Every other argument
+ * and error as kda_chunk_fwd_split; KDA_ERR_HIP also when the array's device
+ * address cannot be obtained (kda_last_hip_error() holds the hipError_t).
+ */
+kda_status kda_chunk_fwd_split_noalloc(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
+                                       const float* alpha, const float* beta, const float* S0,
+                                       void* o, kda_dtype o_dtype, float* S_T,
+                                       int B, int T, int H, int d_k, int d_v, int chunk,
+                                       int parts, int num_cus, hipStream_t stream);
+
 /*
  * kda_decode_step with the gate fused in (as kda_chunk_fwd_gated):
  *   z : [B][H][d_k] in qkv_dtype (read)           A : [H] fp32, device (read)

@@ -417,3 +417,38 @@ def _split(lib, parts=4, cus=256, ws=_addr(10), wsb=1 << 30, **over):
 ])
 def test_split_validation(kw, code):
     assert _split(_lib(), **kw) == code
+
+
+def _split_noalloc(lib, parts=4, cus=256, **over):
+    a = dict(q=_addr(0), k=_addr(1), v=_addr(2), dtype=1, alpha=_addr(3), beta=_addr(4), S0=_addr(5),
+             o=_addr(6), odt=0, S_T=_addr(7), B=1, T=4096, H=8, dk=128, dv=128, chunk=64)
+    a.update(over)
+    return lib.kda_chunk_fwd_split_noalloc(a["q"], a["k"], a["v"], a["dtype"], a["alpha"], a["beta"], a["S0"],
+                                           a["o"], a["odt"], a["S_T"], a["B"], a["T"], a["H"], a["dk"], a["dv"],
+                                           a["chunk"], parts, cus, None)
+
+
+SCRATCH = 64 << 20  # KDA_SPLIT_SCRATCH_BYTES
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=4, T=65536, H=32, parts=32), 2),   # the workspace of 32 parts exceeds the scratch
+    (dict(B=2, T=65536, H=16, parts=9), 2),
+    (dict(parts=-1), 2), (dict(cus=-1), 2),
+    (dict(dtype=0, dk=32, dv=32), 4),          # fp32: no split kernel
+    (dict(q=None), 1), (dict(o=_addr(0)), 6), (dict(dtype=9), 3),
+])
+def test_split_noalloc_validation(kw, code):
+    """The allocation-free split refuses, before any HIP call, a part count whose
+    workspace exceeds the library's scratch, and applies kda_chunk_fwd_split's checks."""
+    parts = kw.pop("parts", 4)
+    cus = kw.pop("cus", 256)
+    if "B" in kw:
+        assert _ws_bytes(parts, B=kw["B"], H=kw["H"]) > SCRATCH
+    assert _split_noalloc(_lib(), parts=parts, cus=cus, **kw) == code
+
+
+def test_split_noalloc_scratch_size_is_stated():
+    assert "#define KDA_SPLIT_SCRATCH_BYTES ((size_t)64 << 20)" in HEADER.read_text()
+    import gated_delta_rule_07_amd as kda
+    assert kda.KDA_SPLIT_SCRATCH_BYTES == SCRATCH
