@@ -50,14 +50,17 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int CS = kPipeChunk;  // tokens per chunk
-constexpr int J = 32;   // state columns per workgroup
 constexpr float STEEP = 4.5399930e-05f;  // e^{-10}
 
-template <int DK_>
+template <int DK_, int NST_>
 struct Cfg4 {
   static constexpr int DK = DK_;
-  static constexpr int NKT = DK / 32;   // 32-row channel tiles of S
-  static constexpr int NKS = DK / 16;   // 16-channel reduction steps
+  static constexpr int NST = NST_;       // state waves, 16 state columns each (two here)
+  static constexpr int J = 16 * NST;     // state columns per workgroup
+  static_assert(NST == 2, "the role layout has two state waves (waves 0 and 1)");
+  static constexpr int NKS = DK / 16;   // 16-channel reduction steps (32x32x16 products)
+  static constexpr int NKT = DK / 16;   // 16-row channel tiles of a state wave's S
+  static constexpr int NKB = DK / 32;   // 32-channel reduction steps (16x16x32 products)
   static constexpr int LDK = DK + 8;    // fp16 [token][channel] row stride
   static constexpr int LDC = CS + 8;    // fp16 [row][token] row stride
   static constexpr int LDV = CS + 4;    // bf16 V^T row stride
@@ -72,15 +75,21 @@ struct Cfg4 {
   static constexpr int TQ = 64 / PPW;    // token groups per channel group
   static constexpr int TPL = CS / TQ;    // tokens per scan lane
   static_assert(TQ == 8 && TPL == 4, "scan layout");
+  // the V slab (CS x J bf16) comes in 16-byte loads, J / 8 lanes per token row,
+  // from the last J / 16 scan waves
+  static constexpr int VLW = J / 16;
+  static constexpr int VW0 = NSW - VLW;  // first V-loading scan wave
+  static_assert(CS * J * 2 == VLW * 64 * 16, "V slab split");
 };
 
-// Storage column of logical column c: the four quads of each 16-column group are
-// stored in the order {0, 2, 1, 3}.  A 16-byte read at offset 8h of a group then
-// holds logical columns {4h..4h+3, 8+4h..8+4h+3}: the reduction indices a
-// 32x32x16 B operand built from a C tile in registers carries.
+// Storage position of logical index c (a channel, or a token of the chunk)
+// within its block of 32: the eight quads of 4 are stored in the order
+// {0, 4, 1, 5, 2, 6, 3, 7}.  A 16-byte read at offset 8g of a block then holds
+// indices {4g..4g+3, 16+4g..16+4g+3}: the reduction slots of a 16x16x32 operand
+// whose partner is built from two vertically adjacent C tiles in registers
+// (lane group g of a C tile holds rows 4g..4g+3).
 __device__ __forceinline__ int spos(int c) {
-  const int q = (c >> 2) & 3;
-  return (c & ~15) | (((q & 1) << 1 | (q >> 1)) << 2) | (c & 3);
+  return (c & ~31) | (((c >> 2) & 3) << 3) | (((c >> 4) & 1) << 2) | (c & 3);
 }
 
 template <class C>
@@ -88,7 +97,7 @@ struct ScanSlot {
   alignas(16) h16 kg[CS * C::LDK];    // KG      [t][spos(c)]
   alignas(16) h16 qg[CS * C::LDK];    // QG      [t][spos(c)]
   alignas(16) h16 kh[C::DK * C::LDC]; // -KH^T   [c][spos(t)]
-  alignas(16) __bf16 v[J * C::LDV];   // V slab transposed [j][t]
+  alignas(16) __bf16 v[C::J * C::LDV];  // V slab transposed [j][t]
   alignas(16) float gam[C::DK];       // gamma per channel
   alignas(16) float beta[CS];         // beta (0 outside the item's segment)
 };
@@ -98,12 +107,10 @@ struct Smem4 {
   ScanSlot<C> ss[3];
   alignas(16) h16 kc[2][CS * C::LDK];      // KC [t][spos(c)]
   alignas(16) h16 t[2][CS * C::LDC];       // T  [t][spos(s)]
-  alignas(16) h16 p[3][CS * C::LDC];       // -P [t][spos(s)]
-  alignas(16) h16 sf[2][C::NKS * 64 * 8];  // scaled S as B fragments [step][lane][8]
-  alignas(16) float sexp[2][J];            // 2^e of each column's scale
-  alignas(16) h16 uf[2][2 * 64 * 8];       // Un as B fragments [step][lane][8]
+  alignas(16) h16 p[2][CS * C::LDC];       // -P [t][spos(s)]
   alignas(16) float xch[C::NSW][64][4];    // scan: token-group totals per wave
   alignas(16) int flags[2][C::NSW];        // scan: regroup votes per wave
+  alignas(16) float scol[2][16];           // state waves: 1/scale of each of their columns
 };
 
 // s_waitcnt immediate for "vector memory counter at 0" (gfx9 encoding: vmcnt in
@@ -194,9 +201,7 @@ struct Ctx4 {
 };
 
 // ---- scan waves --------------------------------------------------------------------
-constexpr int VW0 = 2;  // scan waves VW0.. load the V slab (CS x J bf16: 64 lanes x 16 B each)
 constexpr int BW = 1;   // the scan wave that loads beta
-static_assert(CS * J * 2 == (4 - VW0) * 64 * 16, "V slab split");
 // Each load's result is kept as the vector it arrives in: the step loop then
 // carries whole register tuples from one step's prefetch to the next step's
 // scan.  (Kept as separate words, the tuples were reassembled by register
@@ -256,8 +261,9 @@ __device__ ScanSrc scan_src(const Ctx4& cx, int sw, int lane) {
   r.bc = CS * r.br;
   r.ts2 = ts * 2;
   r.vo_k = 2 * (tq * C::TPL * ts + C::CPW * sw + C::CPL * cp);
-  const int vt = 64 * (sw - VW0) + lane;  // V row vt/4, columns 8(vt%4)..+7 (scan waves VW0.. only)
-  r.vo_v = 2 * ((vt / 4) * p.H * p.dv + 8 * (vt % 4));
+  // V row vt / (J/8), columns 8 (vt % (J/8)) .. + 7 (scan waves VW0.. only)
+  const int vt = 64 * (sw - C::VW0) + lane;
+  r.vo_v = 2 * ((vt / (C::J / 8)) * p.H * p.dv + 8 * (vt % (C::J / 8)));
   r.vo_b = 4 * (lane % CS) * p.H;  // beta of token l is kept by lane l
   return r;
 }
@@ -296,7 +302,7 @@ __device__ void load_raw4(Raw4<C>& raw, const Ctx4& cx, const ScanSrc& src, int 
       raw.q[i] = __builtin_bit_cast(WV, __builtin_amdgcn_raw_buffer_load_b32(rq, vk, sk, 0));
     }
   }
-  if (sw >= VW0) {
+  if (sw >= C::VW0) {
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(src.v + (size_t)(unsigned)c * (unsigned)src.vc, rows * src.vr);
     raw.v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, src.vo_v, 0, 0));
   }
@@ -306,11 +312,68 @@ __device__ void load_raw4(Raw4<C>& raw, const Ctx4& cx, const ScanSrc& src, int 
   }
 }
 
+// What a scan lane takes from its raw inputs: decays (alpha, or alpha formed from
+// the gate), keys and queries as fp32, the V words and beta.  Read in one place,
+// before the next chunk is loaded into the same registers.
+template <class C>
+struct ScanIn {
+  float a[C::TPL][C::CPL];
+  float kf[C::TPL][C::CPL];
+  float qf[C::TPL][C::CPL];
+};
+
+// Makes the values read from raw count as used here, so the compiler computes
+// them before a following load overwrites raw.
+template <class C>
+__device__ __forceinline__ void pin(ScanIn<C>& in) {
+#pragma unroll
+  for (int i = 0; i < C::TPL; ++i)
+#pragma unroll
+    for (int e = 0; e < C::CPL; ++e) asm volatile("" : "+v"(in.a[i][e]), "+v"(in.kf[i][e]), "+v"(in.qf[i][e]));
+}
+
+// Also stores the item's V slab (transposed) and beta to its ring slot, which
+// need nothing else.
+template <class C, bool G>
+__device__ __forceinline__ void scan_read(ScanIn<C>& in, Smem4<C>& sm, const Raw4<C>& raw, const Item& it, float eA,
+                                          int sw, int lane) {
+  ScanSlot<C>& sl = sm.ss[it.seq % 3];
+  if (sw >= C::VW0) {
+    // V^T: this lane holds row vt / (J/8), columns 8 (vt % (J/8)) .. + 7
+    const int vt = 64 * (sw - C::VW0) + lane;
+    const int vr = vt / (C::J / 8), vc = 8 * (vt % (C::J / 8));
+    const uint32_t w[4] = {raw.v.x, raw.v.y, raw.v.z, raw.v.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      sl.v[(vc + e) * C::LDV + vr] = __builtin_bit_cast(__bf16, (uint16_t)(w[e / 2] >> (16 * (e % 2))));
+  }
+  if (sw == BW && lane < CS) sl.beta[lane] = (lane >= it.lo && lane < it.hi) ? raw.beta : 0.0f;
+#pragma unroll
+  for (int i = 0; i < C::TPL; ++i) {
+#pragma unroll
+    for (int e = 0; e < C::CPL; ++e) {
+      if constexpr (G) {  // alpha = exp(-5 sigmoid(e^A z)) from the bf16 gate input
+        const uint32_t zw = raw.z[i][e / 2];
+        in.a[i][e] = gate_retention(eA * ((e & 1) ? bf16_hi(zw) : bf16_lo(zw)));
+      } else {
+        in.a[i][e] = raw.a[i][e];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < C::CPL / 2; ++j) {
+      in.kf[i][2 * j] = bf16_lo(raw.k[i][j]);
+      in.kf[i][2 * j + 1] = bf16_hi(raw.k[i][j]);
+      in.qf[i][2 * j] = bf16_lo(raw.q[i][j]);
+      in.qf[i][2 * j + 1] = bf16_hi(raw.q[i][j]);
+    }
+  }
+}
+
 // Scan of item `it` by scan wave sw (one channel pair and TPL consecutive tokens
 // per lane): writes ring slot it.seq % 3, KC slot it.seq % 2 and this wave's
 // regroup vote.  FULL: the item is the whole chunk (no token is masked).
-template <class C, bool FULL, bool G>
-__device__ void scan4_body(Smem4<C>& sm, const Raw4<C>& raw, const Item& it, float eA, int sw, int lane, int par) {
+template <class C, bool FULL>
+__device__ void scan4_body(Smem4<C>& sm, const ScanIn<C>& sin, const Item& it, int sw, int lane, int par) {
   constexpr int L = C::CPL, TP = C::TPL;
   ScanSlot<C>& sl = sm.ss[it.seq % 3];
   h16* kc = sm.kc[it.seq % 2];
@@ -327,15 +390,17 @@ __device__ void scan4_body(Smem4<C>& sm, const Raw4<C>& raw, const Item& it, flo
   for (int i = 0; i < TP; ++i)
 #pragma unroll
     for (int e = 0; e < L; ++e) {
-      float ai;
-      if constexpr (G) {  // alpha = exp(-5 sigmoid(e^A z)) from the bf16 gate input
-        const uint32_t zw = raw.z[i][e / 2];
-        ai = gate_retention(eA * ((e & 1) ? bf16_hi(zw) : bf16_lo(zw)));
-      } else {
-        ai = raw.a[i][e];
-      }
-      a[i][e] = in(i) ? ai : 1.0f;
+      a[i][e] = in(i) ? sin.a[i][e] : 1.0f;
       gt[e] *= a[i][e];
+    }
+  // keys and queries, zero outside the item
+  float kf[TP][L], qf[TP][L];
+#pragma unroll
+  for (int i = 0; i < TP; ++i)
+#pragma unroll
+    for (int e = 0; e < L; ++e) {
+      kf[i][e] = in(i) ? sin.kf[i][e] : 0.0f;
+      qf[i][e] = in(i) ? sin.qf[i][e] : 0.0f;
     }
   // Token-group products of every channel, exchanged within the wave.  Each
   // lane runs the product over the groups in order, keeps the partial product
@@ -397,23 +462,15 @@ __device__ void scan4_body(Smem4<C>& sm, const Raw4<C>& raw, const Item& it, flo
   const int col = spos(ch);
 #pragma unroll
   for (int i = 0; i < TP; ++i) {
-    float kf[L], qf[L];
-#pragma unroll
-    for (int j = 0; j < L / 2; ++j) {
-      kf[2 * j] = in(i) ? bf16_lo(raw.k[i][j]) : 0.0f;
-      kf[2 * j + 1] = in(i) ? bf16_hi(raw.k[i][j]) : 0.0f;
-      qf[2 * j] = in(i) ? bf16_lo(raw.q[i][j]) : 0.0f;
-      qf[2 * j + 1] = in(i) ? bf16_hi(raw.q[i][j]) : 0.0f;
-    }
     h16 kg[L], qg[L], kcv[L];
 #pragma unroll
     for (int e = 0; e < L; ++e) {
-      kmax = fmaxf(kmax, fabsf(kf[e]));
+      kmax = fmaxf(kmax, fabsf(kf[i][e]));
       // fused multiply rounded once to fp16 (a mixed-precision fma): one
       // instruction per element instead of a multiply and half a conversion
-      kg[e] = (h16)__builtin_fmaf(kf[e], pre[i][e], 0.0f);
-      qg[e] = (h16)__builtin_fmaf(qf[e], pre[i][e], 0.0f);
-      const float kh = kf[e] * ns[i][e];  // -KH
+      kg[e] = (h16)__builtin_fmaf(kf[i][e], pre[i][e], 0.0f);
+      qg[e] = (h16)__builtin_fmaf(qf[i][e], pre[i][e], 0.0f);
+      const float kh = kf[i][e] * ns[i][e];  // -KH
       khv[e][i] = (h16)kh;
       kcv[e] = (h16)__builtin_fmaf(kh, -rg[e], 0.0f);  // KC = KH / gamma
     }
@@ -435,16 +492,6 @@ __device__ void scan4_body(Smem4<C>& sm, const Raw4<C>& raw, const Item& it, flo
     if constexpr (L == 4) *reinterpret_cast<f32x4*>(&sl.gam[ch]) = f32x4{gam[0], gam[1], gam[2], gam[3]};
     else *reinterpret_cast<f32x2*>(&sl.gam[ch]) = f32x2{gam[0], gam[1]};
   }
-  if (sw >= VW0) {
-    // V^T: this lane holds row vt/4, columns 8(vt%4)..+7
-    const int vt = 64 * (sw - VW0) + lane;
-    const int vr = vt / 4, vc = 8 * (vt % 4);
-    const uint32_t w[4] = {raw.v.x, raw.v.y, raw.v.z, raw.v.w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      sl.v[(vc + e) * C::LDV + vr] = __builtin_bit_cast(__bf16, (uint16_t)(w[e / 2] >> (16 * (e % 2))));
-  }
-  if (sw == BW && lane < CS) sl.beta[lane] = (FULL || (lane >= lo && lane < hi)) ? raw.beta : 0.0f;
   // Regroup vote: the first token (chunk position) at which some channel's
   // prefix decay falls below e^{-10} or KC = k/pre would leave fp16 range; CS
   // when there is none.  A bound over the whole item (smallest gamma, largest
@@ -464,7 +511,7 @@ __device__ void scan4_body(Smem4<C>& sm, const Raw4<C>& raw, const Item& it, flo
       bool bad = false;
 #pragma unroll
       for (int j = 0; j < L / 2; ++j) {
-        const float k0 = fabsf(bf16_lo(raw.k[i][j])), k1 = fabsf(bf16_hi(raw.k[i][j]));
+        const float k0 = fabsf(kf[i][2 * j]), k1 = fabsf(kf[i][2 * j + 1]);
         const float p0 = pre[i][2 * j], p1 = pre[i][2 * j + 1];
         bad = bad || !(p0 >= STEEP) || !(k0 < 32768.0f * p0) || !(p1 >= STEEP) || !(k1 < 32768.0f * p1);
       }
@@ -480,10 +527,10 @@ __device__ void scan4_body(Smem4<C>& sm, const Raw4<C>& raw, const Item& it, flo
   if (lane == 0) sm.flags[par][sw] = vote;
 }
 
-template <class C, bool G>
-__device__ void scan4(Smem4<C>& sm, const Raw4<C>& raw, const Item& it, float eA, int sw, int lane, int par) {
-  if (it.lo == 0 && it.hi == CS) scan4_body<C, true, G>(sm, raw, it, eA, sw, lane, par);
-  else scan4_body<C, false, G>(sm, raw, it, eA, sw, lane, par);
+template <class C>
+__device__ void scan4(Smem4<C>& sm, const ScanIn<C>& sin, const Item& it, int sw, int lane, int par) {
+  if (it.lo == 0 && it.hi == CS) scan4_body<C, true>(sm, sin, it, sw, lane, par);
+  else scan4_body<C, false>(sm, sin, it, sw, lane, par);
 }
 
 // ---- L, T wave -------------------------------------------------------------------------
@@ -587,7 +634,7 @@ template <class C>
 __device__ void pmat4(Smem4<C>& sm, const Item& it, int lane) {
   const ScanSlot<C>& sl = sm.ss[it.seq % 3];
   const h16* kc = sm.kc[it.seq % 2];
-  h16* pp = sm.p[it.seq % 3];
+  h16* pp = sm.p[it.seq % 2];
   const int h = opaque(lane / 32), m = opaque(lane % 32);
   f32x16 acc = (f32x16)0.0f;
 #pragma unroll
@@ -605,89 +652,135 @@ __device__ void pmat4(Smem4<C>& sm, const Item& it, int lane) {
     }
 }
 
-// ---- state wave --------------------------------------------------------------------------
-// S holds the state times 2^{-e} (e per column, sc = 2^{-e}); Sf the fp16 B
-// fragments of S for the next item, vn the next item's -V * sc in C layout.
+// ---- state waves ---------------------------------------------------------------------------
+// Two waves, each owning 16 of the workgroup's 32 state columns, run the chain on
+// 16x16x32 fp16 matrix cores: lane l (g = l / 16, n = l % 16) holds rows 4g + r
+// of column n of every C tile.  Each also forms the output of its columns, so S
+// and Un never leave its registers:
+//   Xn = KG S - V,  Un = T Xn,  S' = gamma S + (-KH)^T Un,
+//   O^T = S^T QG^T + Un^T (-P)^T      (the transposed output: a lane holds four
+//                                      adjacent columns of one token)
+// Every product's reduction slots are in the stacked order of two C tiles, so
+// operands built from C tiles in registers (S, Xn, Un) pair with rows read from
+// LDS in spos order in one 16-byte read.
 template <class C>
 struct StateRegs {
-  f32x16 S[C::NKT];
-  f16x8 Sf[C::NKS];
-  float vn[16];
-  float sc;
+  f32x4 S[C::NKT];   // the state times sc (per column): rows 16 it + 4g + r, column n
+  f16x8 Sf[C::NKB];  // fp16 S for reduction step kb (channels 32 kb ..)
+  f32x4 vn[2];       // -V * sc of the item: tokens 16 rt + 4g + r
+  float sc;          // 2^-e, this lane's column scale
+  f32x4 usc;         // 1/sc of columns 4g .. 4g + 3 (the output rows this lane holds)
 };
 
+__device__ __forceinline__ f32x4 mma16(const f16x8& a, const f16x8& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+// fp16 operand in stacked order from two C tiles (slots 0..3 from the first)
+__device__ __forceinline__ f16x8 stack2(const f32x4& lo, const f32x4& hi) {
+  return f16x8{(h16)lo[0], (h16)lo[1], (h16)lo[2], (h16)lo[3], (h16)hi[0], (h16)hi[1], (h16)hi[2], (h16)hi[3]};
+}
+
+// One item of the chain for state wave w (columns 16w .. 16w + 15 of the slab),
+// with the output of those columns stored.
 template <class C>
-__device__ void state_step(Smem4<C>& sm, StateRegs<C>& R, const Item& it, int lane) {
+__device__ void state_step(Smem4<C>& sm, StateRegs<C>& R, const Item& it, const Ctx4& cx, int w, int lane) {
   const ScanSlot<C>& sl = sm.ss[it.seq % 3];
   const h16* tt = sm.t[it.seq % 2];
-  const int h = opaque(lane / 32), n = opaque(lane % 32);
+  const h16* pp = sm.p[it.seq % 2];
+  const int g = opaque(lane / 16), n = opaque(lane % 16);
   // operands first, so their reads overlap the products
-  f16x8 A[C::NKS];
+  f16x8 A[2][C::NKB], Q[2][C::NKB], Tf[2];
 #pragma unroll
-  for (int s = 0; s < C::NKS; ++s) A[s] = ld8(&sl.kg[n * C::LDK + 16 * s + 8 * h]);
-  const f16x8 t0 = ld8(&tt[n * C::LDC + 8 * h]), t1 = ld8(&tt[n * C::LDC + 16 + 8 * h]);
-  // Xn = KG S - V (scaled)
-  f32x16 X;
+  for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) X[i] = R.vn[i];
+    for (int kb = 0; kb < C::NKB; ++kb) {
+      A[rt][kb] = ld8(&sl.kg[(16 * rt + n) * C::LDK + 32 * kb + 8 * g]);
+      Q[rt][kb] = ld8(&sl.qg[(16 * rt + n) * C::LDK + 32 * kb + 8 * g]);
+    }
+    Tf[rt] = ld8(&tt[(16 * rt + n) * C::LDC + 8 * g]);
+  }
+  // Xn = KG S - V (scaled), and the first output term S^T QG^T
+  f32x4 X[2] = {R.vn[0], R.vn[1]};
+  f32x4 O[2] = {(f32x4)0.0f, (f32x4)0.0f};
 #pragma unroll
-  for (int s = 0; s < C::NKS; ++s) X = mma32(A[s], R.Sf[s], X);
+  for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      X[rt] = mma16(A[rt][kb], R.Sf[kb], X[rt]);
+      O[rt] = mma16(R.Sf[kb], Q[rt][kb], O[rt]);
+    }
   // decay the state in place while the products run
 #pragma unroll
-  for (int ct = 0; ct < C::NKT; ++ct)
+  for (int i = 0; i < C::NKT; ++i) R.S[i] *= *reinterpret_cast<const f32x4*>(&sl.gam[16 * i + 4 * g]);
+  f16x8 KH[C::NKT];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x4 gv = *reinterpret_cast<const f32x4*>(&sl.gam[32 * ct + 8 * j + 4 * h]);
+  for (int i = 0; i < C::NKT; ++i) KH[i] = ld8(&sl.kh[(16 * i + n) * C::LDC + 8 * g]);
+  f16x8 Pf[2];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) R.S[ct][4 * j + r] *= gv[r];
-    }
-  f16x8 KH[C::NKT][2];
-#pragma unroll
-  for (int ct = 0; ct < C::NKT; ++ct) {
-    const int row = (32 * ct + n) * C::LDC + 8 * h;
-    KH[ct][0] = ld8(&sl.kh[row]);
-    KH[ct][1] = ld8(&sl.kh[row + 16]);
-  }
+  for (int rt = 0; rt < 2; ++rt) Pf[rt] = ld8(&pp[(16 * rt + n) * C::LDC + 8 * g]);
   // Un = T Xn
-  const f16x8 x0 = bfrag(X, 0), x1 = bfrag(X, 1);
-  f32x16 U = (f32x16)0.0f;
-  U = mma32(t0, x0, U);
-  U = mma32(t1, x1, U);
-  const f16x8 u0 = bfrag(U, 0), u1 = bfrag(U, 1);
-  h16* uf = sm.uf[it.seq % 2];
-  *reinterpret_cast<f16x8*>(&uf[lane * 8]) = u0;
-  *reinterpret_cast<f16x8*>(&uf[(64 + lane) * 8]) = u1;
-  // S' = gamma S + (-KH)^T Un
+  const f16x8 xf = stack2(X[0], X[1]);
+  f32x4 U[2];
 #pragma unroll
-  for (int ct = 0; ct < C::NKT; ++ct) {
-    R.S[ct] = mma32(KH[ct][0], u0, R.S[ct]);
-    R.S[ct] = mma32(KH[ct][1], u1, R.S[ct]);
+  for (int rt = 0; rt < 2; ++rt) U[rt] = mma16(Tf[rt], xf, (f32x4)0.0f);
+  const f16x8 uf = stack2(U[0], U[1]);
+  // S' = gamma S + (-KH)^T Un;  O^T += Un^T (-P)^T
+#pragma unroll
+  for (int i = 0; i < C::NKT; ++i) R.S[i] = mma16(KH[i], uf, R.S[i]);
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) O[rt] = mma16(uf, Pf[rt], O[rt]);
+
+  // store: token 16 rt + n, columns 4g .. 4g + 3 of this wave's 16
+  const PrefillParams& p = cx.p;
+  const int rows = chunk_end(it.c, cx.T);
+  const int esz = p.o_f32 ? 4 : 2;
+  const int rs = p.H * p.dv * esz;
+  char* ob = static_cast<char*>(p.o) +
+             (((size_t)(cx.tok0 + it.c * CS) * p.H + cx.h) * p.dv + (cx.o_on ? cx.col0 + 16 * w : 0)) * esz;
+  const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(ob, cx.o_on ? rows * rs : 0);  // zero-length: stores dropped
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const int t = 16 * rt + n;
+    // tokens outside the item are pushed past the range, so their stores are dropped
+    const int voff = t * rs + 4 * g * esz + ((unsigned)(t - it.lo) < (unsigned)(it.hi - it.lo) ? 0 : 0x40000000);
+    const f32x4 y = O[rt] * R.usc;
+    if (p.o_f32) {
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, y), rsrc, voff, 0, 0);
+    } else {
+      // reinterpret the whole vector (single elements are miscompiled)
+      const bf16x4 b = {(__bf16)y[0], (__bf16)y[1], (__bf16)y[2], (__bf16)y[3]};
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, b), rsrc, voff, 0, 0);
+    }
   }
 }
 
 // Prepares item `it` (next for the state wave): column scale, fp16 fragments of
-// S (kept and published for the output wave) and -V * sc.
+// S and -V * sc.
 template <class C>
-__device__ void state_prepare(Smem4<C>& sm, StateRegs<C>& R, const Item& it, int lane) {
+__device__ void state_prepare(Smem4<C>& sm, StateRegs<C>& R, const Item& it, int w, int lane) {
   const ScanSlot<C>& sl = sm.ss[it.seq % 3];
-  const int h = opaque(lane / 32), n = opaque(lane % 32);
-  float vf[16];
+  const int g = opaque(lane / 16), n = opaque(lane % 16);
+  float vf[2][4];
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {  // rows 8jj + 4h .. +3 of column n
-    const u32x2 w = *reinterpret_cast<const u32x2*>(&sl.v[n * C::LDV + 8 * jj + 4 * h]);
-    vf[4 * jj + 0] = __builtin_bit_cast(float, w.x << 16);
-    vf[4 * jj + 1] = __builtin_bit_cast(float, w.x & 0xffff0000u);
-    vf[4 * jj + 2] = __builtin_bit_cast(float, w.y << 16);
-    vf[4 * jj + 3] = __builtin_bit_cast(float, w.y & 0xffff0000u);
+  for (int rt = 0; rt < 2; ++rt) {  // tokens 16 rt + 4g .. + 3 of column 16w + n
+    const u32x2 v2 = *reinterpret_cast<const u32x2*>(&sl.v[(16 * w + n) * C::LDV + 16 * rt + 4 * g]);
+    vf[rt][0] = __builtin_bit_cast(float, v2.x << 16);
+    vf[rt][1] = __builtin_bit_cast(float, v2.x & 0xffff0000u);
+    vf[rt][2] = __builtin_bit_cast(float, v2.y << 16);
+    vf[rt][3] = __builtin_bit_cast(float, v2.y & 0xffff0000u);
   }
   float ms = 0.0f, mv = 0.0f;
 #pragma unroll
-  for (int ct = 0; ct < C::NKT; ++ct)
+  for (int i = 0; i < C::NKT; ++i)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) ms = fmaxf(ms, fabsf(R.S[ct][i]));
+    for (int r = 0; r < 4; ++r) ms = fmaxf(ms, fabsf(R.S[i][r]));
 #pragma unroll
-  for (int i = 0; i < 16; ++i) mv = fmaxf(mv, fabsf(vf[i]));
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mv = fmaxf(mv, fabsf(vf[rt][r]));
+  ms = fmaxf(ms, __shfl_xor(ms, 16));
   ms = fmaxf(ms, __shfl_xor(ms, 32));
+  mv = fmaxf(mv, __shfl_xor(mv, 16));
   mv = fmaxf(mv, __shfl_xor(mv, 32));
   // Keep the scaled column maximum within [2^-4, 2^4]; rescale rarely.  The
   // scale is capped at 2^64: a column whose values have decayed below 2^-68
@@ -702,132 +795,79 @@ __device__ void state_prepare(Smem4<C>& sm, StateRegs<C>& R, const Item& it, int
       f = fminf(__builtin_amdgcn_ldexpf(1.0f, -ex), 0x1p64f / R.sc);  // powers of two: exact
     }
 #pragma unroll
-    for (int ct = 0; ct < C::NKT; ++ct) R.S[ct] *= f;
+    for (int i = 0; i < C::NKT; ++i) R.S[i] *= f;
     R.sc *= f;
+    // the output rows a lane holds are columns 4g .. 4g + 3: exchange the scales
+    if (g == 0) sm.scol[w][n] = __builtin_amdgcn_rcpf(R.sc);
+    wave_lds_sync();
+    R.usc = *reinterpret_cast<const f32x4*>(&sm.scol[w][4 * g]);
   }
 #pragma unroll
-  for (int i = 0; i < 16; ++i) R.vn[i] = -vf[i] * R.sc;
-  h16* sf = sm.sf[it.seq % 2];
+  for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-  for (int s = 0; s < C::NKS; ++s) {
-    R.Sf[s] = bfrag(R.S[s / 2], s % 2);
-    *reinterpret_cast<f16x8*>(&sf[(s * 64 + lane) * 8]) = R.Sf[s];
-  }
-  if (h == 0) sm.sexp[it.seq % 2][n] = __builtin_amdgcn_rcpf(R.sc);
-}
-
-// ---- output wave -------------------------------------------------------------------------
-// The output tile is carried transposed (both products take their operands in
-// swapped order): lane (n, h) holds token n, columns 8g + 4h .. +3 for g = 0..3,
-// so a lane writes four runs of 4 adjacent columns.  Four stores per step
-// instead of one per element: every vector memory instruction costs the
-// workgroup's shared texture addresser about as much whatever its width.
-template <class C>
-__device__ void out_pu_store(Smem4<C>& sm, f32x16& O, const f32x16& usc, const Item& it, const Ctx4& cx, int lane) {
-  const h16* pp = sm.p[it.seq % 3];
-  const h16* uf = sm.uf[it.seq % 2];
-  const int h = opaque(lane / 32), n = opaque(lane % 32);
-  O = mma32(ld8(&uf[lane * 8]), ld8(&pp[n * C::LDC + 8 * h]), O);
-  O = mma32(ld8(&uf[(64 + lane) * 8]), ld8(&pp[n * C::LDC + 16 + 8 * h]), O);
-  const PrefillParams& p = cx.p;
-  const int t0 = it.c * CS;
-  const int rows = chunk_end(it.c, cx.T);
-  const int esz = p.o_f32 ? 4 : 2;
-  const int rs = p.H * p.dv * esz;
-  char* ob = static_cast<char*>(p.o) + (((size_t)(cx.tok0 + t0) * p.H + cx.h) * p.dv + (cx.o_on ? cx.col0 : 0)) * esz;
-  const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(ob, cx.o_on ? rows * rs : 0);  // zero-length: stores dropped
-  // tokens outside the item are pushed past the range, so their stores are dropped
-  const int voff = n * rs + 4 * h * esz + ((unsigned)(n - it.lo) < (unsigned)(it.hi - it.lo) ? 0 : 0x40000000);
-  const f32x16 y = O * usc;
-  if (p.o_f32) {
+    for (int r = 0; r < 4; ++r) R.vn[rt][r] = -vf[rt][r] * R.sc;
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{y[4 * g], y[4 * g + 1], y[4 * g + 2], y[4 * g + 3]}),
-                                             rsrc, voff, 8 * g * 4, 0);
-  } else {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      // reinterpret the whole vector (single elements are miscompiled)
-      const bf16x4 b = {(__bf16)y[4 * g], (__bf16)y[4 * g + 1], (__bf16)y[4 * g + 2], (__bf16)y[4 * g + 3]};
-      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, b), rsrc, voff, 8 * g * 2, 0);
-    }
-  }
-}
-
-// Q_G S for the output wave (transposed), and the scale of each column it holds.
-template <class C>
-__device__ void out_qs(Smem4<C>& sm, f32x16& O, f32x16& usc, const Item& it, int lane) {
-  const ScanSlot<C>& sl = sm.ss[it.seq % 3];
-  const h16* sf = sm.sf[it.seq % 2];
-  const int h = opaque(lane / 32), n = opaque(lane % 32);
-  O = (f32x16)0.0f;
-#pragma unroll
-  for (int s = 0; s < C::NKS; ++s)
-    O = mma32(ld8(&sf[(s * 64 + lane) * 8]), ld8(&sl.qg[n * C::LDK + 16 * s + 8 * h]), O);
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const f32x4 w = *reinterpret_cast<const f32x4*>(&sm.sexp[it.seq % 2][8 * g + 4 * h]);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) usc[4 * g + e] = w[e];
-  }
+  for (int kb = 0; kb < C::NKB; ++kb) R.Sf[kb] = stack2(R.S[2 * kb], R.S[2 * kb + 1]);
 }
 
 // ---- kernel ---------------------------------------------------------------------------------
-enum Role { SCAN, SOLVE, PMAT, STATE, OUT };
+enum Role { SCAN, SOLVE, PMAT, STATE };
 
-// One wave's whole life: its own copy of the item sequence and its own
-// registers (each role is a separate loop, so no role pays for another's live
-// values).  Every role executes exactly one barrier per step.
-// Writes the state wave's S (32 columns; S = R.S / R.sc) to the [d_k][d_v]
+// Writes state wave w's S (16 columns; S = R.S / R.sc) to the [d_k][d_v]
 // matrix whose slab starts at dst.  Buffer stores with a per-lane offset and a
 // scalar row offset: no 64-bit address per element, and the stride is pinned
 // here so nothing of it is hoisted into the step loop around a call.
 template <class C>
-__device__ void store_state(float* dst, const StateRegs<C>& R, int dv_, int lane) {
+__device__ void store_state(float* dst, const StateRegs<C>& R, int dv_, int w, int lane) {
   const int dv = __builtin_amdgcn_readfirstlane(opaque(dv_));
-  const int h = lane / 32, n = lane % 32;
+  const int g = lane / 16, n = lane % 16;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(dst, C::DK * dv * 4);
-  const int voff = (4 * h * dv + n) * 4;
+  const int voff = (4 * g * dv + 16 * w + n) * 4;
   const float usc = __builtin_amdgcn_rcpf(R.sc);
 #pragma unroll
-  for (int ct = 0; ct < C::NKT; ++ct) {
+  for (int i = 0; i < C::NKT; ++i) {
     // Reinterpret the scaled tile as a whole: reinterpreting single elements of
     // a vector is miscompiled by this toolchain (every element reads element 0).
-    const u32x16 w = __builtin_bit_cast(u32x16, R.S[ct] * usc);
+    const u32x4 v = __builtin_bit_cast(u32x4, R.S[i] * usc);
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      __builtin_amdgcn_raw_buffer_store_b32(w[i], rs, voff, (32 * ct + 8 * (i / 4) + (i % 4)) * dv * 4, 0);
+    for (int r = 0; r < 4; ++r) __builtin_amdgcn_raw_buffer_store_b32(v[r], rs, voff, (16 * i + r) * dv * 4, 0);
   }
 }
 
+// One wave's whole life: its own copy of the item sequence and its own
+// registers (each role is a separate loop, so no role pays for another's live
+// values).  Every role executes exactly one barrier per step.
 template <class C, Role ROLE, bool G>
 __device__ void run_role(Smem4<C>& sm, const Ctx4& cx, const SnapList& snap, int lane, int sw) {
   const PrefillParams& p = cx.p;
   StateRegs<C> R;
+  // Scan inputs: the scan reads what it needs of chunk c out of raw first and
+  // then loads chunk c + 1 into it, so the loads have most of a step to land.
+  // rc: the chunk raw holds (a chunk regrouped into segments after that
+  // prefetch is loaded again).
   Raw4<C> raw;
-  int rc = -1;  // chunk held in raw
-  f32x16 O = (f32x16)0.0f;
-  f32x16 usc = (f32x16)1.0f;
+  int rc = -1;
   if constexpr (ROLE == STATE) {
-    const int h = lane / 32, n = lane % 32;
+    // state wave sw owns columns 16 sw .. 16 sw + 15 of the slab
+    const int g = lane / 16, n = lane % 16, col = 16 * sw + n;
 #pragma unroll
-    for (int ct = 0; ct < C::NKT; ++ct) R.S[ct] = (f32x16)0.0f;
+    for (int i = 0; i < C::NKT; ++i) R.S[i] = (f32x4)0.0f;
     if (cx.ident >= 0) {
 #pragma unroll
-      for (int ct = 0; ct < C::NKT; ++ct)
+      for (int i = 0; i < C::NKT; ++i)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) R.S[ct][i] = (32 * ct + 8 * (i / 4) + 4 * h + (i % 4) == cx.ident + n) ? 1.0f : 0.0f;
+        for (int r = 0; r < 4; ++r) R.S[i][r] = (16 * i + 4 * g + r == cx.ident + col) ? 1.0f : 0.0f;
     } else if (cx.s0) {
 #pragma unroll
-      for (int ct = 0; ct < C::NKT; ++ct)
+      for (int i = 0; i < C::NKT; ++i)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) R.S[ct][i] = cx.s0[(size_t)(32 * ct + 8 * (i / 4) + 4 * h + (i % 4)) * cx.s0_ld + n];
+        for (int r = 0; r < 4; ++r) R.S[i][r] = cx.s0[(size_t)(16 * i + 4 * g + r) * cx.s0_ld + col];
     }
     // Wait for the state loads once, here: otherwise the step loop carries a
-    // wait before each write to a state register (dozens of no-op waits per
-    // step on the state wave, which is on the step's critical path).
+    // wait before each write to a state register (no-op waits on the chain).
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
     R.sc = 1.0f;
+    R.usc = (f32x4)1.0f;
   }
   ScanSrc src{};
   if constexpr (ROLE == SCAN) {
@@ -840,44 +880,52 @@ __device__ void run_role(Smem4<C>& sm, const Ctx4& cx, const SnapList& snap, int
   block_sync_lds();  // the zeroed T ring is visible
 
   const Item none = {-1, 0, 0, 0, 0};
-  Item sI = none, bI = none, stI = none, opI = none;
+  Item sI = none, bI = none, stI = none;
   if (cx.nchunks > 0) sI = Item{0, 0, 0, chunk_end(0, cx.T), CS};
   int par = 0;
   int ns = 0;  // state role: next recorded position
-  while (sI.seq >= 0 || bI.seq >= 0 || stI.seq >= 0 || opI.seq >= 0) {
+  while (sI.seq >= 0 || bI.seq >= 0 || stI.seq >= 0) {
     if constexpr (ROLE == SCAN) {
       if (sI.seq >= 0) {
-        if (rc != sI.c) {
-          load_raw4<C, G>(raw, cx, src, sI.c, sw);
-          rc = sI.c;
-        }
-        scan4<C, G>(sm, raw, sI, cx.eA, sw, lane, par);
-        if (sI.hi == chunk_end(sI.c, cx.T) && sI.c + 1 < cx.nchunks) {
-          load_raw4<C, G>(raw, cx, src, sI.c + 1, sw);  // prefetch the next chunk
-          rc = sI.c + 1;
+        ScanIn<C> sin;
+        if (rc == sI.c) {
+          scan_read<C, G>(sin, sm, raw, sI, cx.eA, sw, lane);
+          // raw is read: the item that ends its chunk fetches the next chunk
+          // into it (the values read are pinned first, so no read of raw is
+          // moved after the loads that overwrite it)
+          if (sI.hi == chunk_end(sI.c, cx.T) && sI.c + 1 < cx.nchunks) {
+            pin(sin);
+            load_raw4<C, G>(raw, cx, src, sI.c + 1, sw);
+            rc = sI.c + 1;
+          }
+          scan4<C>(sm, sin, sI, sw, lane, par);
+        } else {
+          // a chunk regrouped after its successor was fetched (rare): loaded
+          // again into a buffer of its own, so raw keeps a single load site
+          Raw4<C> again;
+          load_raw4<C, G>(again, cx, src, sI.c, sw);
+          scan_read<C, G>(sin, sm, again, sI, cx.eA, sw, lane);
+          scan4<C>(sm, sin, sI, sw, lane, par);
         }
       }
     } else if constexpr (ROLE == SOLVE) {
       if (bI.seq >= 0) solve4<C>(sm, bI, lane);
     } else if constexpr (ROLE == PMAT) {
       if (bI.seq >= 0) pmat4<C>(sm, bI, lane);
-    } else if constexpr (ROLE == STATE) {
+    } else {
       if (stI.seq >= 0) {
-        state_step<C>(sm, R, stI, lane);
+        state_step<C>(sm, R, stI, cx, sw, lane);
         // record the state after a listed number of tokens
         if (ns < p.nsnap && stI.hi == chunk_end(stI.c, cx.T) && snap.pos[ns] == stI.c * CS + stI.hi) {
-          store_state<C>(p.snaps + ((size_t)cx.bh * p.nsnap + ns) * C::DK * p.dv + cx.col0, R, p.dv, lane);
+          store_state<C>(p.snaps + ((size_t)cx.bh * p.nsnap + ns) * C::DK * p.dv + cx.col0, R, p.dv, sw, lane);
           ++ns;
           // Drain the stores here, on this rare path: otherwise the next steps
           // carry a wait for them before every write to a register they might
-          // still read (dozens of no-op waits per step on the state wave).
+          // still read.
           __builtin_amdgcn_s_waitcnt(kVmcnt0);
         }
       }
-      if (bI.seq >= 0) state_prepare<C>(sm, R, bI, lane);
-    } else {
-      if (opI.seq >= 0) out_pu_store<C>(sm, O, usc, opI, cx, lane);
-      if (stI.seq >= 0) out_qs<C>(sm, O, usc, stI, lane);
+      if (bI.seq >= 0) state_prepare<C>(sm, R, bI, sw, lane);
     }
     // The scan item's successor is formed before the barrier, so after it only
     // the regroup vote remains to be read.
@@ -894,7 +942,6 @@ __device__ void run_role(Smem4<C>& sm, const Ctx4& cx, const SnapList& snap, int
       first = __builtin_amdgcn_readfirstlane(first);
     }
     const bool steep = first < CS;
-    opI = stI;
     stI = bI;
     bI = (sI.seq >= 0 && !steep) ? sI : none;
     if (sI.seq >= 0) sI = steep ? split_item(sI, first) : nI;
@@ -902,7 +949,7 @@ __device__ void run_role(Smem4<C>& sm, const Ctx4& cx, const SnapList& snap, int
   }
 
   if constexpr (ROLE == STATE) {
-    if (cx.st) store_state<C>(cx.st, R, cx.st_ld, lane);
+    if (cx.st) store_state<C>(cx.st, R, cx.st_ld, sw, lane);
   }
 }
 
@@ -912,12 +959,12 @@ __global__ __launch_bounds__(C::NT, 1) void kda_prefill_pipe_kernel(PrefillParam
   const int tid = threadIdx.x, lane = tid % 64;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   int task, slab;
-  task_of_block((p.split == 1 ? p.dv + C::DK : p.dv) / J, task, slab);
+  task_of_block((p.split == 1 ? p.dv + C::DK : p.dv) / C::J, task, slab);
   __shared__ int seq_lens[kMaxRankedSeqs], seq_pick;
   Ctx4 cx;
   cx.p = p;
   cx.h = task % p.H;
-  cx.col0 = slab * J;
+  cx.col0 = slab * C::J;
   cx.eA = G ? __expf(p.A[cx.h]) : 1.0f;
   const size_t mat = (size_t)C::DK * p.dv;  // elements of one state
   if (p.split) {
@@ -957,27 +1004,27 @@ __global__ __launch_bounds__(C::NT, 1) void kda_prefill_pipe_kernel(PrefillParam
   cx.nchunks = (cx.T + CS - 1) / CS;
   // T's upper-right 16x16 block is read as zeros and never written
   for (int i = tid; i < 2 * CS * C::LDC; i += C::NT) (&sm.t[0][0])[i] = (h16)0.0f;
-  // Waves w and w + 4 share a SIMD.  The scan waves and the state wave carry the
-  // step's critical path, while the L/T, P and output waves wait at the barrier
-  // for a good part of each step, so the former issue first (measured: a 5%
-  // shorter step; raising the scan waves alone starved the state wave).
+  // Waves w and w + 4 share a SIMD: the two state waves (SIMDs 0 and 1) and the
+  // L/T and P waves (SIMDs 2 and 3) each share one with a scan wave.  The scan
+  // and state waves carry the step's critical path, so they issue first.
   if (wave >= 4) {
     __builtin_amdgcn_s_setprio(3);
     run_role<C, SCAN, G>(sm, cx, snap, lane, wave - 4);
-  } else if (wave == 0) {
+  } else if (wave < 2) {
     __builtin_amdgcn_s_setprio(3);
-    run_role<C, STATE, G>(sm, cx, snap, lane, 0);
+    run_role<C, STATE, G>(sm, cx, snap, lane, wave);
+  } else if (wave == 2) {
+    run_role<C, SOLVE, G>(sm, cx, snap, lane, 0);
+  } else {
+    run_role<C, PMAT, G>(sm, cx, snap, lane, 0);
   }
-  else if (wave == 1) run_role<C, SOLVE, G>(sm, cx, snap, lane, 0);
-  else if (wave == 2) run_role<C, PMAT, G>(sm, cx, snap, lane, 0);
-  else run_role<C, OUT, G>(sm, cx, snap, lane, 0);
 }
 
-template <int DK>
+template <int DK, int NST>
 hipError_t launch_pipe(const PrefillParams& p, const SnapList& snap, hipStream_t s) {
-  using C = Cfg4<DK>;
+  using C = Cfg4<DK, NST>;
   const int tasks = p.B * p.H * (p.split == 1 ? p.nparts - 1 : p.split == 2 ? p.nparts : 1);
-  const unsigned grid = (unsigned)(tasks * ((p.split == 1 ? p.dv + DK : p.dv) / J));
+  const unsigned grid = (unsigned)(tasks * ((p.split == 1 ? p.dv + DK : p.dv) / C::J));
   if (p.z) hipLaunchKernelGGL((kda_prefill_pipe_kernel<C, true>), dim3(grid), dim3(C::NT), 0, s, p, snap);
   else hipLaunchKernelGGL((kda_prefill_pipe_kernel<C, false>), dim3(grid), dim3(C::NT), 0, s, p, snap);
   return hipGetLastError();
@@ -988,13 +1035,13 @@ hipError_t launch_pipe(const PrefillParams& p, const SnapList& snap, hipStream_t
 bool prefill_pipe_supported(int io_dtype, int dk, int dv, int chunk, int H) {
   // per-chunk buffer ranges (32 tokens of every head) must fit 31 bits
   const long long chunk_bytes = (long long)CS * H * (dk > dv ? dk : dv) * 4;
-  return io_dtype == 1 && (dk == 64 || dk == 128) && dv % J == 0 && (chunk == 32 || chunk == 64) &&
+  return io_dtype == 1 && (dk == 64 || dk == 128) && dv % 32 == 0 && (chunk == 32 || chunk == 64) &&
          chunk_bytes < (1LL << 31);
 }
 
 hipError_t launch_prefill_pipe(const PrefillParams& p, const SnapList& snap, hipStream_t s) {
-  if (p.dk == 128) return launch_pipe<128>(p, snap, s);
-  if (p.dk == 64) return launch_pipe<64>(p, snap, s);
+  if (p.dk == 128) return launch_pipe<128, 2>(p, snap, s);
+  if (p.dk == 64) return launch_pipe<64, 2>(p, snap, s);
   return hipErrorInvalidValue;
 }
 
