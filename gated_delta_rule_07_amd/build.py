@@ -20,12 +20,14 @@ LIB = PKG / "libkda.so"
 TEST_LIB = PKG / "libkda_testhooks.so"
 OBJDIR = PKG / "_build"
 
-SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_prefill.hip", "kda_prefill_pipe.hip", "kda_spec.hip",
-           "kda_split.hip"]
+SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_prefill.hip", "kda_prefill_pipe.hip", "kda_prep.hip",
+           "kda_spec.hip", "kda_split.hip"]
 
 ARCH = "gfx950"
-# Packed-fp32 VALU forms are disabled: plain fp32 code only.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Packed-fp32 VALU forms are disabled: plain fp32 code only.  Matrix-core
+# accumulators stay in ordinary VGPRs: with one wave per SIMD the compiler would
+# otherwise park them in AccVGPRs and copy them out for every VALU use.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 

@@ -7,6 +7,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "../../include/kda.h"
@@ -55,11 +56,13 @@ bool sizes_ok(long long B, long long T, long long H, long long dk, long long dv)
   return true;
 }
 
-// Prefill kernel choice.  The pipeline kernel serves bf16 q/k/v with d_k in
-// {64,128}, d_v % 32 == 0 and chunk 32 or 64 (it runs 32-token chunks); the
+// Prefill kernel choice.  bf16 q/k/v with d_k in {64,128}, d_v % 32 == 0 and
+// chunk 32 or 64 run 32-token chunks: by the two-stage prefill (chunk records
+// for all chunks at once, then the chain), or by the single-kernel pipeline
+// where the records' workspace cannot be had (and for split calls).  The
 // generic 16x16-tile kernel serves everything else, with 16 state columns per
 // workgroup unless 32-column slabs still give one workgroup per compute unit.
-enum PrefillImpl { IMPL_GENERIC, IMPL_PIPE };
+enum PrefillImpl { IMPL_GENERIC, IMPL_PIPE, IMPL_CHAIN };
 struct PrefillPlan {
   PrefillImpl impl;
   int slab;
@@ -69,8 +72,9 @@ struct PrefillPlan {
 // Test builds only (libkda_testhooks.so): a process-wide override of the kernel
 // choice, so tests can run the generic kernel on shapes the pipeline kernel
 // would take and pick its slab width.  The product library has no such state.
-int g_force_impl = -1;  // -1: the library's choice; 0: generic; 1: pipeline
+int g_force_impl = -1;  // -1: the library's choice; 0: generic; 1: pipeline; 2: two-stage
 int g_force_slab = 0;   // 0: the library's choice; 16 or 32
+size_t g_rec_cap = 0;   // 0: the library's cap on the two-stage workspace
 #endif
 
 PrefillPlan plan_prefill(int B, int H, int dk, int dv, int chunk, int io) {
@@ -79,7 +83,8 @@ PrefillPlan plan_prefill(int B, int H, int dk, int dv, int chunk, int io) {
   impl = g_force_impl;
   if ((g_force_slab == 16 || g_force_slab == 32) && dv % g_force_slab == 0) forced = g_force_slab;
 #endif
-  if (impl != 0 && !forced && kda::prefill_pipe_supported(io, dk, dv, chunk, H)) return {IMPL_PIPE, 32};
+  if (impl != 0 && !forced && kda::prefill_pipe_supported(io, dk, dv, chunk, H))
+    return {impl == 1 ? IMPL_PIPE : IMPL_CHAIN, 32};
   if (forced) return {IMPL_GENERIC, forced};
   if (io == 1 && dv % 32 == 0 && (long long)B * H * (dv / 32) >= 256) return {IMPL_GENERIC, 32};
   return {IMPL_GENERIC, 16};
@@ -155,6 +160,100 @@ int device_cus() {
   return n;
 }
 
+// ---- two-stage prefill: the chunk records' workspace ----------------------------------
+// The records (one per sequence, head and 32-token chunk) live in a memory pool
+// the library owns on each device, allocated and freed in stream order on the
+// caller's stream around the two stages; the pool keeps its memory, so later
+// calls reuse it without synchronising.  At most kRecCapBytes at a time: a longer
+// batch of equal-length sequences runs in blocks of chunks (stage 1 then stage 2
+// per block, the state carried through S_T or a pool buffer); a packed batch
+// whose records exceed the cap runs on the single-kernel pipeline instead.
+constexpr size_t kRecCapBytes = (size_t)1 << 30;
+
+size_t rec_cap() {
+#ifdef KDA_TEST_HOOKS
+  if (g_rec_cap) return g_rec_cap;
+#endif
+  return kRecCapBytes;
+}
+
+constexpr int kMaxPoolDevices = 64;
+std::mutex g_pool_mu;
+hipMemPool_t g_pool[kMaxPoolDevices];
+
+hipError_t pool_of_current_device(hipMemPool_t* out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxPoolDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_pool_mu);
+  if (!g_pool[dev]) {
+    hipMemPoolProps props;
+    memset(&props, 0, sizeof props);
+    props.allocType = hipMemAllocationTypePinned;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t pool = nullptr;
+    e = hipMemPoolCreate(&pool, &props);
+    if (e != hipSuccess) return e;
+    uint64_t keep = UINT64_MAX;  // never hand memory back at synchronisation
+    e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+    if (e != hipSuccess) {
+      (void)hipMemPoolDestroy(pool);
+      return e;
+    }
+    g_pool[dev] = pool;
+  }
+  *out = g_pool[dev];
+  return hipSuccess;
+}
+
+// Runs the two-stage prefill.  *ran = false (nothing enqueued, hipSuccess) when
+// the workspace is over the cap or cannot be allocated: the caller then runs
+// the single-kernel pipeline.
+hipError_t run_two_stage(kda::PrefillParams p, const kda::SnapList& snap, hipStream_t hs, bool* ran) {
+  *ran = false;
+  const size_t rb = (size_t)kda::chunk_rec_bytes(p.dk);
+  const size_t cap = rec_cap();
+  const long long nch = ((long long)p.T + kda::kPipeChunk - 1) / kda::kPipeChunk;
+  long long nslots, nc = 0, nblk = 1;
+  if (p.cu) {
+    nslots = (long long)p.T / kda::kPipeChunk + p.B + 1;  // slots cu[b] / 32 + b + c
+    if ((size_t)nslots * p.H * rb > cap) return hipSuccess;
+  } else {
+    const size_t per_chunk = (size_t)p.B * p.H * rb;  // one chunk of every sequence
+    if (per_chunk > cap) return hipSuccess;
+    nc = std::max(1LL, std::min(nch, (long long)(cap / per_chunk)));
+    nblk = std::max(1LL, (nch + nc - 1) / nc);
+    nslots = (long long)p.B * nc;
+  }
+  const size_t rec_bytes = (size_t)nslots * p.H * rb;
+  const size_t carry_bytes = (nblk > 1 && !p.S_T) ? (size_t)4 * p.B * p.H * p.dk * p.dv : 0;
+  hipMemPool_t pool = nullptr;
+  hipError_t e = pool_of_current_device(&pool);
+  if (e != hipSuccess) return e;
+  void* ws = nullptr;
+  if (hipMallocFromPoolAsync(&ws, rec_bytes + carry_bytes, pool, hs) != hipSuccess || !ws) {
+    (void)hipGetLastError();  // out of memory here is not an error of the call
+    return hipSuccess;
+  }
+  *ran = true;
+  const float* S0 = p.S0;
+  float* S_T = p.S_T;
+  float* carry = S_T ? S_T : reinterpret_cast<float*>(static_cast<char*>(ws) + rec_bytes);
+  p.rec = static_cast<char*>(ws);
+  for (long long blk = 0; blk < nblk && e == hipSuccess; ++blk) {
+    p.rec_c0 = (int)(blk * nc);
+    p.rec_nc = (int)nc;
+    p.S0 = blk == 0 ? S0 : carry;         // each workgroup reads its slab of S0 before
+    p.S_T = blk == nblk - 1 ? S_T : carry;  // it writes the same slab of S_T
+    e = kda::launch_prefill_prep(p, nslots, hs);
+    if (e == hipSuccess) e = kda::launch_prefill_chain(p, snap, hs);
+  }
+  const hipError_t fe = hipFreeAsync(ws, hs);
+  return e != hipSuccess ? e : fe;
+}
+
 // A split request: parts == 0 lets the library choose (num_cus == 0: the current
 // device's compute units).
 struct SplitReq {
@@ -218,11 +317,59 @@ int kda_version(void) { return kVersion; }
 
 #ifdef KDA_TEST_HOOKS
 // Test builds only: force the prefill kernel (impl -1: the library's choice, 0:
-// the generic kernel, 1: the pipeline kernel where it applies) and the generic
+// the generic kernel, 1: the single-kernel pipeline where it applies, 2: the
+// two-stage prefill where it applies) and the generic
 // kernel's slab width (0: the library's choice, 16 or 32).  Not thread-safe.
 void kda_test_force_prefill(int impl, int slab) {
   g_force_impl = impl;
   g_force_slab = slab;
+}
+// Test builds only: the two-stage prefill's workspace cap in bytes (0: the
+// library's), so small calls exercise the blocked path.  Not thread-safe.
+void kda_test_set_rec_cap(unsigned long long bytes) { g_rec_cap = (size_t)bytes; }
+
+// Test builds only: the two stages of the two-stage prefill run alone, on B
+// sequences of T tokens (bf16 q/k/v, d_k in {64, 128}, no checks beyond the
+// shape): stage 1 writes the records of every chunk to rec (ceil(T/32) * B * H
+// records, slot b * ceil(T/32) + c); stage 2 runs the chain from records in rec.
+int kda_test_prep(const void* q, const void* k, const float* alpha, const float* beta, int B, int T, int H,
+                  int d_k, void* rec, hipStream_t stream) {
+  if (kda::chunk_rec_bytes(d_k) == 0 || B < 1 || H < 1 || T < 1) return KDA_ERR_UNSUPPORTED;
+  kda::PrefillParams p{};
+  p.q = q;
+  p.k = k;
+  p.alpha = alpha;
+  p.beta = beta;
+  p.B = B;
+  p.T = T;
+  p.H = H;
+  p.dk = d_k;
+  p.rec = static_cast<char*>(rec);
+  p.rec_c0 = 0;
+  p.rec_nc = (T + kda::kPipeChunk - 1) / kda::kPipeChunk;
+  const hipError_t e = kda::launch_prefill_prep(p, (long long)B * p.rec_nc, stream);
+  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+int kda_test_chain(const void* v, const void* rec, const float* S0, float* o, float* S_T, int B, int T, int H,
+                   int d_k, int d_v, hipStream_t stream) {
+  if (kda::chunk_rec_bytes(d_k) == 0 || B < 1 || H < 1 || T < 1 || d_v % 32) return KDA_ERR_UNSUPPORTED;
+  kda::PrefillParams p{};
+  p.v = v;
+  p.S0 = S0;
+  p.o = o;
+  p.S_T = S_T;
+  p.B = B;
+  p.T = T;
+  p.H = H;
+  p.dk = d_k;
+  p.dv = d_v;
+  p.o_f32 = 1;
+  p.rec = static_cast<char*>(const_cast<void*>(rec));
+  p.rec_c0 = 0;
+  p.rec_nc = (T + kda::kPipeChunk - 1) / kda::kPipeChunk;
+  kda::SnapList snap{};
+  const hipError_t e = kda::launch_prefill_chain(p, snap, stream);
+  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 #endif
 
@@ -290,7 +437,7 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, int qkv_d
   if (split) {
     if (split->parts < 0 || split->num_cus < 0) return KDA_ERR_SHAPE;
     if (split->parts != 1 && (cu || n_snap > 0)) return KDA_ERR_UNSUPPORTED;
-    if (plan.impl != IMPL_PIPE) {
+    if (plan.impl == IMPL_GENERIC) {
       if (split->parts > 1) return KDA_ERR_UNSUPPORTED;
     } else if (split->parts > 1) {
       sh = split_shape_for(T, split->parts);
@@ -345,9 +492,15 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, int qkv_d
     if (e == hipSuccess) e = kda::launch_split_combine(p, hs);
     p.split = 2;
     if (e == hipSuccess) e = kda::launch_prefill_pipe(p, snap, hs);
+  } else if (plan.impl == IMPL_CHAIN && !(split && split->scratch)) {
+    // (a one-part split is this same single pass; the allocation-free call
+    // takes the pipeline, which needs no workspace)
+    bool ran = false;
+    e = run_two_stage(p, snap, hs, &ran);
+    if (e == hipSuccess && !ran) e = kda::launch_prefill_pipe(p, snap, hs);
   } else {
-    e = plan.impl == IMPL_PIPE ? kda::launch_prefill_pipe(p, snap, hs)
-                               : kda::launch_prefill(p, snap, io, chunk, plan.slab, hs);
+    e = plan.impl == IMPL_GENERIC ? kda::launch_prefill(p, snap, io, chunk, plan.slab, hs)
+                                  : kda::launch_prefill_pipe(p, snap, hs);
   }
   if (e != hipSuccess) {
     g_last_hip_error = (int)e;
@@ -404,7 +557,7 @@ kda_status kda_chunk_fwd_run_chunk(kda_dtype qkv_dtype, int H, int d_k, int d_v,
   if (!run_chunk) return KDA_ERR_NULL;
   const int io = io_of(raw_enum(qkv_dtype));
   const PrefillPlan plan = plan_prefill(1, H, d_k, d_v, chunk, io);
-  if (plan.impl == IMPL_PIPE) {
+  if (plan.impl == IMPL_PIPE || plan.impl == IMPL_CHAIN) {
     *run_chunk = kda::kPipeChunk;
     return KDA_OK;
   }
@@ -424,7 +577,7 @@ kda_status kda_chunk_fwd_split_plan(kda_dtype qkv_dtype, int B, int T, int H, in
   if (!parts_out || !workspace_bytes) return KDA_ERR_NULL;
   const int io = io_of(raw_enum(qkv_dtype));
   SplitShape sh{1, T};
-  if (plan_prefill(B, H, d_k, d_v, chunk, io).impl != IMPL_PIPE) {
+  if (plan_prefill(B, H, d_k, d_v, chunk, io).impl == IMPL_GENERIC) {  // splits run the pipeline kernel
     if (parts > 1) return KDA_ERR_UNSUPPORTED;
   } else if (parts > 1) {
     sh = split_shape_for(T, parts);

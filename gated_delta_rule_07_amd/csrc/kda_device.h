@@ -154,4 +154,39 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+
+// ---- 16x16 matrix-core steps on C tiles --------------------------------------
+// A C tile feeds a B operand as it is; the A operand of a matrix M is the C tile
+// of M^T, so a matrix that multiplies from the left is also carried transposed.
+__device__ __forceinline__ f32x4 mma16x32(const f16x8& a, const f16x8& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16x16(const f16x4& a, const f16x4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f16x4 h4(const f32x4& v) {
+  return f16x4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+}
+
+// (I + L_bb)^{-1} for a strictly lower 16x16 block, given N = -L_bb and N^T as C
+// tiles: the product (I + N)(I + N^2)(I + N^4)(I + N^8), exact because N^16 = 0.
+// Returns D = (I + L_bb)^{-1} and D^T.
+__device__ __forceinline__ void unit_lower_inverse(f32x4 P, f32x4 Pt, const f32x4& eye, f32x4& R, f32x4& Rt) {
+  R = eye + P;
+  Rt = eye + Pt;
+#pragma unroll
+  for (int lv = 0; lv < 3; ++lv) {
+    const f16x4 p = h4(P), pt = h4(Pt);
+    const f32x4 P2 = mma16x16(pt, p, (f32x4)0.0f);  // P P
+    const f16x4 ip2 = h4(eye + P2);
+    const f16x4 rt = h4(Rt);
+    R = mma16x16(rt, ip2, (f32x4)0.0f);    // R (I + P^2)
+    Rt = mma16x16(ip2, rt, (f32x4)0.0f);   // (I + P^2)^T R^T
+    if (lv < 2) {
+      Pt = mma16x16(p, pt, (f32x4)0.0f);   // P^T P^T
+      P = P2;
+    }
+  }
+}
+
 }  // namespace kda

@@ -40,6 +40,12 @@ struct PrefillParams {
   float* ws_trans;
   float* ws_in;
   float* ws_tree;  // nparts >= kTreeParts: a second [B][nparts-1][H][dk][dv+dk] buffer
+  // Two-stage prefill: the chunk records of stage 1 (ChunkRec layout), indexed
+  // by slot * H + h.  Without cu, slot = b * rec_nc + (c - rec_c0) for the chunks
+  // c in [rec_c0, rec_c0 + rec_nc) of every sequence (one block of a sequence
+  // processed in several blocks); with cu, slot = cu[b] / 32 + b + c (rec_c0 = 0).
+  char* rec;
+  int rec_c0, rec_nc;
 };
 
 // Part counts from which the combine runs as a tree over the parts (log2 levels)
@@ -144,6 +150,40 @@ hipError_t launch_prefill(const PrefillParams& p, const SnapList& snap, int io_d
 constexpr int kPipeChunk = 32;
 bool prefill_pipe_supported(int io_dtype, int dk, int dv, int chunk, int H);
 hipError_t launch_prefill_pipe(const PrefillParams& p, const SnapList& snap, hipStream_t s);
+
+// ---- two-stage prefill -------------------------------------------------------------
+// Stage 1 (prep) computes, for every (sequence, head, 32-token chunk) at once,
+// the chunk-local operands of the chunkwise form; stage 2 (chain) streams them
+// through the sequential state update.  The record of one chunk: fp16 matrix-core
+// fragments of 64 lanes x 16 bytes, then gamma.  Lane l = 16 g + n of a fragment
+// holds 8 values (columns listed in slot order):
+//   KG, QG [rt][kb] : token 16 rt + n, channels 32 kb + {4g..4g+3, 16+4g..16+4g+3}
+//   T, -P  [rt]     : row 16 rt + n, columns {4g..4g+3, 16+4g..16+4g+3}
+//   -KH^T  [i]      : channel 16 i + n, tokens {4g..4g+3, 16+4g..16+4g+3}
+//   gamma           : d_k fp32
+template <int DK>
+struct ChunkRec {
+  static constexpr int NKB = DK / 32, NKT = DK / 16;
+  static constexpr int KG = 0;
+  static constexpr int QG = KG + 2 * NKB * 1024;
+  static constexpr int TT = QG + 2 * NKB * 1024;
+  static constexpr int PP = TT + 2 * 1024;
+  static constexpr int KH = PP + 2 * 1024;
+  static constexpr int GAM = KH + NKT * 1024;
+  static constexpr int BYTES = GAM + DK * 4;
+};
+// Bytes of one chunk record (0: no two-stage kernels for d_k).
+inline int chunk_rec_bytes(int dk) {
+  return dk == 128 ? ChunkRec<128>::BYTES : dk == 64 ? ChunkRec<64>::BYTES : 0;
+}
+// bf16 q/k/v, d_k in {64, 128}, d_v % 32 == 0.
+bool prefill_chain_supported(int io_dtype, int dk, int dv, int chunk, int H);
+// Stage 1 over the records that p.rec, p.rec_c0 and p.rec_nc describe (nslots
+// slots of H records each).
+hipError_t launch_prefill_prep(const PrefillParams& p, long long nslots, hipStream_t s);
+// Stage 2: without cu, the chunks [rec_c0, rec_c0 + rec_nc) of every sequence,
+// from S0 to S_T (either may be null: zeros / not written).
+hipError_t launch_prefill_chain(const PrefillParams& p, const SnapList& snap, hipStream_t s);
 
 // Between the two split passes: ws_in[b][0] = S0 (zeros when null) and
 // ws_in[b][j+1] = M_j ws_in[b][j] + N_j from ws_trans, for every (b, h): a

@@ -534,41 +534,8 @@ __device__ void scan4(Smem4<C>& sm, const ScanIn<C>& sin, const Item& it, int sw
 }
 
 // ---- L, T wave -------------------------------------------------------------------------
-// 16x16 matrix-core steps: lane (g = l/16, n = l%16); C tiles hold rows 4g+j,
-// column n.  A C tile feeds a B operand directly; the A operand of M is the C
-// tile of M^T, so every matrix is also carried transposed.
-typedef _Float16 f16x4v __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f32x4 mma16x32(const f16x8& a, const f16x8& b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mma16x16(const f16x4v& a, const f16x4v& b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f16x4v h4(const f32x4& v) { return f16x4v{(h16)v[0], (h16)v[1], (h16)v[2], (h16)v[3]}; }
-
-// (I + L_bb)^{-1} for a strictly lower 16x16 block given N = -L_bb and N^T (C
-// tiles): the product (I + N)(I + N^2)(I + N^4)(I + N^8), exact because N^16 = 0.
-// Returns D and D^T.
-__device__ __forceinline__ void unit_lower_inverse(f32x4 P, f32x4 Pt, const f32x4& eye, f32x4& R, f32x4& Rt) {
-  R = eye + P;
-  Rt = eye + Pt;
-#pragma unroll
-  for (int lv = 0; lv < 3; ++lv) {
-    const f16x4v p = h4(P), pt = h4(Pt);
-    const f32x4 P2 = mma16x16(pt, p, (f32x4)0.0f);  // P P
-    const f16x4v ip2 = h4(eye + P2);
-    const f16x4v r = h4(R), rt = h4(Rt);
-    R = mma16x16(rt, ip2, (f32x4)0.0f);    // R (I + P^2)
-    Rt = mma16x16(ip2, rt, (f32x4)0.0f);   // (I + P^2)^T R^T
-    if (lv < 2) {
-      Pt = mma16x16(p, pt, (f32x4)0.0f);   // P^T P^T
-      P = P2;
-    }
-    (void)r;
-  }
-}
-
+// 16x16 matrix-core steps on C tiles (lane g = l/16, n = l%16 holds rows 4g+j of
+// column n); the helpers are in kda_device.h.
 template <class C>
 __device__ void solve4(Smem4<C>& sm, const Item& it, int lane) {
   const ScanSlot<C>& sl = sm.ss[it.seq % 3];
@@ -680,6 +647,34 @@ __device__ __forceinline__ f16x8 stack2(const f32x4& lo, const f32x4& hi) {
   return f16x8{(h16)lo[0], (h16)lo[1], (h16)lo[2], (h16)lo[3], (h16)hi[0], (h16)hi[1], (h16)hi[2], (h16)hi[3]};
 }
 
+// Stores a state wave's output tiles (token 16 rt + n, columns 4g .. 4g + 3 of the
+// wave's 16, times their column scales usc) of item `it`.
+__device__ __forceinline__ void store_out(const Ctx4& cx, const Item& it, const f32x4 (&O)[2], const f32x4& usc, int w,
+                                          int lane) {
+  const int g = opaque(lane / 16), n = opaque(lane % 16);
+  const PrefillParams& p = cx.p;
+  const int rows = chunk_end(it.c, cx.T);
+  const int esz = p.o_f32 ? 4 : 2;
+  const int rs = p.H * p.dv * esz;
+  char* ob = static_cast<char*>(p.o) +
+             (((size_t)(cx.tok0 + it.c * CS) * p.H + cx.h) * p.dv + (cx.o_on ? cx.col0 + 16 * w : 0)) * esz;
+  const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(ob, cx.o_on ? rows * rs : 0);  // zero-length: stores dropped
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const int t = 16 * rt + n;
+    // tokens outside the item are pushed past the range, so their stores are dropped
+    const int voff = t * rs + 4 * g * esz + ((unsigned)(t - it.lo) < (unsigned)(it.hi - it.lo) ? 0 : 0x40000000);
+    const f32x4 y = O[rt] * usc;
+    if (p.o_f32) {
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, y), rsrc, voff, 0, 0);
+    } else {
+      // reinterpret the whole vector (single elements are miscompiled)
+      const bf16x4 b = {(__bf16)y[0], (__bf16)y[1], (__bf16)y[2], (__bf16)y[3]};
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, b), rsrc, voff, 0, 0);
+    }
+  }
+}
+
 // One item of the chain for state wave w (columns 16w .. 16w + 15 of the slab),
 // with the output of those columns stored.
 template <class C>
@@ -730,28 +725,63 @@ __device__ void state_step(Smem4<C>& sm, StateRegs<C>& R, const Item& it, const 
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) O[rt] = mma16(uf, Pf[rt], O[rt]);
 
-  // store: token 16 rt + n, columns 4g .. 4g + 3 of this wave's 16
-  const PrefillParams& p = cx.p;
-  const int rows = chunk_end(it.c, cx.T);
-  const int esz = p.o_f32 ? 4 : 2;
-  const int rs = p.H * p.dv * esz;
-  char* ob = static_cast<char*>(p.o) +
-             (((size_t)(cx.tok0 + it.c * CS) * p.H + cx.h) * p.dv + (cx.o_on ? cx.col0 + 16 * w : 0)) * esz;
-  const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(ob, cx.o_on ? rows * rs : 0);  // zero-length: stores dropped
+  store_out(cx, it, O, R.usc, w, lane);
+}
+
+// Maximum over the four lanes l % 16 == n (the four lane groups of a C-tile
+// column): lane swaps across halves and across rows, no trip through LDS.
+__device__ __forceinline__ float column_max(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto h = __builtin_amdgcn_permlane32_swap(u, u, false, false);    // lanes l and l ^ 32
+  const float y = fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+  const unsigned v = __float_as_uint(y);
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);    // lanes l and l ^ 16
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Column scale of a state wave for its next item, given the item's V values vf
+// (tokens 16 rt + 4g + r of column n), and the fp16 fragments of S and -V * sc.
+// scol: the wave's 16 column reciprocals in LDS.
+template <class C>
+__device__ __forceinline__ void state_rescale(StateRegs<C>& R, const float (&vf)[2][4], float* scol, int g, int n) {
+  // this lane's maxima of |S| (a tree, not a chain) and of |V| times the scale
+  float t[C::NKT];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const int t = 16 * rt + n;
-    // tokens outside the item are pushed past the range, so their stores are dropped
-    const int voff = t * rs + 4 * g * esz + ((unsigned)(t - it.lo) < (unsigned)(it.hi - it.lo) ? 0 : 0x40000000);
-    const f32x4 y = O[rt] * R.usc;
-    if (p.o_f32) {
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, y), rsrc, voff, 0, 0);
-    } else {
-      // reinterpret the whole vector (single elements are miscompiled)
-      const bf16x4 b = {(__bf16)y[0], (__bf16)y[1], (__bf16)y[2], (__bf16)y[3]};
-      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, b), rsrc, voff, 0, 0);
+  for (int i = 0; i < C::NKT; ++i)
+    t[i] = fmaxf(fmaxf(fabsf(R.S[i][0]), fabsf(R.S[i][1])), fmaxf(fabsf(R.S[i][2]), fabsf(R.S[i][3])));
+#pragma unroll
+  for (int w = C::NKT / 2; w >= 1; w /= 2)
+#pragma unroll
+    for (int i = 0; i < w; ++i) t[i] = fmaxf(t[i], t[i + w]);
+  const float mv = fmaxf(fmaxf(fmaxf(fabsf(vf[0][0]), fabsf(vf[0][1])), fmaxf(fabsf(vf[0][2]), fabsf(vf[0][3]))),
+                         fmaxf(fmaxf(fabsf(vf[1][0]), fabsf(vf[1][1])), fmaxf(fabsf(vf[1][2]), fabsf(vf[1][3]))));
+  // Keep the scaled column maximum within [2^-4, 2^4]; rescale rarely.  The
+  // scale is capped at 2^64: a column whose values have decayed below 2^-68
+  // with no value input (a transition column, or an all-zero V column) stays
+  // there, so the scale never overflows to infinity (0 * inf would be NaN).
+  // (The four lanes of a column share its scale, so the maximum is taken once.)
+  const float m = column_max(fmaxf(t[0], mv * R.sc));
+  const bool bad = m > 16.0f || (m > 0.0f && m < 0.0625f && R.sc < 0x1p64f);
+  if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+    float f = 1.0f;
+    if (bad) {
+      const int ex = __builtin_amdgcn_frexp_expf(m);  // m = frac * 2^ex, frac in [0.5, 1)
+      f = fminf(__builtin_amdgcn_ldexpf(1.0f, -ex), 0x1p64f / R.sc);  // powers of two: exact
     }
+#pragma unroll
+    for (int i = 0; i < C::NKT; ++i) R.S[i] *= f;
+    R.sc *= f;
+    // the output rows a lane holds are columns 4g .. 4g + 3: exchange the scales
+    if (g == 0) scol[n] = __builtin_amdgcn_rcpf(R.sc);
+    wave_lds_sync();
+    R.usc = *reinterpret_cast<const f32x4*>(&scol[4 * g]);
   }
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) R.vn[rt][r] = -vf[rt][r] * R.sc;
+#pragma unroll
+  for (int kb = 0; kb < C::NKB; ++kb) R.Sf[kb] = stack2(R.S[2 * kb], R.S[2 * kb + 1]);
 }
 
 // Prepares item `it` (next for the state wave): column scale, fp16 fragments of
@@ -769,45 +799,7 @@ __device__ void state_prepare(Smem4<C>& sm, StateRegs<C>& R, const Item& it, int
     vf[rt][2] = __builtin_bit_cast(float, v2.y << 16);
     vf[rt][3] = __builtin_bit_cast(float, v2.y & 0xffff0000u);
   }
-  float ms = 0.0f, mv = 0.0f;
-#pragma unroll
-  for (int i = 0; i < C::NKT; ++i)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) ms = fmaxf(ms, fabsf(R.S[i][r]));
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) mv = fmaxf(mv, fabsf(vf[rt][r]));
-  ms = fmaxf(ms, __shfl_xor(ms, 16));
-  ms = fmaxf(ms, __shfl_xor(ms, 32));
-  mv = fmaxf(mv, __shfl_xor(mv, 16));
-  mv = fmaxf(mv, __shfl_xor(mv, 32));
-  // Keep the scaled column maximum within [2^-4, 2^4]; rescale rarely.  The
-  // scale is capped at 2^64: a column whose values have decayed below 2^-68
-  // with no value input (a transition column, or an all-zero V column) stays
-  // there, so the scale never overflows to infinity (0 * inf would be NaN).
-  const float m = fmaxf(ms, mv * R.sc);
-  const bool bad = m > 16.0f || (m > 0.0f && m < 0.0625f && R.sc < 0x1p64f);
-  if (__builtin_amdgcn_ballot_w64(bad) != 0) {
-    float f = 1.0f;
-    if (bad) {
-      const int ex = __builtin_amdgcn_frexp_expf(m);  // m = frac * 2^ex, frac in [0.5, 1)
-      f = fminf(__builtin_amdgcn_ldexpf(1.0f, -ex), 0x1p64f / R.sc);  // powers of two: exact
-    }
-#pragma unroll
-    for (int i = 0; i < C::NKT; ++i) R.S[i] *= f;
-    R.sc *= f;
-    // the output rows a lane holds are columns 4g .. 4g + 3: exchange the scales
-    if (g == 0) sm.scol[w][n] = __builtin_amdgcn_rcpf(R.sc);
-    wave_lds_sync();
-    R.usc = *reinterpret_cast<const f32x4*>(&sm.scol[w][4 * g]);
-  }
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) R.vn[rt][r] = -vf[rt][r] * R.sc;
-#pragma unroll
-  for (int kb = 0; kb < C::NKB; ++kb) R.Sf[kb] = stack2(R.S[2 * kb], R.S[2 * kb + 1]);
+  state_rescale<C>(R, vf, sm.scol[w], g, n);
 }
 
 // ---- kernel ---------------------------------------------------------------------------------
@@ -1030,6 +1022,254 @@ hipError_t launch_pipe(const PrefillParams& p, const SnapList& snap, hipStream_t
   return hipGetLastError();
 }
 
+
+// ---- two-stage prefill, stage 2: the chain kernel ---------------------------------------
+// The records of stage 1 (kda_prep.hip: KG, QG, T, -P and -KH^T as matrix-core
+// fragments, and gamma) and the V slab stream into an LDS ring by direct-to-LDS
+// loads from two loader waves, which keep DEPTH chunks in flight; the NST state
+// waves run only the chain, with the step of the pipeline kernel above:
+//   Xn = KG S - V,  Un = T Xn,  S' = gamma S + (-KH)^T Un,  O^T = S^T QG^T + Un^T (-P)^T.
+// One barrier per chunk.  Every chunk is one item: stage 1 needs no regrouping.
+template <int DK_, int NST_>
+struct CfgC {
+  static constexpr int DK = DK_, NST = NST_, J = 16 * NST;
+  static constexpr int NKT = DK / 16, NKB = DK / 32;
+  using R = ChunkRec<DK>;
+  static constexpr int RECK = (R::BYTES + 1023) / 1024;  // 1 KB transfers per record
+  static constexpr int VROW = J * 2;                      // bytes of one token's row of the V slab
+  static constexpr int VK = CS * VROW / 1024;             // 1 KB transfers per V slab
+  static constexpr int NK = RECK + VK;
+  static constexpr int SLOT = NK * 1024;
+  static constexpr int NL = 2;       // loader waves
+  static constexpr int DEPTH = 3;    // chunks in flight
+  static constexpr int RING = DEPTH + 1;
+  static constexpr int NW = NST + NL, NT = 64 * NW;
+  static constexpr int nk_of(int lw) { return (NK - lw + NL - 1) / NL; }  // transfers of loader lw
+  static_assert(VROW % 16 == 0 && (CS * VROW) % 1024 == 0, "V slab transfers");
+};
+
+template <class C>
+struct SmemC {
+  alignas(16) char ring[C::RING][C::SLOT];
+  alignas(16) float scol[C::NST][16];  // state waves: 1/scale of each of their columns
+};
+
+// s_waitcnt immediate for "at most n vector memory operations outstanding".
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Where a task's chunks lie.
+struct ChainSrc {
+  const char* rec;     // record of the task's first chunk
+  long long rec_step;  // bytes between the records of consecutive chunks
+  const char* v;       // the slab's V at the task's first token
+  int vrow;            // bytes between V token rows
+  int nchunks, T;
+};
+
+// Loader wave LW's share of chunk c (every NL-th 1 KB transfer) into `slot`.  A
+// chunk past the end is a zero-length range (reads zeros), so every step has the
+// same number of transfers in flight and one wait count fits all steps.
+template <class C, int LW>
+__device__ __forceinline__ void chain_issue(char* slot, const ChainSrc& q, int c, int lane) {
+  const bool on = c < q.nchunks;
+  const int rows = on ? min(CS, q.T - c * CS) : 0;
+  const __amdgpu_buffer_rsrc_t rr = make_rsrc(q.rec + (on ? (long long)c * q.rec_step : 0), on ? C::R::BYTES : 0);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(q.v + (on ? (long long)c * CS * q.vrow : 0), rows * q.vrow);
+#pragma unroll
+  for (int i = LW; i < C::NK; i += C::NL) {
+    if (i < C::RECK) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_void*)(slot + 1024 * i), 16, 16 * lane, 1024 * i, 0, 0);
+    } else {
+      // V rows of VROW bytes, LPR lanes each: LDS holds the slab row-major
+      constexpr int LPR = C::VROW / 16;
+      const int row = (i - C::RECK) * (64 / LPR) + lane / LPR;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(slot + 1024 * i), 16, row * q.vrow + 16 * (lane % LPR),
+                                               0, 0, 0);
+    }
+  }
+}
+
+template <class C, int LW>
+__device__ void chain_loader(SmemC<C>& sm, const ChainSrc& q, int lane) {
+  constexpr int WAIT = vmcnt_imm((C::DEPTH - 1) * C::nk_of(LW));  // the oldest chunk has landed
+#pragma unroll
+  for (int c = 0; c < C::DEPTH; ++c) chain_issue<C, LW>(sm.ring[c], q, c, lane);
+  __builtin_amdgcn_s_waitcnt(WAIT);
+  for (int n = 0; n < q.nchunks; ++n) {
+    block_sync_lds();  // chunk n is in its slot; the slot of chunk n - 1 is free
+    chain_issue<C, LW>(sm.ring[(n + C::DEPTH) % C::RING], q, n + C::DEPTH, lane);
+    __builtin_amdgcn_s_waitcnt(WAIT);
+  }
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
+}
+
+// The operands of a chunk that the serial part of the step reads first.
+template <class C>
+struct ChainOps {
+  f16x8 A[2][C::NKB];  // KG
+  f16x8 Tf[2];         // T
+};
+
+template <class C>
+__device__ __forceinline__ f16x8 slot_frag(const char* lb, int off, int f) {
+  return *reinterpret_cast<const f16x8*>(lb + off + f * 1024);
+}
+
+// One chunk of the chain for state wave w, from the ring slot sb (lb: this
+// lane's 16 bytes of the first fragment).  The serial part -- Xn, Un, S' -- is
+// issued first; the output's products follow it, so they run while the next
+// step's column scale is formed.
+template <class C>
+__device__ void chain_step(const char* sb, const char* lb, const ChainOps<C>& op, StateRegs<C>& R, const Item& it,
+                           const Ctx4& cx, int w, int lane) {
+  using RC = typename C::R;
+  const int g = opaque(lane / 16);
+  f32x4 X[2] = {R.vn[0], R.vn[1]};
+#pragma unroll
+  for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) X[rt] = mma16(op.A[rt][kb], R.Sf[kb], X[rt]);
+  f16x8 KH[C::NKT];
+#pragma unroll
+  for (int i = 0; i < C::NKT; ++i) KH[i] = slot_frag<C>(lb, RC::KH, i);
+#pragma unroll
+  for (int i = 0; i < C::NKT; ++i) R.S[i] *= *reinterpret_cast<const f32x4*>(sb + RC::GAM + (16 * i + 4 * g) * 4);
+  const f16x8 xf = stack2(X[0], X[1]);
+  f32x4 U[2];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) U[rt] = mma16(op.Tf[rt], xf, (f32x4)0.0f);
+  const f16x8 uf = stack2(U[0], U[1]);
+#pragma unroll
+  for (int i = 0; i < C::NKT; ++i) R.S[i] = mma16(KH[i], uf, R.S[i]);
+  // the output: O^T = S^T QG^T + Un^T (-P)^T, from the state before this chunk
+  f16x8 Q[2][C::NKB], Pf[2];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb) Q[rt][kb] = slot_frag<C>(lb, RC::QG, rt * C::NKB + kb);
+    Pf[rt] = slot_frag<C>(lb, RC::PP, rt);
+  }
+  f32x4 O[2] = {(f32x4)0.0f, (f32x4)0.0f};
+#pragma unroll
+  for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) O[rt] = mma16(R.Sf[kb], Q[rt][kb], O[rt]);
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) O[rt] = mma16(uf, Pf[rt], O[rt]);
+  store_out(cx, it, O, R.usc, w, lane);
+}
+
+template <class C>
+__device__ void chain_state(SmemC<C>& sm, const Ctx4& cx, const SnapList& snap, int pos0, int w, int lane) {
+  const PrefillParams& p = cx.p;
+  StateRegs<C> R;
+  {
+    const int g = lane / 16, n = lane % 16, col = 16 * w + n;
+#pragma unroll
+    for (int i = 0; i < C::NKT; ++i) R.S[i] = (f32x4)0.0f;
+    if (cx.s0) {
+#pragma unroll
+      for (int i = 0; i < C::NKT; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) R.S[i][r] = cx.s0[(size_t)(16 * i + 4 * g + r) * cx.s0_ld + col];
+    }
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    R.sc = 1.0f;
+    R.usc = (f32x4)1.0f;
+  }
+  int ns = 0;  // next listed position (positions up to pos0 belong to earlier blocks)
+  while (ns < p.nsnap && snap.pos[ns] <= pos0) ++ns;
+  for (int n = 0; n < cx.nchunks; ++n) {
+    block_sync_lds();
+    const char* sb = sm.ring[n % C::RING];
+    const char* lb = sb + 16 * opaque(lane);
+    const Item it = {n, n, 0, chunk_end(n, cx.T), CS};
+    // the serial part's operands first: their reads overlap the column scale
+    ChainOps<C> op;
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb) op.A[rt][kb] = slot_frag<C>(lb, C::R::KG, rt * C::NKB + kb);
+      op.Tf[rt] = slot_frag<C>(lb, C::R::TT, rt);
+    }
+    {
+      const int g = opaque(lane / 16), nn = opaque(lane % 16);
+      const __bf16* vs = reinterpret_cast<const __bf16*>(sb + C::RECK * 1024);
+      float vf[2][4];
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vf[rt][r] = (float)vs[(16 * rt + 4 * g + r) * C::J + 16 * w + nn];
+      state_rescale<C>(R, vf, sm.scol[w], g, nn);
+    }
+    chain_step<C>(sb, lb, op, R, it, cx, w, lane);
+    if (ns < p.nsnap && snap.pos[ns] == pos0 + n * CS + it.hi) {
+      store_state<C>(p.snaps + ((size_t)cx.bh * p.nsnap + ns) * C::DK * p.dv + cx.col0, R, p.dv, w, lane);
+      ++ns;
+      __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    }
+  }
+  if (cx.st) store_state<C>(cx.st, R, cx.st_ld, w, lane);
+}
+
+template <class C>
+__global__ __launch_bounds__(C::NT, 1) void kda_chain_kernel(PrefillParams p, SnapList snap) {
+  __shared__ SmemC<C> sm;
+  __shared__ int seq_lens[kMaxRankedSeqs], seq_pick;
+  const int tid = threadIdx.x, lane = tid % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  int task, slab;
+  task_of_block(p.dv / C::J, task, slab);
+  Ctx4 cx;
+  cx.p = p;
+  cx.h = task % p.H;
+  cx.col0 = slab * C::J;
+  cx.eA = 1.0f;
+  cx.b = __builtin_amdgcn_readfirstlane(seq_by_length_rank(p.cu, p.B, p.T, task / p.H, seq_lens, &seq_pick));
+  cx.bh = cx.b * p.H + cx.h;
+  long long slot0;
+  int pos0 = 0;
+  if (p.cu) {
+    seq_range(p, cx.b, cx.tok0, cx.T);
+    slot0 = cx.tok0 / CS + cx.b;
+  } else {
+    pos0 = p.rec_c0 * CS;
+    cx.tok0 = (long long)cx.b * p.T + pos0;
+    cx.T = max(0, min(p.T - pos0, p.rec_nc * CS));
+    slot0 = (long long)cx.b * p.rec_nc;
+  }
+  cx.nchunks = (cx.T + CS - 1) / CS;
+  cx.v_on = cx.o_on = true;
+  cx.ident = -1;
+  cx.s0_ld = cx.st_ld = p.dv;
+  const size_t mat = (size_t)C::DK * p.dv;
+  cx.s0 = p.S0 ? p.S0 + (size_t)cx.bh * mat + cx.col0 : nullptr;
+  cx.st = p.S_T ? p.S_T + (size_t)cx.bh * mat + cx.col0 : nullptr;
+  if (wave < C::NST) {
+    chain_state<C>(sm, cx, snap, pos0, wave, lane);
+  } else {
+    ChainSrc q;
+    q.rec = p.rec + (slot0 * p.H + cx.h) * C::R::BYTES;
+    q.rec_step = (long long)p.H * C::R::BYTES;
+    q.vrow = p.H * p.dv * 2;
+    q.v = static_cast<const char*>(p.v) + ((cx.tok0 * p.H + cx.h) * p.dv + cx.col0) * 2;
+    q.nchunks = cx.nchunks;
+    q.T = cx.T;
+    if (wave == C::NST) chain_loader<C, 0>(sm, q, lane);
+    else chain_loader<C, 1>(sm, q, lane);
+  }
+}
+
+template <int DK, int NST>
+hipError_t launch_chain(const PrefillParams& p, const SnapList& snap, hipStream_t s) {
+  using C = CfgC<DK, NST>;
+  const long long grid = (long long)p.B * p.H * (p.dv / C::J);
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL((kda_chain_kernel<C>), dim3((unsigned)grid), dim3(C::NT), 0, s, p, snap);
+  return hipGetLastError();
+}
 }  // namespace
 
 bool prefill_pipe_supported(int io_dtype, int dk, int dv, int chunk, int H) {
@@ -1042,6 +1282,16 @@ bool prefill_pipe_supported(int io_dtype, int dk, int dv, int chunk, int H) {
 hipError_t launch_prefill_pipe(const PrefillParams& p, const SnapList& snap, hipStream_t s) {
   if (p.dk == 128) return launch_pipe<128, 2>(p, snap, s);
   if (p.dk == 64) return launch_pipe<64, 2>(p, snap, s);
+  return hipErrorInvalidValue;
+}
+
+bool prefill_chain_supported(int io_dtype, int dk, int dv, int chunk, int H) {
+  return prefill_pipe_supported(io_dtype, dk, dv, chunk, H);
+}
+
+hipError_t launch_prefill_chain(const PrefillParams& p, const SnapList& snap, hipStream_t s) {
+  if (p.dk == 128) return launch_chain<128, 2>(p, snap, s);
+  if (p.dk == 64) return launch_chain<64, 2>(p, snap, s);
   return hipErrorInvalidValue;
 }
 

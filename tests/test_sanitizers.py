@@ -24,7 +24,7 @@ import pytest
 ROOT = Path(__file__).resolve().parents[1]
 SAN = ROOT / "tests" / "sanitize"
 BUILD = ROOT / "gated_delta_rule_07_amd" / "_build"
-KERNEL_OBJS = ["kda_decode.o", "kda_prefill.o", "kda_prefill_pipe.o", "kda_spec.o", "kda_split.o"]
+KERNEL_OBJS = ["kda_decode.o", "kda_prefill.o", "kda_prefill_pipe.o", "kda_prep.o", "kda_spec.o", "kda_split.o"]
 HOST_SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
             "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
 
@@ -56,7 +56,10 @@ def test_c_abi_validation_under_asan_ubsan(tmp_path):
     common = ["-x", "hip", "--offload-host-only", "-O1", "-g", "-std=c++17", f"-I{ROOT / 'include'}",
               f"-I{ROOT / 'gated_delta_rule_07_amd' / 'csrc'}", *HOST_SAN]
     api_o, main_o, exe = tmp_path / "api.o", tmp_path / "main.o", tmp_path / "api_san"
-    _run([hipcc, *common, "-c", str(ROOT / "gated_delta_rule_07_amd" / "csrc" / "kda_api.cpp"), "-o", str(api_o)])
+    # kda_api.cpp holds a device array (the allocation-free entry point's scratch):
+    # its device part is built too, the sanitizers apply to the host part only
+    api_flags = [f for f in common if f != "--offload-host-only"] + ["--offload-arch=gfx950"]
+    _run([hipcc, *api_flags, "-c", str(ROOT / "gated_delta_rule_07_amd" / "csrc" / "kda_api.cpp"), "-o", str(api_o)])
     _run([hipcc, *common, "-c", str(SAN / "api_main.cpp"), "-o", str(main_o)])
     _run([hipcc, *HOST_SAN, "--offload-arch=gfx950", str(main_o), str(api_o), *map(str, objs), "-o", str(exe)])
     # the HIP runtime's own allocations at load are not ours to judge: leaks off
