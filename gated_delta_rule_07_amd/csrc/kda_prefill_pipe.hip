@@ -1043,7 +1043,8 @@ struct CfgC {
   static constexpr int NL = 2;       // loader waves
   static constexpr int DEPTH = 3;    // chunks in flight
   static constexpr int RING = DEPTH + 1;
-  static constexpr int NW = NST + NL, NT = 64 * NW;
+  static constexpr int NW = 2 * NST + NL, NT = 64 * NW;  // state, output and loader waves
+  static constexpr int HAND = (NKB + 2) * 1024;        // state -> output handoff per wave: Sf, Un, 1/scale
   static constexpr int nk_of(int lw) { return (NK - lw + NL - 1) / NL; }  // transfers of loader lw
   static_assert(VROW % 16 == 0 && (CS * VROW) % 1024 == 0, "V slab transfers");
 };
@@ -1051,7 +1052,8 @@ struct CfgC {
 template <class C>
 struct SmemC {
   alignas(16) char ring[C::RING][C::SLOT];
-  alignas(16) float scol[C::NST][16];  // state waves: 1/scale of each of their columns
+  alignas(16) char hand[2][C::NST][C::HAND];  // by chunk parity
+  alignas(16) float scol[C::NST][16];         // state waves: 1/scale of each of their columns
 };
 
 // s_waitcnt immediate for "at most n vector memory operations outstanding".
@@ -1102,71 +1104,49 @@ __device__ void chain_loader(SmemC<C>& sm, const ChainSrc& q, int lane) {
     chain_issue<C, LW>(sm.ring[(n + C::DEPTH) % C::RING], q, n + C::DEPTH, lane);
     __builtin_amdgcn_s_waitcnt(WAIT);
   }
+  block_sync_lds();  // the closing barrier of every wave
   __builtin_amdgcn_s_waitcnt(kVmcnt0);
 }
-
-// The operands of a chunk that the serial part of the step reads first.
-template <class C>
-struct ChainOps {
-  f16x8 A[2][C::NKB];  // KG
-  f16x8 Tf[2];         // T
-};
 
 template <class C>
 __device__ __forceinline__ f16x8 slot_frag(const char* lb, int off, int f) {
   return *reinterpret_cast<const f16x8*>(lb + off + f * 1024);
 }
 
-// One chunk of the chain for state wave w, from the ring slot sb (lb: this
-// lane's 16 bytes of the first fragment).  The serial part -- Xn, Un, S' -- is
-// issued first; the output's products follow it, so they run while the next
-// step's column scale is formed.
+// max |S| over this lane's values (a tree, not a chain)
 template <class C>
-__device__ void chain_step(const char* sb, const char* lb, const ChainOps<C>& op, StateRegs<C>& R, const Item& it,
-                           const Ctx4& cx, int w, int lane) {
-  using RC = typename C::R;
-  const int g = opaque(lane / 16);
-  f32x4 X[2] = {R.vn[0], R.vn[1]};
+__device__ __forceinline__ float lane_smax(const StateRegs<C>& R) {
+  float t[C::NKT];
 #pragma unroll
-  for (int kb = 0; kb < C::NKB; ++kb)
+  for (int i = 0; i < C::NKT; ++i)
+    t[i] = fmaxf(fmaxf(fabsf(R.S[i][0]), fabsf(R.S[i][1])), fmaxf(fabsf(R.S[i][2]), fabsf(R.S[i][3])));
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) X[rt] = mma16(op.A[rt][kb], R.Sf[kb], X[rt]);
-  f16x8 KH[C::NKT];
+  for (int h = C::NKT / 2; h >= 1; h /= 2)
 #pragma unroll
-  for (int i = 0; i < C::NKT; ++i) KH[i] = slot_frag<C>(lb, RC::KH, i);
-#pragma unroll
-  for (int i = 0; i < C::NKT; ++i) R.S[i] *= *reinterpret_cast<const f32x4*>(sb + RC::GAM + (16 * i + 4 * g) * 4);
-  const f16x8 xf = stack2(X[0], X[1]);
-  f32x4 U[2];
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt) U[rt] = mma16(op.Tf[rt], xf, (f32x4)0.0f);
-  const f16x8 uf = stack2(U[0], U[1]);
-#pragma unroll
-  for (int i = 0; i < C::NKT; ++i) R.S[i] = mma16(KH[i], uf, R.S[i]);
-  // the output: O^T = S^T QG^T + Un^T (-P)^T, from the state before this chunk
-  f16x8 Q[2][C::NKB], Pf[2];
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-#pragma unroll
-    for (int kb = 0; kb < C::NKB; ++kb) Q[rt][kb] = slot_frag<C>(lb, RC::QG, rt * C::NKB + kb);
-    Pf[rt] = slot_frag<C>(lb, RC::PP, rt);
-  }
-  f32x4 O[2] = {(f32x4)0.0f, (f32x4)0.0f};
-#pragma unroll
-  for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) O[rt] = mma16(R.Sf[kb], Q[rt][kb], O[rt]);
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt) O[rt] = mma16(uf, Pf[rt], O[rt]);
-  store_out(cx, it, O, R.usc, w, lane);
+    for (int i = 0; i < h; ++i) t[i] = fmaxf(t[i], t[i + h]);
+  return t[0];
 }
 
 template <class C>
+__device__ __forceinline__ void pack_sf(StateRegs<C>& R) {
+#pragma unroll
+  for (int kb = 0; kb < C::NKB; ++kb) R.Sf[kb] = stack2(R.S[2 * kb], R.S[2 * kb + 1]);
+}
+
+// State wave w: the serial part of every chunk -- column scale, Xn = KG S - V,
+// Un = T Xn, S' = gamma S + (-KH)^T Un -- and nothing else.  The fp16 S it
+// used, Un and the column scales go to output wave w through the handoff
+// buffer of the chunk's parity.  The state's maximum and fp16 copy for the
+// next chunk are formed at the end of a step, ahead of the barrier (and formed
+// again in the rare step that rescales a column).
+template <class C>
 __device__ void chain_state(SmemC<C>& sm, const Ctx4& cx, const SnapList& snap, int pos0, int w, int lane) {
+  using RC = typename C::R;
   const PrefillParams& p = cx.p;
   StateRegs<C> R;
+  const int g = lane / 16, n16 = lane % 16;
   {
-    const int g = lane / 16, n = lane % 16, col = 16 * w + n;
+    const int col = 16 * w + n16;
 #pragma unroll
     for (int i = 0; i < C::NKT; ++i) R.S[i] = (f32x4)0.0f;
     if (cx.s0) {
@@ -1181,37 +1161,127 @@ __device__ void chain_state(SmemC<C>& sm, const Ctx4& cx, const SnapList& snap, 
   }
   int ns = 0;  // next listed position (positions up to pos0 belong to earlier blocks)
   while (ns < p.nsnap && snap.pos[ns] <= pos0) ++ns;
+  float ms = lane_smax<C>(R);
+  pack_sf<C>(R);
   for (int n = 0; n < cx.nchunks; ++n) {
     block_sync_lds();
     const char* sb = sm.ring[n % C::RING];
     const char* lb = sb + 16 * opaque(lane);
     const Item it = {n, n, 0, chunk_end(n, cx.T), CS};
-    // the serial part's operands first: their reads overlap the column scale
-    ChainOps<C> op;
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-#pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb) op.A[rt][kb] = slot_frag<C>(lb, C::R::KG, rt * C::NKB + kb);
-      op.Tf[rt] = slot_frag<C>(lb, C::R::TT, rt);
-    }
+    f16x8 A[2][C::NKB], Tf[2], KH[C::NKT];
+    float vf[2][4];
     {
-      const int g = opaque(lane / 16), nn = opaque(lane % 16);
       const __bf16* vs = reinterpret_cast<const __bf16*>(sb + C::RECK * 1024);
-      float vf[2][4];
+      const int gg = opaque(lane / 16), nn = opaque(lane % 16);
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) vf[rt][r] = (float)vs[(16 * rt + 4 * g + r) * C::J + 16 * w + nn];
-      state_rescale<C>(R, vf, sm.scol[w], g, nn);
+        for (int r = 0; r < 4; ++r) vf[rt][r] = (float)vs[(16 * rt + 4 * gg + r) * C::J + 16 * w + nn];
     }
-    chain_step<C>(sb, lb, op, R, it, cx, w, lane);
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb) A[rt][kb] = slot_frag<C>(lb, RC::KG, rt * C::NKB + kb);
+      Tf[rt] = slot_frag<C>(lb, RC::TT, rt);
+    }
+#pragma unroll
+    for (int i = 0; i < C::NKT; ++i) KH[i] = slot_frag<C>(lb, RC::KH, i);
+    // column scale: keep the scaled column maximum of S and V within [2^-4, 2^4]
+    // (rarely changed; capped at 2^64 so a column that has decayed to nothing
+    // with no value input never scales to infinity, where 0 * inf would be NaN)
+    {
+      const float mv = fmaxf(fmaxf(fmaxf(fabsf(vf[0][0]), fabsf(vf[0][1])), fmaxf(fabsf(vf[0][2]), fabsf(vf[0][3]))),
+                             fmaxf(fmaxf(fabsf(vf[1][0]), fabsf(vf[1][1])), fmaxf(fabsf(vf[1][2]), fabsf(vf[1][3]))));
+      const float m = column_max(fmaxf(ms, mv * R.sc));
+      const bool bad = m > 16.0f || (m > 0.0f && m < 0.0625f && R.sc < 0x1p64f);
+      if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+        float f = 1.0f;
+        if (bad) {
+          const int ex = __builtin_amdgcn_frexp_expf(m);  // m = frac * 2^ex, frac in [0.5, 1)
+          f = fminf(__builtin_amdgcn_ldexpf(1.0f, -ex), 0x1p64f / R.sc);  // powers of two: exact
+        }
+#pragma unroll
+        for (int i = 0; i < C::NKT; ++i) R.S[i] *= f;
+        R.sc *= f;
+        if (g == 0) sm.scol[w][n16] = __builtin_amdgcn_rcpf(R.sc);  // output rows are columns 4g .. 4g + 3
+        wave_lds_sync();
+        R.usc = *reinterpret_cast<const f32x4*>(&sm.scol[w][4 * g]);
+        pack_sf<C>(R);
+      }
+    }
+    char* hb = sm.hand[n & 1][w] + 16 * lane;
+    f32x4 X[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) X[rt][r] = -vf[rt][r] * R.sc;
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) X[rt] = mma16(A[rt][kb], R.Sf[kb], X[rt]);
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb) *reinterpret_cast<f16x8*>(hb + kb * 1024) = R.Sf[kb];
+    *reinterpret_cast<f32x4*>(hb + (C::NKB + 1) * 1024) = R.usc;
+#pragma unroll
+    for (int i = 0; i < C::NKT; ++i) R.S[i] *= *reinterpret_cast<const f32x4*>(sb + RC::GAM + (16 * i + 4 * g) * 4);
+    const f16x8 xf = stack2(X[0], X[1]);
+    f32x4 U[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) U[rt] = mma16(Tf[rt], xf, (f32x4)0.0f);
+    const f16x8 uf = stack2(U[0], U[1]);
+#pragma unroll
+    for (int i = 0; i < C::NKT; ++i) R.S[i] = mma16(KH[i], uf, R.S[i]);
+    *reinterpret_cast<f16x8*>(hb + C::NKB * 1024) = uf;
+    ms = lane_smax<C>(R);
+    pack_sf<C>(R);
     if (ns < p.nsnap && snap.pos[ns] == pos0 + n * CS + it.hi) {
       store_state<C>(p.snaps + ((size_t)cx.bh * p.nsnap + ns) * C::DK * p.dv + cx.col0, R, p.dv, w, lane);
       ++ns;
       __builtin_amdgcn_s_waitcnt(kVmcnt0);
     }
   }
+  block_sync_lds();  // the last handoff is complete
   if (cx.st) store_state<C>(cx.st, R, cx.st_ld, w, lane);
+}
+
+// Output wave w: chunk n - 1's output during step n, from the handoff of state
+// wave w and chunk n - 1's QG and -P fragments, read into registers during step
+// n - 1 (its slot is refilled in step n):
+//   O^T = S^T QG^T + Un^T (-P)^T.
+template <class C>
+__device__ void chain_output(SmemC<C>& sm, const Ctx4& cx, int w, int lane) {
+  using RC = typename C::R;
+  f16x8 Q[2][C::NKB], Pf[2];
+  auto emit = [&](int c) {  // the output of chunk c
+    const char* hb = sm.hand[c & 1][w] + 16 * lane;
+    f16x8 Sf[C::NKB];
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb) Sf[kb] = *reinterpret_cast<const f16x8*>(hb + kb * 1024);
+    const f16x8 uf = *reinterpret_cast<const f16x8*>(hb + C::NKB * 1024);
+    const f32x4 usc = *reinterpret_cast<const f32x4*>(hb + (C::NKB + 1) * 1024);
+    f32x4 O[2] = {(f32x4)0.0f, (f32x4)0.0f};
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) O[rt] = mma16(Sf[kb], Q[rt][kb], O[rt]);
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) O[rt] = mma16(uf, Pf[rt], O[rt]);
+    const Item it = {c, c, 0, chunk_end(c, cx.T), CS};
+    store_out(cx, it, O, usc, w, lane);
+  };
+  for (int n = 0; n < cx.nchunks; ++n) {
+    block_sync_lds();
+    if (n > 0) emit(n - 1);
+    const char* lb = sm.ring[n % C::RING] + 16 * opaque(lane);
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb) Q[rt][kb] = slot_frag<C>(lb, RC::QG, rt * C::NKB + kb);
+      Pf[rt] = slot_frag<C>(lb, RC::PP, rt);
+    }
+  }
+  block_sync_lds();
+  if (cx.nchunks > 0) emit(cx.nchunks - 1);
 }
 
 template <class C>
@@ -1247,8 +1317,14 @@ __global__ __launch_bounds__(C::NT, 1) void kda_chain_kernel(PrefillParams p, Sn
   const size_t mat = (size_t)C::DK * p.dv;
   cx.s0 = p.S0 ? p.S0 + (size_t)cx.bh * mat + cx.col0 : nullptr;
   cx.st = p.S_T ? p.S_T + (size_t)cx.bh * mat + cx.col0 : nullptr;
+  // waves 0 .. NST-1: state (SIMDs 0 and 1), NST .. 2 NST-1: output (SIMDs 2
+  // and 3), then the two loaders, which share the state waves' SIMDs and give
+  // way to them
   if (wave < C::NST) {
+    __builtin_amdgcn_s_setprio(3);
     chain_state<C>(sm, cx, snap, pos0, wave, lane);
+  } else if (wave < 2 * C::NST) {
+    chain_output<C>(sm, cx, wave - C::NST, lane);
   } else {
     ChainSrc q;
     q.rec = p.rec + (slot0 * p.H + cx.h) * C::R::BYTES;
@@ -1257,7 +1333,7 @@ __global__ __launch_bounds__(C::NT, 1) void kda_chain_kernel(PrefillParams p, Sn
     q.v = static_cast<const char*>(p.v) + ((cx.tok0 * p.H + cx.h) * p.dv + cx.col0) * 2;
     q.nchunks = cx.nchunks;
     q.T = cx.T;
-    if (wave == C::NST) chain_loader<C, 0>(sm, q, lane);
+    if (wave == 2 * C::NST) chain_loader<C, 0>(sm, q, lane);
     else chain_loader<C, 1>(sm, q, lane);
   }
 }
