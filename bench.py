@@ -365,7 +365,8 @@ def main():
         del gz, gA
 
         # fast-forgetting heads (z ~ N(-3, 1), A ~ N(0, 0.3)): most 32-token chunks decay
-        # below e^-10 in some channel and are split into shorter segments
+        # below e^-10 in some channel (the range that needs no special handling in the
+        # two-stage path's bounded factors; the single-kernel pipeline regroups them)
         fz, fA = ki.make_gate((B, T, H, dk), H, w.qkv_dtype, seed=1, device=dev, z_mu=-3.0, z_std=1.0, a_std=0.3)
 
         def fstep(o_=None):
@@ -374,7 +375,7 @@ def main():
 
         fstep(o32)
         torch.cuda.synchronize()
-        f_heads = [hid for hid in range(0, B * H, 8)]  # 8 of the 64 heads
+        f_heads = list(range(B * H))  # every head
         for hid in f_heads:
             gate_check(f"fast-forgetting head {hid}", fz, fA, hid)
         fstep()

@@ -158,7 +158,8 @@ hipError_t launch_prefill_pipe(const PrefillParams& p, const SnapList& snap, hip
 // fragments of 64 lanes x 16 bytes, then gamma.  Lane l = 16 g + n of a fragment
 // holds 8 values (columns listed in slot order):
 //   KG, QG [rt][kb] : token 16 rt + n, channels 32 kb + {4g..4g+3, 16+4g..16+4g+3}
-//   T, -P  [rt]     : row 16 rt + n, columns {4g..4g+3, 16+4g..16+4g+3}
+//   T, -P T [rt]    : row 16 rt + n, columns {4g..4g+3, 16+4g..16+4g+3}
+//   (-P T)_lo [rt]  : the fp16 rounding remainder of -P T, same layout
 //   -KH^T  [i]      : channel 16 i + n, tokens {4g..4g+3, 16+4g..16+4g+3}
 //   gamma           : d_k fp32
 template <int DK>
@@ -168,7 +169,8 @@ struct ChunkRec {
   static constexpr int QG = KG + 2 * NKB * 1024;
   static constexpr int TT = QG + 2 * NKB * 1024;
   static constexpr int PP = TT + 2 * 1024;
-  static constexpr int KH = PP + 2 * 1024;
+  static constexpr int PL = PP + 2 * 1024;
+  static constexpr int KH = PL + 2 * 1024;
   static constexpr int GAM = KH + NKT * 1024;
   static constexpr int BYTES = GAM + DK * 4;
 };

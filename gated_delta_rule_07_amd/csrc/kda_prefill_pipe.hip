@@ -1024,11 +1024,12 @@ hipError_t launch_pipe(const PrefillParams& p, const SnapList& snap, hipStream_t
 
 
 // ---- two-stage prefill, stage 2: the chain kernel ---------------------------------------
-// The records of stage 1 (kda_prep.hip: KG, QG, T, -P and -KH^T as matrix-core
-// fragments, and gamma) and the V slab stream into an LDS ring by direct-to-LDS
-// loads from two loader waves, which keep DEPTH chunks in flight; the NST state
-// waves run only the chain, with the step of the pipeline kernel above:
-//   Xn = KG S - V,  Un = T Xn,  S' = gamma S + (-KH)^T Un,  O^T = S^T QG^T + Un^T (-P)^T.
+// The records of stage 1 (kda_prep.hip: KG, QG, T, -P T and -KH^T as
+// matrix-core fragments, and gamma) and the V slab stream into an LDS ring by
+// direct-to-LDS loads from two loader waves, which keep DEPTH chunks in flight.
+// The state waves run only the serial part, the output waves the output:
+//   Xn = KG S - V,  Un = T Xn,  S' = gamma S + (-KH)^T Un,
+//   O^T = S^T QG^T + Xn^T (-P T)^T    (P U = -(P T) Xn, the product formed in stage 1)
 // One barrier per chunk.  Every chunk is one item: stage 1 needs no regrouping.
 template <int DK_, int NST_>
 struct CfgC {
@@ -1044,7 +1045,7 @@ struct CfgC {
   static constexpr int DEPTH = 3;    // chunks in flight
   static constexpr int RING = DEPTH + 1;
   static constexpr int NW = 2 * NST + NL, NT = 64 * NW;  // state, output and loader waves
-  static constexpr int HAND = (NKB + 2) * 1024;        // state -> output handoff per wave: Sf, Un, 1/scale
+  static constexpr int HAND = (NKB + 2) * 1024;        // state -> output handoff per wave: Sf, Xn, 1/scale
   static constexpr int nk_of(int lw) { return (NK - lw + NL - 1) / NL; }  // transfers of loader lw
   static_assert(VROW % 16 == 0 && (CS * VROW) % 1024 == 0, "V slab transfers");
 };
@@ -1134,8 +1135,8 @@ __device__ __forceinline__ void pack_sf(StateRegs<C>& R) {
 }
 
 // State wave w: the serial part of every chunk -- column scale, Xn = KG S - V,
-// Un = T Xn, S' = gamma S + (-KH)^T Un -- and nothing else.  The fp16 S it
-// used, Un and the column scales go to output wave w through the handoff
+// Un = T Xn, S' = gamma S + (-KH)^T Un -- and nothing else.  The fp16 S and Xn
+// it used and the column scales go to output wave w through the handoff
 // buffer of the chunk's parity.  The state's maximum and fp16 copy for the
 // next chunk are formed at the end of a step, ahead of the barrier (and formed
 // again in the rare step that rescales a column).
@@ -1231,7 +1232,7 @@ __device__ void chain_state(SmemC<C>& sm, const Ctx4& cx, const SnapList& snap, 
     const f16x8 uf = stack2(U[0], U[1]);
 #pragma unroll
     for (int i = 0; i < C::NKT; ++i) R.S[i] = mma16(KH[i], uf, R.S[i]);
-    *reinterpret_cast<f16x8*>(hb + C::NKB * 1024) = uf;
+    *reinterpret_cast<f16x8*>(hb + C::NKB * 1024) = xf;
     ms = lane_smax<C>(R);
     pack_sf<C>(R);
     if (ns < p.nsnap && snap.pos[ns] == pos0 + n * CS + it.hi) {
@@ -1245,19 +1246,19 @@ __device__ void chain_state(SmemC<C>& sm, const Ctx4& cx, const SnapList& snap, 
 }
 
 // Output wave w: chunk n - 1's output during step n, from the handoff of state
-// wave w and chunk n - 1's QG and -P fragments, read into registers during step
-// n - 1 (its slot is refilled in step n):
-//   O^T = S^T QG^T + Un^T (-P)^T.
+// wave w and chunk n - 1's QG and -P T fragments, read into registers during
+// step n - 1 (its slot is refilled in step n):
+//   O^T = S^T QG^T + Xn^T (-P T)^T.
 template <class C>
 __device__ void chain_output(SmemC<C>& sm, const Ctx4& cx, int w, int lane) {
   using RC = typename C::R;
-  f16x8 Q[2][C::NKB], Pf[2];
+  f16x8 Q[2][C::NKB], Pf[2], Pl[2];
   auto emit = [&](int c) {  // the output of chunk c
     const char* hb = sm.hand[c & 1][w] + 16 * lane;
     f16x8 Sf[C::NKB];
 #pragma unroll
     for (int kb = 0; kb < C::NKB; ++kb) Sf[kb] = *reinterpret_cast<const f16x8*>(hb + kb * 1024);
-    const f16x8 uf = *reinterpret_cast<const f16x8*>(hb + C::NKB * 1024);
+    const f16x8 xf = *reinterpret_cast<const f16x8*>(hb + C::NKB * 1024);
     const f32x4 usc = *reinterpret_cast<const f32x4*>(hb + (C::NKB + 1) * 1024);
     f32x4 O[2] = {(f32x4)0.0f, (f32x4)0.0f};
 #pragma unroll
@@ -1265,7 +1266,9 @@ __device__ void chain_output(SmemC<C>& sm, const Ctx4& cx, int w, int lane) {
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) O[rt] = mma16(Sf[kb], Q[rt][kb], O[rt]);
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) O[rt] = mma16(uf, Pf[rt], O[rt]);
+    for (int rt = 0; rt < 2; ++rt) O[rt] = mma16(xf, Pl[rt], O[rt]);
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) O[rt] = mma16(xf, Pf[rt], O[rt]);
     const Item it = {c, c, 0, chunk_end(c, cx.T), CS};
     store_out(cx, it, O, usc, w, lane);
   };
@@ -1278,6 +1281,7 @@ __device__ void chain_output(SmemC<C>& sm, const Ctx4& cx, int w, int lane) {
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb) Q[rt][kb] = slot_frag<C>(lb, RC::QG, rt * C::NKB + kb);
       Pf[rt] = slot_frag<C>(lb, RC::PP, rt);
+      Pl[rt] = slot_frag<C>(lb, RC::PL, rt);
     }
   }
   block_sync_lds();

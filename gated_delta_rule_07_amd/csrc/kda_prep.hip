@@ -13,7 +13,7 @@
 //   KG = K o pre   QG = Q o pre   KH = K o suf
 //   L_ij = beta_i sum_c k_ic k_jc r_c(i,j)  (j < i)     r_c(i,j) = prod_{j<s<=i} a_sc
 //   P_ij =        sum_c q_ic k_jc r_c(i,j)  (j <= i)
-//   T = (I + L)^{-1} diag(beta)
+//   T = (I + L)^{-1} diag(beta),  and the output's intra-chunk operator P T
 //
 // Bounded factors for L and P.  Every ratio r(i,j) is a product of decays, at
 // most 1, but factoring it as pre_i / pre_j (one product per side) needs 1/pre,
@@ -386,19 +386,69 @@ __global__ __launch_bounds__(64 * kPrepWaves, 2) void kda_prep_kernel(PrefillPar
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, t0), rr, lane * 16, R::TT, 0);
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, t1), rr, lane * 16, R::TT + 1024, 0);
   }
-  // -P, lower triangle with the diagonal
+  // -P T: the output's intra-chunk operator, applied in the chain to Xn (one
+  // fp16 rounding of the product, instead of one each of P, T and Un).  T in
+  // fp32 to the D_L buffer (free after the solve), then the lower 16x16 tiles of
+  // P T from fp16 high/low parts of both factors (three products per tile:
+  // fp32-grade, the low-by-low term is below fp32 rounding), into the factor
+  // buffer (free as well) as fp32 rows.
+  float* tl = sm.dl;                               // T [row][col], stride LDL
+  float* pt = reinterpret_cast<float*>(sm.f);      // P T [row][col], stride LDP
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    tl[n * C::LDL + 4 * g + j] = d0t[j] * b_r0[j];
+    tl[n * C::LDL + 16 + 4 * g + j] = 0.0f;
+    tl[(16 + n) * C::LDL + 4 * g + j] = -zt[j] * b_r0[j];
+    tl[(16 + n) * C::LDL + 16 + 4 * g + j] = d1t[j] * b_r1[j];
+  }
+  wave_lds_sync();
+  auto split = [](float x, h16& hi) { hi = (h16)x; return (h16)(x - (float)hi); };
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int ct = 0; ct <= rt; ++ct) {
+      // A: P rows 16 rt + n, k = 8g .. 8g + 7; B: T rows k, column 16 ct + n (natural packing)
+      const int row = 16 * rt + n;
+      const f32x4 p0 = *reinterpret_cast<const f32x4*>(&sm.dp[row * C::LDP + 8 * g]);
+      const f32x4 p1 = *reinterpret_cast<const f32x4*>(&sm.dp[row * C::LDP + 8 * g + 4]);
+      f16x8 ah, al, bh, bl;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int kk = 8 * g + e;
+        const float pv = kk <= row ? (e < 4 ? p0[e] : p1[e - 4]) : 0.0f;
+        h16 hp, ht;
+        al[e] = split(pv, hp);
+        ah[e] = hp;
+        bl[e] = split(tl[kk * C::LDL + 16 * ct + n], ht);
+        bh[e] = ht;
+      }
+      f32x4 acc = mma16x32(ah, bh, (f32x4)0.0f);
+      acc = mma16x32(ah, bl, acc);
+      acc = mma16x32(al, bh, acc);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pt[(16 * rt + 4 * g + j) * C::LDP + 16 * ct + n] = acc[j];
+    }
+  wave_lds_sync();
+  // -P T fragments, lower triangle with the diagonal, as fp16 high and low parts
+  // (the output's intra-chunk term is the largest part of a fast-forgetting
+  // head's output; one fp16 rounding of it dominated the error there)
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
     const int row = 16 * rt + n;
-    const f32x4 lo = *reinterpret_cast<const f32x4*>(&sm.dp[row * C::LDP + 4 * g]);
-    const f32x4 hi = *reinterpret_cast<const f32x4*>(&sm.dp[row * C::LDP + 16 + 4 * g]);
-    f16x8 pf;
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(&pt[row * C::LDP + 4 * g]);
+    const f32x4 hi = *reinterpret_cast<const f32x4*>(&pt[row * C::LDP + 16 + 4 * g]);
+    f16x8 pf, pl;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      pf[j] = (4 * g + j <= row) ? (h16)(-lo[j]) : (h16)0.0f;
-      pf[4 + j] = (16 + 4 * g + j <= row) ? (h16)(-hi[j]) : (h16)0.0f;
+      const float a0 = (4 * g + j <= row) ? -lo[j] : 0.0f;
+      const float a1 = (16 + 4 * g + j <= row) ? -hi[j] : 0.0f;
+      pf[j] = (h16)a0;
+      pf[4 + j] = (h16)a1;
+      pl[j] = (h16)(a0 - (float)pf[j]);
+      pl[4 + j] = (h16)(a1 - (float)pf[4 + j]);
     }
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, pf), rr, lane * 16, R::PP + 1024 * rt, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, pl), rr, lane * 16, R::PL + 1024 * rt, 0);
   }
 }
 

@@ -8,9 +8,11 @@ putting the recurrence on the GPU), for one 32-token chunk with decays a [32, d_
   pre_t = prod_{s<=t} a_s, suf_t = prod_{s>t} a_s, gamma = pre_31,
   KG = k pre, QG = q pre, KH = k suf,
   L_ij = beta_i sum_c k_ic k_jc r_c(i,j) (j < i), P_ij = sum_c q_ic k_jc r_c(i,j) (j <= i),
-  r(i,j) = prod_{j<s<=i} a_s, T = (I + L)^{-1} diag(beta).
+  r(i,j) = prod_{j<s<=i} a_s, T = (I + L)^{-1} diag(beta); the record holds the
+  output's intra-chunk operator P T in place of P.
 Record: fp16 fragments of 64 lanes x 8 values (lane 16 g + n, slot e), then gamma:
-  KG, QG [rt][kb]: token 16 rt + n, channel 32 kb + st(g, e); T, -P [rt]: row
+  KG, QG [rt][kb]: token 16 rt + n, channel 32 kb + st(g, e); T, -P T [rt] (then
+  its fp16 remainder, same layout): row
   16 rt + n, column st(g, e); -KH^T [i]: channel 16 i + n, token st(g, e);
   st(g, e) = 4 g + e (e < 4) or 16 + 4 g + e - 4.
 """
@@ -25,7 +27,8 @@ def offsets(dk):
     o["QG"] = o["KG"] + 2 * nkb * 1024
     o["TT"] = o["QG"] + 2 * nkb * 1024
     o["PP"] = o["TT"] + 2 * 1024
-    o["KH"] = o["PP"] + 2 * 1024
+    o["PL"] = o["PP"] + 2 * 1024
+    o["KH"] = o["PL"] + 2 * 1024
     o["GAM"] = o["KH"] + nkt * 1024
     o["BYTES"] = o["GAM"] + dk * 4
     return o
@@ -63,7 +66,8 @@ def chunk_operands(q, k, a, beta):
 
 
 def pack(dk, KG, QG, KH, T, P, gam):
-    """The record bytes (uint8) of one chunk's operands."""
+    """The record bytes (uint8) of one chunk's operands (P: the chunk's P; the
+    record stores -P T)."""
     o = offsets(dk)
     rec = np.zeros(o["BYTES"], np.uint8)
     h = rec[: o["GAM"]].view(np.float16)
@@ -77,7 +81,9 @@ def pack(dk, KG, QG, KH, T, P, gam):
             put(o["KG"], rt * (dk // 32) + kb, KG[16 * rt + _ROW, 32 * kb + _COL])
             put(o["QG"], rt * (dk // 32) + kb, QG[16 * rt + _ROW, 32 * kb + _COL])
         put(o["TT"], rt, T[16 * rt + _ROW, _COL])
-        put(o["PP"], rt, -P[16 * rt + _ROW, _COL])
+        npt = -(P @ T)[16 * rt + _ROW, _COL]
+        put(o["PP"], rt, npt)
+        put(o["PL"], rt, npt - npt.astype(np.float16).astype(np.float64))
     for i in range(dk // 16):
         put(o["KH"], i, -KH[_COL, 16 * i + _ROW])
     rec[o["GAM"]:].view(np.float32)[:] = gam
@@ -85,7 +91,7 @@ def pack(dk, KG, QG, KH, T, P, gam):
 
 
 def unpack(dk, rec):
-    """Inverse of pack: (KG, QG, KH, T, P, gamma) as float64 from record bytes."""
+    """Inverse of pack: (KG, QG, KH, T, P T, gamma) as float64 from record bytes."""
     o = offsets(dk)
     h = rec[: o["GAM"]].view(np.float16).astype(np.float64)
 
@@ -100,7 +106,7 @@ def unpack(dk, rec):
             KG[16 * rt + _ROW, 32 * kb + _COL] = get(o["KG"], rt * (dk // 32) + kb)
             QG[16 * rt + _ROW, 32 * kb + _COL] = get(o["QG"], rt * (dk // 32) + kb)
         T[16 * rt + _ROW, _COL] = get(o["TT"], rt)
-        P[16 * rt + _ROW, _COL] = -get(o["PP"], rt)
+        P[16 * rt + _ROW, _COL] = -(get(o["PP"], rt) + get(o["PL"], rt))
     for i in range(dk // 16):
         KH[_COL, 16 * i + _ROW] = -get(o["KH"], i)
     return KG, QG, KH, T, P, rec[o["GAM"]:].view(np.float32).astype(np.float64)
