@@ -733,10 +733,12 @@ __device__ void state_step(Smem4<C>& sm, StateRegs<C>& R, const Item& it, const 
 __device__ __forceinline__ float column_max(float x) {
   const unsigned u = __float_as_uint(x);
   const auto h = __builtin_amdgcn_permlane32_swap(u, u, false, false);    // lanes l and l ^ 32
-  const float y = fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+  float y, z;
+  asm("v_max_f32 %0, %1, %2" : "=v"(y) : "v"(h[0]), "v"(h[1]));
   const unsigned v = __float_as_uint(y);
   const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);    // lanes l and l ^ 16
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  asm("v_max_f32 %0, %1, %2" : "=v"(z) : "v"(r[0]), "v"(r[1]));
+  return z;
 }
 
 // Column scale of a state wave for its next item, given the item's V values vf
@@ -1094,14 +1096,18 @@ __device__ __forceinline__ void chain_issue(char* slot, const ChainSrc& q, int c
   }
 }
 
+// At barrier n chunks n and n + 1 are in their slots (the state waves read
+// chunk n + 1 during step n), and chunk n - 1's slot is refilled with chunk
+// n + DEPTH - 1: each chunk has DEPTH - 1 steps to land.
 template <class C, int LW>
 __device__ void chain_loader(SmemC<C>& sm, const ChainSrc& q, int lane) {
-  constexpr int WAIT = vmcnt_imm((C::DEPTH - 1) * C::nk_of(LW));  // the oldest chunk has landed
+  static_assert(C::DEPTH >= 2 && C::RING == C::DEPTH + 1, "ring of DEPTH chunks in flight plus the one in use");
+  constexpr int WAIT = vmcnt_imm((C::DEPTH - 2) * C::nk_of(LW));  // all but the newest DEPTH - 2 chunks have landed
 #pragma unroll
   for (int c = 0; c < C::DEPTH; ++c) chain_issue<C, LW>(sm.ring[c], q, c, lane);
   __builtin_amdgcn_s_waitcnt(WAIT);
   for (int n = 0; n < q.nchunks; ++n) {
-    block_sync_lds();  // chunk n is in its slot; the slot of chunk n - 1 is free
+    block_sync_lds();  // chunks n and n + 1 are in their slots; the slot of chunk n - 1 is free
     chain_issue<C, LW>(sm.ring[(n + C::DEPTH) % C::RING], q, n + C::DEPTH, lane);
     __builtin_amdgcn_s_waitcnt(WAIT);
   }
@@ -1114,18 +1120,24 @@ __device__ __forceinline__ f16x8 slot_frag(const char* lb, int off, int f) {
   return *reinterpret_cast<const f16x8*>(lb + off + f * 1024);
 }
 
-// max |S| over this lane's values (a tree, not a chain)
+// max(|a|, |b|, |c|): one instruction where the operands come straight from
+// arithmetic in the same block (known canonical, so no quieting maximum is added)
+__device__ __forceinline__ float max3_abs(float a, float b, float c) {
+  return __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(a), __builtin_fabsf(b)), __builtin_fabsf(c));
+}
+
+// max |S| over this lane's values: four chains over the tiles' rows
 template <class C>
 __device__ __forceinline__ float lane_smax(const StateRegs<C>& R) {
-  float t[C::NKT];
+  static_assert(C::NKT >= 3, "three tiles at least");
+  float m[4];
 #pragma unroll
-  for (int i = 0; i < C::NKT; ++i)
-    t[i] = fmaxf(fmaxf(fabsf(R.S[i][0]), fabsf(R.S[i][1])), fmaxf(fabsf(R.S[i][2]), fabsf(R.S[i][3])));
+  for (int r = 0; r < 4; ++r) {
+    m[r] = max3_abs(R.S[0][r], R.S[1][r], R.S[2][r]);
 #pragma unroll
-  for (int h = C::NKT / 2; h >= 1; h /= 2)
-#pragma unroll
-    for (int i = 0; i < h; ++i) t[i] = fmaxf(t[i], t[i + h]);
-  return t[0];
+    for (int i = 3; i < C::NKT; i += 2) m[r] = max3_abs(m[r], R.S[i][r], R.S[i + 1 < C::NKT ? i + 1 : i][r]);
+  }
+  return max3_abs(m[0], m[1], max3_abs(m[2], m[3], m[3]));
 }
 
 template <class C>
@@ -1134,15 +1146,57 @@ __device__ __forceinline__ void pack_sf(StateRegs<C>& R) {
   for (int kb = 0; kb < C::NKB; ++kb) R.Sf[kb] = stack2(R.S[2 * kb], R.S[2 * kb + 1]);
 }
 
-// State wave w: the serial part of every chunk -- column scale, Xn = KG S - V,
-// Un = T Xn, S' = gamma S + (-KH)^T Un -- and nothing else.  The fp16 S and Xn
-// it used and the column scales go to output wave w through the handoff
-// buffer of the chunk's parity.  The state's maximum and fp16 copy for the
-// next chunk are formed at the end of a step, ahead of the barrier (and formed
-// again in the rare step that rescales a column).
+// A state wave's operands of one chunk, read from the chunk's ring slot.
+template <class C>
+struct ChainFrags {
+  f16x8 A[2][C::NKB], Tf[2], KH[C::NKT];  // KG, T and -KH^T fragments
+  f32x4 gam[C::NKT];                      // gamma of rows 16 i + 4g ..
+  s16x4 va[2];                            // V as bf16 A operands: token 16 rt + n, columns 4g .. 4g + 3
+  f32x4 x0[2];                            // -V * sc in the C layout of X (tokens 16 rt + 4g + r, column n)
+};
+
+template <class C>
+__device__ __forceinline__ void chain_fetch(const SmemC<C>& sm, int c, int w, int lane, ChainFrags<C>& F) {
+  using RC = typename C::R;
+  const char* sb = sm.ring[c % C::RING];
+  const char* lb = sb + 16 * opaque(lane);
+  const int gg = opaque(lane / 16), nn = opaque(lane % 16);
+  // V first: the column-scale check that follows waits only for it
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+    F.va[rt] = *reinterpret_cast<const s16x4*>(sb + C::RECK * 1024 + (16 * rt + nn) * C::VROW + (16 * w + 4 * gg) * 2);
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb) F.A[rt][kb] = slot_frag<C>(lb, RC::KG, rt * C::NKB + kb);
+    F.Tf[rt] = slot_frag<C>(lb, RC::TT, rt);
+  }
+#pragma unroll
+  for (int i = 0; i < C::NKT; ++i) F.KH[i] = slot_frag<C>(lb, RC::KH, i);
+#pragma unroll
+  for (int i = 0; i < C::NKT; ++i) F.gam[i] = *reinterpret_cast<const f32x4*>(sb + RC::GAM + (16 * i + 4 * gg) * 4);
+}
+
+// -sc times the identity as a bf16 B operand (lane (g, n) holds rows 4g .. 4g + 3
+// of column n): V times it is -V * sc in the C layout, exactly (sc is a power of two).
+__device__ __forceinline__ s16x4 neg_scaled_eye(float sc, int g, int n) {
+  const uint32_t h = __float_as_uint(-sc) >> 16;
+  const int j = n - 4 * g;  // the row of this lane's four that is on the diagonal, if any
+  const uint32_t w0 = j == 0 ? h : j == 1 ? h << 16 : 0u;
+  const uint32_t w1 = j == 2 ? h : j == 3 ? h << 16 : 0u;
+  return __builtin_bit_cast(s16x4, u32x2{w0, w1});
+}
+
+// State wave w: the serial part of every chunk -- Xn = KG S - V, Un = T Xn,
+// S' = gamma S + (-KH)^T Un -- and nothing else.  The fp16 S and Xn it used and
+// the column scales go to output wave w through the handoff buffer of the
+// chunk's parity.  Everything that does not depend on the new state -- reading
+// the next chunk's operands out of LDS, and -V * sc on the matrix cores -- is
+// issued right after the state update, so it overlaps the matrix-core
+// products; the state's maximum, fp16 copy and column scale for the next chunk
+// follow, ahead of the barrier.
 template <class C>
 __device__ void chain_state(SmemC<C>& sm, const Ctx4& cx, const SnapList& snap, int pos0, int w, int lane) {
-  using RC = typename C::R;
   const PrefillParams& p = cx.p;
   StateRegs<C> R;
   const int g = lane / 16, n16 = lane % 16;
@@ -1160,81 +1214,79 @@ __device__ void chain_state(SmemC<C>& sm, const Ctx4& cx, const SnapList& snap, 
     R.sc = 1.0f;
     R.usc = (f32x4)1.0f;
   }
+  s16x4 neye = neg_scaled_eye(R.sc, g, n16);
   int ns = 0;  // next listed position (positions up to pos0 belong to earlier blocks)
   while (ns < p.nsnap && snap.pos[ns] <= pos0) ++ns;
   float ms = lane_smax<C>(R);
   pack_sf<C>(R);
+  // -V * sc of the next chunk, then its column scale: keep the scaled column
+  // maximum of S and V within [2^-4, 2^4] (rarely changed; capped at 2^64 so a
+  // column that has decayed to nothing with no value input never scales to
+  // infinity, where 0 * inf would be NaN).  A lane whose own maximum is in range
+  // proves its column is not too large, and not too small either unless all
+  // four lanes of the column are small, so the per-column maximum is formed
+  // only when some lane is out of range.
+  auto start_chunk = [&](ChainFrags<C>& F) {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) F.x0[rt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(F.va[rt], neye, (f32x4)0.0f, 0, 0, 0);
+    const float lm = max3_abs(max3_abs(ms, F.x0[0][0], F.x0[0][1]), max3_abs(F.x0[0][2], F.x0[0][3], F.x0[1][0]),
+                              max3_abs(F.x0[1][1], F.x0[1][2], F.x0[1][3]));
+    // (bitwise operators: straight-line compares, no branches)
+    const bool room = R.sc < 0x1p64f;
+    if (__builtin_amdgcn_ballot_w64((lm > 16.0f) | ((lm < 0.0625f) & room)) == 0) return;
+    const float m = column_max(lm);
+    const bool bad = (m > 16.0f) | ((m > 0.0f) & (m < 0.0625f) & room);
+    if (__builtin_amdgcn_ballot_w64(bad) == 0) return;
+    float f = 1.0f;
+    if (bad) {
+      const int ex = __builtin_amdgcn_frexp_expf(m);  // m = frac * 2^ex, frac in [0.5, 1)
+      f = fminf(__builtin_amdgcn_ldexpf(1.0f, -ex), 0x1p64f / R.sc);  // powers of two: exact
+    }
+#pragma unroll
+    for (int i = 0; i < C::NKT; ++i) R.S[i] *= f;
+    F.x0[0] *= f;
+    F.x0[1] *= f;
+    R.sc *= f;
+    neye = neg_scaled_eye(R.sc, g, n16);
+    if (g == 0) sm.scol[w][n16] = __builtin_amdgcn_rcpf(R.sc);  // output rows are columns 4g .. 4g + 3
+    wave_lds_sync();
+    R.usc = *reinterpret_cast<const f32x4*>(&sm.scol[w][4 * g]);
+    pack_sf<C>(R);
+  };
+  ChainFrags<C> F;
+  block_sync_lds();  // chunks 0 and 1 are in their slots
+  if (cx.nchunks > 0) {
+    chain_fetch<C>(sm, 0, w, lane, F);
+    start_chunk(F);
+  }
   for (int n = 0; n < cx.nchunks; ++n) {
-    block_sync_lds();
-    const char* sb = sm.ring[n % C::RING];
-    const char* lb = sb + 16 * opaque(lane);
+    if (n > 0) block_sync_lds();  // chunk n + 1 is in its slot; the handoff of chunk n - 2 is free
     const Item it = {n, n, 0, chunk_end(n, cx.T), CS};
-    f16x8 A[2][C::NKB], Tf[2], KH[C::NKT];
-    float vf[2][4];
-    {
-      const __bf16* vs = reinterpret_cast<const __bf16*>(sb + C::RECK * 1024);
-      const int gg = opaque(lane / 16), nn = opaque(lane % 16);
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) vf[rt][r] = (float)vs[(16 * rt + 4 * gg + r) * C::J + 16 * w + nn];
-    }
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-#pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb) A[rt][kb] = slot_frag<C>(lb, RC::KG, rt * C::NKB + kb);
-      Tf[rt] = slot_frag<C>(lb, RC::TT, rt);
-    }
-#pragma unroll
-    for (int i = 0; i < C::NKT; ++i) KH[i] = slot_frag<C>(lb, RC::KH, i);
-    // column scale: keep the scaled column maximum of S and V within [2^-4, 2^4]
-    // (rarely changed; capped at 2^64 so a column that has decayed to nothing
-    // with no value input never scales to infinity, where 0 * inf would be NaN)
-    {
-      const float mv = fmaxf(fmaxf(fmaxf(fabsf(vf[0][0]), fabsf(vf[0][1])), fmaxf(fabsf(vf[0][2]), fabsf(vf[0][3]))),
-                             fmaxf(fmaxf(fabsf(vf[1][0]), fabsf(vf[1][1])), fmaxf(fabsf(vf[1][2]), fabsf(vf[1][3]))));
-      const float m = column_max(fmaxf(ms, mv * R.sc));
-      const bool bad = m > 16.0f || (m > 0.0f && m < 0.0625f && R.sc < 0x1p64f);
-      if (__builtin_amdgcn_ballot_w64(bad) != 0) {
-        float f = 1.0f;
-        if (bad) {
-          const int ex = __builtin_amdgcn_frexp_expf(m);  // m = frac * 2^ex, frac in [0.5, 1)
-          f = fminf(__builtin_amdgcn_ldexpf(1.0f, -ex), 0x1p64f / R.sc);  // powers of two: exact
-        }
-#pragma unroll
-        for (int i = 0; i < C::NKT; ++i) R.S[i] *= f;
-        R.sc *= f;
-        if (g == 0) sm.scol[w][n16] = __builtin_amdgcn_rcpf(R.sc);  // output rows are columns 4g .. 4g + 3
-        wave_lds_sync();
-        R.usc = *reinterpret_cast<const f32x4*>(&sm.scol[w][4 * g]);
-        pack_sf<C>(R);
-      }
-    }
     char* hb = sm.hand[n & 1][w] + 16 * lane;
-    f32x4 X[2];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) X[rt][r] = -vf[rt][r] * R.sc;
+    f32x4 X[2] = {F.x0[0], F.x0[1]};
 #pragma unroll
     for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) X[rt] = mma16(A[rt][kb], R.Sf[kb], X[rt]);
+      for (int rt = 0; rt < 2; ++rt) X[rt] = mma16(F.A[rt][kb], R.Sf[kb], X[rt]);
 #pragma unroll
     for (int kb = 0; kb < C::NKB; ++kb) *reinterpret_cast<f16x8*>(hb + kb * 1024) = R.Sf[kb];
     *reinterpret_cast<f32x4*>(hb + (C::NKB + 1) * 1024) = R.usc;
 #pragma unroll
-    for (int i = 0; i < C::NKT; ++i) R.S[i] *= *reinterpret_cast<const f32x4*>(sb + RC::GAM + (16 * i + 4 * g) * 4);
+    for (int i = 0; i < C::NKT; ++i) R.S[i] *= F.gam[i];
     const f16x8 xf = stack2(X[0], X[1]);
     f32x4 U[2];
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) U[rt] = mma16(Tf[rt], xf, (f32x4)0.0f);
+    for (int rt = 0; rt < 2; ++rt) U[rt] = mma16(F.Tf[rt], xf, (f32x4)0.0f);
     const f16x8 uf = stack2(U[0], U[1]);
 #pragma unroll
-    for (int i = 0; i < C::NKT; ++i) R.S[i] = mma16(KH[i], uf, R.S[i]);
+    for (int i = 0; i < C::NKT; ++i) R.S[i] = mma16(F.KH[i], uf, R.S[i]);
     *reinterpret_cast<f16x8*>(hb + C::NKB * 1024) = xf;
+    // (after the last chunk this reads a slot the loaders filled with zeros: no
+    // branch, so the maxima below see the products' results directly)
+    chain_fetch<C>(sm, n + 1, w, lane, F);
     ms = lane_smax<C>(R);
     pack_sf<C>(R);
+    start_chunk(F);
     if (ns < p.nsnap && snap.pos[ns] == pos0 + n * CS + it.hi) {
       store_state<C>(p.snaps + ((size_t)cx.bh * p.nsnap + ns) * C::DK * p.dv + cx.col0, R, p.dv, w, lane);
       ++ns;
