@@ -75,6 +75,7 @@ struct PrefillPlan {
 int g_force_impl = -1;  // -1: the library's choice; 0: generic; 1: pipeline; 2: two-stage
 int g_force_slab = 0;   // 0: the library's choice; 16 or 32
 size_t g_rec_cap = 0;   // 0: the library's cap on the two-stage workspace
+int g_force_overlap = -1;  // -1: the library's choice; 0: never; 1: for every blocked batch
 #endif
 
 PrefillPlan plan_prefill(int B, int H, int dk, int dv, int chunk, int io) {
@@ -208,15 +209,50 @@ hipError_t pool_of_current_device(hipMemPool_t* out) {
   return hipSuccess;
 }
 
+int overlap_mode() {
+#ifdef KDA_TEST_HOOKS
+  return g_force_overlap;
+#else
+  return -1;
+#endif
+}
+
+// Compute units of the current device (queried once per device).
+std::mutex g_cus_mu;
+int g_cus[kMaxPoolDevices];
+hipError_t cus_of_current_device(int* out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxPoolDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_cus_mu);
+  if (!g_cus[dev]) {
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    g_cus[dev] = n > 0 ? n : 1;
+  }
+  *out = g_cus[dev];
+  return hipSuccess;
+}
+
 // Runs the two-stage prefill.  *ran = false (nothing enqueued, hipSuccess) when
 // the workspace is over the cap or cannot be allocated: the caller then runs
 // the single-kernel pipeline.
+//
+// A batch of equal-length sequences whose records exceed the cap runs in
+// blocks of chunks.  When its chain leaves at least half of the compute units
+// free (few heads: one workgroup per 32-column slab, one per compute unit), the
+// blocks alternate between two record buffers and each launch runs the chain
+// over block k beside stage 1 of block k + 1; otherwise stage 1 and the chain
+// of each block run one after the other in one buffer.
 hipError_t run_two_stage(kda::PrefillParams p, const kda::SnapList& snap, hipStream_t hs, bool* ran) {
   *ran = false;
   const size_t rb = (size_t)kda::chunk_rec_bytes(p.dk);
   const size_t cap = rec_cap();
   const long long nch = ((long long)p.T + kda::kPipeChunk - 1) / kda::kPipeChunk;
   long long nslots, nc = 0, nblk = 1;
+  bool overlap = false;
   if (p.cu) {
     nslots = (long long)p.T / kda::kPipeChunk + p.B + 1;  // slots cu[b] / 32 + b + c
     if ((size_t)nslots * p.H * rb > cap) return hipSuccess;
@@ -226,29 +262,51 @@ hipError_t run_two_stage(kda::PrefillParams p, const kda::SnapList& snap, hipStr
     nc = std::max(1LL, std::min(nch, (long long)(cap / per_chunk)));
     nblk = std::max(1LL, (nch + nc - 1) / nc);
     nslots = (long long)p.B * nc;
+    const int mode = overlap_mode();
+    if (nblk > 1 && mode != 0) {
+      int cus = 0;
+      hipError_t ce = cus_of_current_device(&cus);
+      if (ce != hipSuccess) return ce;
+      const long long chain_grid = (long long)p.B * p.H * (p.dv / 32);
+      overlap = mode == 1 || 2 * chain_grid <= cus;
+    }
   }
-  const size_t rec_bytes = (size_t)nslots * p.H * rb;
+  const int nbuf = overlap ? 2 : 1;
+  const size_t rec_bytes = (size_t)nslots * p.H * rb;  // one buffer
   const size_t carry_bytes = (nblk > 1 && !p.S_T) ? (size_t)4 * p.B * p.H * p.dk * p.dv : 0;
   hipMemPool_t pool = nullptr;
   hipError_t e = pool_of_current_device(&pool);
   if (e != hipSuccess) return e;
   void* ws = nullptr;
-  if (hipMallocFromPoolAsync(&ws, rec_bytes + carry_bytes, pool, hs) != hipSuccess || !ws) {
+  if (hipMallocFromPoolAsync(&ws, nbuf * rec_bytes + carry_bytes, pool, hs) != hipSuccess || !ws) {
     (void)hipGetLastError();  // out of memory here is not an error of the call
     return hipSuccess;
   }
   *ran = true;
   const float* S0 = p.S0;
   float* S_T = p.S_T;
-  float* carry = S_T ? S_T : reinterpret_cast<float*>(static_cast<char*>(ws) + rec_bytes);
-  p.rec = static_cast<char*>(ws);
-  for (long long blk = 0; blk < nblk && e == hipSuccess; ++blk) {
-    p.rec_c0 = (int)(blk * nc);
-    p.rec_nc = (int)nc;
-    p.S0 = blk == 0 ? S0 : carry;         // each workgroup reads its slab of S0 before
-    p.S_T = blk == nblk - 1 ? S_T : carry;  // it writes the same slab of S_T
-    e = kda::launch_prefill_prep(p, nslots, hs);
-    if (e == hipSuccess) e = kda::launch_prefill_chain(p, snap, hs);
+  float* carry = S_T ? S_T : reinterpret_cast<float*>(static_cast<char*>(ws) + nbuf * rec_bytes);
+  auto block = [&](long long blk) {
+    kda::PrefillParams q = p;
+    q.rec = static_cast<char*>(ws) + (blk % nbuf) * rec_bytes;
+    q.rec_c0 = (int)(blk * nc);
+    q.rec_nc = (int)nc;
+    q.S0 = blk == 0 ? S0 : carry;         // each workgroup reads its slab of S0 before
+    q.S_T = blk == nblk - 1 ? S_T : carry;  // it writes the same slab of S_T
+    return q;
+  };
+  if (!overlap) {
+    for (long long blk = 0; blk < nblk && e == hipSuccess; ++blk) {
+      const kda::PrefillParams q = block(blk);
+      e = kda::launch_prefill_prep(q, nslots, hs);
+      if (e == hipSuccess) e = kda::launch_prefill_chain(q, snap, hs);
+    }
+  } else {
+    e = kda::launch_prefill_prep(block(0), nslots, hs);
+    for (long long blk = 0; blk < nblk && e == hipSuccess; ++blk) {
+      if (blk + 1 < nblk) e = kda::launch_prefill_chain_prep(block(blk), block(blk + 1), nslots, snap, hs);
+      else e = kda::launch_prefill_chain(block(blk), snap, hs);
+    }
   }
   const hipError_t fe = hipFreeAsync(ws, hs);
   return e != hipSuccess ? e : fe;
@@ -327,6 +385,10 @@ void kda_test_force_prefill(int impl, int slab) {
 // Test builds only: the two-stage prefill's workspace cap in bytes (0: the
 // library's), so small calls exercise the blocked path.  Not thread-safe.
 void kda_test_set_rec_cap(unsigned long long bytes) { g_rec_cap = (size_t)bytes; }
+// Test builds only: whether blocked two-stage batches run each block's chain
+// beside stage 1 of the next (-1: the library's choice, 0: never, 1: always).
+// Not thread-safe.
+void kda_test_set_overlap(int mode) { g_force_overlap = mode; }
 
 // Test builds only: the two stages of the two-stage prefill run alone, on B
 // sequences of T tokens (bf16 q/k/v, d_k in {64, 128}, no checks beyond the

@@ -84,14 +84,13 @@ __device__ __forceinline__ int seq_by_length_rank(const int* cu, int n, int T, i
   return *pick;
 }
 
-// Workgroup -> (task, slab), a task being one (sequence rank, head) pair served
+// Workgroup bi of G -> (task, slab), a task being one (sequence rank, head) pair served
 // by nslab workgroups.  Workgroups are dispatched in index order, round-robin
 // over the 8 XCDs (each with its own L2): a task's slabs go to one XCD, so they
 // share its L2 for the task's keys, queries and decays, and consecutive tasks
 // go to consecutive XCDs, so the tasks dispatched first -- the longest
 // sequences of a packed batch -- are spread over all of them.
-__device__ __forceinline__ void task_of_block(int nslab, int& task, int& slab) {
-  const int G = gridDim.x, bi = blockIdx.x;
+__device__ __forceinline__ void task_of_index(int nslab, int G, int bi, int& task, int& slab) {
   if ((G / nslab) % 8 == 0) {
     const int x = bi % 8, q = bi / 8;
     slab = q % nslab;
@@ -100,6 +99,10 @@ __device__ __forceinline__ void task_of_block(int nslab, int& task, int& slab) {
     task = bi / nslab;
     slab = bi % nslab;
   }
+}
+// The same for this workgroup of a launch of its tasks alone.
+__device__ __forceinline__ void task_of_block(int nslab, int& task, int& slab) {
+  task_of_index(nslab, gridDim.x, blockIdx.x, task, slab);
 }
 
 // Token range of sequence b: first packed token and length.
@@ -186,6 +189,10 @@ hipError_t launch_prefill_prep(const PrefillParams& p, long long nslots, hipStre
 // Stage 2: without cu, the chunks [rec_c0, rec_c0 + rec_nc) of every sequence,
 // from S0 to S_T (either may be null: zeros / not written).
 hipError_t launch_prefill_chain(const PrefillParams& p, const SnapList& snap, hipStream_t s);
+// The chain over the block of chunks pc describes and, beside it in the same
+// launch, stage 1 of the block pp describes (nslots record slots).
+hipError_t launch_prefill_chain_prep(const PrefillParams& pc, const PrefillParams& pp, long long nslots,
+                                     const SnapList& snap, hipStream_t s);
 
 // Between the two split passes: ws_in[b][0] = S0 (zeros when null) and
 // ws_in[b][j+1] = M_j ws_in[b][j] + N_j from ws_trans, for every (b, h): a

@@ -38,6 +38,7 @@
 // S' = gamma S + (-KH)^T Un and O = QG S + (-P) Un.
 #include "kda_device.h"
 #include "kda_launch.h"
+#include "kda_prep_impl.h"
 
 
 namespace kda {
@@ -1254,8 +1255,8 @@ __device__ void chain_state(SmemC<C>& sm, const Ctx4& cx, const SnapList& snap, 
     pack_sf<C>(R);
   };
   ChainFrags<C> F;
-  block_sync_lds();  // chunks 0 and 1 are in their slots
   if (cx.nchunks > 0) {
+    block_sync_lds();  // chunks 0 and 1 are in their slots
     chain_fetch<C>(sm, 0, w, lane, F);
     start_chunk(F);
   }
@@ -1340,20 +1341,22 @@ __device__ void chain_output(SmemC<C>& sm, const Ctx4& cx, int w, int lane) {
   if (cx.nchunks > 0) emit(cx.nchunks - 1);
 }
 
+// Workgroup bi of a chain launch over G workgroups (one per slab task).  Waves
+// past the chain's NW (a launch shared with stage 1 has more) only take part in
+// its barriers.
 template <class C>
-__global__ __launch_bounds__(C::NT, 1) void kda_chain_kernel(PrefillParams p, SnapList snap) {
-  __shared__ SmemC<C> sm;
-  __shared__ int seq_lens[kMaxRankedSeqs], seq_pick;
+__device__ __forceinline__ void chain_block(SmemC<C>& sm, int* seq_lens, int* seq_pick, const PrefillParams& p,
+                                            const SnapList& snap, int G, int bi) {
   const int tid = threadIdx.x, lane = tid % 64;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   int task, slab;
-  task_of_block(p.dv / C::J, task, slab);
+  task_of_index(p.dv / C::J, G, bi, task, slab);
   Ctx4 cx;
   cx.p = p;
   cx.h = task % p.H;
   cx.col0 = slab * C::J;
   cx.eA = 1.0f;
-  cx.b = __builtin_amdgcn_readfirstlane(seq_by_length_rank(p.cu, p.B, p.T, task / p.H, seq_lens, &seq_pick));
+  cx.b = __builtin_amdgcn_readfirstlane(seq_by_length_rank(p.cu, p.B, p.T, task / p.H, seq_lens, seq_pick));
   cx.bh = cx.b * p.H + cx.h;
   long long slot0;
   int pos0 = 0;
@@ -1381,7 +1384,7 @@ __global__ __launch_bounds__(C::NT, 1) void kda_chain_kernel(PrefillParams p, Sn
     chain_state<C>(sm, cx, snap, pos0, wave, lane);
   } else if (wave < 2 * C::NST) {
     chain_output<C>(sm, cx, wave - C::NST, lane);
-  } else {
+  } else if (wave < C::NW) {
     ChainSrc q;
     q.rec = p.rec + (slot0 * p.H + cx.h) * C::R::BYTES;
     q.rec_step = (long long)p.H * C::R::BYTES;
@@ -1391,6 +1394,41 @@ __global__ __launch_bounds__(C::NT, 1) void kda_chain_kernel(PrefillParams p, Sn
     q.T = cx.T;
     if (wave == 2 * C::NST) chain_loader<C, 0>(sm, q, lane);
     else chain_loader<C, 1>(sm, q, lane);
+  } else {
+    for (int n = 0; n <= cx.nchunks; ++n) block_sync_lds();  // every role's nchunks + 1 barriers
+  }
+}
+
+template <class C>
+__global__ __launch_bounds__(C::NT, 1) void kda_chain_kernel(PrefillParams p, SnapList snap) {
+  __shared__ SmemC<C> sm;
+  __shared__ int seq_lens[kMaxRankedSeqs], seq_pick;
+  chain_block<C>(sm, seq_lens, &seq_pick, p, snap, gridDim.x, blockIdx.x);
+}
+
+// One launch for two blocks of chunks of a long batch: workgroups 0 .. G-1 run
+// the chain over block k (records written by the previous launch), the rest
+// run stage 1 of block k + 1 into the other record buffer, eight records each.
+// The chain's workgroups come first, so they are placed first (one per
+// compute unit); stage 1 runs on the compute units the chain leaves free and
+// refills them as its workgroups finish.  Every workgroup reserves the larger
+// of the two roles' LDS, which for stage 1 is that of eight waves.
+constexpr int kFusedWaves = 8;
+template <class C, class PC, bool G>
+__global__ __launch_bounds__(64 * kFusedWaves, 1) void kda_chain_prep_kernel(PrefillParams pc, PrefillParams pp,
+                                                                           SnapList snap, int chain_grid,
+                                                                           long long nrec) {
+  static_assert(C::NW <= kFusedWaves, "chain waves fit the launch");
+  constexpr size_t LC = sizeof(SmemC<C>), LP = kFusedWaves * sizeof(prep::PrepLds<PC>);
+  __shared__ __attribute__((aligned(16))) char smem[LC > LP ? LC : LP];
+  __shared__ int seq_lens[kMaxRankedSeqs], seq_pick;
+  if ((int)blockIdx.x < chain_grid) {
+    chain_block<C>(*reinterpret_cast<SmemC<C>*>(smem), seq_lens, &seq_pick, pc, snap, chain_grid, blockIdx.x);
+  } else {
+    const int lane = threadIdx.x % 64;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    const long long rec = (long long)(blockIdx.x - chain_grid) * kFusedWaves + wave;
+    if (rec < nrec) prep::prep_record<PC, G>(pp, rec, reinterpret_cast<prep::PrepLds<PC>*>(smem)[wave], lane);
   }
 }
 
@@ -1400,6 +1438,24 @@ hipError_t launch_chain(const PrefillParams& p, const SnapList& snap, hipStream_
   const long long grid = (long long)p.B * p.H * (p.dv / C::J);
   if (grid <= 0) return hipSuccess;
   hipLaunchKernelGGL((kda_chain_kernel<C>), dim3((unsigned)grid), dim3(C::NT), 0, s, p, snap);
+  return hipGetLastError();
+}
+
+template <int DK, int NST>
+hipError_t launch_chain_prep(const PrefillParams& pc, const PrefillParams& pp, long long nslots, const SnapList& snap,
+                             hipStream_t s) {
+  using C = CfgC<DK, NST>;
+  using PC = prep::PCfg<DK>;
+  const long long chain_grid = (long long)pc.B * pc.H * (pc.dv / C::J);
+  const long long nrec = nslots * pp.H;
+  const long long grid = chain_grid + (nrec + kFusedWaves - 1) / kFusedWaves;
+  if (chain_grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (pp.z)
+    hipLaunchKernelGGL((kda_chain_prep_kernel<C, PC, true>), dim3((unsigned)grid), dim3(64 * kFusedWaves), 0, s, pc, pp,
+                       snap, (int)chain_grid, nrec);
+  else
+    hipLaunchKernelGGL((kda_chain_prep_kernel<C, PC, false>), dim3((unsigned)grid), dim3(64 * kFusedWaves), 0, s, pc,
+                       pp, snap, (int)chain_grid, nrec);
   return hipGetLastError();
 }
 }  // namespace
@@ -1424,6 +1480,13 @@ bool prefill_chain_supported(int io_dtype, int dk, int dv, int chunk, int H) {
 hipError_t launch_prefill_chain(const PrefillParams& p, const SnapList& snap, hipStream_t s) {
   if (p.dk == 128) return launch_chain<128, 2>(p, snap, s);
   if (p.dk == 64) return launch_chain<64, 2>(p, snap, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_chain_prep(const PrefillParams& pc, const PrefillParams& pp, long long nslots,
+                                     const SnapList& snap, hipStream_t s) {
+  if (pc.dk == 128) return launch_chain_prep<128, 2>(pc, pp, nslots, snap, s);
+  if (pc.dk == 64) return launch_chain_prep<64, 2>(pc, pp, nslots, snap, s);
   return hipErrorInvalidValue;
 }
 

@@ -106,13 +106,15 @@ class PerHeadSeqErr:
         return float((self.maxd / np.maximum(rms, 1e-30)).max())
 
 
-def forced_prefill(impl, slab=0, rec_cap=0):
+def forced_prefill(impl, slab=0, rec_cap=0, overlap=-1):
     """Context manager: run the binding's calls through libkda_testhooks.so (the
     same kernels, with test switches in the C ABI) with the prefill kernel forced
     (impl -1: the library's choice, 0: the generic kernel, 1: the single-kernel
     pipeline, 2: the two-stage prefill, where they apply; slab: the generic
     kernel's columns per workgroup, 0: the library's choice; rec_cap: the
-    two-stage workspace cap in bytes, 0: the library's)."""
+    two-stage workspace cap in bytes, 0: the library's; overlap: whether a
+    blocked two-stage batch runs each block's chain beside stage 1 of the next,
+    -1: the library's choice, 0: never, 1: always)."""
     import contextlib
     import ctypes
 
@@ -128,15 +130,19 @@ def forced_prefill(impl, slab=0, rec_cap=0):
             _HOOKS.kda_test_force_prefill.restype = None
             _HOOKS.kda_test_set_rec_cap.argtypes = [ctypes.c_ulonglong]
             _HOOKS.kda_test_set_rec_cap.restype = None
+            _HOOKS.kda_test_set_overlap.argtypes = [ctypes.c_int]
+            _HOOKS.kda_test_set_overlap.restype = None
         saved = kda._lib
         kda._lib = _HOOKS
         _HOOKS.kda_test_force_prefill(int(impl), int(slab))
         _HOOKS.kda_test_set_rec_cap(int(rec_cap))
+        _HOOKS.kda_test_set_overlap(int(overlap))
         try:
             yield
         finally:
             _HOOKS.kda_test_force_prefill(-1, 0)
             _HOOKS.kda_test_set_rec_cap(0)
+            _HOOKS.kda_test_set_overlap(-1)
             kda._lib = saved
 
     return cm()

@@ -166,15 +166,18 @@ def test_two_stage_any_decay(gpu, dk):
 
 @pytest.mark.parametrize("nblk_chunks", [1, 3, 5])
 @pytest.mark.parametrize("with_st", [True, False])
-def test_blocked_sequence(gpu, nblk_chunks, with_st):
+@pytest.mark.parametrize("overlap", [0, 1])
+def test_blocked_sequence(gpu, nblk_chunks, with_st, overlap):
     """A workspace cap of a few chunks per sequence: the sequence runs in blocks,
-    the state carried through S_T (or a pool buffer when S_T is not wanted)."""
+    the state carried through S_T (or a pool buffer when S_T is not wanted);
+    one block's stage 1 then its chain, or (overlap) each block's chain in one
+    launch with stage 1 of the next, in two alternating record buffers."""
     kda = _kda()
     B, T, H = 2, 300, 2
     inp = _inp(gpu, B, T, H, 128, 128, seed=60 + nblk_chunks)
     cap = nblk_chunks * B * H * REC128
-    log(f"blocked: {nblk_chunks} chunks per block, S_T {'wanted' if with_st else 'not wanted'}")
-    with forced_prefill(2, rec_cap=cap):
+    log(f"blocked: {nblk_chunks} chunks per block, S_T {'wanted' if with_st else 'not wanted'}, overlap {overlap}")
+    with forced_prefill(2, rec_cap=cap, overlap=overlap):
         o, st = kda.kda_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["S0"],
                                   want_state=with_st)
         torch.cuda.synchronize()
@@ -188,7 +191,8 @@ def test_blocked_sequence(gpu, nblk_chunks, with_st):
     assert_close(gpu_o_heads(o), ro, True, "blocked o")
 
 
-def test_blocked_in_place_state_and_snapshots(gpu):
+@pytest.mark.parametrize("overlap", [0, 1])
+def test_blocked_in_place_state_and_snapshots(gpu, overlap):
     """S0 and S_T one buffer, snapshots on and between block edges."""
     kda = _kda()
     B, T, H = 1, 333, 2
@@ -196,7 +200,7 @@ def test_blocked_in_place_state_and_snapshots(gpu):
     pos = [32, 64, 96, 160, 320, 333]
     cap = 2 * B * H * REC64  # 64-token blocks
     S = inp["S0"].clone()
-    with forced_prefill(2, rec_cap=cap):
+    with forced_prefill(2, rec_cap=cap, overlap=overlap):
         o, st, sn = kda.kda_chunk_fwd_snapshots(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], S,
                                                 snap_tokens=pos, chunk=32, S_T=S)
         torch.cuda.synchronize()
@@ -261,3 +265,22 @@ def test_gated_two_stage(gpu, dk):
     eo = assert_close(gpu_o_heads(o), ro, True, f"gated two-stage d={dk} o")
     assert_close(gpu_s_heads(st), rs, True, f"gated two-stage d={dk} S_T")
     log(f"  fast-forgetting worst head: {eo:.2e}")
+
+
+@pytest.mark.parametrize("dk", [128, 64])
+def test_blocked_gated_overlap(gpu, dk):
+    """The gated call in blocks with each block's chain beside the next block's
+    stage 1 (the gate formed there): bit-equal to one block and to the serial
+    blocks."""
+    kda = _kda()
+    B, T, H = 1, 420, 3
+    inp = ki.make_prefill(B, T, H, dk, dk, torch.bfloat16, 3.0, 0.1, seed=95 + dk, device=gpu)
+    z, A = ki.make_gate((B, T, H, dk), H, torch.bfloat16, seed=96 + dk, device=gpu)
+    cap = 4 * B * H * cr.offsets(dk)["BYTES"]  # 128-token blocks, the last one ragged
+    outs = []
+    for rec_cap, overlap in ((0, -1), (cap, 0), (cap, 1)):
+        with forced_prefill(2, rec_cap=rec_cap, overlap=overlap):
+            outs.append(kda.kda_chunk_fwd_gated(inp["q"], inp["k"], inp["v"], z, A, inp["beta"], inp["S0"], chunk=32))
+            torch.cuda.synchronize()
+    for o, st in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(st, outs[0][1])
