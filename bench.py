@@ -480,7 +480,7 @@ def main():
     # ------- few long chains: the split prefill (kda_chunk_fwd_split) against the single pass -------
     if "split" in legs:
         split_res = []
-        for sB, sT, sH, sseed in ((1, 4096, 8, 5), (1, 65536, 2, 6)):
+        for sB, sT, sH, sseed in ((1, 16384, 2, 5), (1, 65536, 2, 6)):
             sx = ki.make_prefill(sB, sT, sH, dk, dv, w.qkv_dtype, w.alpha_mu, w.s0_std, seed=sseed, device=dev)
             n_parts, ws_bytes = kda.kda_chunk_fwd_split_plan(w.qkv_dtype, sB, sT, sH, dk, dv, chunk=C)
             s_ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)

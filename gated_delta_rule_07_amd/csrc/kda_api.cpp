@@ -122,17 +122,21 @@ double combine_steps(int P) {
 // The part count with the smallest modelled time.  The model counts pipeline
 // steps: a launch of G workgroups on `cus` compute units runs ceil(G / cus)
 // rounds of (chunks per part + 3) steps; the combine as above, and the two
-// extra launches about two steps.  A split is taken only when it models at
-// least 10% faster than the single pass.
+// extra launches about two steps.  The single pass it is weighed against is
+// the two-stage prefill where that is what one part runs (its chain steps
+// about 0.42 pipeline steps, after stage 1 at about 160 records per pipeline
+// step on 256 compute units), else the pipeline.  A split is taken only when
+// it models at least 25% (two-stage) or 10% (pipeline) faster.
 size_t split_ws_bytes(int B, int H, int dk, int dv, int P);
 
-SplitShape split_shape_auto(int B, int T, int H, int dk, int dv, int cus, size_t max_ws = SIZE_MAX) {
+SplitShape split_shape_auto(int B, int T, int H, int dk, int dv, int cus, bool two_stage, size_t max_ws = SIZE_MAX) {
   const int nch = (T + 31) / 32;
   const long long bh = (long long)B * H, ns = dv / 32, nsa = (dv + dk) / 32;
   auto rounds = [&](long long g) { return (double)((g + cus - 1) / cus); };
-  const double single = rounds(bh * ns) * (nch + 3);
+  const double single = two_stage ? rounds(bh * ns) * (nch + 3) * 0.42 + (double)bh * nch / (160.0 * cus / 256) + 2.0
+                                  : rounds(bh * ns) * (nch + 3);
   SplitShape best{1, T};
-  double best_cost = 0.9 * single;
+  double best_cost = (two_stage ? 0.75 : 0.9) * single;
   for (int P = 2; P <= nch && P <= kMaxParts; ++P) {
     const SplitShape sh = split_shape_for(T, P);
     if (sh.parts != P || split_ws_bytes(B, H, dk, dv, P) > max_ws) continue;
@@ -509,7 +513,9 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, int qkv_d
         g_last_hip_error = (int)hipErrorNoDevice;
         return KDA_ERR_HIP;
       }
-      sh = split_shape_auto(B, T, H, d_k, d_v, cus, split->scratch ? KDA_SPLIT_SCRATCH_BYTES : SIZE_MAX);
+      // one part of the allocation-free call runs the pipeline (no workspace)
+      sh = split_shape_auto(B, T, H, d_k, d_v, cus, plan.impl == IMPL_CHAIN && !split->scratch,
+                            split->scratch ? KDA_SPLIT_SCRATCH_BYTES : SIZE_MAX);
     }
   }
   char* ws = nullptr;
@@ -639,7 +645,8 @@ kda_status kda_chunk_fwd_split_plan(kda_dtype qkv_dtype, int B, int T, int H, in
   if (!parts_out || !workspace_bytes) return KDA_ERR_NULL;
   const int io = io_of(raw_enum(qkv_dtype));
   SplitShape sh{1, T};
-  if (plan_prefill(B, H, d_k, d_v, chunk, io).impl == IMPL_GENERIC) {  // splits run the pipeline kernel
+  const PrefillImpl impl = plan_prefill(B, H, d_k, d_v, chunk, io).impl;
+  if (impl == IMPL_GENERIC) {  // splits run the pipeline kernel
     if (parts > 1) return KDA_ERR_UNSUPPORTED;
   } else if (parts > 1) {
     sh = split_shape_for(T, parts);
@@ -649,7 +656,7 @@ kda_status kda_chunk_fwd_split_plan(kda_dtype qkv_dtype, int B, int T, int H, in
       g_last_hip_error = (int)hipErrorNoDevice;
       return KDA_ERR_HIP;
     }
-    sh = split_shape_auto(B, T, H, d_k, d_v, cus);
+    sh = split_shape_auto(B, T, H, d_k, d_v, cus, impl == IMPL_CHAIN);
   }
   *parts_out = sh.parts;
   *workspace_bytes = split_ws_bytes(B, H, d_k, d_v, sh.parts);

@@ -13,8 +13,18 @@
  *
  * Conventions shared by every call:
  *  - All tensor pointers are DEVICE pointers (HIP global memory) owned by the
- *    caller.  The library allocates nothing and keeps no state beyond a
- *    thread-local copy of the last HIP error.  Calls are reentrant.
+ *    caller.  The bf16 prefill with d_k in {64, 128} (kda_chunk_fwd, its
+ *    snapshot, packed-batch and gated forms, and a split of one part) keeps its
+ *    per-chunk intermediates ("chunk records", about 1 KB per token and head) in
+ *    device memory it takes from a memory pool the library creates on each
+ *    device at first use and keeps: allocated and freed in stream order on
+ *    `stream` around the call, at most 1 GiB of records per buffer (2 GiB when a
+ *    long batch's blocks overlap); when that memory cannot be had, or a packed
+ *    batch's records exceed the cap, the call runs a kernel that needs none.
+ *    kda_chunk_fwd_split_noalloc never allocates.  Beyond that pool the library
+ *    keeps, per device, its compute-unit count and the address of the
+ *    allocation-free call's array, and a thread-local copy of the last HIP
+ *    error.  Calls are reentrant.
  *  - `stream` is the hipStream_t the work is enqueued on (NULL = the default
  *    stream).  Each call only enqueues work on that stream and returns without
  *    synchronising; a device-side fault surfaces at the caller's next
@@ -27,16 +37,20 @@
  *  - Supported sizes: d_k, d_v in {16, 32, 64, 128}, for bf16 and fp32 q/k/v.
  *  - Arithmetic.  The state is carried in fp32 and every product accumulates in
  *    fp32.  With fp32 q/k/v all matrix-core operands are fp32.  With bf16 q/k/v
- *    the matrix-core operands are fp16: the decayed keys and queries (bounded by
- *    |k|, |q|), the inverse-decayed keys (at most e^10 |k|: a chunk whose decay
- *    would exceed that is processed as shorter exact segments), and the state
- *    and values rescaled by a power of two per state column, so their magnitude
- *    is not restricted.  q and k entries should stay below 6.5e4 in magnitude.
+ *    the matrix-core operands are fp16: the decayed keys and queries, the
+ *    factors of the intra-chunk key products (each bounded by |k| or |q|: every
+ *    decay ratio inside a chunk is split at a power-of-two block boundary into
+ *    two products of decays; the single-kernel form used without a workspace
+ *    takes inverse-decayed keys, at most e^10 |k|, and processes a chunk whose
+ *    decay would exceed that as shorter exact segments), and the state and
+ *    values rescaled by a power of two per state column, so their magnitude is
+ *    not restricted.  q and k entries should stay below 6.5e4 in magnitude.
  *    (Head sizes served by the generic kernel form the intra-chunk key products
  *    from bf16 high/low pairs instead, about 16 significant bits.)
  *  - Input domain: alpha in [exp(-5), 1] (the lower-bounded decay of section 3.5
- *    of the same page); results outside it are not guaranteed.  beta may be any
- *    finite value (it is not clamped).
+ *    of the same page); results outside it are not guaranteed, except that the
+ *    bf16 prefill with d_k in {64, 128} on its chunk-record path accepts any
+ *    alpha in [0, 1].  beta may be any finite value (it is not clamped).
  */
 #ifndef KDA_H
 #define KDA_H
@@ -219,7 +233,8 @@ kda_status kda_chunk_fwd_gated(const void* q, const void* k, const void* v, kda_
  * are whole 32-token chunks.
  *
  *   parts     : 0 = the library's choice (a step-count model of the launches
- *               on num_cus compute units; 1 part when splitting does not pay);
+ *               on num_cus compute units against the single pass the call would
+ *               otherwise run; 1 part when splitting does not pay);
  *               1 = the single pass (kda_chunk_fwd); >= 2 = that many parts, or
  *               fewer when T has fewer 32-token chunks.
  *   num_cus   : compute units for the model; 0 = those of the current device.

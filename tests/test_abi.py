@@ -361,8 +361,10 @@ def test_split_plan_choices():
     """The part count the library picks for 256 compute units, and the workspace
     it asks for (host logic only: an explicit compute-unit count makes no HIP call)."""
     lib = _lib()
-    st, n, ws = _plan(lib, B=1, T=4096, H=8)      # 32 chains of 128 chunks: split
-    assert st == 0 and 2 <= n <= 16 and ws == _ws_bytes(n)
+    # 32 chains of 128 chunks: the single pass (its chain steps are short) is not beaten
+    assert _plan(lib, B=1, T=4096, H=8) == (0, 1, 0)
+    st, n, ws = _plan(lib, B=1, T=16384, H=2)     # 8 chains of 512 chunks: split
+    assert st == 0 and 2 <= n <= 64 and ws == _ws_bytes(n, H=2)
     st, n, _ = _plan(lib, B=1, T=65536, H=2)      # 8 chains of 2048 chunks: many parts
     assert st == 0 and n >= 16
     assert _plan(lib, B=2, T=65536, H=32) == (0, 1, 0)   # 256 chains fill the GPU already

@@ -152,7 +152,10 @@ def test_split_through_steep_decay(gpu):
 
 
 def test_split_4k_workload_auto(gpu):
-    """B=1, H=8, T=4096: the library's part count; every head against the oracle."""
+    """B=1, H=8, T=4096: the library's part count (one: the two-stage single pass
+    models faster than any split) and an explicit split; every head against the
+    oracle."""
     inp = ki.make_workload_prefill(1, seed=2, device=gpu)
     n = _check(inp, 0, "4K workload auto")
-    assert n > 1, "the 4K workload should be split on this GPU"
+    assert n == 1, "the 4K workload's single pass beats a split on this GPU"
+    _check(inp, 5, "4K workload, 5 parts")
