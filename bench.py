@@ -111,18 +111,25 @@ def med(xs):
     return float(statistics.median(xs))
 
 
-def back_to_back_ms(fn, n, torch):
-    """Mean ms per launch of n launches of fn() back to back between one pair of
-    HIP events on the current stream (no markers between launches, so short
-    kernels are not charged for them)."""
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(n):
+def back_to_back_ms(fn, n, torch, groups=5, warm=5):
+    """Median over `groups` groups of n launches of fn() back to back (after
+    `warm` untimed groups, which carry the first milliseconds of a new load,
+    while the clocks settle) of the mean ms per launch; each group sits between
+    one pair of HIP events on the current stream (no markers between launches,
+    so short kernels are not charged for them)."""
+    for _ in range(warm * n):
         fn()
-    e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / n
+    ts = []
+    for _ in range(groups):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) / n)
+    return sorted(ts)[len(ts) // 2]
 
 
 def rel_err_heads(got, ref):
@@ -709,7 +716,8 @@ def main():
         d1 = res["decode"]["step_ms"] if "decode" in res else None
         out["spec_decode"] = {"workload": f"decode B=256 H=32 d=128 with {r['SK']} draft tokens per sequence: "
                                           f"kda_decode_verify (bf16 o), then kda_decode_commit with 0..{r['SK']} "
-                                          f"accepted ({r['n_commit']} of 256 sequences commit)",
+                                          f"accepted ({r['n_commit']} of 256 sequences commit); each time the "
+                                          f"median of 5 groups of 20 launches back to back, after 100 untimed launches",
                               "verify_us": r["ver_ms"] * 1e3, "commit_us": r["com_ms"] * 1e3,
                               "verify_gbps": r["ver_bytes"] / r["ver_ms"] / 1e6,
                               "commit_gbps": r["com_bytes"] / r["com_ms"] / 1e6,

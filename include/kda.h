@@ -309,9 +309,12 @@ kda_status kda_decode_step_gated(const void* q, const void* k, const void* v, kd
  * in place, so a rejected draft token could not be taken back afterwards (the
  * second page, "Kimi 모델 분석", serving section on speculative decoding; the
  * first page, section 13, on restoring the state after rejected draft tokens).
- * This call reads S once and applies the K tokens in registers, exactly as K
- * kda_decode_step calls would (same recurrence, fp32), and stores what the
- * commit pass needs instead of the state.
+ * This call reads S once and gives what K kda_decode_step calls would (the
+ * same recurrence, restated, in fp32): S is multiplied once by every draft's
+ * key and query, each decayed to the draft's position, and the drafts' effect
+ * on one another is resolved on those products with coefficients formed from
+ * k, q and alpha alone.  It stores what the commit pass needs instead of the
+ * state.
  *
  *   q, k   : [B][K][H][d_k] qkv_dtype     v: [B][K][H][d_v] qkv_dtype   (read)
  *   alpha  : [B][K][H][d_k] fp32          beta: [B][K][H] fp32          (read)

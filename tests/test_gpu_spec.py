@@ -94,8 +94,9 @@ def test_verify_steep_decay(gpu, dk, dv, dtype):
     """Channels whose decay over the drafts leaves fp32's comfortable range:
     alpha = 0 (the channel is wiped), alpha = 1e-30, and alpha = 2^-20 on every
     draft (the running product passes 2^-64 at the fourth), beside ordinary
-    channels; the state is carried undecayed inside the kernel, so these take
-    the path that folds the decay into the state row."""
+    channels; the kernel multiplies the state by keys and queries decayed to
+    each draft's position, whose decay products reach zero or the subnormal
+    range on these channels."""
     B, H, K = 2, 3, 8
     log(f"verify steep decay d={dk}x{dv} {dtype} K={K}")
     d, S = _drafts(gpu, B, K, H, dk, dv, dtype, seed=dk + 5)
