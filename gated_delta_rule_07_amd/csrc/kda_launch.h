@@ -157,9 +157,11 @@ hipError_t launch_prefill_pipe(const PrefillParams& p, const SnapList& snap, hip
 // ---- two-stage prefill -------------------------------------------------------------
 // Stage 1 (prep) computes, for every (sequence, head, 32-token chunk) at once,
 // the chunk-local operands of the chunkwise form; stage 2 (chain) streams them
-// through the sequential state update.  The record of one chunk: fp16 matrix-core
-// fragments of 64 lanes x 16 bytes, then gamma.  Lane l = 16 g + n of a fragment
-// holds 8 values (columns listed in slot order):
+// through the sequential state update.  The record of one chunk: KG, T, -KH^T
+// and gamma (the chain's state part), then QG, -P T and its remainder (the
+// output part); every matrix as fp16 matrix-core fragments of 64 lanes x 16
+// bytes.  Lane l = 16 g + n of a fragment holds 8 values (columns listed in slot
+// order):
 //   KG, QG [rt][kb] : token 16 rt + n, channels 32 kb + {4g..4g+3, 16+4g..16+4g+3}
 //   T, -P T [rt]    : row 16 rt + n, columns {4g..4g+3, 16+4g..16+4g+3}
 //   (-P T)_lo [rt]  : the fp16 rounding remainder of -P T, same layout
@@ -168,14 +170,16 @@ hipError_t launch_prefill_pipe(const PrefillParams& p, const SnapList& snap, hip
 template <int DK>
 struct ChunkRec {
   static constexpr int NKB = DK / 32, NKT = DK / 16;
+  // what the chain's state waves read, then what its output waves read
   static constexpr int KG = 0;
-  static constexpr int QG = KG + 2 * NKB * 1024;
-  static constexpr int TT = QG + 2 * NKB * 1024;
-  static constexpr int PP = TT + 2 * 1024;
-  static constexpr int PL = PP + 2 * 1024;
-  static constexpr int KH = PL + 2 * 1024;
+  static constexpr int TT = KG + 2 * NKB * 1024;
+  static constexpr int KH = TT + 2 * 1024;
   static constexpr int GAM = KH + NKT * 1024;
-  static constexpr int BYTES = GAM + DK * 4;
+  static constexpr int OUT = GAM + DK * 4;
+  static constexpr int QG = OUT;
+  static constexpr int PP = QG + 2 * NKB * 1024;
+  static constexpr int PL = PP + 2 * 1024;
+  static constexpr int BYTES = PL + 2 * 1024;
 };
 // Bytes of one chunk record (0: no two-stage kernels for d_k).
 inline int chunk_rec_bytes(int dk) {

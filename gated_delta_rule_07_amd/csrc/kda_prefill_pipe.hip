@@ -1028,8 +1028,10 @@ hipError_t launch_pipe(const PrefillParams& p, const SnapList& snap, hipStream_t
 
 // ---- two-stage prefill, stage 2: the chain kernel ---------------------------------------
 // The records of stage 1 (kda_prep.hip: KG, QG, T, -P T and -KH^T as
-// matrix-core fragments, and gamma) and the V slab stream into an LDS ring by
-// direct-to-LDS loads from two loader waves, which keep DEPTH chunks in flight.
+// matrix-core fragments, and gamma) and the V slab stream into LDS by
+// direct-to-LDS loads from two loader waves: each record's state part (KG, T,
+// -KH^T, gamma, with the V slab) into one ring and its output part (QG, -P T)
+// into another, every part LAT steps ahead of the step that reads it.
 // The state waves run only the serial part, the output waves the output:
 //   Xn = KG S - V,  Un = T Xn,  S' = gamma S + (-KH)^T Un,
 //   O^T = S^T QG^T + Xn^T (-P T)^T    (P U = -(P T) Xn, the product formed in stage 1)
@@ -1039,23 +1041,33 @@ struct CfgC {
   static constexpr int DK = DK_, NST = NST_, J = 16 * NST;
   static constexpr int NKT = DK / 16, NKB = DK / 32;
   using R = ChunkRec<DK>;
-  static constexpr int RECK = (R::BYTES + 1023) / 1024;  // 1 KB transfers per record
-  static constexpr int VROW = J * 2;                      // bytes of one token's row of the V slab
-  static constexpr int VK = CS * VROW / 1024;             // 1 KB transfers per V slab
-  static constexpr int NK = RECK + VK;
-  static constexpr int SLOT = NK * 1024;
-  static constexpr int NL = 2;       // loader waves
-  static constexpr int DEPTH = 3;    // chunks in flight
-  static constexpr int RING = DEPTH + 1;
+  static constexpr int RECS = (R::OUT + 1023) / 1024;             // 1 KB transfers: a record's state part
+  static constexpr int RECO = (R::BYTES - R::OUT + 1023) / 1024;  // ... and its output part
+  static constexpr int VROW = J * 2;                              // bytes of one token's row of the V slab
+  static constexpr int VK = CS * VROW / 1024;                     // 1 KB transfers per V slab
+  static constexpr int NKS = RECS + VK, NKO = RECO;               // transfers into a state / output slot
+  static constexpr int SLOTS = NKS * 1024, SLOTO = NKO * 1024;
+  static constexpr int NL = 2;        // loader waves
+  static constexpr int LAT = 3;       // steps each transfer has to land
+  static constexpr int RING = LAT + 1;  // slots of each ring: LAT in flight, one being read
   static constexpr int NW = 2 * NST + NL, NT = 64 * NW;  // state, output and loader waves
   static constexpr int HAND = (NKB + 2) * 1024;        // state -> output handoff per wave: Sf, Xn, 1/scale
-  static constexpr int nk_of(int lw) { return (NK - lw + NL - 1) / NL; }  // transfers of loader lw
+  // transfers of loader lw per state part, per output part, per step
+  static constexpr int nks_of(int lw) { return (NKS - lw + NL - 1) / NL; }
+  static constexpr int nko_of(int lw) { return (NKO - lw + NL - 1) / NL; }
+  static constexpr int nk_of(int lw) { return nks_of(lw) + nko_of(lw); }
   static_assert(VROW % 16 == 0 && (CS * VROW) % 1024 == 0, "V slab transfers");
+  static_assert((R::BYTES - R::OUT) % 1024 == 0 && R::OUT % 16 == 0, "output part: whole transfers");
+  static_assert(LAT * (nks_of(0) + nko_of(0)) <= 63, "transfers in flight fit the wait counter");
 };
+
+// Barriers each wave of a chain workgroup passes over nchunks chunks.
+__device__ __forceinline__ int chain_barriers(int nchunks) { return nchunks > 0 ? nchunks + 2 : 1; }
 
 template <class C>
 struct SmemC {
-  alignas(16) char ring[C::RING][C::SLOT];
+  alignas(16) char sring[C::RING][C::SLOTS];  // state parts (with V) of chunk c in slot c % RING
+  alignas(16) char oring[C::RING][C::SLOTO];  // output parts
   alignas(16) char hand[2][C::NST][C::HAND];  // by chunk parity
   alignas(16) float scol[C::NST][16];         // state waves: 1/scale of each of their columns
 };
@@ -1074,42 +1086,69 @@ struct ChainSrc {
   int nchunks, T;
 };
 
-// Loader wave LW's share of chunk c (every NL-th 1 KB transfer) into `slot`.  A
-// chunk past the end is a zero-length range (reads zeros), so every step has the
-// same number of transfers in flight and one wait count fits all steps.
+// Loader wave LW's share (every NL-th 1 KB transfer) of chunk c's state part
+// and V slab, or of its output part, into `slot`.  A chunk past the end is a
+// zero-length range (reads zeros), so every step has the same number of
+// transfers in flight and one wait count fits all steps.
 template <class C, int LW>
-__device__ __forceinline__ void chain_issue(char* slot, const ChainSrc& q, int c, int lane) {
+__device__ __forceinline__ void chain_issue_state(char* slot, const ChainSrc& q, int c, int lane) {
   const bool on = c < q.nchunks;
   const int rows = on ? min(CS, q.T - c * CS) : 0;
-  const __amdgpu_buffer_rsrc_t rr = make_rsrc(q.rec + (on ? (long long)c * q.rec_step : 0), on ? C::R::BYTES : 0);
+  const __amdgpu_buffer_rsrc_t rr = make_rsrc(q.rec + (on ? (long long)c * q.rec_step : 0), on ? C::R::OUT : 0);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(q.v + (on ? (long long)c * CS * q.vrow : 0), rows * q.vrow);
 #pragma unroll
-  for (int i = LW; i < C::NK; i += C::NL) {
-    if (i < C::RECK) {
+  for (int i = LW; i < C::NKS; i += C::NL) {
+    if (i < C::RECS) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_void*)(slot + 1024 * i), 16, 16 * lane, 1024 * i, 0, 0);
     } else {
       // V rows of VROW bytes, LPR lanes each: LDS holds the slab row-major
       constexpr int LPR = C::VROW / 16;
-      const int row = (i - C::RECK) * (64 / LPR) + lane / LPR;
+      const int row = (i - C::RECS) * (64 / LPR) + lane / LPR;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(slot + 1024 * i), 16, row * q.vrow + 16 * (lane % LPR),
                                                0, 0, 0);
     }
   }
 }
+template <class C, int LW>
+__device__ __forceinline__ void chain_issue_out(char* slot, const ChainSrc& q, int c, int lane) {
+  const bool on = c < q.nchunks;
+  const __amdgpu_buffer_rsrc_t rr =
+      make_rsrc(q.rec + C::R::OUT + (on ? (long long)c * q.rec_step : 0), on ? C::R::BYTES - C::R::OUT : 0);
+#pragma unroll
+  for (int i = LW; i < C::NKO; i += C::NL)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_void*)(slot + 1024 * i), 16, 16 * lane, 1024 * i, 0, 0);
+}
 
-// At barrier n chunks n and n + 1 are in their slots (the state waves read
-// chunk n + 1 during step n), and chunk n - 1's slot is refilled with chunk
-// n + DEPTH - 1: each chunk has DEPTH - 1 steps to land.
+// The state waves read chunk c's state part during step c - 1 (chunk 0's
+// before barrier 0, after an opening barrier) and the output waves its output
+// part during step c.  At barrier n the loaders refill the slots of chunk n's
+// state part and chunk n - 1's output part with the state part of chunk
+// n + LAT + 1 and the output part of chunk n + LAT, both needed LAT barriers
+// later; every wait leaves the newest LAT - 1 steps' transfers in flight.
 template <class C, int LW>
 __device__ void chain_loader(SmemC<C>& sm, const ChainSrc& q, int lane) {
-  static_assert(C::DEPTH >= 2 && C::RING == C::DEPTH + 1, "ring of DEPTH chunks in flight plus the one in use");
-  constexpr int WAIT = vmcnt_imm((C::DEPTH - 2) * C::nk_of(LW));  // all but the newest DEPTH - 2 chunks have landed
+  static_assert(C::LAT >= 2 && C::RING == C::LAT + 1, "LAT slots in flight plus the one being read");
+  constexpr int L = C::LAT;
+  constexpr int WAIT = vmcnt_imm((L - 1) * C::nk_of(LW));
+  if (q.nchunks <= 0) {
+    block_sync_lds();  // the closing barrier of every wave
+    return;
+  }
+  // in the order the parts are needed: state 0, then output 0 and state 1
+  // (barrier 0), then output c and state c + 1 (barrier c)
+  chain_issue_state<C, LW>(sm.sring[0], q, 0, lane);
 #pragma unroll
-  for (int c = 0; c < C::DEPTH; ++c) chain_issue<C, LW>(sm.ring[c], q, c, lane);
+  for (int c = 0; c < L; ++c) {
+    chain_issue_out<C, LW>(sm.oring[c], q, c, lane);
+    chain_issue_state<C, LW>(sm.sring[c + 1], q, c + 1, lane);
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(L * C::nk_of(LW)));  // state 0
+  block_sync_lds();                                           // the opening barrier
   __builtin_amdgcn_s_waitcnt(WAIT);
   for (int n = 0; n < q.nchunks; ++n) {
-    block_sync_lds();  // chunks n and n + 1 are in their slots; the slot of chunk n - 1 is free
-    chain_issue<C, LW>(sm.ring[(n + C::DEPTH) % C::RING], q, n + C::DEPTH, lane);
+    block_sync_lds();  // barrier n
+    chain_issue_out<C, LW>(sm.oring[(n + L) % C::RING], q, n + L, lane);
+    chain_issue_state<C, LW>(sm.sring[(n + L + 1) % C::RING], q, n + L + 1, lane);
     __builtin_amdgcn_s_waitcnt(WAIT);
   }
   block_sync_lds();  // the closing barrier of every wave
@@ -1159,13 +1198,13 @@ struct ChainFrags {
 template <class C>
 __device__ __forceinline__ void chain_fetch(const SmemC<C>& sm, int c, int w, int lane, ChainFrags<C>& F) {
   using RC = typename C::R;
-  const char* sb = sm.ring[c % C::RING];
+  const char* sb = sm.sring[c % C::RING];
   const char* lb = sb + 16 * opaque(lane);
   const int gg = opaque(lane / 16), nn = opaque(lane % 16);
   // V first: the column-scale check that follows waits only for it
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
-    F.va[rt] = *reinterpret_cast<const s16x4*>(sb + C::RECK * 1024 + (16 * rt + nn) * C::VROW + (16 * w + 4 * gg) * 2);
+    F.va[rt] = *reinterpret_cast<const s16x4*>(sb + C::RECS * 1024 + (16 * rt + nn) * C::VROW + (16 * w + 4 * gg) * 2);
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
@@ -1256,12 +1295,12 @@ __device__ void chain_state(SmemC<C>& sm, const Ctx4& cx, const SnapList& snap, 
   };
   ChainFrags<C> F;
   if (cx.nchunks > 0) {
-    block_sync_lds();  // chunks 0 and 1 are in their slots
+    block_sync_lds();  // the opening barrier: chunk 0's state part is in its slot
     chain_fetch<C>(sm, 0, w, lane, F);
     start_chunk(F);
   }
   for (int n = 0; n < cx.nchunks; ++n) {
-    if (n > 0) block_sync_lds();  // chunk n + 1 is in its slot; the handoff of chunk n - 2 is free
+    block_sync_lds();  // chunk n + 1's state part is in its slot; the handoff of chunk n - 2 is free
     const Item it = {n, n, 0, chunk_end(n, cx.T), CS};
     char* hb = sm.hand[n & 1][w] + 16 * lane;
     f32x4 X[2] = {F.x0[0], F.x0[1]};
@@ -1325,16 +1364,17 @@ __device__ void chain_output(SmemC<C>& sm, const Ctx4& cx, int w, int lane) {
     const Item it = {c, c, 0, chunk_end(c, cx.T), CS};
     store_out(cx, it, O, usc, w, lane);
   };
+  if (cx.nchunks > 0) block_sync_lds();  // the opening barrier
   for (int n = 0; n < cx.nchunks; ++n) {
-    block_sync_lds();
+    block_sync_lds();  // chunk n's output part is in its slot
     if (n > 0) emit(n - 1);
-    const char* lb = sm.ring[n % C::RING] + 16 * opaque(lane);
+    const char* lb = sm.oring[n % C::RING] + 16 * opaque(lane);
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb) Q[rt][kb] = slot_frag<C>(lb, RC::QG, rt * C::NKB + kb);
-      Pf[rt] = slot_frag<C>(lb, RC::PP, rt);
-      Pl[rt] = slot_frag<C>(lb, RC::PL, rt);
+      for (int kb = 0; kb < C::NKB; ++kb) Q[rt][kb] = slot_frag<C>(lb, RC::QG - RC::OUT, rt * C::NKB + kb);
+      Pf[rt] = slot_frag<C>(lb, RC::PP - RC::OUT, rt);
+      Pl[rt] = slot_frag<C>(lb, RC::PL - RC::OUT, rt);
     }
   }
   block_sync_lds();
@@ -1379,11 +1419,11 @@ __device__ __forceinline__ void chain_block(SmemC<C>& sm, int* seq_lens, int* se
   // waves 0 .. NST-1: state (SIMDs 0 and 1), NST .. 2 NST-1: output (SIMDs 2
   // and 3), then the two loaders, which share the state waves' SIMDs and give
   // way to them
-  if (wave < C::NST) {
+  if (wave >= C::NST && wave < 2 * C::NST) {
     __builtin_amdgcn_s_setprio(3);
-    chain_state<C>(sm, cx, snap, pos0, wave, lane);
-  } else if (wave < 2 * C::NST) {
-    chain_output<C>(sm, cx, wave - C::NST, lane);
+    chain_state<C>(sm, cx, snap, pos0, wave - C::NST, lane);
+  } else if (wave < C::NST) {
+    chain_output<C>(sm, cx, wave, lane);
   } else if (wave < C::NW) {
     ChainSrc q;
     q.rec = p.rec + (slot0 * p.H + cx.h) * C::R::BYTES;
@@ -1395,7 +1435,7 @@ __device__ __forceinline__ void chain_block(SmemC<C>& sm, int* seq_lens, int* se
     if (wave == 2 * C::NST) chain_loader<C, 0>(sm, q, lane);
     else chain_loader<C, 1>(sm, q, lane);
   } else {
-    for (int n = 0; n <= cx.nchunks; ++n) block_sync_lds();  // every role's nchunks + 1 barriers
+    for (int n = chain_barriers(cx.nchunks); n > 0; --n) block_sync_lds();  // as many barriers as every role
   }
 }
 

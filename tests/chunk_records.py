@@ -10,7 +10,8 @@ putting the recurrence on the GPU), for one 32-token chunk with decays a [32, d_
   L_ij = beta_i sum_c k_ic k_jc r_c(i,j) (j < i), P_ij = sum_c q_ic k_jc r_c(i,j) (j <= i),
   r(i,j) = prod_{j<s<=i} a_s, T = (I + L)^{-1} diag(beta); the record holds the
   output's intra-chunk operator P T in place of P.
-Record: fp16 fragments of 64 lanes x 8 values (lane 16 g + n, slot e), then gamma:
+Record: fp16 fragments of 64 lanes x 8 values (lane 16 g + n, slot e) and gamma
+(fp32), in the order KG, T, -KH^T, gamma, QG, -P T, its remainder:
   KG, QG [rt][kb]: token 16 rt + n, channel 32 kb + st(g, e); T, -P T [rt] (then
   its fp16 remainder, same layout): row
   16 rt + n, column st(g, e); -KH^T [i]: channel 16 i + n, token st(g, e);
@@ -22,15 +23,17 @@ CS = 32
 
 
 def offsets(dk):
+    """Byte offsets: the state part (KG, T, -KH^T, gamma), then the output part
+    (QG, -P T, its remainder)."""
     nkb, nkt = dk // 32, dk // 16
     o = {"KG": 0}
-    o["QG"] = o["KG"] + 2 * nkb * 1024
-    o["TT"] = o["QG"] + 2 * nkb * 1024
-    o["PP"] = o["TT"] + 2 * 1024
-    o["PL"] = o["PP"] + 2 * 1024
-    o["KH"] = o["PL"] + 2 * 1024
+    o["TT"] = o["KG"] + 2 * nkb * 1024
+    o["KH"] = o["TT"] + 2 * 1024
     o["GAM"] = o["KH"] + nkt * 1024
-    o["BYTES"] = o["GAM"] + dk * 4
+    o["OUT"] = o["QG"] = o["GAM"] + dk * 4
+    o["PP"] = o["QG"] + 2 * nkb * 1024
+    o["PL"] = o["PP"] + 2 * 1024
+    o["BYTES"] = o["PL"] + 2 * 1024
     return o
 
 
@@ -70,7 +73,7 @@ def pack(dk, KG, QG, KH, T, P, gam):
     record stores -P T)."""
     o = offsets(dk)
     rec = np.zeros(o["BYTES"], np.uint8)
-    h = rec[: o["GAM"]].view(np.float16)
+    h = rec.view(np.float16)
 
     def put(base, f, m):  # m: [64, 8] values of fragment f
         s = (base + f * 1024) // 2
@@ -86,14 +89,14 @@ def pack(dk, KG, QG, KH, T, P, gam):
         put(o["PL"], rt, npt - npt.astype(np.float16).astype(np.float64))
     for i in range(dk // 16):
         put(o["KH"], i, -KH[_COL, 16 * i + _ROW])
-    rec[o["GAM"]:].view(np.float32)[:] = gam
+    rec[o["GAM"]:o["OUT"]].view(np.float32)[:] = gam
     return rec
 
 
 def unpack(dk, rec):
     """Inverse of pack: (KG, QG, KH, T, P T, gamma) as float64 from record bytes."""
     o = offsets(dk)
-    h = rec[: o["GAM"]].view(np.float16).astype(np.float64)
+    h = rec.view(np.float16).astype(np.float64)
 
     def get(base, f):
         s = (base + f * 1024) // 2
@@ -109,7 +112,7 @@ def unpack(dk, rec):
         P[16 * rt + _ROW, _COL] = -(get(o["PP"], rt) + get(o["PL"], rt))
     for i in range(dk // 16):
         KH[_COL, 16 * i + _ROW] = -get(o["KH"], i)
-    return KG, QG, KH, T, P, rec[o["GAM"]:].view(np.float32).astype(np.float64)
+    return KG, QG, KH, T, P, rec[o["GAM"]:o["OUT"]].view(np.float32).astype(np.float64)
 
 
 def records(q, k, alpha, beta):
