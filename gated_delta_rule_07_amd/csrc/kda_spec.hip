@@ -55,13 +55,15 @@ struct SCfg {
 template <int DK, int DV>
 struct VCfg {
   static constexpr int CGW = DV >= 32 ? 8 : DV / 4;  // float4 column groups per wave
-  static constexpr int RGW = 64 / CGW;               // row groups per wave = vectors per pass
+  static constexpr int RGW = 64 / CGW;               // row groups per wave
+  static constexpr int VPP = 4;                      // vectors per pass over the state
   static constexpr int NW = DV / (4 * CGW);
   static constexpr int NT = 64 * NW;
   static constexpr int RPT = DK / RGW;                 // state rows per lane
   static constexpr int CPI = DK < 16 ? DK : 16;        // key channels per coefficient work item
   static constexpr int NCB = DK / CPI;
   static_assert(RPT >= 1 && DK % RGW == 0 && DV % (4 * CGW) == 0, "verify block shape");
+  static_assert(RGW >= 2 * VPP && RGW * CGW == 64, "a pass's vectors reduce over the row-group lanes");
 };
 
 // The verify kernel's LDS (floats, every region a multiple of 4), for K drafts.
@@ -71,8 +73,8 @@ struct VLay {
   int nvp, np;                   // vectors padded to whole passes; token pairs s <= t
   int k, q, a, xs, v, b, pv, cp, dp, cc, dd, total;
   __host__ __device__ static int r4(int n) { return (n + 3) & ~3; }
-  __host__ __device__ VLay(int K, int dk, int dv, int rgw, int ncb) {
-    nvp = (2 * K + rgw - 1) / rgw * rgw;
+  __host__ __device__ VLay(int K, int dk, int dv, int vpp, int ncb) {
+    nvp = (2 * K + vpp - 1) / vpp * vpp;
     np = K * (K + 1) / 2;
     k = 0;
     q = k + r4(K * dk);
@@ -111,68 +113,92 @@ __device__ __forceinline__ void reduce_scatter(f32x4* acc, int lane) {
 
 __device__ __forceinline__ void block_sync_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <typename IO, int DK, int DV>
+// NS states per workgroup, (b, h) = NS blockIdx.x + st: a workgroup that
+// streams two 64 KB states reads HBM faster than two workgroups that stream one
+// each.  MAXK bounds the drafts (the registers the drafts' inputs take while
+// the states are in flight).
+template <typename IO, int DK, int DV, int MAXK, int NS>
 __global__ __launch_bounds__((VCfg<DK, DV>::NT)) void kda_verify_kernel(VerifyParams p) {
   using C = VCfg<DK, DV>;
   extern __shared__ f32x4 verify_lds[];
-  float* sm = reinterpret_cast<float*>(verify_lds);
   const int K = p.K;
-  const VLay L(K, DK, DV, C::RGW, C::NCB);
+  const VLay L(K, DK, DV, C::VPP, C::NCB);
   const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
-  const int bh = blockIdx.x, b = bh / p.H, h = bh % p.H;
-  const size_t row0 = (size_t)b * K * p.H + h;  // row (b, t, h) of the [B][K][H][d] inputs is row0 + t H
+  const int nbh = p.B * p.H, bh0 = blockIdx.x * NS;
+  // a state past the last (an odd count): its loads repeat the last state's, its results are not stored
+  float* smb[NS];
+  size_t row0[NS];  // row (b, t, h) of the [B][K][H][d] inputs is row0 + t H
+  int bhs[NS];
+#pragma unroll
+  for (int st = 0; st < NS; ++st) {
+    smb[st] = reinterpret_cast<float*>(verify_lds) + st * L.total;
+    bhs[st] = min(bh0 + st, nbh - 1);
+    row0[st] = (size_t)(bhs[st] / p.H) * K * p.H + bhs[st] % p.H;
+  }
 
-  // the drafts' keys, queries, decays, values and betas, then the state: all
+  // the drafts' keys, queries, decays, values and betas, then the states: all
   // loads in flight at once (small indices clamped into range, so no branch
   // splits them); storing the small ones to LDS waits only for them
-  constexpr int EK = (kMaxDraft * DK + C::NT - 1) / C::NT, EV = (kMaxDraft * DV + C::NT - 1) / C::NT;
+  constexpr int EK = (MAXK * DK + C::NT - 1) / C::NT, EV = (MAXK * DV + C::NT - 1) / C::NT;
   const int nk = K * DK, nv = K * DV;
-  IO rk[EK], rq[EK], rv[EV];
-  float ra[EK];
+  IO rk[NS][EK], rq[NS][EK], rv[NS][EV];
+  float ra[NS][EK], rb[NS];
 #pragma unroll
-  for (int j = 0; j < EK; ++j) {
-    const int e = min(tid + j * C::NT, nk - 1);
-    const size_t at = (row0 + (size_t)(e / DK) * p.H) * DK + e % DK;
-    rk[j] = static_cast<const IO*>(p.k)[at];
-    rq[j] = static_cast<const IO*>(p.q)[at];
-    ra[j] = p.alpha[at];
-  }
+  for (int st = 0; st < NS; ++st) {
 #pragma unroll
-  for (int j = 0; j < EV; ++j) {
-    const int e = min(tid + j * C::NT, nv - 1);
-    rv[j] = static_cast<const IO*>(p.v)[(row0 + (size_t)(e / DV) * p.H) * DV + e % DV];
+    for (int j = 0; j < EK; ++j) {
+      const int e = min(tid + j * C::NT, nk - 1);
+      const size_t at = (row0[st] + (size_t)(e / DK) * p.H) * DK + e % DK;
+      rk[st][j] = static_cast<const IO*>(p.k)[at];
+      rq[st][j] = static_cast<const IO*>(p.q)[at];
+      ra[st][j] = p.alpha[at];
+    }
+#pragma unroll
+    for (int j = 0; j < EV; ++j) {
+      const int e = min(tid + j * C::NT, nv - 1);
+      rv[st][j] = static_cast<const IO*>(p.v)[(row0[st] + (size_t)(e / DV) * p.H) * DV + e % DV];
+    }
+    rb[st] = p.beta[row0[st] + (size_t)min(tid, K - 1) * p.H];
   }
-  const float rb = p.beta[row0 + (size_t)min(tid, K - 1) * p.H];
   __builtin_amdgcn_sched_barrier(0);  // (the loads are counted in order: keep the small ones first)
 
   const int cg = lane % C::CGW, rg = lane / C::CGW;
   const int col = 4 * (C::CGW * wave + cg);
-  f32x4 s[C::RPT];
-  const float* S = p.S + (size_t)bh * DK * DV + col;
+  f32x4 s[NS][C::RPT];
 #pragma unroll
-  for (int r = 0; r < C::RPT; ++r)
-    s[r] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + (size_t)(rg + C::RGW * r) * DV));
+  for (int st = 0; st < NS; ++st) {
+    const float* S = p.S + (size_t)bhs[st] * DK * DV + col;
+#pragma unroll
+    for (int r = 0; r < C::RPT; ++r)
+      s[st][r] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + (size_t)(rg + C::RGW * r) * DV));
+  }
   __builtin_amdgcn_sched_barrier(0);
 
   // (unconditional stores: a clamped index stores the value already there, and
-  // no load is moved after the state's)
+  // no load is moved after the states')
 #pragma unroll
-  for (int j = 0; j < EK; ++j) {
-    const int e = min(tid + j * C::NT, nk - 1);
-    sm[L.k + e] = to_f32(rk[j]);
-    sm[L.q + e] = to_f32(rq[j]);
-    sm[L.a + e] = ra[j];
+  for (int st = 0; st < NS; ++st) {
+    float* sm = smb[st];
+#pragma unroll
+    for (int j = 0; j < EK; ++j) {
+      const int e = min(tid + j * C::NT, nk - 1);
+      sm[L.k + e] = to_f32(rk[st][j]);
+      sm[L.q + e] = to_f32(rq[st][j]);
+      sm[L.a + e] = ra[st][j];
+    }
+#pragma unroll
+    for (int j = 0; j < EV; ++j) sm[L.v + min(tid + j * C::NT, nv - 1)] = to_f32(rv[st][j]);
+    sm[L.b + min(tid, K - 1)] = rb[st];
   }
-#pragma unroll
-  for (int j = 0; j < EV; ++j) sm[L.v + min(tid + j * C::NT, nv - 1)] = to_f32(rv[j]);
-  sm[L.b + min(tid, K - 1)] = rb;
   block_sync_lds();
 
-  // while the state is in flight: the 2K vectors P_t k_t and P_t q_t, one key
-  // channel per thread ...
-  for (int i = tid; i < DK; i += C::NT) {
+  // while the states are in flight: the 2K vectors P_t k_t and P_t q_t, one key
+  // channel of one state per work item ...
+  for (int e = tid; e < NS * DK; e += C::NT) {
+    const float* sm = smb[0] + (e / DK) * L.total;
+    const int i = e % DK;
     float P = 1.0f;
-    float* pv = sm + L.pv + i * L.nvp;
+    float* pv = const_cast<float*>(sm) + L.pv + i * L.nvp;
     for (int t = 0; t < K; ++t) {
       P *= sm[L.a + t * DK + i];
       pv[t] = P * sm[L.k + t * DK + i];
@@ -181,7 +207,10 @@ __global__ __launch_bounds__((VCfg<DK, DV>::NT)) void kda_verify_kernel(VerifyPa
     for (int j = 2 * K; j < L.nvp; ++j) pv[j] = 0.0f;
   }
   // ... and c_ts, d_ts for every pair s <= t, in partial sums over CPI channels
-  for (int e = tid; e < L.np * C::NCB; e += C::NT) {
+  const int npc = L.np * C::NCB;
+  for (int e2 = tid; e2 < NS * npc; e2 += C::NT) {
+    float* sm = smb[0] + (e2 / npc) * L.total;
+    const int e = e2 % npc;
     const int pr = e / C::NCB, cb = e % C::NCB;
     int t = 0;
     while ((t + 1) * (t + 2) / 2 <= pr) ++t;
@@ -199,7 +228,9 @@ __global__ __launch_bounds__((VCfg<DK, DV>::NT)) void kda_verify_kernel(VerifyPa
     sm[L.dp + e] = ds;
   }
   block_sync_lds();
-  for (int pr = tid; pr < L.np; pr += C::NT) {
+  for (int e = tid; e < NS * L.np; e += C::NT) {
+    float* sm = smb[0] + (e / L.np) * L.total;
+    const int pr = e % L.np;
     float cs = 0.0f, ds = 0.0f;
     for (int cb = 0; cb < C::NCB; ++cb) {
       cs += sm[L.cp + pr * C::NCB + cb];
@@ -209,34 +240,46 @@ __global__ __launch_bounds__((VCfg<DK, DV>::NT)) void kda_verify_kernel(VerifyPa
     sm[L.dd + pr] = ds;
   }
 
-  // one pass over the state per RGW vectors: the lane's rows, then a
-  // reduce-scatter over the row-group lanes, after which lane rg holds the sum
-  // for vector g0 + rg
-  for (int g0 = 0; g0 < L.nvp; g0 += C::RGW) {
-    f32x4 acc[C::RGW];
+  // one pass over a state per VPP = 4 vectors: the lane's rows, then a
+  // reduce-scatter over lane bits 5 and 4 and a sum over the row-group bits
+  // below them, after which the lanes with those bits clear hold the sum for
+  // vector g0 + lane / 16 (the first state's passes wait only for its loads)
+  static_assert(C::VPP == 4, "the reduce-scatter below takes four vectors");
+  const int vec = lane / 16;
+  const bool writer = (rg & (C::RGW / C::VPP - 1)) == 0;
 #pragma unroll
-    for (int j = 0; j < C::RGW; ++j) acc[j] = (f32x4)0.0f;
+  for (int st = 0; st < NS; ++st) {
+    float* sm = smb[st];
+    for (int g0 = 0; g0 < L.nvp; g0 += C::VPP) {
+      f32x4 acc[C::VPP];
 #pragma unroll
-    for (int r = 0; r < C::RPT; ++r) {
-      const float* pr = sm + L.pv + (rg + C::RGW * r) * L.nvp + g0;
+      for (int j = 0; j < C::VPP; ++j) acc[j] = (f32x4)0.0f;
 #pragma unroll
-      for (int j = 0; j < C::RGW; j += 4) {
-        const f32x4 w = *reinterpret_cast<const f32x4*>(pr + j);
+      for (int r = 0; r < C::RPT; ++r) {
+        const f32x4 w = *reinterpret_cast<const f32x4*>(sm + L.pv + (rg + C::RGW * r) * L.nvp + g0);
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) acc[j + jj] += w[jj] * s[r];
+        for (int jj = 0; jj < 4; ++jj) acc[jj] += w[jj] * s[st][r];
       }
+      reduce_scatter<C::VPP / 2, 32>(acc, lane);
+#pragma unroll
+      for (int m = 8; m >= C::CGW; m /= 2)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[0][c] += __shfl_xor(acc[0][c], m);
+      if (writer) *reinterpret_cast<f32x4*>(sm + L.xs + (g0 + vec) * DV + col) = acc[0];
     }
-    reduce_scatter<C::RGW / 2, 32>(acc, lane);
-    *reinterpret_cast<f32x4*>(sm + L.xs + (g0 + rg) * DV + col) = acc[0];
   }
   block_sync_lds();
 
-  // the substitution over the draft, one value column per thread
-  if (tid < DV) {
-    const int c = tid;
-    float u[kMaxDraft];
+  // the substitution over the draft, one value column of one state per work item
+  for (int e = tid; e < NS * DV; e += C::NT) {
+    const int st = e / DV, c = e % DV;
+    if (bh0 + st >= nbh) continue;
+    const float* sm = smb[0] + st * L.total;
+    const int bh = bh0 + st;
+    const size_t r0 = (size_t)(bh / p.H) * K * p.H + bh % p.H;
+    float u[MAXK];
 #pragma unroll
-    for (int t = 0; t < kMaxDraft; ++t) {
+    for (int t = 0; t < MAXK; ++t) {
       if (t >= K) continue;
       const int pt = t * (t + 1) / 2;
       float x = sm[L.xs + t * DV + c];
@@ -248,7 +291,7 @@ __global__ __launch_bounds__((VCfg<DK, DV>::NT)) void kda_verify_kernel(VerifyPa
       }
       u[t] = sm[L.b + t] * (sm[L.v + t * DV + c] - x);
       y += sm[L.dd + pt + t] * u[t];
-      const size_t orow = row0 + (size_t)t * p.H;
+      const size_t orow = r0 + (size_t)t * p.H;
       if (p.o_f32) static_cast<float*>(p.o)[orow * DV + c] = y;
       else static_cast<__bf16*>(p.o)[orow * DV + c] = (__bf16)y;
       p.u[((size_t)bh * K + t) * DV + c] = u[t];
@@ -295,11 +338,18 @@ __global__ __launch_bounds__(256) void kda_commit_kernel(CommitParams p) {
     __builtin_nontemporal_store(s[r], reinterpret_cast<f32x4*>(S + (size_t)(rg + C::RG * r) * DV + 4 * cg));
 }
 
+// Up to kVerifyPairK drafts: two states per workgroup; more: one.
+constexpr int kVerifyPairK = 4;
 template <typename IO, int DK, int DV>
 hipError_t verify_one(const VerifyParams& p, hipStream_t s) {
   using C = VCfg<DK, DV>;
-  const size_t lds = (size_t)VLay(p.K, DK, DV, C::RGW, C::NCB).total * sizeof(float);
-  hipLaunchKernelGGL((kda_verify_kernel<IO, DK, DV>), dim3((unsigned)(p.B * p.H)), dim3(C::NT), lds, s, p);
+  const size_t lds = (size_t)VLay(p.K, DK, DV, C::VPP, C::NCB).total * sizeof(float);
+  const long long nbh = (long long)p.B * p.H;
+  if (p.K <= kVerifyPairK)
+    hipLaunchKernelGGL((kda_verify_kernel<IO, DK, DV, kVerifyPairK, 2>), dim3((unsigned)((nbh + 1) / 2)), dim3(C::NT),
+                       2 * lds, s, p);
+  else
+    hipLaunchKernelGGL((kda_verify_kernel<IO, DK, DV, kMaxDraft, 1>), dim3((unsigned)nbh), dim3(C::NT), lds, s, p);
   return hipGetLastError();
 }
 template <typename IO, int DK, int DV>

@@ -89,20 +89,31 @@ def test_verify_matches_oracle_and_leaves_state(gpu, dk, dv, dtype, K):
     _check_verify(d, S, B, H, K, dk, dv, dtype)
 
 
+@pytest.mark.parametrize("dk,dv,dtype", [(128, 128, torch.bfloat16), (16, 128, torch.float32), (64, 32, torch.bfloat16)])
+@pytest.mark.parametrize("B,H,K", [(1, 5, 3), (3, 1, 2)])
+def test_verify_odd_state_count(gpu, dk, dv, dtype, B, H, K):
+    """Up to four drafts a workgroup takes two states: an odd count of
+    (sequence, head) states leaves the last workgroup one."""
+    log(f"verify odd count B={B} H={H} d={dk}x{dv} {dtype} K={K}")
+    d, S = _drafts(gpu, B, K, H, dk, dv, dtype, seed=dk + dv + 7 * K + B)
+    _check_verify(d, S, B, H, K, dk, dv, dtype)
+
+
 @pytest.mark.parametrize("dk,dv,dtype", [(128, 128, torch.bfloat16), (32, 32, torch.float32)])
-def test_verify_steep_decay(gpu, dk, dv, dtype):
+@pytest.mark.parametrize("K", [4, 8])
+def test_verify_steep_decay(gpu, dk, dv, dtype, K):
     """Channels whose decay over the drafts leaves fp32's comfortable range:
     alpha = 0 (the channel is wiped), alpha = 1e-30, and alpha = 2^-20 on every
     draft (the running product passes 2^-64 at the fourth), beside ordinary
     channels; the kernel multiplies the state by keys and queries decayed to
     each draft's position, whose decay products reach zero or the subnormal
     range on these channels."""
-    B, H, K = 2, 3, 8
+    B, H = 2, 3
     log(f"verify steep decay d={dk}x{dv} {dtype} K={K}")
     d, S = _drafts(gpu, B, K, H, dk, dv, dtype, seed=dk + 5)
     a = d["alpha"].clone()
     a[:, 2, :, 0::7] = 0.0
-    a[:, 5, :, 1::5] = 1e-30
+    a[:, min(5, K - 1), :, 1::5] = 1e-30
     a[:, :, :, 3::4] = 2.0 ** -20
     a[1, :, 2, :] = 2.0 ** -20  # every channel of one head
     d["alpha"] = a.contiguous()
