@@ -1032,7 +1032,7 @@ hipError_t launch_pipe(const PrefillParams& p, const SnapList& snap, hipStream_t
 // direct-to-LDS loads from two loader waves: each record's state part (KG, T,
 // -KH^T, gamma, with the V slab) into one ring and its output part (QG, -P T)
 // into another, every part LAT steps ahead of the step that reads it.
-// The state waves run only the serial part, the output wave the output of all of them:
+// The state waves run only the serial part, the output waves the output:
 //   Xn = KG S - V,  Un = T Xn,  S' = gamma S + (-KH)^T Un,
 //   O^T = S^T QG^T + Xn^T (-P T)^T    (P U = -(P T) Xn, the product formed in stage 1)
 // One barrier per chunk.  Every chunk is one item: stage 1 needs no regrouping.
@@ -1050,10 +1050,8 @@ struct CfgC {
   static constexpr int NL = 2;        // loader waves
   static constexpr int LAT = 3;       // steps each transfer has to land
   static constexpr int RING = LAT + 1;  // slots of each ring: LAT in flight, one being read
-  static constexpr int NW = NST + 1 + NL, NT = 64 * NW;  // state waves, one output wave, loaders
+  static constexpr int NW = 2 * NST + NL, NT = 64 * NW;  // state, output and loader waves
   static constexpr int HAND = (NKB + 2) * 1024;        // state -> output handoff per wave: Sf, Xn, 1/scale
-  static constexpr int OST = 2 * J + 16;               // output staging row: J bf16 columns and a 16-byte pad
-  static_assert(CS * (4 * J + 16) <= NST * HAND, "an fp32 output tile is staged in the handoff buffers of a parity");
   // transfers of loader lw per state part, per output part, per step
   static constexpr int nks_of(int lw) { return (NKS - lw + NL - 1) / NL; }
   static constexpr int nko_of(int lw) { return (NKO - lw + NL - 1) / NL; }
@@ -1122,7 +1120,7 @@ __device__ __forceinline__ void chain_issue_out(char* slot, const ChainSrc& q, i
 }
 
 // The state waves read chunk c's state part during step c - 1 (chunk 0's
-// before barrier 0, after an opening barrier) and the output wave its output
+// before barrier 0, after an opening barrier) and the output waves its output
 // part during step c.  At barrier n the loaders refill the slots of chunk n's
 // state part and chunk n - 1's output part with the state part of chunk
 // n + LAT + 1 and the output part of chunk n + LAT, both needed LAT barriers
@@ -1339,79 +1337,32 @@ __device__ void chain_state(SmemC<C>& sm, const Ctx4& cx, const SnapList& snap, 
   if (cx.st) store_state<C>(cx.st, R, cx.st_ld, w, lane);
 }
 
-// The output wave: chunk n - 1's output during step n, for all state columns,
-// from the handoffs of the state waves and chunk n - 1's QG and -P T
-// fragments, read into registers during step n - 1 (its slot is refilled in
-// step n) and shared by the columns of every state wave:
+// Output wave w: chunk n - 1's output during step n, from the handoff of state
+// wave w and chunk n - 1's QG and -P T fragments, read into registers during
+// step n - 1 (its slot is refilled in step n):
 //   O^T = S^T QG^T + Xn^T (-P T)^T.
-// The tile goes out through LDS (the chunk's handoff buffers, free once read)
-// so that each token's row of the slab is written whole: 64 bytes (bf16)
-// or 128 bytes (fp32) per token instead of one piece per state wave.
 template <class C>
-__device__ void chain_output(SmemC<C>& sm, const Ctx4& cx, int lane) {
+__device__ void chain_output(SmemC<C>& sm, const Ctx4& cx, int w, int lane) {
   using RC = typename C::R;
-  const PrefillParams& p = cx.p;
   f16x8 Q[2][C::NKB], Pf[2], Pl[2];
-  const int g = opaque(lane / 16), n = opaque(lane % 16);
   auto emit = [&](int c) {  // the output of chunk c
-    f32x4 O[C::NST][2];
+    const char* hb = sm.hand[c & 1][w] + 16 * lane;
+    f16x8 Sf[C::NKB];
 #pragma unroll
-    for (int w = 0; w < C::NST; ++w) {
-      const char* hb = sm.hand[c & 1][w] + 16 * lane;
-      f16x8 Sf[C::NKB];
+    for (int kb = 0; kb < C::NKB; ++kb) Sf[kb] = *reinterpret_cast<const f16x8*>(hb + kb * 1024);
+    const f16x8 xf = *reinterpret_cast<const f16x8*>(hb + C::NKB * 1024);
+    const f32x4 usc = *reinterpret_cast<const f32x4*>(hb + (C::NKB + 1) * 1024);
+    f32x4 O[2] = {(f32x4)0.0f, (f32x4)0.0f};
 #pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb) Sf[kb] = *reinterpret_cast<const f16x8*>(hb + kb * 1024);
-      const f16x8 xf = *reinterpret_cast<const f16x8*>(hb + C::NKB * 1024);
-      const f32x4 usc = *reinterpret_cast<const f32x4*>(hb + (C::NKB + 1) * 1024);
-      O[w][0] = O[w][1] = (f32x4)0.0f;
+    for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb)
+      for (int rt = 0; rt < 2; ++rt) O[rt] = mma16(Sf[kb], Q[rt][kb], O[rt]);
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) O[w][rt] = mma16(Sf[kb], Q[rt][kb], O[w][rt]);
+    for (int rt = 0; rt < 2; ++rt) O[rt] = mma16(xf, Pl[rt], O[rt]);
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) O[w][rt] = mma16(xf, Pl[rt], O[w][rt]);
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) O[w][rt] = mma16(xf, Pf[rt], O[w][rt]) * usc;
-    }
-    // lane (g, n) holds token 16 rt + n, columns 16 w + 4g .. + 3
-    char* const st = sm.hand[c & 1][0];
-    const int rows = chunk_end(c, cx.T);
-    const int esz = p.o_f32 ? 4 : 2;
-    const int rs = p.H * p.dv * esz;
-    char* ob = static_cast<char*>(p.o) + (((size_t)(cx.tok0 + c * CS) * p.H + cx.h) * p.dv + cx.col0) * esz;
-    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(ob, rows * rs);
-    if (p.o_f32) {
-      constexpr int RS = 4 * C::J + 16;  // fp32 row: 32 columns and a 16-byte pad
-#pragma unroll
-      for (int w = 0; w < C::NST; ++w)
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) *reinterpret_cast<f32x4*>(st + (16 * rt + n) * RS + (16 * w + 4 * g) * 4) = O[w][rt];
-      wave_lds_sync();
-      constexpr int LPT = C::J / 4;  // lanes per token row: 16 bytes each
-#pragma unroll
-      for (int i = 0; i < CS * LPT / 64; ++i) {
-        const int t = i * (64 / LPT) + lane / LPT, q = lane % LPT;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(st + t * RS + 16 * q);
-        __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, t * rs + 16 * q, 0, 0);  // tokens past the end: dropped
-      }
-    } else {
-#pragma unroll
-      for (int w = 0; w < C::NST; ++w)
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-          // reinterpret the whole vector (single elements are miscompiled)
-          const bf16x4 b = {(__bf16)O[w][rt][0], (__bf16)O[w][rt][1], (__bf16)O[w][rt][2], (__bf16)O[w][rt][3]};
-          *reinterpret_cast<u32x2*>(st + (16 * rt + n) * C::OST + (16 * w + 4 * g) * 2) = __builtin_bit_cast(u32x2, b);
-        }
-      wave_lds_sync();
-      constexpr int LPT = C::J / 8;  // lanes per token row: 16 bytes (8 columns) each
-#pragma unroll
-      for (int i = 0; i < CS * LPT / 64; ++i) {
-        const int t = i * (64 / LPT) + lane / LPT, q = lane % LPT;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(st + t * C::OST + 16 * q);
-        __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, t * rs + 16 * q, 0, 0);
-      }
-    }
+    for (int rt = 0; rt < 2; ++rt) O[rt] = mma16(xf, Pf[rt], O[rt]);
+    const Item it = {c, c, 0, chunk_end(c, cx.T), CS};
+    store_out(cx, it, O, usc, w, lane);
   };
   if (cx.nchunks > 0) block_sync_lds();  // the opening barrier
   for (int n = 0; n < cx.nchunks; ++n) {
@@ -1465,13 +1416,14 @@ __device__ __forceinline__ void chain_block(SmemC<C>& sm, int* seq_lens, int* se
   const size_t mat = (size_t)C::DK * p.dv;
   cx.s0 = p.S0 ? p.S0 + (size_t)cx.bh * mat + cx.col0 : nullptr;
   cx.st = p.S_T ? p.S_T + (size_t)cx.bh * mat + cx.col0 : nullptr;
-  // wave 0: output; waves 1 .. NST: state, at the highest issue priority; then
-  // the two loaders
-  if (wave >= 1 && wave <= C::NST) {
+  // waves 0 .. NST-1: state (SIMDs 0 and 1), NST .. 2 NST-1: output (SIMDs 2
+  // and 3), then the two loaders, which share the state waves' SIMDs and give
+  // way to them
+  if (wave >= C::NST && wave < 2 * C::NST) {
     __builtin_amdgcn_s_setprio(3);
-    chain_state<C>(sm, cx, snap, pos0, wave - 1, lane);
-  } else if (wave == 0) {
-    chain_output<C>(sm, cx, lane);
+    chain_state<C>(sm, cx, snap, pos0, wave - C::NST, lane);
+  } else if (wave < C::NST) {
+    chain_output<C>(sm, cx, wave, lane);
   } else if (wave < C::NW) {
     ChainSrc q;
     q.rec = p.rec + (slot0 * p.H + cx.h) * C::R::BYTES;
@@ -1480,7 +1432,7 @@ __device__ __forceinline__ void chain_block(SmemC<C>& sm, int* seq_lens, int* se
     q.v = static_cast<const char*>(p.v) + ((cx.tok0 * p.H + cx.h) * p.dv + cx.col0) * 2;
     q.nchunks = cx.nchunks;
     q.T = cx.T;
-    if (wave == C::NST + 1) chain_loader<C, 0>(sm, q, lane);
+    if (wave == 2 * C::NST) chain_loader<C, 0>(sm, q, lane);
     else chain_loader<C, 1>(sm, q, lane);
   } else {
     for (int n = chain_barriers(cx.nchunks); n > 0; --n) block_sync_lds();  // as many barriers as every role
