@@ -1337,32 +1337,73 @@ __device__ void chain_state(SmemC<C>& sm, const Ctx4& cx, const SnapList& snap, 
   if (cx.st) store_state<C>(cx.st, R, cx.st_ld, w, lane);
 }
 
-// Output wave w: chunk n - 1's output during step n, from the handoff of state
-// wave w and chunk n - 1's QG and -P T fragments, read into registers during
-// step n - 1 (its slot is refilled in step n):
+// Lane l of the result takes x from lane l - 1 (SHL false) or l + 1 (SHL true)
+// of its 16-lane row.
+template <bool SHL>
+__device__ __forceinline__ f32x4 row_shift1(const f32x4& x) {
+  const u32x4 u = __builtin_bit_cast(u32x4, x);
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = __builtin_amdgcn_update_dpp(0u, u[i], SHL ? 0x101 : 0x111, 0xf, 0xf, true);
+  return __builtin_bit_cast(f32x4, r);
+}
+
+// Output wave r: tokens 16 r .. 16 r + 15 of chunk n - 1 during step n, for every
+// column of the slab, from the handoffs of both state waves and the chunk's QG
+// and -P T fragments of those tokens, read into registers during step n - 1
+// (its slot is refilled in step n):
 //   O^T = S^T QG^T + Xn^T (-P T)^T.
+// Lane (g, n) ends with columns 16 w + 4g .. + 3 of token 16 r + n for state
+// wave w.  A shift by one lane within each 16-lane row gives each even lane the
+// other half of its token's row and each odd lane its neighbour's, so that every
+// store instruction writes whole rows of the slab: 8 tokens per instruction.
 template <class C>
-__device__ void chain_output(SmemC<C>& sm, const Ctx4& cx, int w, int lane) {
+__device__ void chain_output(SmemC<C>& sm, const Ctx4& cx, int r, int lane) {
+  static_assert(C::NST == 2, "a token's row of the slab: the columns of two state waves");
   using RC = typename C::R;
-  f16x8 Q[2][C::NKB], Pf[2], Pl[2];
+  const PrefillParams& p = cx.p;
+  const int g = opaque(lane / 16), n = opaque(lane % 16);
+  const bool odd = (n & 1) != 0;
+  f16x8 Q[C::NKB], Pf, Pl;
   auto emit = [&](int c) {  // the output of chunk c
-    const char* hb = sm.hand[c & 1][w] + 16 * lane;
-    f16x8 Sf[C::NKB];
+    f32x4 O[2];
 #pragma unroll
-    for (int kb = 0; kb < C::NKB; ++kb) Sf[kb] = *reinterpret_cast<const f16x8*>(hb + kb * 1024);
-    const f16x8 xf = *reinterpret_cast<const f16x8*>(hb + C::NKB * 1024);
-    const f32x4 usc = *reinterpret_cast<const f32x4*>(hb + (C::NKB + 1) * 1024);
-    f32x4 O[2] = {(f32x4)0.0f, (f32x4)0.0f};
+    for (int w = 0; w < 2; ++w) {
+      const char* hb = sm.hand[c & 1][w] + 16 * lane;
+      f16x8 Sf[C::NKB];
 #pragma unroll
-    for (int kb = 0; kb < C::NKB; ++kb)
+      for (int kb = 0; kb < C::NKB; ++kb) Sf[kb] = *reinterpret_cast<const f16x8*>(hb + kb * 1024);
+      const f16x8 xf = *reinterpret_cast<const f16x8*>(hb + C::NKB * 1024);
+      const f32x4 usc = *reinterpret_cast<const f32x4*>(hb + (C::NKB + 1) * 1024);
+      O[w] = (f32x4)0.0f;
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) O[rt] = mma16(Sf[kb], Q[rt][kb], O[rt]);
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) O[rt] = mma16(xf, Pl[rt], O[rt]);
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) O[rt] = mma16(xf, Pf[rt], O[rt]);
-    const Item it = {c, c, 0, chunk_end(c, cx.T), CS};
-    store_out(cx, it, O, usc, w, lane);
+      for (int kb = 0; kb < C::NKB; ++kb) O[w] = mma16(Sf[kb], Q[kb], O[w]);
+      O[w] = mma16(xf, Pl, O[w]);
+      O[w] = mma16(xf, Pf, O[w]) * usc;
+    }
+    // even tokens: the even lane's own first half and the odd lane's copy of the
+    // second half; odd tokens: the odd lane's own second half and the even
+    // lane's copy of the first half
+    const f32x4 prev1 = row_shift1<false>(O[1]), next0 = row_shift1<true>(O[0]);
+    const f32x4 a = odd ? prev1 : O[0];
+    const f32x4 b = odd ? O[1] : next0;
+    const int col = (odd ? 16 : 0) + 4 * g;
+    const int te = 16 * r + (n & ~1), to = 16 * r + (n | 1);
+    const int rows = chunk_end(c, cx.T);
+    const int esz = p.o_f32 ? 4 : 2;
+    const int rs = p.H * p.dv * esz;
+    char* ob = static_cast<char*>(p.o) + (((size_t)(cx.tok0 + c * CS) * p.H + cx.h) * p.dv + cx.col0) * esz;
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(ob, rows * rs);  // tokens past the end: dropped
+    if (p.o_f32) {
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, a), rsrc, te * rs + col * 4, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, b), rsrc, to * rs + col * 4, 0, 0);
+    } else {
+      // reinterpret whole vectors (single elements are miscompiled)
+      const bf16x4 ah = {(__bf16)a[0], (__bf16)a[1], (__bf16)a[2], (__bf16)a[3]};
+      const bf16x4 bh = {(__bf16)b[0], (__bf16)b[1], (__bf16)b[2], (__bf16)b[3]};
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ah), rsrc, te * rs + col * 2, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, bh), rsrc, to * rs + col * 2, 0, 0);
+    }
   };
   if (cx.nchunks > 0) block_sync_lds();  // the opening barrier
   for (int n = 0; n < cx.nchunks; ++n) {
@@ -1370,12 +1411,9 @@ __device__ void chain_output(SmemC<C>& sm, const Ctx4& cx, int w, int lane) {
     if (n > 0) emit(n - 1);
     const char* lb = sm.oring[n % C::RING] + 16 * opaque(lane);
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-#pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb) Q[rt][kb] = slot_frag<C>(lb, RC::QG - RC::OUT, rt * C::NKB + kb);
-      Pf[rt] = slot_frag<C>(lb, RC::PP - RC::OUT, rt);
-      Pl[rt] = slot_frag<C>(lb, RC::PL - RC::OUT, rt);
-    }
+    for (int kb = 0; kb < C::NKB; ++kb) Q[kb] = slot_frag<C>(lb, RC::QG - RC::OUT, r * C::NKB + kb);
+    Pf = slot_frag<C>(lb, RC::PP - RC::OUT, r);
+    Pl = slot_frag<C>(lb, RC::PL - RC::OUT, r);
   }
   block_sync_lds();
   if (cx.nchunks > 0) emit(cx.nchunks - 1);
