@@ -57,7 +57,6 @@ struct PCfg {
   static constexpr int DK = DK_;
   static constexpr int CPT = DK / 64;  // channels per lane
   static constexpr int NKB = DK / 32;  // 32-channel reduction steps
-  static constexpr int NKT = DK / 16;  // 16-channel tiles
   static constexpr int LDF = DK + 8;   // factor rows (fp16): the pad keeps row reads conflict-free
   static constexpr int LDL = CS + 1;   // D_L rows (fp32), read along rows and along columns
   static constexpr int LDP = CS + 4;   // D_P rows (fp32), read as 16-byte runs
@@ -213,19 +212,10 @@ __device__ __forceinline__ void prep_record(const PrefillParams& p, long long re
   const int g = lane / 16, n = lane % 16;
 
   // ---- KG, QG (forward products), gamma --------------------------------------------
-  // The products are staged in LDS in token-major rows (KG in the factor rows,
-  // QG over the L and P sums, both free until the levels below) and written as
-  // whole fragments, 16 bytes per lane: the matrix-core layout scatters one
-  // token's channels over 16-byte slots, and writing them as they are formed
-  // costs four times the write requests.
-  static_assert(offsetof(PrepLds<C>, dp) == offsetof(PrepLds<C>, dl) + sizeof(PrepLds<C>::dl) &&
-                    CS * C::LDF * 2 <= sizeof(PrepLds<C>::dl) + sizeof(PrepLds<C>::dp),
-                "QG staging spans dl and dp");
-  static_assert(8 * DK * 8 <= sizeof(PrepLds<C>::f), "-KH^T staging fits the factor rows");
-  h16* const stg_k = sm.f;
-  h16* const stg_q = reinterpret_cast<h16*>(sm.dl);
-  wave_lds_sync();  // (an earlier record's readers of this LDS are done)
   {
+    // fragment position of channel ch: step kb, lane group gc, slot ec
+    const int kb = ch >> 5, cc = ch & 31, gc = (cc & 15) >> 2, ec = (cc & 3) + 4 * (cc >> 4);
+    const int vo = kb * 1024 + gc * 256 + 2 * ec;
     float run[CPT];
 #pragma unroll
     for (int e = 0; e < CPT; ++e) run[e] = 1.0f;
@@ -234,12 +224,13 @@ __device__ __forceinline__ void prep_record(const PrefillParams& p, long long re
 #pragma unroll
       for (int e = 0; e < CPT; ++e) run[e] *= a[t][e];
       const uint32_t kg = mul_ch<CPT>(kw[t], run), qg = mul_ch<CPT>(qw[t], run);
+      const int to = (t >> 4) * NKB * 1024 + (t & 15) * 16;
       if constexpr (CPT == 2) {
-        *reinterpret_cast<uint32_t*>(&stg_k[t * C::LDF + ch]) = kg;
-        *reinterpret_cast<uint32_t*>(&stg_q[t * C::LDF + ch]) = qg;
+        __builtin_amdgcn_raw_buffer_store_b32(kg, rr, vo, R::KG + to, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(qg, rr, vo, R::QG + to, 0);
       } else {
-        stg_k[t * C::LDF + ch] = __builtin_bit_cast(h16, (uint16_t)kg);
-        stg_q[t * C::LDF + ch] = __builtin_bit_cast(h16, (uint16_t)qg);
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)kg, rr, vo, R::KG + to, 0);
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)qg, rr, vo, R::QG + to, 0);
       }
     }
     if constexpr (CPT == 2)
@@ -247,27 +238,9 @@ __device__ __forceinline__ void prep_record(const PrefillParams& p, long long re
     else
       __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, run[0]), rr, ch * 4, R::GAM, 0);
   }
-  wave_lds_sync();
-  // fragment (rt, kb), lane (g, n): token 16 rt + n, channels 32 kb + 4g .. + 3 in
-  // slots 0..3 and 32 kb + 16 + 4g .. + 3 in slots 4..7
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      const int o = (16 * rt + n) * C::LDF + 32 * kb + 4 * g;
-      const u32x2 k0 = *reinterpret_cast<const u32x2*>(&stg_k[o]), k1 = *reinterpret_cast<const u32x2*>(&stg_k[o + 16]);
-      const u32x2 q0 = *reinterpret_cast<const u32x2*>(&stg_q[o]), q1 = *reinterpret_cast<const u32x2*>(&stg_q[o + 16]);
-      const int fo = (rt * NKB + kb) * 1024;
-      __builtin_amdgcn_raw_buffer_store_b128(u32x4{k0[0], k0[1], k1[0], k1[1]}, rr, lane * 16, R::KG + fo, 0);
-      __builtin_amdgcn_raw_buffer_store_b128(u32x4{q0[0], q0[1], q1[0], q1[1]}, rr, lane * 16, R::QG + fo, 0);
-    }
 
-  // ---- -KH^T (backward products) -----------------------------------------------------
-  // Staged as 8 blocks of 4 tokens, each DK channels x 4 tokens (8 bytes a
-  // channel), then written as whole fragments.
-  wave_lds_sync();  // the KG rows are read
+  // ---- -KH^T (backward products): 8 bytes per (channel, run of 4 tokens) ------------
   {
-    char* const stg = reinterpret_cast<char*>(sm.f);
     float run[CPT];
 #pragma unroll
     for (int e = 0; e < CPT; ++e) run[e] = -1.0f;  // the sign of -KH rides on the products
@@ -281,28 +254,21 @@ __device__ __forceinline__ void prep_record(const PrefillParams& p, long long re
           r[e][t - t4] = run[e];
           run[e] *= a[t][e];
         }
-      char* const blk = stg + (t4 / 4) * (DK * 8) + ch * 8;
-      const uint32_t w0 = mul2<0, 0>(kw[t4], r[0][0], kw[t4 + 1], r[0][1]);
-      const uint32_t w1 = mul2<0, 0>(kw[t4 + 2], r[0][2], kw[t4 + 3], r[0][3]);
-      if constexpr (CPT == 2) {
-        const uint32_t w2 = mul2<1, 1>(kw[t4], r[1][0], kw[t4 + 1], r[1][1]);
-        const uint32_t w3 = mul2<1, 1>(kw[t4 + 2], r[1][2], kw[t4 + 3], r[1][3]);
-        *reinterpret_cast<u32x4*>(blk) = u32x4{w0, w1, w2, w3};
-      } else {
-        *reinterpret_cast<u32x2*>(blk) = u32x2{w0, w1};
-      }
-    }
-  }
-  wave_lds_sync();
-  {
-    // fragment i, lane (g, n): channel 16 i + n, tokens 4g .. + 3 (block g) and
-    // 16 + 4g .. + 3 (block 4 + g)
-    const char* const stg = reinterpret_cast<const char*>(sm.f);
+      // tokens t4..t4+3 fill slots 0..3 (t4 < 16) or 4..7 of lane group (t4 % 16) / 4
+      const int so = R::KH + 16 * ((t4 & 15) >> 2) * 16 + 8 * (t4 >> 4);
 #pragma unroll
-    for (int i = 0; i < C::NKT; ++i) {
-      const u32x2 lo = *reinterpret_cast<const u32x2*>(stg + g * (DK * 8) + (16 * i + n) * 8);
-      const u32x2 hi = *reinterpret_cast<const u32x2*>(stg + (4 + g) * (DK * 8) + (16 * i + n) * 8);
-      __builtin_amdgcn_raw_buffer_store_b128(u32x4{lo[0], lo[1], hi[0], hi[1]}, rr, lane * 16, R::KH + i * 1024, 0);
+      for (int e = 0; e < CPT; ++e) {
+        const int c = ch + e;
+        u32x2 w;
+        if (e == 0) {
+          w[0] = mul2<0, 0>(kw[t4], r[0][0], kw[t4 + 1], r[0][1]);
+          w[1] = mul2<0, 0>(kw[t4 + 2], r[0][2], kw[t4 + 3], r[0][3]);
+        } else {
+          w[0] = mul2<1, 1>(kw[t4], r[CPT - 1][0], kw[t4 + 1], r[CPT - 1][1]);
+          w[1] = mul2<1, 1>(kw[t4 + 2], r[CPT - 1][2], kw[t4 + 3], r[CPT - 1][3]);
+        }
+        __builtin_amdgcn_raw_buffer_store_b64(w, rr, ((c >> 4) * 64 + (c & 15)) * 16, so, 0);
+      }
     }
   }
 
