@@ -99,6 +99,22 @@ def test_prefill_1m(gpu):
     _check("1m S_T (other 28 heads)", s_all[rest], rs_all)
 
 
+def test_prefill_64k_repeatable(gpu):
+    """The 64K-token prefill (blocks of stage 1 then the chain) gives the same o
+    and S_T, bit for bit, on back-to-back calls."""
+    inp = ki.make_workload_prefill(2, seed=1, device=gpu)
+    args = (inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["S0"])
+    o_ref, s_ref = kda.kda_chunk_fwd(*args, chunk=64, o_dtype=torch.bfloat16)
+    o = torch.empty_like(o_ref)
+    s = torch.empty_like(s_ref)
+    for i in range(4):
+        kda.kda_chunk_fwd(*args, chunk=64, o=o, S_T=s)
+        torch.cuda.synchronize()
+        same_o, same_s = torch.equal(o, o_ref), torch.equal(s, s_ref)
+        log(f"  64k call {i + 2}: o identical {same_o}, S_T identical {same_s}")
+        assert same_o and same_s
+
+
 def test_prefill_1m_repeatable(gpu):
     """The 1M-token prefill (each block's chain beside the next block's stage 1)
     gives the same o and S_T, bit for bit, on back-to-back calls.  (A chain
