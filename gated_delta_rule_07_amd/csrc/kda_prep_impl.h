@@ -74,6 +74,14 @@ struct PrepLds {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
 }
+// A 16-byte record store.  A buffer store of more than 8 bytes reads its data
+// registers after it issues, so they must not be rewritten in the next two wait
+// states; the compiler inserts that wait only when the store's scalar offset is
+// not a register, so every offset here goes in the vector offset and the scalar
+// offset is the constant 0.
+__device__ __forceinline__ void st16(u32x4 d, __amdgpu_buffer_rsrc_t r, int off) {
+  __builtin_amdgcn_raw_buffer_store_b128(d, r, off, 0, 0);
+}
 __device__ __forceinline__ float lo16(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float hi16(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
@@ -407,8 +415,8 @@ __device__ __forceinline__ void prep_record(const PrefillParams& p, long long re
       t1[j] = (h16)(-zt[j] * b_r0[j]);
       t1[4 + j] = (h16)(d1t[j] * b_r1[j]);
     }
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, t0), rr, lane * 16, R::TT, 0);
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, t1), rr, lane * 16, R::TT + 1024, 0);
+    st16(__builtin_bit_cast(u32x4, t0), rr, lane * 16 + R::TT);
+    st16(__builtin_bit_cast(u32x4, t1), rr, lane * 16 + R::TT + 1024);
   }
   // -P T: the output's intra-chunk operator, applied in the chain to Xn (one
   // fp16 rounding of the product, instead of one each of P, T and Un).  T in
@@ -471,8 +479,8 @@ __device__ __forceinline__ void prep_record(const PrefillParams& p, long long re
       pl[j] = (h16)(a0 - (float)pf[j]);
       pl[4 + j] = (h16)(a1 - (float)pf[4 + j]);
     }
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, pf), rr, lane * 16, R::PP + 1024 * rt, 0);
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, pl), rr, lane * 16, R::PL + 1024 * rt, 0);
+    st16(__builtin_bit_cast(u32x4, pf), rr, lane * 16 + R::PP + 1024 * rt);
+    st16(__builtin_bit_cast(u32x4, pl), rr, lane * 16 + R::PL + 1024 * rt);
   }
 }
 
