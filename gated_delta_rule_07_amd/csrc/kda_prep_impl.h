@@ -112,6 +112,29 @@ __device__ __forceinline__ uint32_t mul_ch(uint32_t x, const float (&r)[CPT]) {
 }
 __device__ __forceinline__ f16x8 ld8(const h16* p) { return *reinterpret_cast<const f16x8*>(p); }
 
+// One swap step of a 4x4 transpose over four lanes: the lane whose bit (of the
+// two that name its rank) is b gives its partner the elements whose index bit
+// is 1 - b and takes the partner's elements whose index bit is b in their
+// place.  DPP: quad_perm [1,0,3,2] is lane ^ 1, row_ror:8 is lane ^ 8.
+template <int CTRL, int P0, int P1>
+__device__ __forceinline__ void xswap(u32x4& x, bool b) {
+  const uint32_t send = b ? x[P0] : x[P1];
+  const uint32_t recv = __builtin_amdgcn_update_dpp(0u, send, CTRL, 0xf, 0xf, true);
+  if (b) x[P0] = recv;
+  else x[P1] = recv;
+}
+// Lanes of rank r = (lane bit 0) + 2 (lane bit 3) in a group of four hold x_r;
+// afterwards the lane of rank r holds element r of every lane of its group,
+// element s from the lane of rank s.
+__device__ __forceinline__ u32x4 xpose4(u32x4 x, int lane) {
+  const bool b0 = lane & 1, b3 = (lane >> 3) & 1;
+  xswap<0xb1, 0, 1>(x, b0);
+  xswap<0xb1, 2, 3>(x, b0);
+  xswap<0x128, 0, 2>(x, b3);
+  xswap<0x128, 1, 3>(x, b3);
+  return x;
+}
+
 // Row of token t among the 16 tokens of its side at level b (bit b removed).
 __device__ __forceinline__ constexpr int side_row(int t, int b) {
   return ((t >> (b + 1)) << b) | (t & ((1 << b) - 1));
@@ -227,16 +250,36 @@ __device__ __forceinline__ void prep_record(const PrefillParams& p, long long re
     float run[CPT];
 #pragma unroll
     for (int e = 0; e < CPT; ++e) run[e] = 1.0f;
+    if constexpr (CPT == 2) {
+      // The four dwords of a token's 16-byte fragment unit sit in the four lanes
+      // that differ in lane bits 0 and 3 (dword = bit 0 + 2 * bit 3).  A 4x4
+      // transpose over those lanes, per four tokens, gives each lane whole
+      // units (token 4m + rank), stored 16 bytes at a time.
+      const int sr = (lane & 1) | ((lane >> 2) & 2);
+      const int uo = (lane >> 4) * 1024 + ((lane & 7) >> 1) * 256 + sr * 16;
 #pragma unroll
-    for (int t = 0; t < CS; ++t) {
+      for (int m = 0; m < CS / 4; ++m) {
+        u32x4 xk, xq;
 #pragma unroll
-      for (int e = 0; e < CPT; ++e) run[e] *= a[t][e];
-      const uint32_t kg = mul_ch<CPT>(kw[t], run), qg = mul_ch<CPT>(qw[t], run);
-      const int to = (t >> 4) * NKB * 1024 + (t & 15) * 16;
-      if constexpr (CPT == 2) {
-        __builtin_amdgcn_raw_buffer_store_b32(kg, rr, vo, R::KG + to, 0);
-        __builtin_amdgcn_raw_buffer_store_b32(qg, rr, vo, R::QG + to, 0);
-      } else {
+        for (int i = 0; i < 4; ++i) {
+          const int t = 4 * m + i;
+#pragma unroll
+          for (int e = 0; e < CPT; ++e) run[e] *= a[t][e];
+          xk[i] = mul_ch<CPT>(kw[t], run);
+          xq[i] = mul_ch<CPT>(qw[t], run);
+        }
+        xk = xpose4(xk, lane);
+        xq = xpose4(xq, lane);
+        const int to = (m >> 2) * NKB * 1024 + (m & 3) * 64;
+        st16(xk, rr, uo + R::KG + to);
+        st16(xq, rr, uo + R::QG + to);
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < CS; ++t) {
+        run[0] *= a[t][0];
+        const uint32_t kg = mul_ch<CPT>(kw[t], run), qg = mul_ch<CPT>(qw[t], run);
+        const int to = (t >> 4) * NKB * 1024 + (t & 15) * 16;
         __builtin_amdgcn_raw_buffer_store_b16((uint16_t)kg, rr, vo, R::KG + to, 0);
         __builtin_amdgcn_raw_buffer_store_b16((uint16_t)qg, rr, vo, R::QG + to, 0);
       }
@@ -247,8 +290,10 @@ __device__ __forceinline__ void prep_record(const PrefillParams& p, long long re
       __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, run[0]), rr, ch * 4, R::GAM, 0);
   }
 
-  // ---- -KH^T (backward products): 8 bytes per (channel, run of 4 tokens) ------------
+  // ---- -KH^T (backward products): 16 bytes per (channel, tokens t4..t4+3 and
+  //      t4+16..t4+19); the later run's 8 bytes are held until the earlier's ---------
   {
+    u32x2 wh[4][CPT];
     float run[CPT];
 #pragma unroll
     for (int e = 0; e < CPT; ++e) run[e] = -1.0f;  // the sign of -KH rides on the products
@@ -263,7 +308,7 @@ __device__ __forceinline__ void prep_record(const PrefillParams& p, long long re
           run[e] *= a[t][e];
         }
       // tokens t4..t4+3 fill slots 0..3 (t4 < 16) or 4..7 of lane group (t4 % 16) / 4
-      const int so = R::KH + 16 * ((t4 & 15) >> 2) * 16 + 8 * (t4 >> 4);
+      const int so = R::KH + 16 * ((t4 & 15) >> 2) * 16;
 #pragma unroll
       for (int e = 0; e < CPT; ++e) {
         const int c = ch + e;
@@ -275,7 +320,12 @@ __device__ __forceinline__ void prep_record(const PrefillParams& p, long long re
           w[0] = mul2<1, 1>(kw[t4], r[CPT - 1][0], kw[t4 + 1], r[CPT - 1][1]);
           w[1] = mul2<1, 1>(kw[t4 + 2], r[CPT - 1][2], kw[t4 + 3], r[CPT - 1][3]);
         }
-        __builtin_amdgcn_raw_buffer_store_b64(w, rr, ((c >> 4) * 64 + (c & 15)) * 16, so, 0);
+        if (t4 >= 16) {
+          wh[(t4 - 16) >> 2][e] = w;
+        } else {
+          const u32x2 wl = wh[t4 >> 2][e];
+          st16(u32x4{w[0], w[1], wl[0], wl[1]}, rr, ((c >> 4) * 64 + (c & 15)) * 16 + so);
+        }
       }
     }
   }
